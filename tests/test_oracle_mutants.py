@@ -1,0 +1,43 @@
+"""The oracle's pins must catch plausible mistakes: each case below plants one
+mistake in a copy of ring_oracle.c (built into a temporary directory, on the
+CPU), points the oracle at that copy and runs the pin suite, which must fail."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "ring_oracle.c")
+
+MUTANTS = {
+    "causal_excludes_diagonal": ("if (tk > t) return 0;", "if (tk >= t) return 0;"),
+    "gqa_head_map_modulo": ("h / group, d, scale, idx, n, sbuf, obuf", "h % Hkv, d, scale, idx, n, sbuf, obuf"),
+    "scale_dropped": ("s *= scale;", ""),
+    "striped_block_index": ("return t % r->n_blocks;", "return t / r->n_blocks;"),
+    "pass_limit_off_by_one": ("return step < r->passes;", "return step <= r->passes;"),
+    "ring_direction_reversed": ("((block_of(r, t) - block_of(r, tk))", "((block_of(r, tk) - block_of(r, t))"),
+    "lse_without_max": ("*lse = M + log(L);", "*lse = log(L);"),
+    "doc_boundary_ignored": ("if (mask == RO_MASK_DOC_CAUSAL && doc_of[tk] != doc_of[t]) return 0;", ""),
+    "striped_tally_key_block": ("w * N + j : j * B + w", "w * N + i : j * B + w"),
+    "empty_row_lse_zero": ("*lse = -INFINITY;\n        *m_out", "*lse = 0;\n        *m_out"),
+    "value_index_transposed": ("w * view_at(v, idx[a], g, c)", "w * view_at(v, idx[a], g, d - 1 - c)"),
+    "denominator_missing_term": ("L += w;", "if (a > 0) L += w;"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_planted_mistake(name, tmp_path):
+    src = open(SRC).read()
+    before, after = MUTANTS[name]
+    assert before in src, "mutation site vanished: update the mutant table"
+    c_path = tmp_path / (name + ".c")
+    c_path.write_text(src.replace(before, after, 1))
+    so = tmp_path / ("lib_%s.so" % name)
+    subprocess.check_call(["gcc", "-O2", "-fopenmp", "-shared", "-fPIC", "-std=c99", str(c_path),
+                           "-o", str(so), "-lm"])
+    env = dict(os.environ, RING_ORACLE_LIB=str(so), OMP_NUM_THREADS="4")
+    r = subprocess.run([sys.executable, "-m", "pytest", os.path.join(ROOT, "tests", "test_oracle_pins.py"),
+                        "-q", "-x", "-p", "no:cacheprovider"], env=env, capture_output=True, text=True,
+                       cwd=ROOT, timeout=600)
+    assert r.returncode != 0, "planted mistake %r passed every pin:\n%s" % (name, r.stdout[-2000:])
