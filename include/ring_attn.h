@@ -1,0 +1,182 @@
+/*
+ * ring_attn.h -- C ABI of the MI355X (gfx950) ring-attention step library.
+ *
+ * Ring attention keeps one query block per device and passes key/value blocks
+ * around a ring of N devices; at step s device i holds key/value block
+ * j = (i - s) mod N, and the partial softmax results are combined with the same
+ * running-maximum softmax that blockwise attention uses inside one GPU
+ * (Ultralytics glossary page "Ring Attention", section "Come funziona", and its
+ * worked example).  The per-row running state is the maximum m, the
+ * denominator l and the unnormalised output O ("Ring Attention simulation"
+ * gist: running maxima and partial denominators per query row; GitHub issue
+ * "A ring attention with flash attention kernel implementation": outputs, row
+ * maxima and lse are stored and passed back in on the next ring pass).  Here
+ * all N ring blocks live on one GPU as virtual devices.
+ *
+ * Conventions for every entry point:
+ *  - Pointers are DEVICE pointers unless the comment says "host".
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream); all
+ *    GPU work is enqueued on it asynchronously.
+ *  - The caller owns every buffer; the library never allocates or frees memory.
+ *  - Arguments are checked before anything is enqueued: a bad argument returns
+ *    RA_E_ARG (or RA_E_UNSUPPORTED for a valid but unimplemented combination)
+ *    with no side effects.  A failed launch returns RA_E_HIP.
+ *  - Tensors are [tokens, heads, head_dim] views with element strides; the
+ *    head_dim stride must be 1.  This covers plain [T, H, d] tensors, striped
+ *    ring blocks (token stride multiplied by N) and the packed [T, 3, H, d]
+ *    qkv layout (flash-attention's "qkvpacked" inputs, named in the GitHub
+ *    issue) without copies.
+ *  - Query head h reads key/value head h / (Hq / Hkv) (grouped-query
+ *    attention, named on the flash-attention scrape page).
+ *  - Scores are scale * q.k; scale must be finite and > 0.
+ *  - Supported: bf16 inputs with head_dim 64 or 128 (matrix-core path, fp32
+ *    accumulation); f32 inputs with head_dim 1..128 (exact fp32 path).
+ */
+#ifndef RING_ATTN_H
+#define RING_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    RA_OK = 0,
+    RA_E_ARG = 1,          /* invalid argument (shape, stride, pointer, value) */
+    RA_E_UNSUPPORTED = 2,  /* valid but not implemented (dtype / head_dim / mask combination) */
+    RA_E_HIP = 3,          /* a HIP runtime call or kernel launch failed */
+    RA_E_WORKSPACE = 4     /* workspace missing or smaller than ring_attn_forward_workspace_size */
+} ra_status;
+
+typedef enum { RA_F32 = 0, RA_BF16 = 1 } ra_dtype;
+
+/* Masks act on global token positions t (query) and t' (key):
+ *  NONE: every key; CAUSAL: t' <= t; DOC_CAUSAL: t' <= t and both in the same
+ *  document, documents given by cu_seqlens (int32, n_docs + 1 cumulative
+ *  lengths starting at 0, as described on the flash-attention scrape page). */
+typedef enum { RA_MASK_NONE = 0, RA_MASK_CAUSAL = 1, RA_MASK_DOC_CAUSAL = 2 } ra_mask;
+
+/* Assignment of tokens to the N ring blocks: CONTIGUOUS puts tokens
+ * [i*B, (i+1)*B) in block i; STRIPED puts token t in block t mod N (the
+ * glossary page's striped attention, which spreads every device's tokens over
+ * the whole sequence to balance causal work). */
+typedef enum { RA_LAYOUT_CONTIGUOUS = 0, RA_LAYOUT_STRIPED = 1 } ra_layout;
+
+typedef struct {
+    const void* data;      /* device pointer to element [0, 0, 0] */
+    ra_dtype dtype;
+    int64_t n_tok, n_head, head_dim;
+    int64_t stride_tok, stride_head; /* element strides; head_dim stride is 1 */
+} ra_tensor;
+
+/* Work tallies of a forward pass.  A block pair is one (query block i, key
+ * block j) visited at some ring step; a tile is tile_q query rows x tile_k key
+ * columns of a block pair (the last tile on each side may be short).  SKIP: no
+ * allowed (query, key) pair, never computed; FULL: every pair allowed,
+ * computed without a mask; PARTIAL: computed with a per-element mask. */
+typedef struct {
+    int64_t block_pairs_visited, block_pairs_skipped, block_pairs_full, block_pairs_partial;
+    int64_t tiles_skipped, tiles_full, tiles_partial;
+    int64_t allowed_pairs;     /* (query, key) pairs per head that pass mask and ring */
+    int32_t tile_q, tile_k;
+} ra_stats;
+
+/*
+ * One ring step: the query block q_blk against one key/value block, updating
+ * the running state in place.
+ *   q_blk [Bq, Hq, d], k_blk / v_blk [Bk, Hkv, d]: same dtype, same d.
+ *   O [Hq, Bq, d], m [Hq, Bq], l [Hq, Bq]: fp32, contiguous.  After the call,
+ *     for every row: m = max over all keys seen so far of scale*q.k (-inf if
+ *     none), l = sum of exp(scale*q.k - m), O = sum of exp(scale*q.k - m) v.
+ *     With first_step != 0 the incoming state is ignored (treated as empty),
+ *     so O/m/l need no initialisation.
+ *   Positions for the mask: query row u sits at q_offset + u * pos_stride, key
+ *     row w at kv_offset + w * pos_stride (pos_stride = 1 for contiguous
+ *     blocks, N for striped ones).  DOC_CAUSAL needs pos_stride = 1 and
+ *     cu_seqlens (device, n_docs + 1 entries) covering every position used.
+ *   stats_dev: nullable device int64[3]; the step ADDS its tile counts
+ *     {skipped, full, partial} (tile shape as ring_attn_tile_shape reports).
+ */
+ra_status ring_attn_step(const ra_tensor* q_blk, const ra_tensor* k_blk, const ra_tensor* v_blk,
+                         float* O, float* m, float* l, int first_step, float scale,
+                         ra_mask mask_mode, int64_t q_offset, int64_t kv_offset, int64_t pos_stride,
+                         const int32_t* cu_seqlens, int32_t n_docs, int64_t* stats_dev, void* stream);
+
+/*
+ * Normalise a running state: out[u, h, :] = O[h, u, :] / l[h, u] and
+ * lse[h, u] = m[h, u] + ln l[h, u]; a row with l = 0 (no key seen) gets
+ * out = 0 and lse = -inf (the glossary page's worked example divides the
+ * accumulated weighted values by the accumulated weights at the end).
+ *   O [Hq, Bq, d], m/l [Hq, Bq] fp32 contiguous; out is written at
+ *   out + u*out_stride_tok + h*out_stride_head (+ c), dtype out_dtype
+ *   (bf16 rounds to nearest even); lse nullable, [Hq, Bq] contiguous.
+ */
+ra_status ring_attn_finalize(const float* O, const float* m, const float* l, int64_t Hq, int64_t Bq,
+                             int64_t d, void* out, ra_dtype out_dtype, int64_t out_stride_tok,
+                             int64_t out_stride_head, float* lse, void* stream);
+
+/*
+ * Merge a normalised partial result into an accumulator through log-sum-exp
+ * (GitHub issue: returning lse is what lets blockwise attention results be
+ * combined): with w_x = exp(lse_x - max(lse_acc, lse_blk)),
+ *   out_acc = (w_acc out_acc + w_blk out_blk) / (w_acc + w_blk),
+ *   lse_acc = max + ln(w_acc + w_blk);
+ * a side with lse = -inf has weight 0, both -inf gives out 0, lse -inf.
+ *   out_acc / out_blk: [rows, Hq, d] contiguous, dtype `dtype`;
+ *   lse_acc / lse_blk: [Hq, rows] fp32 contiguous.  Updated in place.
+ */
+ra_status ring_attn_merge(void* out_acc, float* lse_acc, const void* out_blk, const float* lse_blk,
+                          ra_dtype dtype, int64_t Hq, int64_t rows, int64_t d, void* stream);
+
+/* Bytes of device workspace ring_attn_forward needs for these shapes. */
+size_t ring_attn_forward_workspace_size(const ra_tensor* q, const ra_tensor* k, int32_t n_blocks,
+                                        int32_t n_docs, int prefetch);
+
+/*
+ * The whole ring on one GPU: the sequence of T tokens is split into n_blocks
+ * ring blocks (virtual devices) by `layout`; for s = 0 .. min(P, N) - 1 every
+ * virtual device i runs one step against block (i - s) mod N, with P =
+ * max_ring_passes (GitHub issue: the maximum number of ring passes; one pass
+ * is one step).  One kernel launch per step covers every virtual device whose
+ * pair is not skipped by the mask; a device's last active step writes its
+ * normalised output directly.
+ *   q [T, Hq, d], k/v [T, Hkv, d] (views allowed, e.g. of a packed qkv).
+ *   out: [T, Hq, d] contiguous, out_dtype (RA_F32 always allowed; RA_BF16 for
+ *     bf16 inputs).  lse: nullable, [Hq, T] fp32 (natural log).
+ *   cu_seqlens_host: HOST pointer, n_docs + 1 entries, needed for DOC_CAUSAL
+ *     (contiguous layout only); copied into the workspace.
+ *   prefetch != 0: every step's key/value blocks are first copied, on a side
+ *     stream, into a double buffer in the workspace while the previous step
+ *     computes (the ring's transfer of the next block, modelled on one GPU);
+ *     results are bit-identical to prefetch = 0.
+ *   stats: nullable HOST pointer; when given the call synchronises `stream`
+ *     and fills it.
+ */
+ra_status ring_attn_forward(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v, void* out,
+                            ra_dtype out_dtype, float* lse, int32_t n_blocks, ra_layout layout,
+                            ra_mask mask_mode, int32_t max_ring_passes, const int32_t* cu_seqlens_host,
+                            int32_t n_docs, float scale, int prefetch, void* workspace,
+                            size_t workspace_bytes, ra_stats* stats, void* stream);
+
+/*
+ * Host-only planning (no GPU work): fills `stats` with the tallies and the
+ * allowed-pair count that ring_attn_forward would produce for these shapes,
+ * from the exact per-tile mask classification.  dtype and head_dim select the
+ * kernel (and so the tile shape).  cu_seqlens_host as for ring_attn_forward.
+ */
+ra_status ring_attn_plan(int64_t T, int32_t n_blocks, ra_layout layout, ra_mask mask_mode,
+                         int32_t max_ring_passes, const int32_t* cu_seqlens_host, int32_t n_docs,
+                         ra_dtype dtype, int64_t head_dim, ra_stats* stats);
+
+/* Tile shape (query rows x key columns) of the kernel for dtype / head_dim;
+ * returns RA_E_UNSUPPORTED when no kernel covers the combination. */
+ra_status ring_attn_tile_shape(ra_dtype dtype, int64_t head_dim, int32_t* tile_q, int32_t* tile_k);
+
+const char* ring_attn_status_string(ra_status s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* RING_ATTN_H */

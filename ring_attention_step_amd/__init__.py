@@ -1,0 +1,286 @@
+"""Python binding of libring_attn.so, the MI355X ring-attention step library.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in include/ring_attn.h.  torch supplies
+device memory and the current stream; tensors must live on the GPU, and a
+missing library raises instead of falling back to anything else.
+
+Entry points (same names as the C ABI):
+  ring_attn_step, ring_attn_finalize, ring_attn_merge,
+  ring_attn_forward_workspace_size, ring_attn_forward, ring_attn_plan,
+  ring_attn_tile_shape
+plus the conveniences ``forward`` and ``forward_qkvpacked`` that allocate the
+output, lse and workspace with torch.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+import torch  # loaded first: the library then binds to torch's HIP runtime
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libring_attn.so")
+
+RA_OK, RA_E_ARG, RA_E_UNSUPPORTED, RA_E_HIP, RA_E_WORKSPACE = range(5)
+RA_F32, RA_BF16 = 0, 1
+RA_MASK_NONE, RA_MASK_CAUSAL, RA_MASK_DOC_CAUSAL = 0, 1, 2
+RA_LAYOUT_CONTIGUOUS, RA_LAYOUT_STRIPED = 0, 1
+
+_i64, _i32, _vp, _f32, _int, _sz = (ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_float,
+                                    ctypes.c_int, ctypes.c_size_t)
+
+
+class RaTensor(ctypes.Structure):
+    _fields_ = [("data", _vp), ("dtype", _int), ("n_tok", _i64), ("n_head", _i64), ("head_dim", _i64),
+                ("stride_tok", _i64), ("stride_head", _i64)]
+
+
+class RaStats(ctypes.Structure):
+    _fields_ = [("block_pairs_visited", _i64), ("block_pairs_skipped", _i64), ("block_pairs_full", _i64),
+                ("block_pairs_partial", _i64), ("tiles_skipped", _i64), ("tiles_full", _i64),
+                ("tiles_partial", _i64), ("allowed_pairs", _i64), ("tile_q", _i32), ("tile_k", _i32)]
+
+    def as_dict(self):
+        return {name: int(getattr(self, name)) for name, _ in self._fields_}
+
+
+class RingAttnError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__("%s failed: %s (status %d)" % (fn, msg, status))
+        self.status = status
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return LIB_PATH
+
+
+def load_library():
+    """Load libring_attn.so (built by ``python -m ring_attention_step_amd.build``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("libring_attn.so is not built (run: python -m ring_attention_step_amd.build)")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.POINTER
+    lib.ring_attn_step.argtypes = [P(RaTensor), P(RaTensor), P(RaTensor), _vp, _vp, _vp, _int, _f32, _int,
+                                   _i64, _i64, _i64, _vp, _i32, _vp, _vp]
+    lib.ring_attn_finalize.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, _vp, _int, _i64, _i64, _vp, _vp]
+    lib.ring_attn_merge.argtypes = [_vp, _vp, _vp, _vp, _int, _i64, _i64, _i64, _vp]
+    lib.ring_attn_forward_workspace_size.argtypes = [P(RaTensor), P(RaTensor), _i32, _i32, _int]
+    lib.ring_attn_forward_workspace_size.restype = _sz
+    lib.ring_attn_forward.argtypes = [P(RaTensor), P(RaTensor), P(RaTensor), _vp, _int, _vp, _i32, _int, _int,
+                                      _i32, _vp, _i32, _f32, _int, _vp, _sz, P(RaStats), _vp]
+    lib.ring_attn_plan.argtypes = [_i64, _i32, _int, _int, _i32, _vp, _i32, _int, _i64, P(RaStats)]
+    lib.ring_attn_tile_shape.argtypes = [_int, _i64, P(_i32), P(_i32)]
+    lib.ring_attn_status_string.argtypes = [_int]
+    lib.ring_attn_status_string.restype = ctypes.c_char_p
+    for fn in ("ring_attn_step", "ring_attn_finalize", "ring_attn_merge", "ring_attn_forward",
+               "ring_attn_plan", "ring_attn_tile_shape"):
+        getattr(lib, fn).restype = _int
+    _lib = lib
+    return lib
+
+
+def _check(fn: str, status: int):
+    if status != RA_OK:
+        raise RingAttnError(fn, status, load_library().ring_attn_status_string(status).decode())
+
+
+def _dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.float32:
+        return RA_F32
+    if dt == torch.bfloat16:
+        return RA_BF16
+    raise TypeError("ring attention takes float32 or bfloat16 tensors, got %s" % dt)
+
+
+def _gpu(x: torch.Tensor, name: str):
+    if not isinstance(x, torch.Tensor) or x.device.type != "cuda":
+        raise ValueError("%s must be a GPU tensor" % name)
+
+
+def _tensor(x: torch.Tensor, name: str) -> RaTensor:
+    _gpu(x, name)
+    if x.dim() != 3 or x.stride(2) != 1:
+        raise ValueError("%s must be a [tokens, heads, head_dim] view with unit head_dim stride" % name)
+    return RaTensor(x.data_ptr(), _dtype_code(x.dtype), x.shape[0], x.shape[1], x.shape[2], x.stride(0),
+                    x.stride(1))
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _ptr(x: Optional[torch.Tensor]):
+    return None if x is None else x.data_ptr()
+
+
+def ring_attn_tile_shape(dtype: torch.dtype, head_dim: int):
+    tq, tk = _i32(), _i32()
+    _check("ring_attn_tile_shape", load_library().ring_attn_tile_shape(_dtype_code(dtype), head_dim,
+                                                                        ctypes.byref(tq), ctypes.byref(tk)))
+    return tq.value, tk.value
+
+
+def ring_attn_step(q_blk, k_blk, v_blk, O, m, l, *, first_step: bool, scale: float, mask_mode: int = RA_MASK_NONE,
+                   q_offset: int = 0, kv_offset: int = 0, pos_stride: int = 1, cu_seqlens=None,
+                   stats: Optional[torch.Tensor] = None, stream=None):
+    """One ring step on the GPU; O [Hq, Bq, d], m / l [Hq, Bq] fp32 are updated in place.
+    cu_seqlens: int32 GPU tensor (doc-causal); stats: int64 GPU tensor of 3 counters (added to)."""
+    qt, kt, vt = _tensor(q_blk, "q_blk"), _tensor(k_blk, "k_blk"), _tensor(v_blk, "v_blk")
+    for x, name in ((O, "O"), (m, "m"), (l, "l")):
+        _gpu(x, name)
+        if x.dtype != torch.float32 or not x.is_contiguous():
+            raise ValueError("%s must be contiguous float32" % name)
+    n_docs = 0
+    if cu_seqlens is not None:
+        _gpu(cu_seqlens, "cu_seqlens")
+        if cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_contiguous():
+            raise ValueError("cu_seqlens must be contiguous int32")
+        n_docs = cu_seqlens.numel() - 1
+    if stats is not None:
+        _gpu(stats, "stats")
+        if stats.dtype != torch.int64 or stats.numel() < 3:
+            raise ValueError("stats must hold 3 int64 counters")
+    st = load_library().ring_attn_step(ctypes.byref(qt), ctypes.byref(kt), ctypes.byref(vt), O.data_ptr(),
+                                       m.data_ptr(), l.data_ptr(), int(bool(first_step)), float(scale),
+                                       int(mask_mode), int(q_offset), int(kv_offset), int(pos_stride),
+                                       _ptr(cu_seqlens), n_docs, _ptr(stats), _stream(stream))
+    _check("ring_attn_step", st)
+
+
+def ring_attn_finalize(O, m, l, out, lse=None, *, stream=None):
+    """out[u, h, :] = O[h, u, :] / l[h, u]; lse[h, u] = m + ln l.  out: [Bq, Hq, d] view."""
+    for x, name in ((O, "O"), (m, "m"), (l, "l"), (out, "out")):
+        _gpu(x, name)
+    Hq, Bq, d = O.shape
+    if out.dim() != 3 or out.stride(2) != 1 or tuple(out.shape) != (Bq, Hq, d):
+        raise ValueError("out must be a [Bq, Hq, d] view with unit last stride")
+    if lse is not None:
+        _gpu(lse, "lse")
+    st = load_library().ring_attn_finalize(O.data_ptr(), m.data_ptr(), l.data_ptr(), Hq, Bq, d, out.data_ptr(),
+                                           _dtype_code(out.dtype), out.stride(0), out.stride(1), _ptr(lse),
+                                           _stream(stream))
+    _check("ring_attn_finalize", st)
+
+
+def ring_attn_merge(out_acc, lse_acc, out_blk, lse_blk, *, stream=None):
+    """In-place log-sum-exp merge; out_* [rows, Hq, d] contiguous, lse_* [Hq, rows] fp32."""
+    for x, name in ((out_acc, "out_acc"), (lse_acc, "lse_acc"), (out_blk, "out_blk"), (lse_blk, "lse_blk")):
+        _gpu(x, name)
+        if not x.is_contiguous():
+            raise ValueError("%s must be contiguous" % name)
+    if out_acc.dtype != out_blk.dtype or out_acc.shape != out_blk.shape:
+        raise ValueError("out_acc and out_blk must match")
+    rows, Hq, d = out_acc.shape
+    if tuple(lse_acc.shape) != (Hq, rows) or tuple(lse_blk.shape) != (Hq, rows):
+        raise ValueError("lse must be [Hq, rows]")
+    st = load_library().ring_attn_merge(out_acc.data_ptr(), lse_acc.data_ptr(), out_blk.data_ptr(),
+                                        lse_blk.data_ptr(), _dtype_code(out_acc.dtype), Hq, rows, d,
+                                        _stream(stream))
+    _check("ring_attn_merge", st)
+
+
+def ring_attn_forward_workspace_size(q, k, n_blocks: int, n_docs: int = 0, prefetch: bool = False) -> int:
+    qt, kt = _tensor(q, "q"), _tensor(k, "k")
+    return int(load_library().ring_attn_forward_workspace_size(ctypes.byref(qt), ctypes.byref(kt), int(n_blocks),
+                                                               int(n_docs), int(bool(prefetch))))
+
+
+def ring_attn_forward(q, k, v, out, lse, *, n_blocks: int, layout: int, mask_mode: int, max_ring_passes: int,
+                      cu_seqlens_host=None, scale: float, prefetch: bool, workspace: torch.Tensor,
+                      want_stats: bool = False, stream=None):
+    """The whole one-GPU ring; out [T, Hq, d] contiguous; lse [Hq, T] fp32 or None.
+    Returns the tallies (dict) when want_stats (this synchronises the stream)."""
+    qt, kt, vt = _tensor(q, "q"), _tensor(k, "k"), _tensor(v, "v")
+    _gpu(out, "out")
+    if not out.is_contiguous():
+        raise ValueError("out must be contiguous")
+    if lse is not None:
+        _gpu(lse, "lse")
+    _gpu(workspace, "workspace")
+    cu_ptr, n_docs, cu_keep = None, 0, None
+    if cu_seqlens_host is not None:
+        cu_keep = torch.as_tensor(cu_seqlens_host).to(device="cpu", dtype=torch.int32).contiguous()
+        cu_ptr, n_docs = cu_keep.data_ptr(), cu_keep.numel() - 1
+    stats = RaStats()
+    st = load_library().ring_attn_forward(
+        ctypes.byref(qt), ctypes.byref(kt), ctypes.byref(vt), out.data_ptr(), _dtype_code(out.dtype), _ptr(lse),
+        int(n_blocks), int(layout), int(mask_mode), int(max_ring_passes), cu_ptr, n_docs, float(scale),
+        int(bool(prefetch)), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+        ctypes.byref(stats) if want_stats else None, _stream(stream))
+    _check("ring_attn_forward", st)
+    return stats.as_dict() if want_stats else None
+
+
+def ring_attn_plan(T: int, n_blocks: int, *, layout: int, mask_mode: int, max_ring_passes: int,
+                   cu_seqlens_host=None, dtype: torch.dtype, head_dim: int) -> dict:
+    """Host-only: tallies and allowed-pair count the forward would produce."""
+    cu_ptr, n_docs, cu_keep = None, 0, None
+    if cu_seqlens_host is not None:
+        cu_keep = torch.as_tensor(cu_seqlens_host).to(device="cpu", dtype=torch.int32).contiguous()
+        cu_ptr, n_docs = cu_keep.data_ptr(), cu_keep.numel() - 1
+    stats = RaStats()
+    st = load_library().ring_attn_plan(int(T), int(n_blocks), int(layout), int(mask_mode), int(max_ring_passes),
+                                       cu_ptr, n_docs, _dtype_code(dtype), int(head_dim), ctypes.byref(stats))
+    _check("ring_attn_plan", st)
+    return stats.as_dict()
+
+
+_LAYOUTS = {"contiguous": RA_LAYOUT_CONTIGUOUS, "striped": RA_LAYOUT_STRIPED}
+
+
+def forward(q, k, v, *, n_blocks: int, layout: str = "contiguous", causal: bool = False, cu_seqlens=None,
+            max_ring_passes: Optional[int] = None, scale: Optional[float] = None, prefetch: bool = False,
+            out_dtype: Optional[torch.dtype] = None, return_lse: bool = False, return_stats: bool = False,
+            workspace: Optional[torch.Tensor] = None):
+    """Ring attention over q [T, Hq, d], k / v [T, Hkv, d] on one GPU as n_blocks virtual devices.
+    cu_seqlens (documents, implies per-document causal) may be a CPU or GPU int tensor or a list."""
+    T, Hq, d = q.shape
+    mask = RA_MASK_NONE
+    if causal:
+        mask = RA_MASK_CAUSAL
+    if cu_seqlens is not None:
+        mask = RA_MASK_DOC_CAUSAL
+        cu_seqlens = torch.as_tensor(cu_seqlens).to(device="cpu", dtype=torch.int32)
+    n_docs = 0 if cu_seqlens is None else cu_seqlens.numel() - 1
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    P = n_blocks if max_ring_passes is None else max_ring_passes
+    out = torch.empty(T, Hq, d, device=q.device, dtype=out_dtype or q.dtype)
+    lse = torch.empty(Hq, T, device=q.device, dtype=torch.float32) if return_lse else None
+    ws_bytes = ring_attn_forward_workspace_size(q, k, n_blocks, n_docs, prefetch)
+    if workspace is None or workspace.numel() * workspace.element_size() < ws_bytes:
+        workspace = torch.empty(ws_bytes, device=q.device, dtype=torch.uint8)
+    stats = ring_attn_forward(q, k, v, out, lse, n_blocks=n_blocks, layout=_LAYOUTS[layout], mask_mode=mask,
+                              max_ring_passes=P, cu_seqlens_host=cu_seqlens, scale=scale, prefetch=prefetch,
+                              workspace=workspace, want_stats=return_stats)
+    res = [out]
+    if return_lse:
+        res.append(lse)
+    if return_stats:
+        res.append(stats)
+    return res[0] if len(res) == 1 else tuple(res)
+
+
+def forward_qkvpacked(qkv, **kw):
+    """Ring attention over a packed [T, 3, H, d] tensor (read through strided views, no copy)."""
+    if qkv.dim() != 4 or qkv.shape[1] != 3:
+        raise ValueError("qkv must be [T, 3, H, d]")
+    return forward(qkv[:, 0], qkv[:, 1], qkv[:, 2], **kw)
+
+
+__all__ = ["ring_attn_step", "ring_attn_finalize", "ring_attn_merge", "ring_attn_forward_workspace_size",
+           "ring_attn_forward", "ring_attn_plan", "ring_attn_tile_shape", "forward", "forward_qkvpacked",
+           "load_library", "RingAttnError"]

@@ -1,0 +1,465 @@
+// C ABI entry points: argument checks, the one-GPU ring driver, optional
+// side-stream prefetch of the next key/value blocks, and tallies.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+#include "kernels.h"
+#include "plan.h"
+#include "ring_attn.h"
+
+namespace ra {
+namespace {
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+size_t elem_size(ra_dtype t) { return t == RA_BF16 ? 2 : 4; }
+
+bool valid_dtype(int t) { return t == RA_F32 || t == RA_BF16; }
+
+bool tensor_ok(const ra_tensor* x) {
+    return x && x->data && valid_dtype(x->dtype) && x->n_tok >= 0 && x->n_head >= 1 && x->head_dim >= 1 &&
+           x->stride_tok >= 0 && x->stride_head >= 0;
+}
+
+// Which kernel serves (dtype, head_dim); RA_OK when one does.
+ra_status kernel_for(ra_dtype dt, int64_t d, int* tq, int* tk) {
+    if (dt == RA_BF16) {
+        if (d != 64 && d != 128) return RA_E_UNSUPPORTED;
+        *tq = kBf16TileQ;
+        *tk = kBf16TileK;
+        return RA_OK;
+    }
+    if (dt == RA_F32) {
+        if (d < 1 || d > 128) return RA_E_UNSUPPORTED;
+        *tq = kF32TileQ;
+        *tk = kF32TileK;
+        return RA_OK;
+    }
+    return RA_E_ARG;
+}
+
+// The matrix-core kernel reads 16-byte vectors: base pointers and strides
+// must keep every row of 8 bf16 aligned.
+bool bf16_aligned(const ra_tensor* x) {
+    return ((uintptr_t)x->data % 16 == 0) && x->stride_tok % 8 == 0 && x->stride_head % 8 == 0;
+}
+
+bool scale_ok(float s) { return std::isfinite(s) && s > 0.f; }
+
+hipError_t launch(const StepArgs& a, ra_dtype dt, hipStream_t st) {
+    return dt == RA_BF16 ? launch_step_bf16(a, st) : launch_step_f32(a, st);
+}
+
+// Side stream + events used by the prefetch path, created once per device.
+struct PrefetchCtx {
+    hipStream_t copy = nullptr;
+    hipEvent_t copied[2] = {nullptr, nullptr};
+    hipEvent_t consumed[2] = {nullptr, nullptr};
+};
+
+hipError_t prefetch_ctx(PrefetchCtx** out) {
+    static std::mutex mu;
+    static std::vector<PrefetchCtx> ctx;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> g(mu);
+    if ((int)ctx.size() <= dev) ctx.resize(dev + 1);
+    PrefetchCtx& c = ctx[dev];
+    if (!c.copy) {
+        if ((e = hipStreamCreateWithFlags(&c.copy, hipStreamNonBlocking)) != hipSuccess) return e;
+        for (int b = 0; b < 2; b++) {
+            if ((e = hipEventCreateWithFlags(&c.copied[b], hipEventDisableTiming)) != hipSuccess) return e;
+            if ((e = hipEventCreateWithFlags(&c.consumed[b], hipEventDisableTiming)) != hipSuccess) return e;
+        }
+    }
+    *out = &c;
+    return hipSuccess;
+}
+
+struct Workspace {
+    unsigned long long* counters = nullptr;  // 4 x u64
+    int32_t* cu = nullptr;
+    float* O = nullptr;
+    float* m = nullptr;
+    float* l = nullptr;
+    char* kv = nullptr;    // prefetch double buffer: [2][N][B][Hkv][d] for K, then the same for V
+    size_t kv_half = 0;    // bytes of one tensor's double buffer
+    size_t total = 0;
+};
+
+Workspace carve(void* base, int64_t T, int64_t Hq, int64_t Hkv, int64_t d, int64_t n_docs, ra_dtype dt,
+                bool prefetch) {
+    Workspace w;
+    size_t off = 0;
+    char* b = (char*)base;
+    auto take = [&](size_t bytes) {
+        char* p = b ? b + off : nullptr;
+        off += align_up(bytes);
+        return p;
+    };
+    w.counters = (unsigned long long*)take(4 * sizeof(unsigned long long));
+    w.cu = (int32_t*)take(sizeof(int32_t) * (size_t)(n_docs + 1));
+    w.O = (float*)take(sizeof(float) * (size_t)(T * Hq * d));
+    w.m = (float*)take(sizeof(float) * (size_t)(T * Hq));
+    w.l = (float*)take(sizeof(float) * (size_t)(T * Hq));
+    if (prefetch) {
+        w.kv_half = 2 * (size_t)T * Hkv * d * elem_size(dt);
+        w.kv = take(2 * w.kv_half);
+    }
+    w.total = off;
+    return w;
+}
+
+}  // namespace
+}  // namespace ra
+
+using namespace ra;
+
+extern "C" {
+
+const char* ring_attn_status_string(ra_status s) {
+    switch (s) {
+        case RA_OK: return "ok";
+        case RA_E_ARG: return "invalid argument";
+        case RA_E_UNSUPPORTED: return "unsupported dtype / head_dim / mask combination";
+        case RA_E_HIP: return "HIP runtime error";
+        case RA_E_WORKSPACE: return "workspace missing or too small";
+    }
+    return "unknown status";
+}
+
+ra_status ring_attn_tile_shape(ra_dtype dtype, int64_t head_dim, int32_t* tile_q, int32_t* tile_k) {
+    if (!tile_q || !tile_k) return RA_E_ARG;
+    int tq = 0, tk = 0;
+    ra_status s = kernel_for(dtype, head_dim, &tq, &tk);
+    if (s != RA_OK) return s;
+    *tile_q = tq;
+    *tile_k = tk;
+    return RA_OK;
+}
+
+ra_status ring_attn_step(const ra_tensor* q_blk, const ra_tensor* k_blk, const ra_tensor* v_blk, float* O, float* m,
+                         float* l, int first_step, float scale, ra_mask mask_mode, int64_t q_offset,
+                         int64_t kv_offset, int64_t pos_stride, const int32_t* cu_seqlens, int32_t n_docs,
+                         int64_t* stats_dev, void* stream) {
+    if (!tensor_ok(q_blk) || !tensor_ok(k_blk) || !tensor_ok(v_blk)) return RA_E_ARG;
+    if (q_blk->dtype != k_blk->dtype || q_blk->dtype != v_blk->dtype) return RA_E_ARG;
+    const int64_t d = q_blk->head_dim;
+    if (k_blk->head_dim != d || v_blk->head_dim != d) return RA_E_ARG;
+    if (k_blk->n_tok != v_blk->n_tok || k_blk->n_head != v_blk->n_head) return RA_E_ARG;
+    if (q_blk->n_head % k_blk->n_head) return RA_E_ARG;
+    if (!O || !m || !l || !scale_ok(scale) || pos_stride < 1) return RA_E_ARG;
+    if (mask_mode < RA_MASK_NONE || mask_mode > RA_MASK_DOC_CAUSAL) return RA_E_ARG;
+    if (mask_mode == RA_MASK_DOC_CAUSAL && (!cu_seqlens || n_docs < 1)) return RA_E_ARG;
+    if (mask_mode == RA_MASK_DOC_CAUSAL && pos_stride != 1) return RA_E_UNSUPPORTED;
+    int tq = 0, tk = 0;
+    ra_status ks = kernel_for(q_blk->dtype, d, &tq, &tk);
+    if (ks != RA_OK) return ks;
+    if (q_blk->dtype == RA_BF16 && (!bf16_aligned(q_blk) || !bf16_aligned(k_blk) || !bf16_aligned(v_blk)))
+        return RA_E_UNSUPPORTED;
+    const int64_t Bq = q_blk->n_tok, Hq = q_blk->n_head;
+    const int64_t n_qtiles = (Bq + tq - 1) / tq;
+    if (n_qtiles * Hq > INT32_MAX) return RA_E_UNSUPPORTED;
+    if (Bq == 0) return RA_OK;
+
+    StepArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.q = q_blk->data;
+    a.k = k_blk->data;
+    a.v = v_blk->data;
+    a.q_row_stride = q_blk->stride_tok;
+    a.q_head_stride = q_blk->stride_head;
+    a.k_row_stride = k_blk->stride_tok;
+    a.k_head_stride = k_blk->stride_head;
+    a.v_row_stride = v_blk->stride_tok;
+    a.v_head_stride = v_blk->stride_head;
+    a.Bq = Bq;
+    a.Bk = k_blk->n_tok;
+    a.pos_stride = pos_stride;
+    a.Hq = (int32_t)Hq;
+    a.group = (int32_t)(Hq / k_blk->n_head);
+    a.d = (int32_t)d;
+    a.mask = mask_mode;
+    a.scale = scale;
+    a.c2 = scale * 1.4426950408889634f;
+    a.cu = cu_seqlens;
+    a.n_docs = n_docs;
+    a.stats = (unsigned long long*)stats_dev;
+    a.n_qtiles = (int32_t)n_qtiles;
+    a.n_pairs = 1;
+    PairDesc& p = a.pairs[0];
+    p.q_pos0 = q_offset;
+    p.k_pos0 = kv_offset;
+    p.O = O;
+    p.m = m;
+    p.l = l;
+    p.load_state = first_step ? 0 : 1;
+    p.finalize = 0;
+    if (launch(a, q_blk->dtype, (hipStream_t)stream) != hipSuccess) return RA_E_HIP;
+    return RA_OK;
+}
+
+ra_status ring_attn_finalize(const float* O, const float* m, const float* l, int64_t Hq, int64_t Bq, int64_t d,
+                             void* out, ra_dtype out_dtype, int64_t out_stride_tok, int64_t out_stride_head,
+                             float* lse, void* stream) {
+    if (!O || !m || !l || !out || Hq < 1 || Bq < 0 || d < 1 || !valid_dtype(out_dtype)) return RA_E_ARG;
+    if (out_stride_tok < 0 || out_stride_head < 0) return RA_E_ARG;
+    if (launch_finalize(O, m, l, Hq, Bq, d, out, out_dtype == RA_BF16, out_stride_tok, out_stride_head, lse,
+                        (hipStream_t)stream) != hipSuccess)
+        return RA_E_HIP;
+    return RA_OK;
+}
+
+ra_status ring_attn_merge(void* out_acc, float* lse_acc, const void* out_blk, const float* lse_blk,
+                          ra_dtype dtype, int64_t Hq, int64_t rows, int64_t d, void* stream) {
+    if (!out_acc || !lse_acc || !out_blk || !lse_blk || !valid_dtype(dtype) || Hq < 1 || rows < 0 || d < 1)
+        return RA_E_ARG;
+    if (launch_merge(out_acc, lse_acc, out_blk, lse_blk, dtype == RA_BF16, Hq, rows, d, (hipStream_t)stream) !=
+        hipSuccess)
+        return RA_E_HIP;
+    return RA_OK;
+}
+
+size_t ring_attn_forward_workspace_size(const ra_tensor* q, const ra_tensor* k, int32_t n_blocks, int32_t n_docs,
+                                        int prefetch) {
+    if (!q || !k || n_blocks < 1 || n_docs < 0 || !valid_dtype(q->dtype)) return 0;
+    return carve(nullptr, q->n_tok, q->n_head, k->n_head, q->head_dim, n_docs, q->dtype, prefetch != 0).total;
+}
+
+ra_status ring_attn_plan(int64_t T, int32_t n_blocks, ra_layout layout, ra_mask mask_mode, int32_t max_ring_passes,
+                         const int32_t* cu_seqlens_host, int32_t n_docs, ra_dtype dtype, int64_t head_dim,
+                         ra_stats* stats) {
+    if (!stats || T < 0 || n_blocks < 1 || T % n_blocks || max_ring_passes < 1) return RA_E_ARG;
+    if (layout != RA_LAYOUT_CONTIGUOUS && layout != RA_LAYOUT_STRIPED) return RA_E_ARG;
+    if (mask_mode < RA_MASK_NONE || mask_mode > RA_MASK_DOC_CAUSAL) return RA_E_ARG;
+    if (mask_mode == RA_MASK_DOC_CAUSAL) {
+        if (!cu_seqlens_host || n_docs < 1 || cu_seqlens_host[0] != 0 || cu_seqlens_host[n_docs] != T)
+            return RA_E_ARG;
+        for (int32_t i = 0; i < n_docs; i++)
+            if (cu_seqlens_host[i + 1] < cu_seqlens_host[i]) return RA_E_ARG;
+        if (layout == RA_LAYOUT_STRIPED) return RA_E_UNSUPPORTED;
+    }
+    int tq = 0, tk = 0;
+    ra_status ks = kernel_for(dtype, head_dim, &tq, &tk);
+    if (ks != RA_OK) return ks;
+    Ring r;
+    r.T = T;
+    r.N = n_blocks;
+    r.B = T / n_blocks;
+    r.layout = layout;
+    r.mask = mask_mode;
+    r.passes = std::min<int64_t>(max_ring_passes, n_blocks);
+    r.cu = cu_seqlens_host;
+    r.n_docs = n_docs;
+    Plan p = make_plan(r, tq, tk);
+    int64_t c[3];
+    tile_tallies(r, tq, tk, c);
+    stats->block_pairs_visited = p.visited;
+    stats->block_pairs_skipped = p.skipped;
+    stats->block_pairs_full = p.full;
+    stats->block_pairs_partial = p.partial;
+    stats->tiles_skipped = c[0];
+    stats->tiles_full = c[1];
+    stats->tiles_partial = c[2];
+    stats->allowed_pairs = allowed_pairs(r);
+    stats->tile_q = tq;
+    stats->tile_k = tk;
+    return RA_OK;
+}
+
+ra_status ring_attn_forward(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v, void* out,
+                            ra_dtype out_dtype, float* lse, int32_t n_blocks, ra_layout layout, ra_mask mask_mode,
+                            int32_t max_ring_passes, const int32_t* cu_seqlens_host, int32_t n_docs, float scale,
+                            int prefetch, void* workspace, size_t workspace_bytes, ra_stats* stats, void* stream) {
+    // ---- arguments ----
+    if (!tensor_ok(q) || !tensor_ok(k) || !tensor_ok(v) || !out) return RA_E_ARG;
+    if (q->dtype != k->dtype || q->dtype != v->dtype || !valid_dtype(out_dtype)) return RA_E_ARG;
+    const int64_t T = q->n_tok, Hq = q->n_head, Hkv = k->n_head, d = q->head_dim;
+    if (k->n_tok != T || v->n_tok != T || v->n_head != Hkv || k->head_dim != d || v->head_dim != d) return RA_E_ARG;
+    if (Hq % Hkv) return RA_E_ARG;
+    if (n_blocks < 1 || T % n_blocks || max_ring_passes < 1 || !scale_ok(scale)) return RA_E_ARG;
+    if (layout != RA_LAYOUT_CONTIGUOUS && layout != RA_LAYOUT_STRIPED) return RA_E_ARG;
+    if (mask_mode < RA_MASK_NONE || mask_mode > RA_MASK_DOC_CAUSAL) return RA_E_ARG;
+    if (mask_mode == RA_MASK_DOC_CAUSAL) {
+        if (!cu_seqlens_host || n_docs < 1 || cu_seqlens_host[0] != 0 || cu_seqlens_host[n_docs] != T)
+            return RA_E_ARG;
+        for (int32_t i = 0; i < n_docs; i++)
+            if (cu_seqlens_host[i + 1] < cu_seqlens_host[i]) return RA_E_ARG;
+        if (layout == RA_LAYOUT_STRIPED) return RA_E_UNSUPPORTED;
+    } else {
+        n_docs = 0;
+    }
+    if (out_dtype == RA_BF16 && q->dtype != RA_BF16) return RA_E_UNSUPPORTED;
+    int tq = 0, tk = 0;
+    ra_status ks = kernel_for(q->dtype, d, &tq, &tk);
+    if (ks != RA_OK) return ks;
+    if (q->dtype == RA_BF16 && (!bf16_aligned(q) || !bf16_aligned(k) || !bf16_aligned(v)))
+        return RA_E_UNSUPPORTED;
+    if (prefetch && (k->stride_head != d || v->stride_head != d)) return RA_E_UNSUPPORTED;
+    if (q->dtype == RA_BF16 && (uintptr_t)out % 16) return RA_E_UNSUPPORTED;
+    const int64_t N = n_blocks, B = T / N;
+    const int64_t n_qtiles = (B + tq - 1) / tq;
+    if (n_qtiles * Hq * kMaxPairs > INT32_MAX) return RA_E_UNSUPPORTED;
+    Workspace ws = carve(workspace, T, Hq, Hkv, d, n_docs, q->dtype, prefetch != 0);
+    if (!workspace || workspace_bytes < ws.total) return RA_E_WORKSPACE;
+    if ((uintptr_t)workspace % kAlign) return RA_E_WORKSPACE;
+
+    hipStream_t st = (hipStream_t)stream;
+    Ring r;
+    r.T = T;
+    r.N = N;
+    r.B = B;
+    r.layout = layout;
+    r.mask = mask_mode;
+    r.passes = std::min<int64_t>(max_ring_passes, N);
+    r.cu = cu_seqlens_host;
+    r.n_docs = n_docs;
+    const Plan plan = make_plan(r, tq, tk);
+    const bool striped = layout == RA_LAYOUT_STRIPED;
+    const int64_t out_tok = Hq * d;  // out is [T, Hq, d] contiguous
+
+    PrefetchCtx* pf = nullptr;
+    if (prefetch && r.passes > 1) {
+        if (prefetch_ctx(&pf) != hipSuccess) return RA_E_HIP;
+    }
+
+    // ---- enqueue ----
+    if (stats && launch_fill_u64(ws.counters, 4, st) != hipSuccess) return RA_E_HIP;
+    if (n_docs > 0 && hipMemcpyAsync(ws.cu, cu_seqlens_host, sizeof(int32_t) * (size_t)(n_docs + 1),
+                                     hipMemcpyHostToDevice, st) != hipSuccess)
+        return RA_E_HIP;
+
+    StepArgs base;
+    std::memset(&base, 0, sizeof base);
+    base.Bq = B;
+    base.Bk = B;
+    base.pos_stride = striped ? N : 1;
+    base.Hq = (int32_t)Hq;
+    base.group = (int32_t)(Hq / Hkv);
+    base.d = (int32_t)d;
+    base.mask = mask_mode;
+    base.scale = scale;
+    base.c2 = scale * 1.4426950408889634f;
+    base.cu = ws.cu;
+    base.n_docs = n_docs;
+    base.out_bf16 = out_dtype == RA_BF16;
+    base.out = out;
+    base.out_row_stride = (striped ? N : 1) * out_tok;
+    base.out_head_stride = d;
+    base.lse = lse;
+    base.lse_row_stride = striped ? N : 1;
+    base.lse_head_stride = T;
+    base.stats = stats ? ws.counters : nullptr;
+    base.n_qtiles = (int32_t)n_qtiles;
+    base.q = q->data;
+    base.q_row_stride = (striped ? N : 1) * q->stride_tok;
+    base.q_head_stride = q->stride_head;
+
+    const size_t es = elem_size(q->dtype);
+    const int64_t blk_elems = B * Hkv * d;  // one contiguous prefetched block
+    auto kv_slot = [&](int which, int slot, int64_t i) {  // which: 0 = K, 1 = V
+        return ws.kv + which * ws.kv_half + ((size_t)slot * N + i) * blk_elems * es;
+    };
+    auto row_off = [&](int64_t blk, int64_t stride_tok) { return striped ? blk * stride_tok : blk * B * stride_tok; };
+
+    for (int64_t s = 0; s < r.passes; s++) {
+        const std::vector<StepPair>& pairs = plan.steps[s];
+        const bool use_buf = pf && s > 0;
+        const int slot = (int)(s & 1);
+        if (use_buf) {
+            // The copy engine may overwrite this slot once step s-2 has read it.
+            if (s >= 2 && hipStreamWaitEvent(pf->copy, pf->consumed[slot], 0) != hipSuccess) return RA_E_HIP;
+            for (const StepPair& sp : pairs) {
+                const ra_tensor* src[2] = {k, v};
+                for (int which = 0; which < 2; which++) {
+                    const ra_tensor* x = src[which];
+                    const char* sb = (const char*)x->data + row_off(sp.j, x->stride_tok) * es;
+                    const size_t spitch = (size_t)(striped ? N : 1) * x->stride_tok * es;
+                    if (hipMemcpy2DAsync(kv_slot(which, slot, sp.i), (size_t)Hkv * d * es, sb, spitch,
+                                         (size_t)Hkv * d * es, (size_t)B, hipMemcpyDeviceToDevice,
+                                         pf->copy) != hipSuccess)
+                        return RA_E_HIP;
+                }
+            }
+            if (hipEventRecord(pf->copied[slot], pf->copy) != hipSuccess) return RA_E_HIP;
+            if (hipStreamWaitEvent(st, pf->copied[slot], 0) != hipSuccess) return RA_E_HIP;
+        }
+        if (pf && s == 0) {
+            // Step 1's copies must not start before the caller's earlier work
+            // (which produced k and v) is done.
+            if (hipEventRecord(pf->consumed[1], st) != hipSuccess) return RA_E_HIP;
+            if (hipStreamWaitEvent(pf->copy, pf->consumed[1], 0) != hipSuccess) return RA_E_HIP;
+        }
+        for (size_t c0 = 0; c0 < pairs.size(); c0 += kMaxPairs) {
+            StepArgs a = base;
+            a.n_pairs = (int32_t)std::min<size_t>(kMaxPairs, pairs.size() - c0);
+            if (use_buf) {
+                a.k = ws.kv;
+                a.v = ws.kv + ws.kv_half;
+                a.k_row_stride = a.v_row_stride = Hkv * d;
+                a.k_head_stride = a.v_head_stride = d;
+            } else {
+                a.k = k->data;
+                a.v = v->data;
+                a.k_row_stride = (striped ? N : 1) * k->stride_tok;
+                a.v_row_stride = (striped ? N : 1) * v->stride_tok;
+                a.k_head_stride = k->stride_head;
+                a.v_head_stride = v->stride_head;
+            }
+            for (int32_t x = 0; x < a.n_pairs; x++) {
+                const StepPair& sp = pairs[c0 + x];
+                PairDesc& p = a.pairs[x];
+                p.q_off = row_off(sp.i, q->stride_tok);
+                if (use_buf) {
+                    p.k_off = p.v_off = (((int64_t)slot * N + sp.i) * blk_elems);
+                } else {
+                    p.k_off = row_off(sp.j, k->stride_tok);
+                    p.v_off = row_off(sp.j, v->stride_tok);
+                }
+                p.q_pos0 = striped ? sp.i : sp.i * B;
+                p.k_pos0 = striped ? sp.j : sp.j * B;
+                p.O = ws.O + (size_t)sp.i * Hq * B * d;
+                p.m = ws.m + (size_t)sp.i * Hq * B;
+                p.l = ws.l + (size_t)sp.i * Hq * B;
+                p.out_off = striped ? sp.i * out_tok : sp.i * B * out_tok;
+                p.lse_off = striped ? sp.i : sp.i * B;
+                p.load_state = sp.load_state;
+                p.finalize = sp.finalize;
+            }
+            if (launch(a, q->dtype, st) != hipSuccess) return RA_E_HIP;
+        }
+        if (use_buf && hipEventRecord(pf->consumed[slot], st) != hipSuccess) return RA_E_HIP;
+    }
+    for (int32_t i : plan.empty_devices) {
+        const int64_t o_off = striped ? i * out_tok : i * B * out_tok;
+        if (launch_empty_rows(out, out_dtype == RA_BF16, o_off, base.out_row_stride, d, lse, striped ? i : i * B,
+                              base.lse_row_stride, T, B, Hq, d, st) != hipSuccess)
+            return RA_E_HIP;
+    }
+
+    if (stats) {
+        unsigned long long c[4] = {0, 0, 0, 0};
+        if (hipMemcpyAsync(c, ws.counters, sizeof c, hipMemcpyDeviceToHost, st) != hipSuccess) return RA_E_HIP;
+        if (hipStreamSynchronize(st) != hipSuccess) return RA_E_HIP;
+        stats->block_pairs_visited = plan.visited;
+        stats->block_pairs_skipped = plan.skipped;
+        stats->block_pairs_full = plan.full;
+        stats->block_pairs_partial = plan.partial;
+        stats->tiles_skipped = (int64_t)c[0] + plan.tiles_in_skipped_pairs;
+        stats->tiles_full = (int64_t)c[1];
+        stats->tiles_partial = (int64_t)c[2];
+        stats->allowed_pairs = allowed_pairs(r);
+        stats->tile_q = tq;
+        stats->tile_k = tk;
+    }
+    return RA_OK;
+}
+
+}  // extern "C"

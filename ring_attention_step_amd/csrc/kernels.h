@@ -1,0 +1,66 @@
+// Launch descriptors shared by the C ABI driver and the HIP kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace ra {
+
+// One (query block, key/value block) pair of a ring step.
+struct PairDesc {
+    int64_t q_off, k_off, v_off;   // element offset of local row 0 in q / k / v
+    int64_t q_pos0, k_pos0;        // global position of local row 0 (mask coordinates)
+    float* O;                      // running state of the query block: [Hq, Bq, d]
+    float* m;                      //   [Hq, Bq]
+    float* l;                      //   [Hq, Bq]
+    int64_t out_off;               // element offset of local row 0 in out (finalize)
+    int64_t lse_off;               // offset of (head 0, local row 0) in lse (finalize)
+    int32_t load_state;            // state holds earlier steps' keys
+    int32_t finalize;              // write out / lse instead of the state
+};
+
+constexpr int kMaxPairs = 16;
+
+struct StepArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    int64_t q_row_stride, q_head_stride;   // elements, per local row / head
+    int64_t k_row_stride, k_head_stride;
+    int64_t v_row_stride, v_head_stride;
+    int64_t Bq, Bk;                        // rows in the query block / key block
+    int64_t pos_stride;                    // position step between local rows
+    int32_t Hq, group;                     // query heads; query heads per kv head
+    int32_t d;
+    int32_t mask;
+    float scale;                           // scores are scale * q.k
+    float c2;                              // scale * log2(e)
+    const int32_t* cu;                     // device cu_seqlens (doc-causal)
+    int32_t n_docs;
+    int32_t out_bf16;
+    void* out;
+    int64_t out_row_stride, out_head_stride;
+    float* lse;                            // nullable
+    int64_t lse_row_stride, lse_head_stride;
+    unsigned long long* stats;             // nullable, 3 counters
+    int32_t n_qtiles, n_pairs;
+    PairDesc pairs[kMaxPairs];
+};
+
+// Kernel tile shapes (query rows x key columns per workgroup tile).
+constexpr int kBf16TileQ = 128, kBf16TileK = 64;
+constexpr int kF32TileQ = 64, kF32TileK = 64;
+
+hipError_t launch_step_bf16(const StepArgs& a, hipStream_t stream);
+hipError_t launch_step_f32(const StepArgs& a, hipStream_t stream);
+hipError_t launch_finalize(const float* O, const float* m, const float* l, int64_t Hq, int64_t Bq,
+                           int64_t d, void* out, int out_bf16, int64_t out_stride_tok,
+                           int64_t out_stride_head, float* lse, hipStream_t stream);
+hipError_t launch_merge(void* out_acc, float* lse_acc, const void* out_blk, const float* lse_blk,
+                        int bf16, int64_t Hq, int64_t rows, int64_t d, hipStream_t stream);
+hipError_t launch_fill_u64(unsigned long long* p, int64_t n, hipStream_t stream);
+hipError_t launch_empty_rows(void* out, int out_bf16, int64_t out_off, int64_t out_row_stride,
+                             int64_t out_head_stride, float* lse, int64_t lse_off,
+                             int64_t lse_row_stride, int64_t lse_head_stride, int64_t rows,
+                             int64_t Hq, int64_t d, hipStream_t stream);
+
+}  // namespace ra

@@ -1,0 +1,327 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle on the same
+seeded inputs.  Tolerances (fp32 outputs compared with the oracle):
+  fp32 inputs: max |diff| <= 1e-5;
+  bf16 inputs (fp32 accumulation): max |diff| <= 2e-2 and mean |diff| <= 1e-2;
+  tallies: exact.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+F32_TOL = 1e-5
+BF16_MAX, BF16_MEAN = 2e-2, 1e-2
+
+
+@pytest.fixture(scope="module")
+def ra():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import ring_attention_step_amd as mod
+    mod.load_library()
+    return mod
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+
+
+def _dev(*xs):
+    return [x.cuda() for x in xs]
+
+
+def _check_bf16(out, ref, what):
+    diff = np.abs(out - ref)
+    _say(what, "max", float(diff.max()), "mean", float(diff.mean()))
+    assert diff.max() <= BF16_MAX and diff.mean() <= BF16_MEAN, (what, diff.max(), diff.mean())
+
+
+# ---------------------------------------------------------------------------
+# fp32 path: the pages' two worked examples
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["p4_ring4_b8_d16", "p2_1024tok_d2_16blk"])
+def test_f32_worked_examples_forward(ra, name):
+    w = W.WORKLOADS[name]
+    x = W.make_inputs(w)
+    _say(name)
+    q, k, v = _dev(x["q"], x["k"], x["v"])
+    out, lse, st = ra.forward(q, k, v, n_blocks=w.n_blocks, scale=w.scale, return_lse=True, return_stats=True)
+    ref = oracle.forward(x["q"], x["k"], x["v"], n_blocks=w.n_blocks, scale=w.scale)
+    assert np.abs(out.cpu().double().numpy() - ref["out"]).max() <= F32_TOL
+    assert np.abs(lse.cpu().double().numpy() - ref["lse"]).max() <= F32_TOL
+    tal = oracle.tallies(w.T, w.n_blocks, tile_q=st["tile_q"], tile_k=st["tile_k"])
+    assert all(st[k_] == v_ for k_, v_ in tal.items())
+
+
+@pytest.mark.parametrize("name", ["p4_ring4_b8_d16", "p2_1024tok_d2_16blk"])
+def test_f32_step_by_step_state(ra, name):
+    """Drive ring_attn_step in ring order; after step s the state of device i
+    must be the oracle's state over blocks i, i-1, ..., i-s."""
+    w = W.WORKLOADS[name]
+    x = W.make_inputs(w)
+    N, B = w.n_blocks, w.block
+    q, k, v = _dev(x["q"], x["k"], x["v"])
+    O = torch.empty(N, 1, B, w.d, device="cuda")
+    m = torch.empty(N, 1, B, device="cuda")
+    l = torch.empty(N, 1, B, device="cuda")
+    for s in range(N):
+        _say(name, "step", s)
+        for i in range(N):
+            j = (i - s) % N
+            ra.ring_attn_step(q[i * B:(i + 1) * B], k[j * B:(j + 1) * B], v[j * B:(j + 1) * B], O[i], m[i], l[i],
+                              first_step=(s == 0), scale=w.scale, q_offset=i * B, kv_offset=j * B)
+        ref = oracle.forward(x["q"], x["k"], x["v"], n_blocks=N, scale=w.scale, max_ring_passes=s + 1)
+        got_m = m.cpu().double().numpy().reshape(1, -1)
+        got_l = l.cpu().double().numpy().reshape(1, -1)
+        got_O = O.cpu().double().numpy().reshape(-1, w.d)
+        assert np.abs(got_m - ref["m"]).max() <= F32_TOL
+        assert np.abs(got_l / ref["l"] - 1).max() <= F32_TOL
+        assert np.abs(got_O / got_l.reshape(-1, 1) - ref["out"][:, 0]).max() <= F32_TOL
+    out = torch.empty(w.T, 1, w.d, device="cuda")
+    lse = torch.empty(N, 1, B, device="cuda")
+    for i in range(N):
+        ra.ring_attn_finalize(O[i], m[i], l[i], out[i * B:(i + 1) * B], lse[i])
+    ref = oracle.forward(x["q"], x["k"], x["v"], n_blocks=N, scale=w.scale)
+    assert np.abs(out.cpu().double().numpy() - ref["out"]).max() <= F32_TOL
+    assert np.abs(lse.cpu().double().numpy().reshape(1, -1) - ref["lse"]).max() <= F32_TOL
+
+
+def test_f32_merge_path_equals_forward(ra):
+    """Each step on a fresh state, finalised, then merged through lse."""
+    w = W.WORKLOADS["p4_ring4_b8_d16"]
+    x = W.make_inputs(w)
+    N, B, d = w.n_blocks, w.block, w.d
+    q, k, v = _dev(x["q"], x["k"], x["v"])
+    acc = torch.empty(w.T, 1, d, device="cuda")
+    lse_acc = torch.empty(1, w.T, device="cuda")
+    O = torch.empty(1, B, d, device="cuda")
+    m = torch.empty(1, B, device="cuda")
+    l = torch.empty(1, B, device="cuda")
+    part = torch.empty(B, 1, d, device="cuda")
+    lse_p = torch.empty(1, B, device="cuda")
+    for i in range(N):
+        for s in range(N):
+            j = (i - s) % N
+            ra.ring_attn_step(q[i * B:(i + 1) * B], k[j * B:(j + 1) * B], v[j * B:(j + 1) * B], O, m, l,
+                              first_step=True, scale=w.scale, q_offset=i * B, kv_offset=j * B)
+            if s == 0:
+                ra.ring_attn_finalize(O, m, l, acc[i * B:(i + 1) * B], lse_acc[:, i * B:(i + 1) * B])
+            else:
+                ra.ring_attn_finalize(O, m, l, part, lse_p)
+                a_blk = acc[i * B:(i + 1) * B].clone()
+                l_blk = lse_acc[:, i * B:(i + 1) * B].clone()
+                ra.ring_attn_merge(a_blk, l_blk, part, lse_p)
+                acc[i * B:(i + 1) * B] = a_blk
+                lse_acc[:, i * B:(i + 1) * B] = l_blk
+    ref = oracle.forward(x["q"], x["k"], x["v"], n_blocks=N, scale=w.scale)
+    assert np.abs(acc.cpu().double().numpy() - ref["out"]).max() <= F32_TOL
+    assert np.abs(lse_acc.cpu().double().numpy() - ref["lse"]).max() <= F32_TOL
+
+
+def test_f32_fully_masked_step_leaves_empty_state(ra):
+    q, k, v = _dev(*W.random_qkv(16, 2, 2, 8, "f32", 3))
+    O = torch.full((2, 8, 8), 7.0, device="cuda")
+    m = torch.full((2, 8), 7.0, device="cuda")
+    l = torch.full((2, 8), 7.0, device="cuda")
+    stats = torch.zeros(3, dtype=torch.int64, device="cuda")
+    # queries at positions 0..7, keys at 8..15: causal allows nothing
+    ra.ring_attn_step(q[:8], k[8:], v[8:], O, m, l, first_step=True, scale=0.3, mask_mode=ra.RA_MASK_CAUSAL,
+                      q_offset=0, kv_offset=8, stats=stats)
+    assert torch.isneginf(m).all() and (l == 0).all() and (O == 0).all()
+    assert stats.tolist() == [1, 0, 0]
+    out = torch.empty(8, 2, 8, device="cuda")
+    lse = torch.empty(2, 8, device="cuda")
+    ra.ring_attn_finalize(O, m, l, out, lse)
+    assert (out == 0).all() and torch.isneginf(lse).all()
+
+
+# ---------------------------------------------------------------------------
+# bf16 matrix-core path on small shapes (several tiles, ragged tails)
+# ---------------------------------------------------------------------------
+
+SMALL = [
+    # T, N, Hq, Hkv, d, layout, mask, P, docs
+    (888, 3, 4, 2, 128, 0, 1, 3, None),       # B = 296: ragged q and k tiles
+    (888, 3, 4, 4, 128, 0, 0, 3, None),
+    (888, 3, 4, 1, 128, 1, 1, 3, None),       # striped, MQA
+    (1200, 4, 2, 2, 64, 0, 1, 4, None),
+    (1200, 4, 4, 2, 64, 1, 1, 2, None),       # striped with a pass limit
+    (1024, 4, 2, 2, 128, 0, 0, 1, None),      # own block only
+    (960, 4, 2, 2, 128, 0, 2, 4, [0, 100, 101, 400, 700, 960]),
+    (2048, 4, 2, 1, 128, 0, 2, 2, "random"),
+    (256, 1, 2, 2, 128, 0, 1, 1, None),       # one virtual device
+    (520, 8, 2, 2, 128, 1, 1, 8, None),       # B = 65: a single 1-key ragged tail
+]
+
+
+@pytest.mark.parametrize("case", range(len(SMALL)))
+def test_bf16_forward_small(ra, case):
+    T, N, Hq, Hkv, d, layout, mask, P, docs = SMALL[case]
+    if docs == "random":
+        docs = W.random_doc_cu_seqlens(T, 16, 900, seed=case).tolist()
+    _say("bf16 small", SMALL[case])
+    qh, kh, vh = W.random_qkv(T, Hq, Hkv, d, "bf16", 1000 + case)
+    q, k, v = _dev(qh, kh, vh)
+    lay = "striped" if layout == 1 else "contiguous"
+    out, lse, st = ra.forward(q, k, v, n_blocks=N, layout=lay, causal=mask == 1, cu_seqlens=docs,
+                              max_ring_passes=P, out_dtype=torch.float32, return_lse=True, return_stats=True)
+    ref = oracle.forward(qh, kh, vh, n_blocks=N, layout=layout, mask=mask, max_ring_passes=P, cu_seqlens=docs)
+    _check_bf16(out.cpu().double().numpy(), ref["out"], "out")
+    assert np.abs(lse.cpu().double().numpy() - ref["lse"]).max() <= 1e-3
+    tal = oracle.tallies(T, N, layout=layout, mask=mask, max_ring_passes=P, cu_seqlens=docs,
+                         tile_q=st["tile_q"], tile_k=st["tile_k"])
+    for key, val in tal.items():
+        assert st[key] == val, key
+    # bf16 output is the round-to-nearest-even of the fp32 one, bit for bit
+    out_bf = ra.forward(q, k, v, n_blocks=N, layout=lay, causal=mask == 1, cu_seqlens=docs, max_ring_passes=P)
+    assert out_bf.dtype == torch.bfloat16
+    assert torch.equal(out_bf, out.to(torch.bfloat16))
+
+
+def test_bf16_packed_qkv_views(ra):
+    T, H, d = 1024, 2, 128
+    qh, kh, vh = W.random_qkv(T, H, H, d, "bf16", 77, packed=True)
+    qkv = torch.stack([qh, kh, vh], dim=1).cuda()
+    out = ra.forward_qkvpacked(qkv, n_blocks=4, causal=True, out_dtype=torch.float32)
+    ref = oracle.forward(qh, kh, vh, n_blocks=4, mask=oracle.MASK_CAUSAL)
+    _check_bf16(out.cpu().double().numpy(), ref["out"], "packed")
+
+
+def test_bf16_prefetch_is_bit_identical(ra):
+    for layout, docs in (("contiguous", None), ("striped", None), ("contiguous", [0, 300, 301, 1024])):
+        qkv = W.random_qkv(1024, 4, 2, 128, "bf16", 5, packed=False)
+        q, k, v = _dev(*qkv)
+        kw = dict(n_blocks=4, layout=layout, causal=docs is None, cu_seqlens=docs, return_lse=True)
+        a, la = ra.forward(q, k, v, prefetch=False, **kw)
+        b, lb = ra.forward(q, k, v, prefetch=True, **kw)
+        torch.cuda.synchronize()
+        _say("prefetch", layout, docs is not None)
+        assert torch.equal(a, b) and torch.equal(la, lb)
+
+
+def _ring_steps(ra, q, k, v, N, B, d, Hq, scale, order, state=None, mask=1):
+    O, m, l = state if state is not None else (torch.empty(N, Hq, B, d, device="cuda"),
+                                              torch.empty(N, Hq, B, device="cuda"),
+                                              torch.empty(N, Hq, B, device="cuda"))
+    for (i, j, first) in order:
+        ra.ring_attn_step(q[i * B:(i + 1) * B], k[j * B:(j + 1) * B], v[j * B:(j + 1) * B], O[i], m[i], l[i],
+                          first_step=first, scale=scale, mask_mode=mask, q_offset=i * B, kv_offset=j * B)
+    return O, m, l
+
+
+def test_bf16_resume_from_saved_state_is_bit_identical(ra):
+    """The (O, m, l) triple is the whole resume state: copy it to the host
+    after step 2, wipe the device copy, restore and finish the ring."""
+    N, B, Hq, d = 4, 256, 2, 128
+    q, k, v = _dev(*W.random_qkv(N * B, Hq, Hq, d, "bf16", 9))
+    sched = [(i, (i - s) % N, s == 0) for s in range(N) for i in range(N)]
+    full = _ring_steps(ra, q, k, v, N, B, d, Hq, 0.088, sched, mask=0)
+    cut = 3 * N
+    part = _ring_steps(ra, q, k, v, N, B, d, Hq, 0.088, sched[:cut], mask=0)
+    saved = [x.cpu() for x in part]
+    for x in part:
+        x.fill_(float("nan"))
+    restored = [x.cuda() for x in saved]
+    resumed = _ring_steps(ra, q, k, v, N, B, d, Hq, 0.088, sched[cut:], state=restored, mask=0)
+    for a, b in zip(full, resumed):
+        assert torch.equal(a, b)
+
+
+def test_bf16_shuffled_step_order_within_tolerance(ra):
+    N, B, Hq, d = 4, 200, 2, 128
+    qh, kh, vh = W.random_qkv(N * B, Hq, Hq, d, "bf16", 10)
+    q, k, v = _dev(qh, kh, vh)
+    rng = np.random.default_rng(0)
+    sched = []
+    for i in range(N):
+        js = rng.permutation(N)
+        sched += [(i, int(j), n == 0) for n, j in enumerate(js)]
+    O, m, l = _ring_steps(ra, q, k, v, N, B, d, Hq, 1 / math.sqrt(d), sched, mask=1)
+    out = torch.empty(N * B, Hq, d, device="cuda")
+    for i in range(N):
+        ra.ring_attn_finalize(O[i], m[i], l[i], out[i * B:(i + 1) * B])
+    ref = oracle.forward(qh, kh, vh, n_blocks=N, mask=oracle.MASK_CAUSAL)
+    _check_bf16(out.cpu().double().numpy(), ref["out"], "shuffled")
+
+
+def test_bf16_step_api_striped_positions(ra):
+    """ring_attn_step on striped blocks given as strided views, positions
+    q_offset + u * N; the state must equal the oracle's block state."""
+    T, N, Hq, d = 1024, 4, 2, 128
+    qh, kh, vh = W.random_qkv(T, Hq, Hq, d, "bf16", 11)
+    q, k, v = _dev(qh, kh, vh)
+    i, j = 1, 3
+    B = T // N
+    O = torch.empty(Hq, B, d, device="cuda")
+    m = torch.empty(Hq, B, device="cuda")
+    l = torch.empty(Hq, B, device="cuda")
+    ra.ring_attn_step(q[i::N], k[j::N], v[j::N], O, m, l, first_step=True, scale=1 / math.sqrt(d),
+                      mask_mode=ra.RA_MASK_CAUSAL, q_offset=i, kv_offset=j, pos_stride=N)
+    ref = oracle.block(qh[i::N], kh[j::N], vh[j::N], np.arange(B) * N + i, np.arange(B) * N + j,
+                       mask=oracle.MASK_CAUSAL)
+    got_l = l.cpu().double().numpy()
+    ok = ref["l"] > 0
+    assert np.array_equal(got_l > 0, ok)
+    out = (O.cpu().double().numpy() / np.where(ok, got_l, 1)[..., None])
+    _check_bf16(out[ok], ref["out"][ok], "striped step")
+    assert np.abs(m.cpu().double().numpy()[ok] - ref["m"][ok]).max() <= 1e-3
+
+
+# ---------------------------------------------------------------------------
+# Full-size long-context workloads, in the benchmark's launch configuration:
+# sampled rows against the oracle, tallies exactly.
+# ---------------------------------------------------------------------------
+
+def _sample_rows(w, rng, n=48):
+    B = w.block
+    toks = [0, 1, B - 1, B, w.T - 1, w.T // 2]
+    toks += list(rng.integers(0, w.T, size=n - len(toks)))
+    heads = list(rng.integers(0, w.Hq, size=len(toks)))
+    return np.asarray(heads), np.asarray(toks)
+
+
+@pytest.mark.parametrize("name", ["causal32k_h32_d128_8blk", "gqa_striped64k_h32kv8_d128_16blk",
+                                  "varlen_packed128k_h32_d128_8blk_p4"])
+def test_long_workload_sampled_rows(ra, name):
+    w = W.WORKLOADS[name]
+    _say(name, "generating inputs")
+    x = W.make_inputs(w)
+    if w.packed:
+        qkv = x["qkv"].cuda()
+        q, k, v = qkv[:, 0], qkv[:, 1], qkv[:, 2]
+    else:
+        q, k, v = _dev(x["q"], x["k"], x["v"])
+    cu = x.get("cu_seqlens")
+    _say(name, "forward")
+    out, lse, st = ra.forward(q, k, v, n_blocks=w.n_blocks, layout="striped" if w.layout else "contiguous",
+                              causal=w.mask == 1, cu_seqlens=cu, max_ring_passes=w.max_ring_passes,
+                              out_dtype=torch.float32, return_lse=True, return_stats=True)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all() and torch.isfinite(lse).all()
+    rng = np.random.default_rng(w.seed)
+    heads, toks = _sample_rows(w, rng)
+    group = w.Hq // w.Hkv
+    # oracle on the sampled heads only: q head h reads kv head h // group
+    uh = sorted(set(int(h) for h in heads))
+    qs = x["q"][:, uh]
+    ks = x["k"][:, [h // group for h in uh]]
+    vs = x["v"][:, [h // group for h in uh]]
+    idx = {h: n for n, h in enumerate(uh)}
+    _say(name, "oracle on", len(toks), "rows")
+    ref = oracle.forward(qs, ks, vs, n_blocks=w.n_blocks, layout=w.layout, mask=w.mask,
+                         max_ring_passes=w.max_ring_passes, cu_seqlens=cu, scale=w.scale,
+                         rows=(np.array([idx[int(h)] for h in heads]), toks))
+    got = out.cpu()[toks, heads].double().numpy()
+    _check_bf16(got, ref["out"], name)
+    assert np.abs(lse.cpu()[heads, toks].double().numpy() - ref["lse"]).max() <= 1e-3
+    tal = oracle.tallies(w.T, w.n_blocks, layout=w.layout, mask=w.mask, max_ring_passes=w.max_ring_passes,
+                         cu_seqlens=cu, tile_q=st["tile_q"], tile_k=st["tile_k"])
+    for key, val in tal.items():
+        assert st[key] == val, key

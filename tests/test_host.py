@@ -1,0 +1,188 @@
+"""CPU tests of the C-ABI library's host side: it loads and exports every
+symbol its header declares, its planner's tallies and pair counts equal the
+oracle's brute force, and bad arguments are refused before any GPU work."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+import ring_attention_step_amd as ra
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ring_attn.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return ra.load_library()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(ring_attn_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    for fn in ("ring_attn_step", "ring_attn_finalize", "ring_attn_merge", "ring_attn_forward",
+               "ring_attn_forward_workspace_size", "ring_attn_plan", "ring_attn_tile_shape",
+               "ring_attn_status_string"):
+        assert fn in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for fn in _declared_functions():
+        assert hasattr(lib, fn), fn
+
+
+def test_library_links_no_torch():
+    import subprocess
+    out = subprocess.run(["readelf", "-d", ra.library_path()], capture_output=True, text=True).stdout
+    needed = re.findall(r"\[(.*?)\]", "\n".join(l for l in out.splitlines() if "NEEDED" in l))
+    assert not any("torch" in n or "c10" in n for n in needed), needed
+
+
+def test_status_strings(lib):
+    for s in range(5):
+        assert lib.ring_attn_status_string(s)
+
+
+def test_tile_shapes():
+    assert ra.ring_attn_tile_shape(torch.bfloat16, 128) == (128, 64)
+    assert ra.ring_attn_tile_shape(torch.bfloat16, 64) == (128, 64)
+    assert ra.ring_attn_tile_shape(torch.float32, 16) == (64, 64)
+    with pytest.raises(ra.RingAttnError):
+        ra.ring_attn_tile_shape(torch.bfloat16, 96)
+    with pytest.raises(ra.RingAttnError):
+        ra.ring_attn_tile_shape(torch.float32, 200)
+
+
+PLAN_CASES = [
+    # T, N, layout, mask, P, dtype, d, cu
+    (32, 4, 0, 0, 4, torch.float32, 16, None),
+    (1024, 16, 0, 0, 16, torch.float32, 2, None),
+    (888, 3, 0, 1, 3, torch.bfloat16, 128, None),
+    (888, 3, 1, 1, 3, torch.bfloat16, 128, None),
+    (1200, 4, 0, 1, 2, torch.bfloat16, 64, None),
+    (1200, 4, 1, 0, 3, torch.bfloat16, 64, None),
+    (960, 4, 0, 2, 4, torch.bfloat16, 128, [0, 100, 101, 400, 700, 960]),
+    (960, 4, 0, 2, 1, torch.float32, 8, [0, 100, 101, 400, 700, 960]),
+    (4096, 8, 0, 2, 4, torch.bfloat16, 128, "random"),
+    (640, 5, 1, 1, 9, torch.float32, 32, None),
+]
+
+
+@pytest.mark.parametrize("case", range(len(PLAN_CASES)))
+def test_plan_matches_oracle_brute_force(case):
+    T, N, layout, mask, P, dt, d, cu = PLAN_CASES[case]
+    if cu == "random":
+        cu = W.random_doc_cu_seqlens(T, 64, 700, seed=case).tolist()
+    tq, tk = ra.ring_attn_tile_shape(dt, d)
+    got = ra.ring_attn_plan(T, N, layout=layout, mask_mode=mask, max_ring_passes=P, cu_seqlens_host=cu,
+                            dtype=dt, head_dim=d)
+    want = oracle.tallies(T, N, layout=layout, mask=mask, max_ring_passes=P, cu_seqlens=cu, tile_q=tq, tile_k=tk)
+    for key, val in want.items():
+        assert got[key] == val, key
+    assert got["allowed_pairs"] == oracle.allowed_pairs(T, N, layout=layout, mask=mask, max_ring_passes=P,
+                                                        cu_seqlens=cu)
+    assert (got["tile_q"], got["tile_k"]) == (tq, tk)
+
+
+@pytest.mark.parametrize("name", ["causal32k_h32_d128_8blk", "gqa_striped64k_h32kv8_d128_16blk",
+                                  "varlen_packed128k_h32_d128_8blk_p4"])
+def test_plan_matches_oracle_on_long_workloads(name):
+    w = W.WORKLOADS[name]
+    cu = W.doc_cu_seqlens(w.seed, w.T, *w.doc_len_range).tolist() if w.doc_len_range else None
+    dt = torch.bfloat16
+    got = ra.ring_attn_plan(w.T, w.n_blocks, layout=w.layout, mask_mode=w.mask, max_ring_passes=w.max_ring_passes,
+                            cu_seqlens_host=cu, dtype=dt, head_dim=w.d)
+    want = oracle.tallies(w.T, w.n_blocks, layout=w.layout, mask=w.mask, max_ring_passes=w.max_ring_passes,
+                          cu_seqlens=cu, tile_q=got["tile_q"], tile_k=got["tile_k"])
+    for key, val in want.items():
+        assert got[key] == val, key
+    if name != "varlen_packed128k_h32_d128_8blk_p4":
+        assert got["allowed_pairs"] == w.T * (w.T + 1) // 2
+    else:
+        assert got["allowed_pairs"] == oracle.allowed_pairs(w.T, w.n_blocks, mask=w.mask,
+                                                            max_ring_passes=w.max_ring_passes, cu_seqlens=cu)
+
+
+def test_plan_rejects_bad_arguments():
+    bad = [
+        dict(T=30, n_blocks=4),                                  # T % N
+        dict(T=32, n_blocks=4, max_ring_passes=0),
+        dict(T=32, n_blocks=4, mask_mode=2),                     # doc mask without cu_seqlens
+        dict(T=32, n_blocks=4, mask_mode=2, cu_seqlens_host=[0, 10, 31]),  # does not end at T
+        dict(T=32, n_blocks=4, mask_mode=2, cu_seqlens_host=[0, 20, 10, 32]),  # decreasing
+        dict(T=32, n_blocks=4, layout=7),
+    ]
+    for b in bad:
+        kw = dict(layout=0, mask_mode=0, max_ring_passes=4, cu_seqlens_host=None, dtype=torch.float32, head_dim=16)
+        kw.update({k: v for k, v in b.items() if k not in ("T", "n_blocks")})
+        with pytest.raises(ra.RingAttnError) as e:
+            ra.ring_attn_plan(b["T"], b["n_blocks"], **kw)
+        assert e.value.status == ra.RA_E_ARG
+    with pytest.raises(ra.RingAttnError) as e:
+        ra.ring_attn_plan(32, 4, layout=1, mask_mode=2, max_ring_passes=4, cu_seqlens_host=[0, 32],
+                          dtype=torch.float32, head_dim=16)
+    assert e.value.status == ra.RA_E_UNSUPPORTED
+
+
+def _fake(T, H, d, dtype=ra.RA_BF16, ptr=1 << 20, st=None):
+    st = st if st is not None else H * d
+    return ra.RaTensor(ptr, dtype, T, H, d, st, d)
+
+
+def test_forward_and_step_refuse_bad_arguments_before_any_gpu_work(lib):
+    # Fake (never dereferenced) device addresses: every call below must fail
+    # argument checks before touching the GPU.
+    q, k, v = _fake(64, 4, 128), _fake(64, 2, 128), _fake(64, 2, 128)
+    out, ws = ctypes.c_void_p(1 << 21), ctypes.c_void_p(1 << 22)
+    F = lib.ring_attn_forward
+    R = ctypes.byref
+
+    def fwd(qq=q, kk=k, vv=v, n_blocks=4, layout=0, mask=1, P=4, cu=None, n_docs=0, scale=0.1, ws_bytes=1 << 40,
+            out_dtype=ra.RA_BF16, o=out):
+        return F(R(qq), R(kk), R(vv), o, out_dtype, None, n_blocks, layout, mask, P, cu, n_docs, scale, 0, ws,
+                 ws_bytes, None, None)
+
+    assert fwd(n_blocks=5) == ra.RA_E_ARG             # 64 % 5
+    assert fwd(P=0) == ra.RA_E_ARG
+    assert fwd(scale=0.0) == ra.RA_E_ARG
+    assert fwd(scale=float("nan")) == ra.RA_E_ARG
+    assert fwd(kk=_fake(64, 3, 128)) == ra.RA_E_ARG   # 4 % 3
+    assert fwd(vv=_fake(60, 2, 128)) == ra.RA_E_ARG
+    assert fwd(o=None) == ra.RA_E_ARG
+    assert fwd(mask=2) == ra.RA_E_ARG                 # no cu_seqlens
+    assert fwd(qq=_fake(64, 4, 96), kk=_fake(64, 2, 96), vv=_fake(64, 2, 96)) == ra.RA_E_UNSUPPORTED
+    assert fwd(qq=_fake(64, 4, 128, ptr=(1 << 20) + 2)) == ra.RA_E_UNSUPPORTED  # misaligned bf16
+    f32 = [_fake(64, 4, 16, ra.RA_F32), _fake(64, 2, 16, ra.RA_F32), _fake(64, 2, 16, ra.RA_F32)]
+    assert fwd(*f32, out_dtype=ra.RA_BF16) == ra.RA_E_UNSUPPORTED
+    assert fwd(ws_bytes=16) == ra.RA_E_WORKSPACE
+    cu = (ctypes.c_int32 * 3)(0, 10, 64)
+    assert fwd(mask=2, cu=cu, n_docs=2, layout=1) == ra.RA_E_UNSUPPORTED
+    cu_bad = (ctypes.c_int32 * 3)(0, 70, 64)
+    assert fwd(mask=2, cu=cu_bad, n_docs=2) == ra.RA_E_ARG
+
+    S = lib.ring_attn_step
+    state = ctypes.c_void_p(1 << 23)
+    assert S(R(q), R(k), R(v), state, state, state, 1, -1.0, 0, 0, 0, 1, None, 0, None, None) == ra.RA_E_ARG
+    assert S(R(q), R(k), R(v), None, state, state, 1, 0.1, 0, 0, 0, 1, None, 0, None, None) == ra.RA_E_ARG
+    assert S(R(q), R(k), R(v), state, state, state, 1, 0.1, 0, 0, 0, 0, None, 0, None, None) == ra.RA_E_ARG
+    assert S(R(q), R(k), R(v), state, state, state, 1, 0.1, 2, 0, 0, 1, None, 0, None, None) == ra.RA_E_ARG
+    assert S(R(q), R(_fake(64, 2, 64)), R(v), state, state, state, 1, 0.1, 0, 0, 0, 1, None, 0, None,
+             None) == ra.RA_E_ARG
+
+
+def test_workspace_size_grows_with_prefetch(lib):
+    q, k = _fake(4096, 32, 128), _fake(4096, 8, 128)
+    a = lib.ring_attn_forward_workspace_size(ctypes.byref(q), ctypes.byref(k), 8, 0, 0)
+    b = lib.ring_attn_forward_workspace_size(ctypes.byref(q), ctypes.byref(k), 8, 0, 1)
+    state = 4096 * 32 * 128 * 4 + 2 * 4096 * 32 * 4
+    assert a >= state and b >= a + 2 * 2 * 4096 * 8 * 128 * 2
