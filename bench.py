@@ -1,0 +1,217 @@
+"""Benchmark of the one-GPU ring-attention forward.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--prefetch]
+                    [--no-cpu-baseline]
+
+A step is one ring_attn_forward call: every ring step of every virtual device
+plus the fused finalize, on synthetic bf16 inputs already resident in HBM.
+Default workload: 32768 tokens, 32 heads, d = 128, 8 contiguous ring blocks of
+4096, causal mask, scale 1/sqrt(128).  Throughput is causal-adjusted: FLOP =
+4 * d * Hq * (allowed (query, key) pairs), i.e. only the two contractions over
+pairs the mask lets through.  Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak (AMD published figure)
+DEFAULT_WORKLOAD = "causal32k_h32_d128_8blk"
+KERNEL = "step_bf16_kernel<128>"
+KERNEL_SOURCES = ["ring_attention_step_amd/csrc/step_bf16.hip", "ring_attention_step_amd/csrc/plan.h",
+                  "ring_attention_step_amd/csrc/kernels.h"]
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(workload: str, prefetch: bool):
+    """HBM bytes per launch of the dominant kernel from the committed rocprofv3
+    counter summary, or None when it is missing or the kernel changed since."""
+    path = os.path.join(ROOT, "profiles", "traffic_%s%s.json" % (workload, "_prefetch" if prefetch else ""))
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_src_sha") != kernel_source_sha():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, x, pairs_fn):
+    """The fp64 oracle, untuned, on a bounded sample of the workload's rows:
+    every head at n_tok evenly spaced query tokens (full key sets)."""
+    import numpy as np
+
+    import oracle
+
+    n_tok = int(os.environ.get("RING_BENCH_CPU_TOKENS", "256"))
+    toks = np.linspace(0, w.T - 1, n_tok).astype(np.int64)
+    heads = np.repeat(np.arange(w.Hq), n_tok)
+    rows_t = np.tile(toks, w.Hq)
+    cu = x.get("cu_seqlens")
+    t0 = time.perf_counter()
+    oracle.forward(x["q"], x["k"], x["v"], n_blocks=w.n_blocks, layout=w.layout, mask=w.mask,
+                   max_ring_passes=w.max_ring_passes, cu_seqlens=cu, scale=w.scale, rows=(heads, rows_t))
+    dt = time.perf_counter() - t0
+    pairs = pairs_fn(rows_t)
+    flop = 4.0 * w.d * pairs
+    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": "%d query rows (all %d heads x %d evenly spaced tokens, full key sets) of %s in %.1f s"
+                      % (len(heads), w.Hq, n_tok, w.name, dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--prefetch", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="instead of the benchmark, run a plain device copy of BYTES bytes 5 times "
+                         "(reference reading for the HBM byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures the ring on one GPU (all ring blocks are virtual devices on it); "
+              "--gpus %d is not supported" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import ring_attention_step_amd as ra
+    import workloads as W
+
+    if args.copy_calibration:
+        n = args.copy_calibration // 4 * 4
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            torch.mul(src, 1.0, out=dst)  # an element-wise kernel: reads n bytes, writes n bytes
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "launches": 5}), flush=True)
+        return
+
+    w = W.WORKLOADS[args.workload]
+    if w.dtype != "bf16":
+        print("bench workloads are the bf16 long-context ones", file=sys.stderr)
+        sys.exit(2)
+    x = W.make_inputs(w)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    if w.packed:
+        qkv = x["qkv"].to(dev)
+        q, k, v = qkv[:, 0], qkv[:, 1], qkv[:, 2]
+    else:
+        q, k, v = x["q"].to(dev), x["k"].to(dev), x["v"].to(dev)
+    cu = x.get("cu_seqlens")
+    n_docs = 0 if cu is None else cu.numel() - 1
+    plan = ra.ring_attn_plan(w.T, w.n_blocks, layout=w.layout, mask_mode=w.mask,
+                             max_ring_passes=w.max_ring_passes, cu_seqlens_host=cu, dtype=torch.bfloat16,
+                             head_dim=w.d)
+    flop = 4.0 * w.d * w.Hq * plan["allowed_pairs"]
+    out = torch.empty(w.T, w.Hq, w.d, device=dev, dtype=torch.bfloat16)
+    lse = torch.empty(w.Hq, w.T, device=dev, dtype=torch.float32)
+    ws = torch.empty(ra.ring_attn_forward_workspace_size(q, k, w.n_blocks, n_docs, args.prefetch), device=dev,
+                     dtype=torch.uint8)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        ra.ring_attn_forward(q, k, v, out, lse, n_blocks=w.n_blocks, layout=w.layout, mask_mode=w.mask,
+                             max_ring_passes=w.max_ring_passes, cu_seqlens_host=cu, scale=w.scale,
+                             prefetch=args.prefetch, workspace=ws, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_event = ev0.elapsed_time(ev1) / args.steps
+    ms_wall = wall * 1e3 / args.steps
+    n_launch = sum(1 for s in range(min(w.max_ring_passes, w.n_blocks)))  # one launch per ring step
+    value = flop / (ms_wall * 1e-3) / 1e12
+    achieved = flop / (ms_event * 1e-3) / 1e12
+    traffic = traffic_from_profile(w.name, args.prefetch)
+
+    res = {
+        "metric": "causal-adjusted attention TFLOP/s and % bf16 MFMA peak, 32K ring fwd, 1 GPU",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_wall, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "tokens": w.T, "q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": w.d,
+                   "ring_blocks": w.n_blocks, "layout": ["contiguous", "striped"][w.layout],
+                   "mask": ["none", "causal", "doc-causal"][w.mask], "max_ring_passes": w.max_ring_passes,
+                   "prefetch": bool(args.prefetch), "flop_per_step": flop,
+                   "allowed_pairs_per_head": plan["allowed_pairs"]},
+        "pct_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "roofline": {"bound": "mfma", "kernel": KERNEL, "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                     "launches_per_step": n_launch, "avg_launch_ms": round(ms_event / n_launch, 4)},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_for(w, x)
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline_for(w, x):
+    import numpy as np
+
+    def pairs_fn(toks):
+        # allowed keys of each sampled row under this workload's mask and ring
+        tot = 0
+        N, B, P = w.n_blocks, w.block, min(w.max_ring_passes, w.n_blocks)
+        cu = x.get("cu_seqlens")
+        for t in toks:
+            t = int(t)
+            lo, hi = 0, w.T - 1
+            if w.mask:
+                hi = t
+            if w.mask == 2:
+                c = cu.numpy()
+                lo = int(c[np.searchsorted(c, t, side="right") - 1])
+            bi = t % N if w.layout == 1 else t // B
+            for s in range(P):
+                j = (bi - s) % N
+                if w.layout == 1:
+                    keys = np.arange(B) * N + j
+                    tot += int(((keys >= lo) & (keys <= hi)).sum())
+                else:
+                    a, b = max(lo, j * B), min(hi, j * B + B - 1)
+                    tot += max(0, b - a + 1)
+        return tot
+
+    return cpu_baseline(w, x, pairs_fn)
+
+
+if __name__ == "__main__":
+    main()
