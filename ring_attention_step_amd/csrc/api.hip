@@ -50,6 +50,12 @@ bool bf16_aligned(const ra_tensor* x) {
     return ((uintptr_t)x->data % 16 == 0) && x->stride_tok % 8 == 0 && x->stride_head % 8 == 0;
 }
 
+// The matrix-core kernel addresses a 64-row key tile with 32-bit byte offsets
+// from the tile's first row.
+bool bf16_tile_addressable(int64_t row_stride_elems) {
+    return row_stride_elems >= 0 && row_stride_elems * 2 * kBf16TileK < ((int64_t)1 << 31);
+}
+
 bool scale_ok(float s) { return std::isfinite(s) && s > 0.f; }
 
 hipError_t launch(const StepArgs& a, ra_dtype dt, hipStream_t st) {
@@ -162,7 +168,9 @@ ra_status ring_attn_step(const ra_tensor* q_blk, const ra_tensor* k_blk, const r
     int tq = 0, tk = 0;
     ra_status ks = kernel_for(q_blk->dtype, d, &tq, &tk);
     if (ks != RA_OK) return ks;
-    if (q_blk->dtype == RA_BF16 && (!bf16_aligned(q_blk) || !bf16_aligned(k_blk) || !bf16_aligned(v_blk)))
+    if (q_blk->dtype == RA_BF16 && (!bf16_aligned(q_blk) || !bf16_aligned(k_blk) || !bf16_aligned(v_blk) ||
+                                    !bf16_tile_addressable(k_blk->stride_tok) ||
+                                    !bf16_tile_addressable(v_blk->stride_tok)))
         return RA_E_UNSUPPORTED;
     const int64_t Bq = q_blk->n_tok, Hq = q_blk->n_head;
     const int64_t n_qtiles = (Bq + tq - 1) / tq;
@@ -300,7 +308,10 @@ ra_status ring_attn_forward(const ra_tensor* q, const ra_tensor* k, const ra_ten
     int tq = 0, tk = 0;
     ra_status ks = kernel_for(q->dtype, d, &tq, &tk);
     if (ks != RA_OK) return ks;
-    if (q->dtype == RA_BF16 && (!bf16_aligned(q) || !bf16_aligned(k) || !bf16_aligned(v)))
+    const int64_t row_mult = layout == RA_LAYOUT_STRIPED ? n_blocks : 1;
+    if (q->dtype == RA_BF16 && (!bf16_aligned(q) || !bf16_aligned(k) || !bf16_aligned(v) ||
+                                !bf16_tile_addressable(row_mult * k->stride_tok) ||
+                                !bf16_tile_addressable(row_mult * v->stride_tok)))
         return RA_E_UNSUPPORTED;
     if (prefetch && (k->stride_head != d || v->stride_head != d)) return RA_E_UNSUPPORTED;
     if (q->dtype == RA_BF16 && (uintptr_t)out % 16) return RA_E_UNSUPPORTED;

@@ -24,6 +24,7 @@
 // and one final rescale to the true maximum runs before the state is written,
 // so the stored (m, l, O) is exactly the state relative to the running max.
 #include <cmath>
+#include <type_traits>
 
 #include "kernels.h"
 #include "plan.h"
@@ -45,59 +46,68 @@ constexpr int BK = kBf16TileK;   // 64 keys per tile
 constexpr int THREADS = 256;     // 4 waves of 64
 constexpr float kLazyRescale = 8.0f;
 
+// LDS tiles hold 64 keys x D dims, row-major, 16-byte chunks XOR-swizzled
+// per row (no padding): logical chunk c of key row r sits in slot
+// c ^ swz(r).  The K swizzle spreads the 16 rows an MFMA operand read takes
+// in one pass over distinct banks; the V swizzle does the same for the
+// transposing reads, which take 4 rows x 2-4 chunks per pass.
 template <int D>
-struct Smem {
-    // K rows are skewed by 16 bytes so the 32 rows an MFMA operand read
-    // touches fall in distinct banks; V rows by 64 bytes for the transposing
-    // reads, which take 4 rows x 64 bytes per half-wave.
-    static constexpr int KP = D + 8;
-    static constexpr int VP = D + 32;
-    bf16 k[2][BK * KP];
-    bf16 v[2][BK * VP];
+struct Tiles {
+    static constexpr int CH = D / 8;                      // 16-byte chunks per row
+    static constexpr int ELEMS = BK * D;                  // one tile, elements
+    static constexpr int LOADS = BK * CH / 64 / (THREADS / 64);  // 1 KB loads per wave per tensor
+    __device__ static constexpr int swz_k(int r) { return r & (CH - 1); }
+    __device__ static constexpr int swz_v(int r) { return (4 * (r & 3) + 2 * ((r >> 1) & 1)) & (CH - 1); }
 };
 
-template <int D>
-struct Stage {
-    static constexpr int N = BK * D / 8 / THREADS;  // 16-byte chunks per thread per tensor
-    u32x4 k[N], v[N];
-};
 
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Direct global -> LDS copy of one key tile (rows w0 .. w0 + 63 of K and V)
+// into k_dst / v_dst: every lane moves one 16-byte chunk per load and the
+// hardware writes lane l's chunk to lds + 16 l, so each lane picks the global
+// chunk that belongs in its slot.  Addresses are a uniform tile base plus a
+// 32-bit per-lane byte offset.  Rows past the end of the block (last_row <
+// 63) re-read the last row: their scores are masked to -inf, so they only
+// ever meet a zero weight.
 template <int D>
-__device__ __forceinline__ void load_tile(Stage<D>& st, const bf16* kb, const bf16* vb, int64_t k_rs,
-                                          int64_t v_rs, int64_t w0, int64_t Bk) {
+__device__ __forceinline__ void issue_tile(bf16* k_dst, bf16* v_dst, const bf16* k_tile, const bf16* v_tile,
+                                           uint32_t k_rs_bytes, uint32_t v_rs_bytes, int last_row, int wave) {
+    using T = Tiles<D>;
+    constexpr int RPI = 64 / T::CH;  // rows per load instruction
+    const int lane = threadIdx.x & 63;
+    const int slot = lane % T::CH;
 #pragma unroll
-    for (int r = 0; r < Stage<D>::N; r++) {
-        const int c = threadIdx.x + r * THREADS;
-        const int key = c / (D / 8), col = (c % (D / 8)) * 8;
-        const int64_t w = w0 + key;
-        if (w < Bk) {
-            st.k[r] = *(const u32x4*)(kb + w * k_rs + col);
-            st.v[r] = *(const u32x4*)(vb + w * v_rs + col);
-        } else {
-            st.k[r] = u32x4{0, 0, 0, 0};
-            st.v[r] = u32x4{0, 0, 0, 0};
-        }
+    for (int i = 0; i < T::LOADS; i++) {
+        const int n = wave * T::LOADS + i;  // wave-uniform
+        const int r = RPI * n + lane / T::CH;
+        const uint32_t row = (uint32_t)(r < last_row ? r : last_row);
+        const uint32_t ko = row * k_rs_bytes + 16u * (uint32_t)(slot ^ T::swz_k(r));
+        const uint32_t vo = row * v_rs_bytes + 16u * (uint32_t)(slot ^ T::swz_v(r));
+        __builtin_amdgcn_global_load_lds((const char*)k_tile + ko, (lds_void*)(k_dst + 512 * n), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const char*)v_tile + vo, (lds_void*)(v_dst + 512 * n), 16, 0, 0);
     }
 }
 
-template <int D>
-__device__ __forceinline__ void store_tile(Smem<D>& sm, int buf, const Stage<D>& st) {
-#pragma unroll
-    for (int r = 0; r < Stage<D>::N; r++) {
-        const int c = threadIdx.x + r * THREADS;
-        const int key = c / (D / 8), col = (c % (D / 8)) * 8;
-        *(u32x4*)&sm.k[buf][key * Smem<D>::KP + col] = st.k[r];
-        *(u32x4*)&sm.v[buf][key * Smem<D>::VP + col] = st.v[r];
-    }
-}
+__device__ __forceinline__ void wait_tile_loads() { __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 __device__ __forceinline__ i16x4 lds_read_tr(const bf16* p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p));
 }
 
+// Value of x in lane l ^ 32, through the half-swapping permute.
+__device__ __forceinline__ float other_half(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
+}
+
 template <int D>
 __global__ __launch_bounds__(THREADS, 2) void step_bf16_kernel(const StepArgs a) {
-    __shared__ Smem<D> sm;
+    // Two K and two V tile buffers as four distinct arrays: the compiler can
+    // then tell the direct-to-LDS loads into one buffer from the reads of the
+    // other and does not wait for the former before the latter.
+    __shared__ bf16 k_buf0[Tiles<D>::ELEMS], k_buf1[Tiles<D>::ELEMS];
+    __shared__ bf16 v_buf0[Tiles<D>::ELEMS], v_buf1[Tiles<D>::ELEMS];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int half = lane >> 5, col = lane & 31;
 
@@ -180,37 +190,76 @@ __global__ __launch_bounds__(THREADS, 2) void step_bf16_kernel(const StepArgs a)
 
     const bf16* kbase = (const bf16*)a.k + pd.k_off + kvh * a.k_head_stride;
     const bf16* vbase = (const bf16*)a.v + pd.v_off + kvh * a.v_head_stride;
+    using TL = Tiles<D>;
+    // Per-lane LDS element offsets of the MFMA operands (buffer 0).
+    //  K (A operand of S^T): key row col (+32 kb), logical chunk 2 kc + half.
+    //  (2 kc + half) ^ swz = 2 (kc ^ kx) + half_x with kx = swz >> 1, half_x = half ^ (swz & 1).
+    const int kx = TL::swz_k(col) >> 1, half_x = half ^ (TL::swz_k(col) & 1);
+    //  V (A operand of O^T, transposing read): key row 4 half + j/4 (+ 32 kb + 16 cp + 8 second),
+    //  dims 32 db + 16 g + 4 (j % 4) .. +3, i.e. chunk 4 db + 2 g + (j % 4) / 2, half-chunk j % 2.
     const int j16 = lane & 15, g16 = (lane >> 4) & 1;
-    const int tr_row = 4 * half + (j16 >> 2), tr_col = 16 * g16 + 4 * (j16 & 3);
+    const int vrow = 4 * half + (j16 >> 2);
+    int v_off[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; db++)
+        v_off[db] = vrow * D + 8 * ((4 * db + 2 * g16 + ((j16 & 3) >> 1)) ^ TL::swz_v(vrow)) + 4 * (j16 & 1);
     unsigned n_full = 0, n_part = 0;
 
-    if (kt_lo <= kt_hi) {
-        Stage<D> st;
-        load_tile<D>(st, kbase, vbase, a.k_row_stride, a.v_row_stride, (int64_t)kt_lo * BK, a.Bk);
-        store_tile<D>(sm, 0, st);
-        __syncthreads();
-        for (int kt = kt_lo; kt <= kt_hi; kt++) {
-            const int buf = (kt - kt_lo) & 1;
-            const bool has_next = kt < kt_hi;
-            if (has_next)
-                load_tile<D>(st, kbase, vbase, a.k_row_stride, a.v_row_stride, (int64_t)(kt + 1) * BK, a.Bk);
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    const uint32_t k_rs_bytes = (uint32_t)(a.k_row_stride * 2), v_rs_bytes = (uint32_t)(a.v_row_stride * 2);
+    auto issue_next = [&](int kt, bf16* kd, bf16* vd) {
+        const int64_t w0 = (int64_t)kt * BK;
+        const int64_t rem = a.Bk - 1 - w0;
+        issue_tile<D>(kd, vd, kbase + w0 * a.k_row_stride, vbase + w0 * a.v_row_stride, k_rs_bytes, v_rs_bytes,
+                      rem < BK ? (int)rem : BK, wave_u);
+    };
+    // One key tile: compute on buffer B while the next tile streams into the other.
+    auto tile = [&](int kt, auto bufc) {
+            constexpr int B = decltype(bufc)::value;
+            const bf16* ks = B ? k_buf1 : k_buf0;
+            const bf16* vs = B ? v_buf1 : v_buf0;
+            // The other buffer was last read in the previous iteration, which
+            // every wave has left (barrier at its end): refill it now.
+            if (kt < kt_hi) issue_next(kt + 1, B ? k_buf0 : k_buf1, B ? v_buf0 : v_buf1);
             const Cls c = tile_cls(kt);
             n_full += c == kFull;
             n_part += c == kPartial;
             const bool ragged = (int64_t)(kt + 1) * BK > a.Bk;
 
-            // S^T = K Q^T
-            f32x16 s[2];
-            const bf16* kl = &sm.k[buf][col * Smem<D>::KP + 8 * half];
+            // S^T = K Q^T: 2 x D/16 MFMAs alternating between the two key
+            // blocks, operands read 8 ahead.
+            constexpr int NS = 2 * (D / 16);
+            f32x16 s[2] = {f32x16{}, f32x16{}};
+            constexpr int KA = 4;  // K operands in flight
+            bf16x8 ka[KA];
+            auto k_frag = [&](int n) {  // n = 2 kc + kb
+                const int kc = n >> 1;
+                const int off = col * D + 8 * half_x + 16 * (kc ^ kx);
+                return *(const bf16x8*)(ks + 32 * D * (n & 1) + off);
+            };
 #pragma unroll
-            for (int kb = 0; kb < 2; kb++) {
-                s[kb] = f32x16{};
+            for (int i = 0; i < KA; i++) ka[i] = k_frag(i);
 #pragma unroll
-                for (int kc = 0; kc < D / 16; kc++) {
-                    const bf16x8 ka = *(const bf16x8*)(kl + 32 * kb * Smem<D>::KP + 16 * kc);
-                    s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[kc], s[kb], 0, 0, 0);
-                }
+            for (int i = 0; i < NS; i++) {
+                s[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[i % KA], qf[i >> 1], s[i & 1], 0, 0, 0);
+                if (i + KA < NS) ka[i % KA] = k_frag(i + KA);
             }
+
+            // First V operands: they do not depend on P, so their latency hides
+            // behind the softmax arithmetic.
+            // PV order: pair q = (kb, cp) outer, db inner (consecutive MFMAs use
+            // different accumulators).
+            constexpr int NP = 4 * (D / 32);
+            bf16x8 va[4];
+            auto v_frag = [&](int n) {
+                const int q = n / (D / 32), db = n % (D / 32);
+                const bf16* p1 = vs + (32 * (q >> 1) + 16 * (q & 1)) * D + v_off[db];
+                const i16x4 r1 = lds_read_tr(p1);
+                const i16x4 r2 = lds_read_tr(p1 + 8 * D);
+                return __builtin_bit_cast(bf16x8, __builtin_shufflevector(r1, r2, 0, 1, 2, 3, 4, 5, 6, 7));
+            };
+#pragma unroll
+            for (int i = 0; i < 4; i++) va[i] = v_frag(i);
 
             if (c == kPartial || ragged) {
                 // Key x of the tile (0..BK-1) sits at position tk0 + x * pos_stride; turn the
@@ -243,7 +292,7 @@ __global__ __launch_bounds__(THREADS, 2) void step_bf16_kernel(const StepArgs a)
             for (int kb = 0; kb < 2; kb++)
 #pragma unroll
                 for (int i = 0; i < 16; i++) mt = fmaxf(mt, s[kb][i]);
-            mt = fmaxf(mt, __shfl_xor(mt, 32));
+            mt = fmaxf(mt, other_half(mt));
             const float mnew = fmaxf(mx, mt);
             const float mnc = mnew * a.c2;
             const bool need = mnc > mrc + kLazyRescale;  // false while the row has no key
@@ -268,23 +317,24 @@ __global__ __launch_bounds__(THREADS, 2) void step_bf16_kernel(const StepArgs a)
                 }
 
             // O^T += V^T P^T
-            const bf16* vl = &sm.v[buf][tr_row * Smem<D>::VP + tr_col];
 #pragma unroll
-            for (int db = 0; db < D / 32; db++)
-#pragma unroll
-                for (int kb = 0; kb < 2; kb++)
-#pragma unroll
-                    for (int cp = 0; cp < 2; cp++) {
-                        const bf16* p1 = vl + (32 * kb + 16 * cp) * Smem<D>::VP + 32 * db;
-                        const i16x4 r1 = lds_read_tr(p1);
-                        const i16x4 r2 = lds_read_tr(p1 + 8 * Smem<D>::VP);
-                        const i16x8 r = __builtin_shufflevector(r1, r2, 0, 1, 2, 3, 4, 5, 6, 7);
-                        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, r),
-                                                                         pb[kb][cp], o[db], 0, 0, 0);
-                    }
+            for (int n = 0; n < NP; n++) {
+                const int q = n / (D / 32), db = n % (D / 32);
+                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[n & 3], pb[q >> 1][q & 1], o[db], 0, 0, 0);
+                if (n + 4 < NP) va[n & 3] = v_frag(n + 4);
+            }
 
-            if (has_next) store_tile<D>(sm, buf ^ 1, st);
+            // Next tile landed (own loads) and everyone is done with this one.
+            wait_tile_loads();
             __syncthreads();
+    };
+    if (kt_lo <= kt_hi) {
+        issue_next(kt_lo, k_buf0, v_buf0);
+        wait_tile_loads();
+        __syncthreads();
+        for (int kt = kt_lo; kt <= kt_hi; kt += 2) {
+            tile(kt, std::integral_constant<int, 0>{});
+            if (kt + 1 <= kt_hi) tile(kt + 1, std::integral_constant<int, 1>{});
         }
     }
 
@@ -296,7 +346,7 @@ __global__ __launch_bounds__(THREADS, 2) void step_bf16_kernel(const StepArgs a)
 
     // Both halves of a row combine their denominators; then rescale to the
     // true maximum.
-    float ltot = lsum + __shfl_xor(lsum, 32);
+    float ltot = lsum + other_half(lsum);
     if (mx != -INFINITY) {
         const float beta = __builtin_amdgcn_exp2f(mrc - mx * a.c2);
         ltot *= beta;
