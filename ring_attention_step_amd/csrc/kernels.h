@@ -47,7 +47,7 @@ struct StepArgs {
 };
 
 // Kernel tile shapes (query rows x key columns per workgroup tile).
-constexpr int kBf16TileQ = 128, kBf16TileK = 64;
+constexpr int kBf16TileQ = 256, kBf16TileK = 64;
 constexpr int kF32TileQ = 64, kF32TileK = 64;
 
 hipError_t launch_step_bf16(const StepArgs& a, hipStream_t stream);

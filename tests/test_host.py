@@ -54,8 +54,8 @@ def test_status_strings(lib):
 
 
 def test_tile_shapes():
-    assert ra.ring_attn_tile_shape(torch.bfloat16, 128) == (128, 64)
-    assert ra.ring_attn_tile_shape(torch.bfloat16, 64) == (128, 64)
+    assert ra.ring_attn_tile_shape(torch.bfloat16, 128) == (256, 64)
+    assert ra.ring_attn_tile_shape(torch.bfloat16, 64) == (256, 64)
     assert ra.ring_attn_tile_shape(torch.float32, 16) == (64, 64)
     with pytest.raises(ra.RingAttnError):
         ra.ring_attn_tile_shape(torch.bfloat16, 96)
