@@ -95,12 +95,13 @@ struct Workspace {
     float* O = nullptr;
     float* m = nullptr;
     float* l = nullptr;
-    char* kv = nullptr;    // prefetch double buffer: [2][N][B][Hkv][d] for K, then the same for V
-    size_t kv_half = 0;    // bytes of one tensor's double buffer
+    char* vt = nullptr;     // packed V^T of all blocks (bf16 path): [N][Hkv][d][Bp]
+    char* kv = nullptr;     // prefetch double buffers: K [2][N][B][Hkv][d], then V (f32) or V^T (bf16)
+    size_t k_half = 0;      // bytes of the K double buffer
     size_t total = 0;
 };
 
-Workspace carve(void* base, int64_t T, int64_t Hq, int64_t Hkv, int64_t d, int64_t n_docs, ra_dtype dt,
+Workspace carve(void* base, int64_t T, int64_t N, int64_t Hq, int64_t Hkv, int64_t d, int64_t n_docs, ra_dtype dt,
                 bool prefetch) {
     Workspace w;
     size_t off = 0;
@@ -110,14 +111,19 @@ Workspace carve(void* base, int64_t T, int64_t Hq, int64_t Hkv, int64_t d, int64
         off += align_up(bytes);
         return p;
     };
+    const int64_t B = N > 0 ? T / N : 0;
+    const size_t es = elem_size(dt);
+    const size_t vt_bytes = dt == RA_BF16 ? (size_t)N * Hkv * d * vt_padded_keys(B) * 2 : 0;
     w.counters = (unsigned long long*)take(4 * sizeof(unsigned long long));
     w.cu = (int32_t*)take(sizeof(int32_t) * (size_t)(n_docs + 1));
     w.O = (float*)take(sizeof(float) * (size_t)(T * Hq * d));
     w.m = (float*)take(sizeof(float) * (size_t)(T * Hq));
     w.l = (float*)take(sizeof(float) * (size_t)(T * Hq));
+    if (dt == RA_BF16) w.vt = take(vt_bytes);
     if (prefetch) {
-        w.kv_half = 2 * (size_t)T * Hkv * d * elem_size(dt);
-        w.kv = take(2 * w.kv_half);
+        w.k_half = 2 * (size_t)T * Hkv * d * es;
+        const size_t v_half = dt == RA_BF16 ? 2 * vt_bytes : w.k_half;
+        w.kv = take(w.k_half + v_half);
     }
     w.total = off;
     return w;
@@ -238,7 +244,8 @@ ra_status ring_attn_merge(void* out_acc, float* lse_acc, const void* out_blk, co
 size_t ring_attn_forward_workspace_size(const ra_tensor* q, const ra_tensor* k, int32_t n_blocks, int32_t n_docs,
                                         int prefetch) {
     if (!q || !k || n_blocks < 1 || n_docs < 0 || !valid_dtype(q->dtype)) return 0;
-    return carve(nullptr, q->n_tok, q->n_head, k->n_head, q->head_dim, n_docs, q->dtype, prefetch != 0).total;
+    if (q->n_tok % n_blocks) return 0;
+    return carve(nullptr, q->n_tok, n_blocks, q->n_head, k->n_head, q->head_dim, n_docs, q->dtype, prefetch != 0).total;
 }
 
 ra_status ring_attn_plan(int64_t T, int32_t n_blocks, ra_layout layout, ra_mask mask_mode, int32_t max_ring_passes,
@@ -318,7 +325,7 @@ ra_status ring_attn_forward(const ra_tensor* q, const ra_tensor* k, const ra_ten
     const int64_t N = n_blocks, B = T / N;
     const int64_t n_qtiles = (B + tq - 1) / tq;
     if (n_qtiles * Hq * kMaxPairs > INT32_MAX) return RA_E_UNSUPPORTED;
-    Workspace ws = carve(workspace, T, Hq, Hkv, d, n_docs, q->dtype, prefetch != 0);
+    Workspace ws = carve(workspace, T, n_blocks, Hq, Hkv, d, n_docs, q->dtype, prefetch != 0);
     if (!workspace || workspace_bytes < ws.total) return RA_E_WORKSPACE;
     if ((uintptr_t)workspace % kAlign) return RA_E_WORKSPACE;
 
@@ -374,65 +381,96 @@ ra_status ring_attn_forward(const ra_tensor* q, const ra_tensor* k, const ra_ten
     base.q_head_stride = q->stride_head;
 
     const size_t es = elem_size(q->dtype);
-    const int64_t blk_elems = B * Hkv * d;  // one contiguous prefetched block
-    auto kv_slot = [&](int which, int slot, int64_t i) {  // which: 0 = K, 1 = V
-        return ws.kv + which * ws.kv_half + ((size_t)slot * N + i) * blk_elems * es;
+    const bool use_vt = q->dtype == RA_BF16;
+    const int64_t Bp = vt_padded_keys(B);
+    const int64_t vt_blk = Hkv * d * Bp;    // elements of one packed V^T block
+    const int64_t blk_elems = B * Hkv * d;  // one contiguous prefetched K (or V) block
+    auto k_slot = [&](int slot, int64_t i) { return ws.kv + ((size_t)slot * N + i) * blk_elems * es; };
+    auto v_slot = [&](int slot, int64_t i) {
+        return ws.kv + ws.k_half + ((size_t)slot * N + i) * (use_vt ? vt_blk * 2 : blk_elems * es);
     };
     auto row_off = [&](int64_t blk, int64_t stride_tok) { return striped ? blk * stride_tok : blk * B * stride_tok; };
+
+    if (use_vt && launch_pack_vt(v->data, v->stride_tok, v->stride_head, N, B, striped, Hkv, d, ws.vt, st) !=
+                      hipSuccess)
+        return RA_E_HIP;
 
     for (int64_t s = 0; s < r.passes; s++) {
         const std::vector<StepPair>& pairs = plan.steps[s];
         const bool use_buf = pf && s > 0;
         const int slot = (int)(s & 1);
+        if (pf && s == 0) {
+            // Step 1's copies must not start before the caller's earlier work
+            // (which produced k and v) and the V^T pack are done.
+            if (hipEventRecord(pf->consumed[1], st) != hipSuccess) return RA_E_HIP;
+            if (hipStreamWaitEvent(pf->copy, pf->consumed[1], 0) != hipSuccess) return RA_E_HIP;
+        }
         if (use_buf) {
             // The copy engine may overwrite this slot once step s-2 has read it.
             if (s >= 2 && hipStreamWaitEvent(pf->copy, pf->consumed[slot], 0) != hipSuccess) return RA_E_HIP;
             for (const StepPair& sp : pairs) {
-                const ra_tensor* src[2] = {k, v};
-                for (int which = 0; which < 2; which++) {
-                    const ra_tensor* x = src[which];
-                    const char* sb = (const char*)x->data + row_off(sp.j, x->stride_tok) * es;
-                    const size_t spitch = (size_t)(striped ? N : 1) * x->stride_tok * es;
-                    if (hipMemcpy2DAsync(kv_slot(which, slot, sp.i), (size_t)Hkv * d * es, sb, spitch,
-                                         (size_t)Hkv * d * es, (size_t)B, hipMemcpyDeviceToDevice,
-                                         pf->copy) != hipSuccess)
+                const char* kb = (const char*)k->data + row_off(sp.j, k->stride_tok) * es;
+                const size_t kpitch = (size_t)(striped ? N : 1) * k->stride_tok * es;
+                if (hipMemcpy2DAsync(k_slot(slot, sp.i), (size_t)Hkv * d * es, kb, kpitch, (size_t)Hkv * d * es,
+                                     (size_t)B, hipMemcpyDeviceToDevice, pf->copy) != hipSuccess)
+                    return RA_E_HIP;
+                if (use_vt) {
+                    if (hipMemcpyAsync(v_slot(slot, sp.i), ws.vt + (size_t)sp.j * vt_blk * 2, (size_t)vt_blk * 2,
+                                       hipMemcpyDeviceToDevice, pf->copy) != hipSuccess)
+                        return RA_E_HIP;
+                } else {
+                    const char* vb = (const char*)v->data + row_off(sp.j, v->stride_tok) * es;
+                    const size_t vpitch = (size_t)(striped ? N : 1) * v->stride_tok * es;
+                    if (hipMemcpy2DAsync(v_slot(slot, sp.i), (size_t)Hkv * d * es, vb, vpitch, (size_t)Hkv * d * es,
+                                         (size_t)B, hipMemcpyDeviceToDevice, pf->copy) != hipSuccess)
                         return RA_E_HIP;
                 }
             }
             if (hipEventRecord(pf->copied[slot], pf->copy) != hipSuccess) return RA_E_HIP;
             if (hipStreamWaitEvent(st, pf->copied[slot], 0) != hipSuccess) return RA_E_HIP;
         }
-        if (pf && s == 0) {
-            // Step 1's copies must not start before the caller's earlier work
-            // (which produced k and v) is done.
-            if (hipEventRecord(pf->consumed[1], st) != hipSuccess) return RA_E_HIP;
-            if (hipStreamWaitEvent(pf->copy, pf->consumed[1], 0) != hipSuccess) return RA_E_HIP;
-        }
         for (size_t c0 = 0; c0 < pairs.size(); c0 += kMaxPairs) {
             StepArgs a = base;
             a.n_pairs = (int32_t)std::min<size_t>(kMaxPairs, pairs.size() - c0);
             if (use_buf) {
                 a.k = ws.kv;
-                a.v = ws.kv + ws.kv_half;
-                a.k_row_stride = a.v_row_stride = Hkv * d;
-                a.k_head_stride = a.v_head_stride = d;
+                a.k_row_stride = Hkv * d;
+                a.k_head_stride = d;
+                if (use_vt) {
+                    a.vt = ws.kv + ws.k_half;
+                } else {
+                    a.v = ws.kv + ws.k_half;
+                    a.v_row_stride = Hkv * d;
+                    a.v_head_stride = d;
+                }
             } else {
                 a.k = k->data;
-                a.v = v->data;
                 a.k_row_stride = (striped ? N : 1) * k->stride_tok;
-                a.v_row_stride = (striped ? N : 1) * v->stride_tok;
                 a.k_head_stride = k->stride_head;
-                a.v_head_stride = v->stride_head;
+                if (use_vt) {
+                    a.vt = ws.vt;
+                } else {
+                    a.v = v->data;
+                    a.v_row_stride = (striped ? N : 1) * v->stride_tok;
+                    a.v_head_stride = v->stride_head;
+                }
+            }
+            if (use_vt) {
+                a.vt_row_stride = Bp;
+                a.vt_head_stride = d * Bp;
             }
             for (int32_t x = 0; x < a.n_pairs; x++) {
                 const StepPair& sp = pairs[c0 + x];
                 PairDesc& p = a.pairs[x];
                 p.q_off = row_off(sp.i, q->stride_tok);
                 if (use_buf) {
-                    p.k_off = p.v_off = (((int64_t)slot * N + sp.i) * blk_elems);
+                    p.k_off = ((int64_t)slot * N + sp.i) * blk_elems;
+                    p.v_off = p.k_off;
+                    p.vt_off = ((int64_t)slot * N + sp.i) * vt_blk;
                 } else {
                     p.k_off = row_off(sp.j, k->stride_tok);
                     p.v_off = row_off(sp.j, v->stride_tok);
+                    p.vt_off = (int64_t)sp.j * vt_blk;
                 }
                 p.q_pos0 = striped ? sp.i : sp.i * B;
                 p.k_pos0 = striped ? sp.j : sp.j * B;

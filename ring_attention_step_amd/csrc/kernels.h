@@ -14,6 +14,7 @@ struct PairDesc {
     float* l;                      //   [Hq, Bq]
     int64_t out_off;               // element offset of local row 0 in out (finalize)
     int64_t lse_off;               // offset of (head 0, local row 0) in lse (finalize)
+    int64_t vt_off;                // element offset of this key block in the packed V^T
     int32_t load_state;            // state holds earlier steps' keys
     int32_t finalize;              // write out / lse instead of the state
 };
@@ -27,6 +28,8 @@ struct StepArgs {
     int64_t q_row_stride, q_head_stride;   // elements, per local row / head
     int64_t k_row_stride, k_head_stride;
     int64_t v_row_stride, v_head_stride;
+    const void* vt;                        // packed V^T (bf16 matrix-core path) or null
+    int64_t vt_row_stride, vt_head_stride; // elements per dim row / per head of a packed block
     int64_t Bq, Bk;                        // rows in the query block / key block
     int64_t pos_stride;                    // position step between local rows
     int32_t Hq, group;                     // query heads; query heads per kv head
@@ -58,6 +61,14 @@ hipError_t launch_finalize(const float* O, const float* m, const float* l, int64
 hipError_t launch_merge(void* out_acc, float* lse_acc, const void* out_blk, const float* lse_blk,
                         int bf16, int64_t Hq, int64_t rows, int64_t d, hipStream_t stream);
 hipError_t launch_fill_u64(unsigned long long* p, int64_t n, hipStream_t stream);
+
+// Packed V^T of the ring blocks: vt[j][g][c][p] (p < Bp = B rounded up to the
+// key tile) holds V of key w of block j, kv head g, dim c, where p is w with
+// bits 2 and 3 swapped inside each 16-key group (the order in which the S^T
+// accumulators hold their keys); zero for w >= B.
+int64_t vt_padded_keys(int64_t B);
+hipError_t launch_pack_vt(const void* v, int64_t v_stride_tok, int64_t v_stride_head, int64_t N, int64_t B,
+                          int striped, int64_t Hkv, int64_t d, void* vt, hipStream_t stream);
 hipError_t launch_empty_rows(void* out, int out_bf16, int64_t out_off, int64_t out_row_stride,
                              int64_t out_head_stride, float* lse, int64_t lse_off,
                              int64_t lse_row_stride, int64_t lse_head_stride, int64_t rows,

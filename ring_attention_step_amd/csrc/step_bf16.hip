@@ -6,34 +6,43 @@
 // in opposite phases separated by workgroup barriers:
 //
 //   M phase (matrix cores):  O^T += V^T P^T for the previous key tile and
-//                            S^T = K Q^T for the current one, interleaved;
+//                            S^T = K Q^T for the current one, interleaved,
+//                            operands read from LDS a few MFMAs ahead;
 //   V phase (vector ALUs):   mask, row max, online-softmax update, P = exp2.
 //
 // While one group of a SIMD runs its M phase the other runs its V phase, so
 // the matrix-core and vector work of the two overlap by construction.
 //
 // Per key tile and wave (64 keys):
-//   S^T = K Q^T      2 x 8 MFMA 32x32x16 (keys x queries), K from LDS, Q in
-//                    registers.  Working on S^T puts one query row in each
+//   S^T = K Q^T      2 x D/16 MFMA 32x32x16 (keys x queries), K from LDS, Q
+//                    in registers.  Working on S^T puts one query row in each
 //                    lane (lanes l and l+32 hold the two halves of its keys),
 //                    so row max and row sum need one half-swap permute.
 //   online softmax   the running-max recurrence of the "Ring Attention
 //                    simulation" gist applied to a whole tile (Zhihu article,
 //                    local vs. global softmax): tile max, rescale of the state
 //                    when the max grows, P = exp2(S*c - m*c), c = scale*log2 e.
-//   O^T += V^T P^T   4 x 4 MFMA 32x32x16 (dims x queries); P converted to bf16
-//                    straight from the S^T accumulators (its lane layout is
-//                    already the B operand), V^T read from a row-major LDS
-//                    tile with the transposing ds_read_b64_tr_b16.
+//                    Row sums add up P in fp32, before its bf16 rounding.
+//   O^T += V^T P^T   4 x D/32 MFMA 32x32x16 (dims x queries); P converted to
+//                    bf16 straight from the S^T accumulators (its lane layout
+//                    is already the B operand).
 // The O rescale is lazy: it is applied only when some row's maximum grows by
 // more than 8 in log2 units (P stays <= 256), and one final rescale to the
 // true maximum runs before the state is written, so the stored (m, l, O) is
 // exactly the state relative to the running maximum.
 //
+// V operands come either from a row-major V tile through the transposing
+// ds_read_b64_tr_b16 (VT = false: the step entry point), or -- for the ring
+// forward, which packs V^T once per call -- from a V^T tile with plain 16-byte
+// reads (VT = true).  The plain reads cost the LDS a fifth of the transposing
+// ones, and, unlike them, let the compiler see that they do not touch the
+// buffer the next stage is streaming into, so it does not wait for that
+// stream before them.
+//
 // LDS stages: stage j holds K of key tile j and V of key tile j - 1 (the two
 // operands one M phase reads); the two groups read a stage in two
-// consecutive phases while the next stage streams into the other buffer with
-// direct global -> LDS loads.
+// consecutive phases while the next two stages stream into the other two
+// buffers with direct global -> LDS loads.
 #include <cmath>
 #include <type_traits>
 
@@ -55,52 +64,94 @@ constexpr int BK = kBf16TileK;   // 64 keys per tile
 constexpr int WAVES = 8;
 constexpr int THREADS = 64 * WAVES;
 constexpr float kLazyRescale = 8.0f;
+static_assert(BK == 64, "the lane layouts below assume 64-key tiles");
 
 template <int I>
 using ic = std::integral_constant<int, I>;
 
-// LDS tiles hold 64 keys x D dims, row-major, 16-byte chunks XOR-swizzled per
-// row (no padding): logical chunk c of key row r sits in slot c ^ swz(r).  The
-// K swizzle spreads the 16 rows an MFMA operand read takes in one pass over
-// distinct banks; the V swizzle does the same for the transposing reads,
-// which take 4 rows x 2-4 chunks per pass.
-template <int D>
-struct Tiles {
-    static constexpr int CH = D / 8;                 // 16-byte chunks per row
-    static constexpr int ELEMS = BK * D;             // one tile, elements
-    static constexpr int LOADS = BK * CH / 64 / (WAVES / 2);  // 1 KB loads per issuing wave per tile
-    __device__ static constexpr int swz_k(int r) { return r & (CH - 1); }
-    __device__ static constexpr int swz_v(int r) { return (4 * (r & 3) + 2 * ((r >> 1) & 1)) & (CH - 1); }
-};
-
 typedef __attribute__((address_space(3))) void lds_void;
 
-// Direct global -> LDS copy of one 64-row tile of K (SWZ_V = false) or V into
-// dst, by the four waves of one group (gwave = 0..3 within the group): every
-// lane moves one 16-byte chunk per load and the hardware writes
-// lane l's chunk to dst + 16 l, so each lane picks the global chunk that
-// belongs in its slot.  Addresses are a uniform tile base plus a 32-bit
-// per-lane byte offset.  Rows past the end of the block (last_row < 63)
-// re-read the last row: their scores are masked to -inf, so they only ever
-// meet a zero weight.
-template <int D, bool SWZ_V>
+// LDS tiles, 16-byte chunks XOR-swizzled per row (no padding): logical chunk
+// c of row r sits in slot c ^ swz(r).
+//  K tile   [64 keys][D]:  swz = r & (D/8 - 1); the 16 rows one MFMA operand
+//           read takes per pass land in distinct banks.
+//  V tile   [64 keys][D] (transposing reads): swz = 4(r&3) + 2((r>>1)&1),
+//           the same for the 4 rows x 2-4 chunks such a read takes per pass.
+//  V^T tile [D][64 keys] (128-byte rows): swz = (r >> 1) & 7.
+template <int D>
+struct Tiles {
+    static constexpr int CH = D / 8;                    // 16-byte chunks per K / V row
+    static constexpr int ELEMS = BK * D;                // one tile, elements (any layout)
+    static constexpr int LOADS = ELEMS * 2 / 1024 / 4;  // 1 KB loads per issuing wave per tile
+    __device__ static constexpr int swz_k(int r) { return r & (CH - 1); }
+    __device__ static constexpr int swz_v(int r) { return (4 * (r & 3) + 2 * ((r >> 1) & 1)) & (CH - 1); }
+    __device__ static constexpr int swz_vt(int r) { return (r >> 1) & 7; }
+};
+
+// Lane-dependent values that the loop re-derives on every use: an empty asm
+// statement hides where the value came from, so the compiler cannot hoist
+// the (cheap) address arithmetic built on it out of the loop and keep one
+// register per address alive across the whole loop.
+__device__ __forceinline__ int fresh_lane() {
+    int l = threadIdx.x & 63;
+    __asm__ volatile("" : "+v"(l));
+    return l;
+}
+
+// Marks a register value as produced here: the compiler can no longer sink
+// its computation past this point (into a later phase, next to its use).
+template <typename T>
+__device__ __forceinline__ void pin(T& x) {
+    __asm__ volatile("" : "+v"(x));
+}
+
+// Direct global -> LDS copy of one tile into dst by the four waves of one
+// group (gwave = 0..3): every lane moves one 16-byte chunk per load and the
+// hardware writes lane l's chunk to dst + 16 l, so each lane picks the global
+// chunk that belongs in its slot.  Addresses are a uniform tile base plus a
+// 32-bit per-lane byte offset.
+//  K, V (KIND 0, 1): rows are keys, D/8 chunks each, row r at r * rs_bytes;
+//    rows past last_row re-read last_row (their scores are masked to -inf).
+//  V^T (KIND 2): rows are dims (D of them), 8 chunks of 8 keys each, row r at
+//    r * rs_bytes (the packed V^T is zero beyond the block: no clamp needed).
+template <int D, int KIND>
 __device__ __forceinline__ void issue_tile(bf16* dst, const bf16* tile, uint32_t rs_bytes, int last_row, int gwave) {
     using T = Tiles<D>;
-    constexpr int RPI = 64 / T::CH;  // rows per load instruction
-    const int lane = threadIdx.x & 63;
-    const int slot = lane % T::CH;
+    constexpr int CPR = KIND == 2 ? 8 : T::CH;  // chunks per row
+    constexpr int RPI = 64 / CPR;               // rows per load instruction
+    const int lane = fresh_lane();
+    const int slot = lane % CPR;
 #pragma unroll
     for (int i = 0; i < T::LOADS; i++) {
         const int n = gwave * T::LOADS + i;  // wave-uniform
-        const int r = RPI * n + lane / T::CH;
-        const uint32_t row = (uint32_t)(r < last_row ? r : last_row);
-        const int swz = SWZ_V ? T::swz_v(r) : T::swz_k(r);
+        const int r = RPI * n + lane / CPR;
+        const int swz = KIND == 0 ? T::swz_k(r) : (KIND == 1 ? T::swz_v(r) : T::swz_vt(r));
+        const uint32_t row = (uint32_t)(KIND == 2 ? r : (r < last_row ? r : last_row));
         const uint32_t off = row * rs_bytes + 16u * (uint32_t)(slot ^ swz);
         __builtin_amdgcn_global_load_lds((const char*)tile + off, (lds_void*)(dst + 512 * n), 16, 0, 0);
     }
 }
 
-__device__ __forceinline__ void wait_tile_loads() { __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// s_waitcnt vmcnt(N): all but this wave's N most recent vector-memory loads
+// have landed (lgkmcnt and expcnt left at their maxima).  Issued through the
+// builtin so that the compiler's own wait bookkeeping sees it: it then knows
+// which stage loads are done and adds no wait of its own before later reads.
+template <int N>
+__device__ __forceinline__ void wait_loads_but() {
+    static_assert(N >= 0 && N < 16, "vmcnt field");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
+
+// Workgroup barrier between phases.  It waits for this wave's LDS traffic
+// only: the direct-to-LDS stage loads stay in flight across it (they are
+// waited for explicitly, with wait_loads_but, before the barrier that hands
+// their buffer to the readers), which a fenced barrier would not allow.  The
+// scheduling barriers keep every instruction in the phase it is written in.
+__device__ __forceinline__ void phase_barrier() {
+    __builtin_amdgcn_sched_barrier(0);
+    __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
 
 __device__ __forceinline__ i16x4 lds_read_tr(const bf16* p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p));
@@ -112,17 +163,16 @@ __device__ __forceinline__ float other_half(float x) {
     return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
 }
 
-template <int D>
+template <int D, bool VT>
 __global__ __launch_bounds__(THREADS, 1) void step_bf16_kernel(const StepArgs a) {
     using TL = Tiles<D>;
-    // Two stage buffers as four distinct arrays: the compiler can then tell
-    // the direct-to-LDS loads into one stage from the reads of the other and
-    // does not wait for the former before the latter.
-    __shared__ bf16 k_buf0[TL::ELEMS], k_buf1[TL::ELEMS];
-    __shared__ bf16 v_buf0[TL::ELEMS], v_buf1[TL::ELEMS];
+    // Three stage buffers as six distinct arrays: the compiler can then tell
+    // the direct-to-LDS loads into one stage from the reads of another.
+    __shared__ bf16 k_buf0[TL::ELEMS], k_buf1[TL::ELEMS], k_buf2[TL::ELEMS];
+    __shared__ bf16 v_buf0[TL::ELEMS], v_buf1[TL::ELEMS], v_buf2[TL::ELEMS];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int grp = wave >> 2;
+    const int grp = wave >> 2, gwave = wave & 3;
     const int half = lane >> 5, col = lane & 31;
 
     // Workgroup -> (pair, head, q-tile).  Consecutive workgroup ids go to
@@ -170,11 +220,23 @@ __global__ __launch_bounds__(THREADS, 1) void step_bf16_kernel(const StepArgs a)
         atomicAdd(&a.stats[2], (unsigned long long)n_part);
     }
 
-    // This lane's query row.
+    // This lane's query row, and the keys of the block it may see as one
+    // index range [w_lo, w_hi) (keys sit at k_pos0 + w * pos_stride):
+    //  causal: w * pos_stride <= t - k_pos0;  doc-causal (pos_stride 1) also
+    //  w >= doc_start(t) - k_pos0;  and always w < Bk.
     const int64_t u = u0 + wave * 32 + col;
     const bool row_ok = u < a.Bq;
-    const int64_t t = pd.q_pos0 + u * a.pos_stride;
-    const int64_t ds = (a.mask == kMaskDoc && row_ok) ? doc_start(a.cu, a.n_docs, t) : 0;
+    int w_lo = 0, w_hi = (int)a.Bk;
+    if (row_ok && a.mask != kMaskNone) {
+        const int64_t t = pd.q_pos0 + u * a.pos_stride;
+        const int64_t lim = t - pd.k_pos0;
+        const int64_t last = lim < 0 ? -1 : (a.pos_stride == 1 ? lim : lim / a.pos_stride);
+        if (last + 1 < w_hi) w_hi = (int)(last + 1);
+        if (a.mask == kMaskDoc) {
+            const int64_t lo = doc_start(a.cu, a.n_docs, t) - pd.k_pos0;
+            if (lo > 0) w_lo = lo > a.Bk ? (int)a.Bk : (int)lo;
+        }
+    }
 
     // Q^T as the B operand: lane holds q[row][16*kc + 8*half .. +7].
     bf16x8 qf[D / 16];
@@ -215,55 +277,74 @@ __global__ __launch_bounds__(THREADS, 1) void step_bf16_kernel(const StepArgs a)
         }
     }
 
+    // ---- stage loads ----
     const bf16* kbase = (const bf16*)a.k + pd.k_off + kvh * a.k_head_stride;
-    const bf16* vbase = (const bf16*)a.v + pd.v_off + kvh * a.v_head_stride;
-    const uint32_t k_rs_bytes = (uint32_t)(a.k_row_stride * 2), v_rs_bytes = (uint32_t)(a.v_row_stride * 2);
+    const bf16* vbase = VT ? (const bf16*)a.vt + pd.vt_off + kvh * a.vt_head_stride
+                           : (const bf16*)a.v + pd.v_off + kvh * a.v_head_stride;
+    const uint32_t k_rs_bytes = (uint32_t)(a.k_row_stride * 2);
+    const uint32_t v_rs_bytes = (uint32_t)((VT ? a.vt_row_stride : a.v_row_stride) * 2);
     auto last_row = [&](int kt) __attribute__((always_inline)) {
         const int64_t rem = a.Bk - 1 - (int64_t)kt * BK;
         return rem < BK ? (int)rem : BK;
     };
     auto issue_k = [&](int kt, bf16* dst) __attribute__((always_inline)) {
-        issue_tile<D, false>(dst, kbase + (int64_t)kt * BK * a.k_row_stride, k_rs_bytes, last_row(kt), wave & 3);
+        issue_tile<D, 0>(dst, kbase + (int64_t)kt * BK * a.k_row_stride, k_rs_bytes, last_row(kt), gwave);
     };
     auto issue_v = [&](int kt, bf16* dst) __attribute__((always_inline)) {
-        issue_tile<D, true>(dst, vbase + (int64_t)kt * BK * a.v_row_stride, v_rs_bytes, last_row(kt), wave & 3);
+        if (VT) issue_tile<D, 2>(dst, vbase + (int64_t)kt * BK, v_rs_bytes, 0, gwave);
+        else issue_tile<D, 1>(dst, vbase + (int64_t)kt * BK * a.v_row_stride, v_rs_bytes, last_row(kt), gwave);
     };
 
-    // Per-lane LDS element offsets of the MFMA operands.
-    //  K (A operand of S^T): key row col (+32 kb), logical chunk 2 kc + half
-    //  = 2 (kc ^ kx) + half_x in swizzled slots.
-    const int kx = TL::swz_k(col) >> 1, half_x = half ^ (TL::swz_k(col) & 1);
-    //  V (A operand of O^T, transposing read): key row 4 half + j/4 (+ 32 kb + 16 cp + 8 second),
-    //  dims 32 db + 16 g + 4 (j % 4) .. +3, i.e. chunk 4 db + 2 g + (j % 4) / 2, half-chunk j % 2.
-    const int j16 = lane & 15, g16 = (lane >> 4) & 1;
-    const int vrow = 4 * half + (j16 >> 2);
-    int v_off[D / 32];
-#pragma unroll
-    for (int db = 0; db < D / 32; db++)
-        v_off[db] = vrow * D + 8 * ((4 * db + 2 * g16 + ((j16 & 3) >> 1)) ^ TL::swz_v(vrow)) + 4 * (j16 & 1);
-
-    f32x16 s[2];        // S^T of the current tile (M phase -> V phase)
-    bf16x8 pb[2][2];    // P of the previous tile  (V phase -> next M phase)
+    f32x16 s[2];        // S^T of the current tile, 32 keys each (M phase -> V phase)
+    bf16x8 pb[2][2];    // P of the previous tile, one bf16x8 per 16-key chunk (V phase -> next M phase)
 #pragma unroll
     for (int kb = 0; kb < 2; kb++) pb[kb][0] = pb[kb][1] = bf16x8{};
 
     // ---- M phase: O^T += V^T P^T (previous tile) and S^T = K Q^T (this tile) ----
     // One PV and one S MFMA per step, on independent accumulators, operands
     // read AHEAD steps early.
-    constexpr int NS = 2 * (D / 16);  // S MFMAs: n = 2 kc + kb
+    //  K operand n = 2 kc + kb: key row 32 kb + col, logical chunk 2 kc + half
+    //    = 2 (kc ^ kx) + half_x in swizzled slots.
+    //  V operand n = (D/32) q + db (16-key chunk q, dims 32 db + col):
+    //    V^T tile: row 32 db + col, logical chunk 2 q + half (the packed V^T
+    //    stores each 16-key group in S^T register order), slot ^ swz_vt(col).
+    //    V tile: transposing reads at key rows 16 q + 4 half + j/4 (+8), dims
+    //    32 db + 16 g + 4 (j % 4) (chunk 4 db + 2 g + (j%4)/2, half-chunk j%2).
+    constexpr int NS = 2 * (D / 16);  // S MFMAs
     constexpr int AHEAD = 3;
     static_assert(NS == 4 * (D / 32), "one PV MFMA per S MFMA");
+    // Lane offsets (elements) of the operand reads; the 32-key half kb of K
+    // and the 32-dim block db of V^T are constant offsets on top.
+    int k_off[D / 16];
+    {
+        const int kx = TL::swz_k(col) >> 1, half_x = half ^ (TL::swz_k(col) & 1);
+#pragma unroll
+        for (int kc = 0; kc < D / 16; kc++) k_off[kc] = col * D + 8 * half_x + 16 * (kc ^ kx);
+    }
+    int v_off[4];
+    if (VT) {
+#pragma unroll
+        for (int q = 0; q < 4; q++) v_off[q] = col * BK + 8 * ((2 * q + half) ^ TL::swz_vt(col));
+    } else {
+        const int j16 = lane & 15, g16 = (lane >> 4) & 1, vrow = 4 * half + (j16 >> 2);
+#pragma unroll
+        for (int db = 0; db < D / 32; db++)
+            v_off[db] = vrow * D + 8 * ((4 * db + 2 * g16 + ((j16 & 3) >> 1)) ^ TL::swz_v(vrow)) + 4 * (j16 & 1);
+    }
     auto m_phase = [&](const bf16* ks, const bf16* vs) __attribute__((always_inline)) {
         auto k_frag = [&](int n) __attribute__((always_inline)) {
-            const int kc = n >> 1;
-            return *(const bf16x8*)(ks + 32 * D * (n & 1) + col * D + 8 * half_x + 16 * (kc ^ kx));
+            return *(const bf16x8*)(ks + k_off[n >> 1] + 32 * D * (n & 1));
         };
-        auto v_frag = [&](int n) __attribute__((always_inline)) {  // n = (D/32) q + db, q = 2 kb + cp
+        auto v_frag = [&](int n) __attribute__((always_inline)) {
             const int q = n / (D / 32), db = n % (D / 32);
-            const bf16* p1 = vs + (32 * (q >> 1) + 16 * (q & 1)) * D + v_off[db];
-            const i16x4 r1 = lds_read_tr(p1);
-            const i16x4 r2 = lds_read_tr(p1 + 8 * D);
-            return __builtin_bit_cast(bf16x8, __builtin_shufflevector(r1, r2, 0, 1, 2, 3, 4, 5, 6, 7));
+            if (VT) {
+                return *(const bf16x8*)(vs + v_off[q] + 32 * db * BK);
+            } else {
+                const bf16* p1 = vs + v_off[db] + 16 * q * D;
+                const i16x4 r1 = lds_read_tr(p1);
+                const i16x4 r2 = lds_read_tr(p1 + 8 * D);
+                return __builtin_bit_cast(bf16x8, __builtin_shufflevector(r1, r2, 0, 1, 2, 3, 4, 5, 6, 7));
+            }
         };
         bf16x8 ka[AHEAD], va[AHEAD];
 #pragma unroll
@@ -285,38 +366,32 @@ __global__ __launch_bounds__(THREADS, 1) void step_bf16_kernel(const StepArgs a)
 
     // ---- V phase: mask, max, online-softmax update, P ----
     auto v_phase = [&](int kt) __attribute__((always_inline)) {
-        const Cls c = tile_cls(kt);
+        const Cls cls = tile_cls(kt);
         const bool ragged = (int64_t)(kt + 1) * BK > a.Bk;
-        if (c == kPartial || ragged) {
-            // Key x of the tile (0..BK-1) sits at position tk0 + x * pos_stride; turn the
-            // row's bounds into bounds on x once, then compare small integers.
-            const int64_t w0 = (int64_t)kt * BK;
-            const int64_t tk0 = pd.k_pos0 + w0 * a.pos_stride;
-            int x_end = (int)(a.Bk - w0 < BK ? a.Bk - w0 : BK);  // keys x < x_end exist
-            int x_lo = 0;
-            if (a.mask != kMaskNone) {
-                // tk <= t  <=>  x <= floor((t - tk0) / pos_stride)
-                const int64_t lim = t - tk0;
-                const int64_t xm = lim < 0 ? -1 : (a.pos_stride == 1 ? lim : lim / a.pos_stride);
-                if (xm + 1 < x_end) x_end = (int)(xm + 1);
-            }
-            if (a.mask == kMaskDoc) {
-                const int64_t lo = ds - tk0;  // pos_stride is 1 here
-                x_lo = lo <= 0 ? 0 : (lo > BK ? BK : (int)lo);
-            }
+        if (cls == kPartial || ragged) {
+            // Register i of s[kb] holds tile key 32 kb + 8 (i/4) + 4 half + i%4;
+            // the allowed keys shifted by -4 half leave a constant to compare.
+            const int x_lo = w_lo - kt * BK - 4 * half, x_hi = w_hi - kt * BK - 4 * half;
 #pragma unroll
             for (int kb = 0; kb < 2; kb++)
 #pragma unroll
                 for (int i = 0; i < 16; i++) {
-                    const int x = 32 * kb + 8 * (i / 4) + 4 * half + (i % 4);
-                    if (x < x_lo || x >= x_end) s[kb][i] = -INFINITY;
+                    const int x = 32 * kb + 8 * (i / 4) + (i % 4);
+                    if (x < x_lo || x >= x_hi) s[kb][i] = -INFINITY;
                 }
         }
-        float mt = -INFINITY;
+        // Row maximum: four independent chains of three-way maxima.
+        float m4[4];
 #pragma unroll
-        for (int kb = 0; kb < 2; kb++)
-#pragma unroll
-            for (int i = 0; i < 16; i++) mt = fmaxf(mt, s[kb][i]);
+        for (int c = 0; c < 4; c++) {
+            const f32x16& sv = s[c / 2];
+            const int i = 8 * (c % 2);
+            float t = fmaxf(fmaxf(sv[i], sv[i + 1]), sv[i + 2]);
+            t = fmaxf(fmaxf(t, sv[i + 3]), sv[i + 4]);
+            t = fmaxf(fmaxf(t, sv[i + 5]), sv[i + 6]);
+            m4[c] = fmaxf(t, sv[i + 7]);
+        }
+        float mt = fmaxf(fmaxf(fmaxf(m4[0], m4[1]), m4[2]), m4[3]);
         mt = fmaxf(mt, other_half(mt));
         const float mnew = fmaxf(mx, mt);
         const float mnc = mnew * a.c2;
@@ -330,60 +405,103 @@ __global__ __launch_bounds__(THREADS, 1) void step_bf16_kernel(const StepArgs a)
         }
         mx = mnew;
         const float mref = mrc == -INFINITY ? 0.f : mrc;
+        float ps[4];
 #pragma unroll
         for (int kb = 0; kb < 2; kb++)
 #pragma unroll
             for (int i = 0; i < 16; i++) {
                 const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][i], a.c2, -mref));
-                lsum += p;
+                ps[i % 4] = (kb == 0 && i < 4) ? p : ps[i % 4] + p;
                 pb[kb][i / 8][i % 8] = (bf16)p;
             }
+        lsum += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+#pragma unroll
+        for (int kb = 0; kb < 2; kb++) {
+            pin(pb[kb][0]);
+            pin(pb[kb][1]);
+        }
+        pin(lsum);
     };
 
     // ---- phase schedule ----
     // Every wave runs the same sequence: for j = 0 .. nT, M_j (PV of tile j-1,
-    // S of tile j, both read from stage buffer j % 2) then V_j (softmax of tile
+    // S of tile j, both read from stage buffer j % 3) then V_j (softmax of tile
     // j), with a barrier after each.  Group G1 runs one phase behind G0 (one
     // extra barrier at the start, G0 one at the end), so on every SIMD one
     // wave is in an M phase while the other is in a V phase.  Workgroup phase
     // 2j is G0's M_j and G1's V_{j-1}; phase 2j+1 is G0's V_j and G1's M_j.
-    // Stage j is read during phases 2j and 2j+1.  Stage j+1 is loaded by G1
-    // alone, issued at the start of phase 2j (G1's V phase, so no wave ever
-    // stalls on the memory queue at the start of an M phase) into the buffer
-    // stage j-1 used (read last in phase 2j-1), and G1 waits for it at the end
-    // of phase 2j+1.  M_0 multiplies P = 0 by a zeroed V buffer and M_nT
-    // computes an S that is discarded, so every M phase has the same shape.
-    auto iteration = [&](int j, auto parity) __attribute__((always_inline)) {
-        constexpr int P = decltype(parity)::value;
-        bf16* const kc = P ? k_buf1 : k_buf0;  // stage j's buffers
-        bf16* const vc = P ? v_buf1 : v_buf0;
+    // Stage j is read in phases 2j and 2j+1.  Loads are issued at the start
+    // of V phases, so that no wave queues behind them in an M phase, and the
+    // two groups share them:
+    //   G0 issues K_{j+2} in V_j (phase 2j+1, into the buffer stage j-1 left
+    //      at phase 2j-1) and waits for it at the end of V_{j+1} (phase 2j+3);
+    //   G1 issues V_{j+2} (stage j+3) in V_j (phase 2j+2, into the buffer
+    //      stage j left at phase 2j+1) and waits for it at the end of V_{j+1}
+    //      (phase 2j+4);
+    // so every load has two phases to land.  M_0 multiplies P = 0 by
+    // a zeroed V buffer and M_nT computes an S that is discarded, so every M
+    // phase has the same shape.
+    constexpr int NL = TL::LOADS;
+    auto iteration = [&](int j, auto slot) __attribute__((always_inline)) {
+        constexpr int B = decltype(slot)::value;  // j % 3
+        bf16* const kc = B == 0 ? k_buf0 : (B == 1 ? k_buf1 : k_buf2);  // stage j
+        bf16* const vc = B == 0 ? v_buf0 : (B == 1 ? v_buf1 : v_buf2);
+        bf16* const k_next2 = B == 0 ? k_buf2 : (B == 1 ? k_buf0 : k_buf1);  // stage j+2 (= j-1)
+        __builtin_amdgcn_s_setprio(2);
         m_phase(kc, vc);
-        if (grp == 1) wait_tile_loads();
-        __syncthreads();
-        if (grp == 1) {  // stage j + 2 -> this buffer (G0 finished reading it one barrier ago)
-            if (j + 2 < nT) issue_k(kt_lo + j + 2, kc);
-            if (j + 1 < nT) issue_v(kt_lo + j + 1, vc);
+        phase_barrier();
+        __builtin_amdgcn_s_setprio(0);
+        // Past the last tile the batch re-reads the last tile into a buffer
+        // no later phase reads: every V phase issues exactly one batch.
+        const int kt_pre = kt_lo + (j + 2 < nT ? j + 2 : nT - 1);
+        // (The two distinct empty asm statements stop the compiler from
+        // merging the last load of both branches into one whose LDS target
+        // it can no longer tell apart from the buffers read later, which
+        // would make it wait for that load before every LDS read.)
+        if (grp == 0) {
+            issue_k(kt_pre, k_next2);
+            __asm__ volatile("; K stage issued" ::: "memory");
+        } else {
+            issue_v(kt_pre, vc);
+            __asm__ volatile("; V stage issued" ::: "memory");
         }
         if (j < nT) v_phase(kt_lo + j);
-        __syncthreads();
+        // Everything but this phase's batch has landed: for G0 that is
+        // K_{j+1} (stage j+1, read from phase 2j+2 on), for G1 V_{j+1}
+        // (stage j+2, read from phase 2j+4 on).  Both groups run the same
+        // wait on the same number of loads, which keeps the compiler's
+        // (path-blind) bookkeeping of outstanding loads exact as well.
+        wait_loads_but<NL>();
+        phase_barrier();
     };
 
     if (nT > 0) {
-        // Stage 0 (K of the first tile) and a zero V buffer for M_0.
-        if (grp == 1) issue_k(kt_lo, k_buf0);
-        for (int i = threadIdx.x; i < TL::ELEMS / 8; i += THREADS) ((bf16x8*)v_buf0)[i] = bf16x8{};
-        wait_tile_loads();
-        __syncthreads();
-        if (grp == 1) {  // stage 1, then G1's one-phase offset
-            if (1 < nT) issue_k(kt_lo + 1, k_buf1);
+        // Q and the state are in registers before any stage load is issued
+        // (the waits below then count stage loads only).
+        wait_loads_but<0>();
+        // Stages 0-2: K_0, K_1 by G0; V_0, V_1 by G1; stage 0's V (tile -1)
+        // is a zeroed buffer.
+        const int kt1 = kt_lo + (nT > 1 ? 1 : 0);
+        if (grp == 0) {
+            issue_k(kt_lo, k_buf0);
+            issue_k(kt1, k_buf1);
+            __asm__ volatile("; K stages issued" ::: "memory");
+        } else {
             issue_v(kt_lo, v_buf1);
-            __syncthreads();
+            issue_v(kt1, v_buf2);
+            __asm__ volatile("; V stages issued" ::: "memory");
         }
-        for (int j = 0; j <= nT; j += 2) {
+        for (int i = threadIdx.x; i < TL::ELEMS / 8; i += THREADS) ((bf16x8*)v_buf0)[i] = bf16x8{};
+        wait_loads_but<NL>();  // K_0 (G0), V_0 (G1)
+        phase_barrier();
+        if (grp == 1) phase_barrier();  // G1's one-phase offset
+        for (int j = 0; j <= nT; j += 3) {
             iteration(j, ic<0>{});
             if (j + 1 <= nT) iteration(j + 1, ic<1>{});
+            if (j + 2 <= nT) iteration(j + 2, ic<2>{});
         }
-        if (grp == 0) __syncthreads();
+        if (grp == 0) phase_barrier();
+        wait_loads_but<0>();  // no load may land in LDS after the workgroup ends
     }
 
     // Both halves of a row combine their denominators; then rescale to the
@@ -434,9 +552,16 @@ __global__ __launch_bounds__(THREADS, 1) void step_bf16_kernel(const StepArgs a)
 hipError_t launch_step_bf16(const StepArgs& a, hipStream_t stream) {
     const int64_t nwg = (int64_t)a.n_qtiles * a.Hq * a.n_pairs;
     if (nwg == 0) return hipSuccess;
-    if (a.d == 128) step_bf16_kernel<128><<<dim3((unsigned)nwg), dim3(THREADS), 0, stream>>>(a);
-    else if (a.d == 64) step_bf16_kernel<64><<<dim3((unsigned)nwg), dim3(THREADS), 0, stream>>>(a);
-    else return hipErrorInvalidValue;
+    const dim3 grid((unsigned)nwg), block(THREADS);
+    if (a.vt) {
+        if (a.d == 128) step_bf16_kernel<128, true><<<grid, block, 0, stream>>>(a);
+        else if (a.d == 64) step_bf16_kernel<64, true><<<grid, block, 0, stream>>>(a);
+        else return hipErrorInvalidValue;
+    } else {
+        if (a.d == 128) step_bf16_kernel<128, false><<<grid, block, 0, stream>>>(a);
+        else if (a.d == 64) step_bf16_kernel<64, false><<<grid, block, 0, stream>>>(a);
+        else return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 
