@@ -96,6 +96,8 @@ struct Workspace {
     float* m = nullptr;
     float* l = nullptr;
     char* vt = nullptr;     // packed V^T of all blocks (bf16 path): [N][Hkv][d][Bp]
+    RingWork* works = nullptr;    // one-launch ring forward (bf16): N works
+    RingEntry* entries = nullptr; //   and up to N x N chain entries
     char* kv = nullptr;     // prefetch double buffers: K [2][N][B][Hkv][d], then V (f32) or V^T (bf16)
     size_t k_half = 0;      // bytes of the K double buffer
     size_t total = 0;
@@ -119,7 +121,11 @@ Workspace carve(void* base, int64_t T, int64_t N, int64_t Hq, int64_t Hkv, int64
     w.O = (float*)take(sizeof(float) * (size_t)(T * Hq * d));
     w.m = (float*)take(sizeof(float) * (size_t)(T * Hq));
     w.l = (float*)take(sizeof(float) * (size_t)(T * Hq));
-    if (dt == RA_BF16) w.vt = take(vt_bytes);
+    if (dt == RA_BF16) {
+        w.vt = take(vt_bytes);
+        w.works = (RingWork*)take(sizeof(RingWork) * (size_t)N);
+        w.entries = (RingEntry*)take(sizeof(RingEntry) * (size_t)N * (size_t)N);
+    }
     if (prefetch) {
         w.k_half = 2 * (size_t)T * Hkv * d * es;
         const size_t v_half = dt == RA_BF16 ? 2 * vt_bytes : w.k_half;
@@ -395,7 +401,67 @@ ra_status ring_attn_forward(const ra_tensor* q, const ra_tensor* k, const ra_ten
                       hipSuccess)
         return RA_E_HIP;
 
-    for (int64_t s = 0; s < r.passes; s++) {
+    // ---- bf16 without the side-stream prefetch: the whole ring in one launch ----
+    // Each device's visited (non-skipped) blocks in ring order form its
+    // chain; one workgroup per (device, head, q-tile) runs the chain with
+    // the state in registers and finalises at its end.
+    bool ring_done = false;
+    if (use_vt && !pf) {
+        std::vector<std::vector<int32_t>> chain((size_t)N);
+        for (int64_t s = 0; s < r.passes; s++)
+            for (const StepPair& sp : plan.steps[s]) chain[sp.i].push_back(sp.j);
+        size_t longest = 0;
+        for (const auto& c : chain) longest = std::max(longest, c.size());
+        if (longest <= (size_t)kMaxRingChain && n_qtiles * Hq * N <= INT32_MAX) {
+            std::vector<int32_t> order;
+            for (int64_t i = 0; i < N; i++)
+                if (!chain[i].empty()) order.push_back((int32_t)i);
+            // heaviest first: longest chains, then later devices (more keys under causal masks)
+            std::stable_sort(order.begin(), order.end(), [&](int32_t x, int32_t y) {
+                return chain[x].size() != chain[y].size() ? chain[x].size() > chain[y].size() : x > y;
+            });
+            std::vector<RingWork> works;
+            std::vector<RingEntry> entries;
+            for (int32_t i : order) {
+                RingWork w;
+                w.q_off = row_off(i, q->stride_tok);
+                w.q_pos0 = striped ? i : i * B;
+                w.out_off = striped ? i * out_tok : i * B * out_tok;
+                w.lse_off = striped ? i : i * B;
+                w.first = (int32_t)entries.size();
+                w.count = (int32_t)chain[i].size();
+                works.push_back(w);
+                for (int32_t j : chain[i]) {
+                    RingEntry e;
+                    e.k_off = row_off(j, k->stride_tok);
+                    e.vt_off = (int64_t)j * vt_blk;
+                    e.k_pos0 = striped ? j : j * B;
+                    entries.push_back(e);
+                }
+            }
+            if (!works.empty()) {
+                if (hipMemcpyAsync(ws.works, works.data(), sizeof(RingWork) * works.size(), hipMemcpyHostToDevice,
+                                   st) != hipSuccess ||
+                    hipMemcpyAsync(ws.entries, entries.data(), sizeof(RingEntry) * entries.size(),
+                                   hipMemcpyHostToDevice, st) != hipSuccess)
+                    return RA_E_HIP;
+                StepArgs a = base;
+                a.k = k->data;
+                a.k_row_stride = (striped ? N : 1) * k->stride_tok;
+                a.k_head_stride = k->stride_head;
+                a.vt = ws.vt;
+                a.vt_row_stride = Bp;
+                a.vt_head_stride = d * Bp;
+                a.works = ws.works;
+                a.entries = ws.entries;
+                a.n_pairs = (int32_t)works.size();
+                if (launch(a, q->dtype, st) != hipSuccess) return RA_E_HIP;
+            }
+            ring_done = true;
+        }
+    }
+
+    for (int64_t s = 0; s < (ring_done ? 0 : r.passes); s++) {
         const std::vector<StepPair>& pairs = plan.steps[s];
         const bool use_buf = pf && s > 0;
         const int slot = (int)(s & 1);

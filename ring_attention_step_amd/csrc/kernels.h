@@ -21,6 +21,20 @@ struct PairDesc {
 
 constexpr int kMaxPairs = 16;
 
+// Ring forward in one launch (bf16 path): a workgroup takes one query tile of
+// one head of virtual device i through every key/value block device i visits,
+// in ring order, with the online-softmax state kept in registers throughout.
+struct RingWork {                  // one virtual device (query block)
+    int64_t q_off, q_pos0;         // as in PairDesc
+    int64_t out_off, lse_off;      // finalize targets
+    int32_t first, count;          // its key/value blocks: entries [first, first + count)
+};
+constexpr int kMaxRingChain = 64;  // chain blocks a workgroup can hold (one per lane)
+struct RingEntry {                 // one key/value block of a device's ring, in visiting order
+    int64_t k_off, vt_off;         // element offsets of the block in k and in the packed V^T
+    int64_t k_pos0;                // global position of its local row 0
+};
+
 struct StepArgs {
     const void* q;
     const void* k;
@@ -47,6 +61,10 @@ struct StepArgs {
     unsigned long long* stats;             // nullable, 3 counters
     int32_t n_qtiles, n_pairs;
     PairDesc pairs[kMaxPairs];
+    // Ring forward in one launch: when works is set, the grid covers n_pairs
+    // RingWork entries (pairs[] is unused), each finalised at its end.
+    const RingWork* works;
+    const RingEntry* entries;
 };
 
 // Kernel tile shapes (query rows x key columns per workgroup tile).

@@ -175,73 +175,165 @@ __global__ __launch_bounds__(THREADS, 1) void step_bf16_kernel(const StepArgs a)
     const int grp = wave >> 2, gwave = wave & 3;
     const int half = lane >> 5, col = lane & 31;
 
-    // Workgroup -> (pair, head, q-tile).  Consecutive workgroup ids go to
-    // different XCDs; the remap gives each XCD a contiguous range of
-    // (pair, head) so that its L2 sees few distinct key/value heads.  Within
-    // a range the q-tiles with the most key tiles (causal) start first.
+    // Workgroup -> (work, head, q-tile).  A work is one (query block,
+    // key/value block) pair of a ring step, or, for the ring forward in one
+    // launch, one query block with the chain of key/value blocks its ring
+    // visits (works come heaviest first).  Consecutive workgroup ids go to
+    // the 8 XCDs in turn; (work, head) groups are dealt to the XCDs round
+    // robin, each group's q-tiles staying on one XCD (its L2 then serves
+    // the group's key/value tiles to all of them), so every XCD gets a like
+    // share of heavy and light groups, heavy ones first.  Within a group the
+    // q-tiles with the most key tiles (causal) start first.
     const int nwg = gridDim.x, b = blockIdx.x;
-    const int logical = (nwg % 8 == 0) ? (b % 8) * (nwg / 8) + b / 8 : b;
-    const int qt = a.n_qtiles - 1 - logical % a.n_qtiles;
-    const int rest = logical / a.n_qtiles;
-    const int head = rest % a.Hq;
-    const PairDesc& pd = a.pairs[rest / a.Hq];
+    const int n_groups = nwg / a.n_qtiles;
+    int grp_id, qt;
+    if (n_groups % 8 == 0) {
+        const int r = b / 8;
+        grp_id = b % 8 + 8 * (r / a.n_qtiles);
+        qt = a.n_qtiles - 1 - r % a.n_qtiles;
+    } else {
+        grp_id = b / a.n_qtiles;
+        qt = a.n_qtiles - 1 - b % a.n_qtiles;
+    }
+    const int head = grp_id % a.Hq;
+    const int widx = grp_id / a.Hq;
     const int kvh = head / a.group;
+    const bool ring = a.works != nullptr;
+
+    // This work: its query block, state and chain of key/value blocks.
+    int64_t q_off, q_pos0, out_off, lse_off;
+    float *st_O = nullptr, *st_m = nullptr, *st_l = nullptr;
+    bool load_state = false, finalize = true;
+    int e_first = 0, n_ent = 1;
+    if (ring) {
+        const RingWork& w = a.works[widx];
+        q_off = w.q_off;
+        q_pos0 = w.q_pos0;
+        out_off = w.out_off;
+        lse_off = w.lse_off;
+        e_first = w.first;
+        n_ent = w.count;
+    } else {
+        const PairDesc& pd = a.pairs[widx];
+        q_off = pd.q_off;
+        q_pos0 = pd.q_pos0;
+        out_off = pd.out_off;
+        lse_off = pd.lse_off;
+        st_O = pd.O;
+        st_m = pd.m;
+        st_l = pd.l;
+        load_state = pd.load_state;
+        finalize = pd.finalize;
+    }
+    // Key/value block e of the chain: element offsets of its rows in k and
+    // v (or the packed V^T), and the global position of its row 0.
+    struct Blk {
+        int64_t k_off, v_off, k_pos0;
+    };
+    auto blk = [&](int e) __attribute__((always_inline)) {
+        if (ring) {
+            const RingEntry& r = a.entries[e_first + e];
+            return Blk{r.k_off, r.vt_off, r.k_pos0};
+        }
+        const PairDesc& pd = a.pairs[widx];
+        return Blk{pd.k_off, VT ? pd.vt_off : pd.v_off, pd.k_pos0};
+    };
 
     const int64_t u0 = (int64_t)qt * BQ;
     const int64_t u_last = (a.Bq < u0 + BQ ? a.Bq : u0 + BQ) - 1;
-    const int64_t t_min = pd.q_pos0 + u0 * a.pos_stride, t_max = pd.q_pos0 + u_last * a.pos_stride;
+    const int64_t t_min = q_pos0 + u0 * a.pos_stride, t_max = q_pos0 + u_last * a.pos_stride;
     int64_t ds_min = 0, ds_max = 0;
     if (a.mask == kMaskDoc) {
         ds_min = doc_start(a.cu, a.n_docs, t_min);
         ds_max = doc_start(a.cu, a.n_docs, t_max);
     }
     const int nkt = (int)((a.Bk + BK - 1) / BK);
-    auto tile_cls = [&](int kt) __attribute__((always_inline)) {
+    auto tile_cls = [&](int kt, int64_t k_pos0) __attribute__((always_inline)) {
         const int64_t w0 = (int64_t)kt * BK, w1 = (a.Bk < w0 + BK ? a.Bk : w0 + BK) - 1;
-        return classify(a.mask, t_min, t_max, ds_min, ds_max, pd.k_pos0 + w0 * a.pos_stride,
-                        pd.k_pos0 + w1 * a.pos_stride);
+        return classify(a.mask, t_min, t_max, ds_min, ds_max, k_pos0 + w0 * a.pos_stride,
+                        k_pos0 + w1 * a.pos_stride);
     };
-    // Non-skipped key tiles form one contiguous range (skips are a prefix
-    // under doc-causal and a suffix under causal masks).
-    int kt_lo = 0, kt_hi = nkt - 1;
-    while (kt_lo <= kt_hi && tile_cls(kt_lo) == kSkip) kt_lo++;
-    while (kt_hi >= kt_lo && tile_cls(kt_hi) == kSkip) kt_hi--;
-    const int nT = kt_hi - kt_lo + 1;
-
-    if (a.stats && head == 0 && threadIdx.x == 0) {
-        unsigned n_full = 0, n_part = 0;
-        for (int kt = kt_lo; kt <= kt_hi; kt++) {
-            const Cls c = tile_cls(kt);
-            n_full += c == kFull;
-            n_part += c == kPartial;
-        }
-        atomicAdd(&a.stats[0], (unsigned long long)(nkt - nT));
-        atomicAdd(&a.stats[1], (unsigned long long)n_full);
-        atomicAdd(&a.stats[2], (unsigned long long)n_part);
+    // The chain table, one block per lane (lane e < n_ent holds block e):
+    // its non-skipped key tiles [lo, hi] (one contiguous range: skips are a
+    // prefix under doc-causal and a suffix under causal masks), the fully
+    // visible ones [flo, fhi] (contiguous too, between the partial tiles at
+    // a document start and at the diagonal), offsets and first key position.
+    // A cursor reads a block's entry with readlane when it moves on to it.
+    int cb_lo = 0, cb_hi = -1, cb_flo = 0, cb_fhi = -1;
+    int64_t cb_koff = 0, cb_voff = 0, cb_kpos = 0;
+    unsigned cb_nfull = 0, cb_npart = 0;
+    if (lane < n_ent) {
+        const Blk bl = blk(lane);
+        cb_koff = bl.k_off;
+        cb_voff = bl.v_off;
+        cb_kpos = bl.k_pos0;
+        cb_lo = 0;
+        cb_hi = nkt - 1;
+        while (cb_lo <= cb_hi && tile_cls(cb_lo, cb_kpos) == kSkip) cb_lo++;
+        while (cb_hi >= cb_lo && tile_cls(cb_hi, cb_kpos) == kSkip) cb_hi--;
+        cb_flo = cb_lo;
+        cb_fhi = cb_hi;
+        while (cb_flo <= cb_fhi && tile_cls(cb_flo, cb_kpos) != kFull) cb_flo++;
+        while (cb_fhi >= cb_flo && tile_cls(cb_fhi, cb_kpos) != kFull) cb_fhi--;
+        if (a.stats && head == 0)
+            for (int kt = cb_lo; kt <= cb_hi; kt++) {
+                const Cls c = tile_cls(kt, cb_kpos);
+                cb_nfull += c == kFull;
+                cb_npart += c == kPartial;
+            }
     }
+    auto rl32 = [&](int x, int e) __attribute__((always_inline)) { return __builtin_amdgcn_readlane(x, e); };
+    auto rl64 = [&](int64_t x, int e) __attribute__((always_inline)) {
+        const uint32_t lo32 = __builtin_amdgcn_readlane((int)(uint32_t)x, e);
+        const uint32_t hi32 = __builtin_amdgcn_readlane((int)(uint32_t)((uint64_t)x >> 32), e);
+        return (int64_t)(((uint64_t)hi32 << 32) | lo32);
+    };
+    // Tiles of the whole chain, and the tallies (counted once per q-tile).
+    int nT = 0;
+    {
+        unsigned n_skip = 0, n_full = 0, n_part = 0;
+        for (int e = 0; e < n_ent; e++) {
+            const int cnt = rl32(cb_hi, e) - rl32(cb_lo, e) + 1;
+            nT += cnt;
+            n_skip += nkt - cnt;
+            n_full += rl32((int)cb_nfull, e);
+            n_part += rl32((int)cb_npart, e);
+        }
+        if (a.stats && head == 0 && threadIdx.x == 0) {
+            atomicAdd(&a.stats[0], (unsigned long long)n_skip);
+            atomicAdd(&a.stats[1], (unsigned long long)n_full);
+            atomicAdd(&a.stats[2], (unsigned long long)n_part);
+        }
+    }
+    const bool ragged_block = a.Bk % BK != 0;
 
-    // This lane's query row, and the keys of the block it may see as one
-    // index range [w_lo, w_hi) (keys sit at k_pos0 + w * pos_stride):
+    // This lane's query row, and the keys of the current block it may see as
+    // one index range [w_lo, w_hi) (keys sit at k_pos0 + w * pos_stride):
     //  causal: w * pos_stride <= t - k_pos0;  doc-causal (pos_stride 1) also
     //  w >= doc_start(t) - k_pos0;  and always w < Bk.
     const int64_t u = u0 + wave * 32 + col;
     const bool row_ok = u < a.Bq;
+    const int64_t t_row = q_pos0 + u * a.pos_stride;
+    const int64_t ds_row = (row_ok && a.mask == kMaskDoc) ? doc_start(a.cu, a.n_docs, t_row) : 0;
     int w_lo = 0, w_hi = (int)a.Bk;
-    if (row_ok && a.mask != kMaskNone) {
-        const int64_t t = pd.q_pos0 + u * a.pos_stride;
-        const int64_t lim = t - pd.k_pos0;
-        const int64_t last = lim < 0 ? -1 : (a.pos_stride == 1 ? lim : lim / a.pos_stride);
-        if (last + 1 < w_hi) w_hi = (int)(last + 1);
-        if (a.mask == kMaskDoc) {
-            const int64_t lo = doc_start(a.cu, a.n_docs, t) - pd.k_pos0;
-            if (lo > 0) w_lo = lo > a.Bk ? (int)a.Bk : (int)lo;
+    auto row_bounds = [&](int64_t k_pos0) __attribute__((always_inline)) {
+        w_lo = 0;
+        w_hi = (int)a.Bk;
+        if (row_ok && a.mask != kMaskNone) {
+            const int64_t lim = t_row - k_pos0;
+            const int64_t last = lim < 0 ? -1 : (a.pos_stride == 1 ? lim : lim / a.pos_stride);
+            if (last + 1 < w_hi) w_hi = (int)(last + 1);
+            if (a.mask == kMaskDoc) {
+                const int64_t lo = ds_row - k_pos0;
+                if (lo > 0) w_lo = lo > a.Bk ? (int)a.Bk : (int)lo;
+            }
         }
-    }
+    };
 
     // Q^T as the B operand: lane holds q[row][16*kc + 8*half .. +7].
     bf16x8 qf[D / 16];
     {
-        const bf16* qp = (const bf16*)a.q + pd.q_off + head * a.q_head_stride + u * a.q_row_stride + 8 * half;
+        const bf16* qp = (const bf16*)a.q + q_off + head * a.q_head_stride + u * a.q_row_stride + 8 * half;
 #pragma unroll
         for (int kc = 0; kc < D / 16; kc++) {
             if (row_ok) qf[kc] = *(const bf16x8*)(qp + 16 * kc);
@@ -257,13 +349,13 @@ __global__ __launch_bounds__(THREADS, 1) void step_bf16_kernel(const StepArgs a)
     float mrc = -INFINITY;  // reference (log2 units) the accumulators are relative to
     float lsum = 0.f;       // this lane's share of the denominator
     const int64_t srow = (int64_t)head * a.Bq + u;
-    if (pd.load_state && row_ok) {
-        const float m_in = pd.m[srow];
+    if (load_state && row_ok) {
+        const float m_in = st_m[srow];
         if (m_in != -INFINITY) {
             mx = m_in / a.scale;
             mrc = m_in * 1.4426950408889634f;
-            lsum = half == 0 ? pd.l[srow] : 0.f;
-            const float* Op = pd.O + srow * D + 4 * half;
+            lsum = half == 0 ? st_l[srow] : 0.f;
+            const float* Op = st_O + srow * D + 4 * half;
 #pragma unroll
             for (int db = 0; db < D / 32; db++)
 #pragma unroll
@@ -278,21 +370,45 @@ __global__ __launch_bounds__(THREADS, 1) void step_bf16_kernel(const StepArgs a)
     }
 
     // ---- stage loads ----
-    const bf16* kbase = (const bf16*)a.k + pd.k_off + kvh * a.k_head_stride;
-    const bf16* vbase = VT ? (const bf16*)a.vt + pd.vt_off + kvh * a.vt_head_stride
-                           : (const bf16*)a.v + pd.v_off + kvh * a.v_head_stride;
+    // Two cursors walk the chain's tiles in order: the load cursor two tiles
+    // ahead of the compute cursor.  Both are wave-uniform; moving on to the
+    // next block finds its tile range (and, for the compute cursor, the
+    // rows' key bounds in it).
+    const bf16* const k_all = (const bf16*)a.k + kvh * a.k_head_stride;
+    const bf16* const v_all = VT ? (const bf16*)a.vt + kvh * a.vt_head_stride
+                                 : (const bf16*)a.v + kvh * a.v_head_stride;
+    struct Cursor {
+        int e, kt, hi;  // block of the chain, tile in it, last tile of the block
+    };
+    auto cur_next = [&](Cursor& c) __attribute__((always_inline)) {  // to the next tile, if any
+        int e = c.e, kt = c.kt + 1, hi = c.hi;
+        while (kt > hi && e + 1 < n_ent) {
+            e++;
+            kt = rl32(cb_lo, e);
+            hi = rl32(cb_hi, e);
+        }
+        if (kt <= hi) c = Cursor{e, kt, hi};
+    };
+    Cursor cl{-1, 0, -1};  // load cursor
+    cur_next(cl);
+    Cursor cc = cl;        // compute cursor
+    const int e0 = cc.e < 0 ? 0 : cc.e;
+    int cc_flo = rl32(cb_flo, e0), cc_fhi = rl32(cb_fhi, e0);
+    row_bounds(rl64(cb_kpos, e0));
     const uint32_t k_rs_bytes = (uint32_t)(a.k_row_stride * 2);
     const uint32_t v_rs_bytes = (uint32_t)((VT ? a.vt_row_stride : a.v_row_stride) * 2);
     auto last_row = [&](int kt) __attribute__((always_inline)) {
         const int64_t rem = a.Bk - 1 - (int64_t)kt * BK;
         return rem < BK ? (int)rem : BK;
     };
-    auto issue_k = [&](int kt, bf16* dst) __attribute__((always_inline)) {
-        issue_tile<D, 0>(dst, kbase + (int64_t)kt * BK * a.k_row_stride, k_rs_bytes, last_row(kt), gwave);
+    auto issue_k = [&](const Cursor& c, bf16* dst) __attribute__((always_inline)) {
+        issue_tile<D, 0>(dst, k_all + rl64(cb_koff, c.e) + (int64_t)c.kt * BK * a.k_row_stride, k_rs_bytes,
+                         last_row(c.kt), gwave);
     };
-    auto issue_v = [&](int kt, bf16* dst) __attribute__((always_inline)) {
-        if (VT) issue_tile<D, 2>(dst, vbase + (int64_t)kt * BK, v_rs_bytes, 0, gwave);
-        else issue_tile<D, 1>(dst, vbase + (int64_t)kt * BK * a.v_row_stride, v_rs_bytes, last_row(kt), gwave);
+    auto issue_v = [&](const Cursor& c, bf16* dst) __attribute__((always_inline)) {
+        if (VT) issue_tile<D, 2>(dst, v_all + rl64(cb_voff, c.e) + (int64_t)c.kt * BK, v_rs_bytes, 0, gwave);
+        else issue_tile<D, 1>(dst, v_all + rl64(cb_voff, c.e) + (int64_t)c.kt * BK * a.v_row_stride, v_rs_bytes,
+                              last_row(c.kt), gwave);
     };
 
     f32x16 s[2];        // S^T of the current tile, 32 keys each (M phase -> V phase)
@@ -366,9 +482,8 @@ __global__ __launch_bounds__(THREADS, 1) void step_bf16_kernel(const StepArgs a)
 
     // ---- V phase: mask, max, online-softmax update, P ----
     auto v_phase = [&](int kt) __attribute__((always_inline)) {
-        const Cls cls = tile_cls(kt);
-        const bool ragged = (int64_t)(kt + 1) * BK > a.Bk;
-        if (cls == kPartial || ragged) {
+        const bool full = kt >= cc_flo && kt <= cc_fhi && !(ragged_block && kt == nkt - 1);
+        if (!full) {
             // Register i of s[kb] holds tile key 32 kb + 8 (i/4) + 4 half + i%4;
             // the allowed keys shifted by -4 half leave a constant to compare.
             const int x_lo = w_lo - kt * BK - 4 * half, x_hi = w_hi - kt * BK - 4 * half;
@@ -453,19 +568,30 @@ __global__ __launch_bounds__(THREADS, 1) void step_bf16_kernel(const StepArgs a)
         __builtin_amdgcn_s_setprio(0);
         // Past the last tile the batch re-reads the last tile into a buffer
         // no later phase reads: every V phase issues exactly one batch.
-        const int kt_pre = kt_lo + (j + 2 < nT ? j + 2 : nT - 1);
+        if (j + 2 < nT) cur_next(cl);  // tile j + 2 (past the end: the last tile again)
         // (The two distinct empty asm statements stop the compiler from
         // merging the last load of both branches into one whose LDS target
         // it can no longer tell apart from the buffers read later, which
         // would make it wait for that load before every LDS read.)
         if (grp == 0) {
-            issue_k(kt_pre, k_next2);
+            issue_k(cl, k_next2);
             __asm__ volatile("; K stage issued" ::: "memory");
         } else {
-            issue_v(kt_pre, vc);
+            issue_v(cl, vc);
             __asm__ volatile("; V stage issued" ::: "memory");
         }
-        if (j < nT) v_phase(kt_lo + j);
+        if (j < nT) {
+            v_phase(cc.kt);
+            if (j + 1 < nT) {  // the compute cursor moves on to tile j + 1
+                const int e_was = cc.e;
+                cur_next(cc);
+                if (cc.e != e_was) {
+                    cc_flo = rl32(cb_flo, cc.e);
+                    cc_fhi = rl32(cb_fhi, cc.e);
+                    row_bounds(rl64(cb_kpos, cc.e));
+                }
+            }
+        }
         // Everything but this phase's batch has landed: for G0 that is
         // K_{j+1} (stage j+1, read from phase 2j+2 on), for G1 V_{j+1}
         // (stage j+2, read from phase 2j+4 on).  Both groups run the same
@@ -481,14 +607,15 @@ __global__ __launch_bounds__(THREADS, 1) void step_bf16_kernel(const StepArgs a)
         wait_loads_but<0>();
         // Stages 0-2: K_0, K_1 by G0; V_0, V_1 by G1; stage 0's V (tile -1)
         // is a zeroed buffer.
-        const int kt1 = kt_lo + (nT > 1 ? 1 : 0);
+        const Cursor c0 = cl;
+        if (nT > 1) cur_next(cl);  // tile 1 (or tile 0 again)
         if (grp == 0) {
-            issue_k(kt_lo, k_buf0);
-            issue_k(kt1, k_buf1);
+            issue_k(c0, k_buf0);
+            issue_k(cl, k_buf1);
             __asm__ volatile("; K stages issued" ::: "memory");
         } else {
-            issue_v(kt_lo, v_buf1);
-            issue_v(kt1, v_buf2);
+            issue_v(c0, v_buf1);
+            issue_v(cl, v_buf2);
             __asm__ volatile("; V stages issued" ::: "memory");
         }
         for (int i = threadIdx.x; i < TL::ELEMS / 8; i += THREADS) ((bf16x8*)v_buf0)[i] = bf16x8{};
@@ -515,10 +642,10 @@ __global__ __launch_bounds__(THREADS, 1) void step_bf16_kernel(const StepArgs a)
     }
     if (!row_ok) return;
 
-    if (pd.finalize) {
+    if (finalize) {
         const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
         char* ob = (char*)a.out;
-        const int64_t oe = pd.out_off + u * a.out_row_stride + head * a.out_head_stride + 4 * half;
+        const int64_t oe = out_off + u * a.out_row_stride + head * a.out_head_stride + 4 * half;
 #pragma unroll
         for (int db = 0; db < D / 32; db++)
 #pragma unroll
@@ -530,10 +657,10 @@ __global__ __launch_bounds__(THREADS, 1) void step_bf16_kernel(const StepArgs a)
                 else *(f32x4*)(ob + 4 * e) = f32x4{x0, x1, x2, x3};
             }
         if (half == 0 && a.lse)
-            a.lse[pd.lse_off + head * a.lse_head_stride + u * a.lse_row_stride] =
+            a.lse[lse_off + head * a.lse_head_stride + u * a.lse_row_stride] =
                 ltot > 0.f ? mx * a.scale + logf(ltot) : -INFINITY;
-    } else if (!pd.load_state || nT > 0) {
-        float* Op = pd.O + srow * D + 4 * half;
+    } else if (!load_state || nT > 0) {
+        float* Op = st_O + srow * D + 4 * half;
 #pragma unroll
         for (int db = 0; db < D / 32; db++)
 #pragma unroll
@@ -541,8 +668,8 @@ __global__ __launch_bounds__(THREADS, 1) void step_bf16_kernel(const StepArgs a)
                 *(f32x4*)(Op + 32 * db + 8 * g) =
                     f32x4{o[db][4 * g], o[db][4 * g + 1], o[db][4 * g + 2], o[db][4 * g + 3]};
         if (half == 0) {
-            pd.m[srow] = ltot > 0.f ? mx * a.scale : -INFINITY;
-            pd.l[srow] = ltot;
+            st_m[srow] = ltot > 0.f ? mx * a.scale : -INFINITY;
+            st_l[srow] = ltot;
         }
     }
 }

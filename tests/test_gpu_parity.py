@@ -194,16 +194,31 @@ def test_bf16_packed_qkv_views(ra):
     _check_bf16(out.cpu().double().numpy(), ref["out"], "packed")
 
 
-def test_bf16_prefetch_is_bit_identical(ra):
+def test_bf16_prefetch_matches_one_launch_ring(ra):
+    """The side-stream prefetch path (one launch per ring step, state through
+    HBM between steps) and the default one-launch ring (state in registers)
+    round differently, so both are held to the oracle and to each other."""
     for layout, docs in (("contiguous", None), ("striped", None), ("contiguous", [0, 300, 301, 1024])):
         qkv = W.random_qkv(1024, 4, 2, 128, "bf16", 5, packed=False)
         q, k, v = _dev(*qkv)
-        kw = dict(n_blocks=4, layout=layout, causal=docs is None, cu_seqlens=docs, return_lse=True)
+        kw = dict(n_blocks=4, layout=layout, causal=docs is None, cu_seqlens=docs, return_lse=True,
+                  out_dtype=torch.float32)
         a, la = ra.forward(q, k, v, prefetch=False, **kw)
         b, lb = ra.forward(q, k, v, prefetch=True, **kw)
         torch.cuda.synchronize()
         _say("prefetch", layout, docs is not None)
-        assert torch.equal(a, b) and torch.equal(la, lb)
+        lay = oracle.LAYOUT_STRIPED if layout == "striped" else oracle.LAYOUT_CONTIGUOUS
+        mask = oracle.MASK_CAUSAL if docs is None else oracle.MASK_DOC_CAUSAL
+        ref = oracle.forward(*qkv, n_blocks=4, layout=lay, mask=mask, cu_seqlens=docs)
+        for x, lx in ((a, la), (b, lb)):
+            _check_bf16(x.cpu().double().numpy(), ref["out"], "prefetch")
+            assert np.abs(lx.cpu().double().numpy() - ref["lse"]).max() <= 1e-3
+        # The two paths differ in where P is rounded to bf16 (relative to the
+        # running reference maximum, which a state hand-off resets): they
+        # agree to bf16 level, not bitwise.
+        dif = (a - b).abs()
+        assert dif.max().item() <= 1e-2 and dif.mean().item() <= 5e-4
+        assert (la - lb).abs().max().item() <= 1e-3
 
 
 def _ring_steps(ra, q, k, v, N, B, d, Hq, scale, order, state=None, mask=1):
