@@ -139,18 +139,24 @@ size_t ring_attn_forward_workspace_size(const ra_tensor* q, const ra_tensor* k, 
  * ring blocks (virtual devices) by `layout`; for s = 0 .. min(P, N) - 1 every
  * virtual device i runs one step against block (i - s) mod N, with P =
  * max_ring_passes (GitHub issue: the maximum number of ring passes; one pass
- * is one step).  One kernel launch per step covers every virtual device whose
- * pair is not skipped by the mask; a device's last active step writes its
- * normalised output directly.
+ * is one step).  Pairs the mask skips entirely are not run.  bf16 inputs
+ * without prefetch: one launch runs the whole ring, every query tile of
+ * every virtual device taking its device's steps in ring order with the
+ * state kept on chip, then writing its normalised output.  Otherwise one
+ * launch per step covers every active virtual device, the state goes
+ * through the workspace between steps, and a device's last active step
+ * writes its normalised output.
  *   q [T, Hq, d], k/v [T, Hkv, d] (views allowed, e.g. of a packed qkv).
  *   out: [T, Hq, d] contiguous, out_dtype (RA_F32 always allowed; RA_BF16 for
  *     bf16 inputs).  lse: nullable, [Hq, T] fp32 (natural log).
  *   cu_seqlens_host: HOST pointer, n_docs + 1 entries, needed for DOC_CAUSAL
  *     (contiguous layout only); copied into the workspace.
- *   prefetch != 0: every step's key/value blocks are first copied, on a side
- *     stream, into a double buffer in the workspace while the previous step
- *     computes (the ring's transfer of the next block, modelled on one GPU);
- *     results are bit-identical to prefetch = 0.
+ *   prefetch != 0: one launch per step; every step's key/value blocks are
+ *     first copied, on a side stream, into a double buffer in the workspace
+ *     while the previous step computes (the ring's transfer of the next
+ *     block, modelled on one GPU).  For fp32 inputs the results are
+ *     bit-identical to prefetch = 0; for bf16 they agree to bf16 rounding
+ *     (the state hand-off changes the reference P is rounded against).
  *   stats: nullable HOST pointer; when given the call synchronises `stream`
  *     and fills it.
  */

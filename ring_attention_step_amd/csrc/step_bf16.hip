@@ -39,6 +39,12 @@
 // buffer the next stage is streaming into, so it does not wait for that
 // stream before them.
 //
+// A workgroup runs a chain of (query block, key/value block) pairs: one
+// pair for the step entry point, or, for the ring forward in one launch, a
+// virtual device's visited blocks in ring order, the state staying in
+// registers from the first block to the fused finalize.  The tile pipeline
+// below runs straight across block boundaries.
+//
 // LDS stages: stage j holds K of key tile j and V of key tile j - 1 (the two
 // operands one M phase reads); the two groups read a stage in two
 // consecutive phases while the next two stages stream into the other two
