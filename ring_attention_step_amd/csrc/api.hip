@@ -324,7 +324,8 @@ ra_status ring_attn_forward(const ra_tensor* q, const ra_tensor* k, const ra_ten
     const int64_t row_mult = layout == RA_LAYOUT_STRIPED ? n_blocks : 1;
     if (q->dtype == RA_BF16 && (!bf16_aligned(q) || !bf16_aligned(k) || !bf16_aligned(v) ||
                                 !bf16_tile_addressable(row_mult * k->stride_tok) ||
-                                !bf16_tile_addressable(row_mult * v->stride_tok)))
+                                !bf16_tile_addressable(row_mult * v->stride_tok) ||
+                                vt_padded_keys(T / n_blocks) * 2 * d >= ((int64_t)1 << 31)))  // V^T tile rows
         return RA_E_UNSUPPORTED;
     if (prefetch && (k->stride_head != d || v->stride_head != d)) return RA_E_UNSUPPORTED;
     if (q->dtype == RA_BF16 && (uintptr_t)out % 16) return RA_E_UNSUPPORTED;
