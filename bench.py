@@ -31,7 +31,7 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak (AMD published figure)
 DEFAULT_WORKLOAD = "causal32k_h32_d128_8blk"
-KERNEL = "step_bf16_kernel<128, true>"
+KERNEL = "step_bf16_kernel<128, true, true>"
 KERNEL_SOURCES = ["ring_attention_step_amd/csrc/step_bf16.hip", "ring_attention_step_amd/csrc/plan.h",
                   "ring_attention_step_amd/csrc/kernels.h"]
 

@@ -70,6 +70,7 @@ constexpr int BK = kBf16TileK;   // 64 keys per tile
 constexpr int WAVES = 8;
 constexpr int THREADS = 64 * WAVES;
 constexpr float kLazyRescale = 8.0f;
+constexpr float kTileSumMax = 16384.0f;  // 2^(kLazyRescale + 6)
 static_assert(BK == 64, "the lane layouts below assume 64-key tiles");
 
 template <int I>
@@ -115,26 +116,36 @@ __device__ __forceinline__ void pin(T& x) {
 // group (gwave = 0..3): every lane moves one 16-byte chunk per load and the
 // hardware writes lane l's chunk to dst + 16 l, so each lane picks the global
 // chunk that belongs in its slot.  Addresses are a uniform tile base plus a
-// 32-bit per-lane byte offset.
+// 32-bit per-lane byte offset; tile_chunk_offset is that offset for load n.
 //  K, V (KIND 0, 1): rows are keys, D/8 chunks each, row r at r * rs_bytes;
 //    rows past last_row re-read last_row (their scores are masked to -inf).
 //  V^T (KIND 2): rows are dims (D of them), 8 chunks of 8 keys each, row r at
 //    r * rs_bytes (the packed V^T is zero beyond the block: no clamp needed).
 template <int D, int KIND>
-__device__ __forceinline__ void issue_tile(bf16* dst, const bf16* tile, uint32_t rs_bytes, int last_row, int gwave) {
+__device__ __forceinline__ uint32_t tile_chunk_offset(int lane, int n, uint32_t rs_bytes, int last_row) {
     using T = Tiles<D>;
     constexpr int CPR = KIND == 2 ? 8 : T::CH;  // chunks per row
     constexpr int RPI = 64 / CPR;               // rows per load instruction
-    const int lane = fresh_lane();
-    const int slot = lane % CPR;
+    const int r = RPI * n + lane / CPR;
+    const int swz = KIND == 0 ? T::swz_k(r) : (KIND == 1 ? T::swz_v(r) : T::swz_vt(r));
+    const uint32_t row = (uint32_t)(KIND == 2 ? r : (r < last_row ? r : last_row));
+    return row * rs_bytes + 16u * (uint32_t)((lane % CPR) ^ swz);
+}
+
+template <int D>
+__device__ __forceinline__ void issue_tile(bf16* dst, const char* tile, const uint32_t (&off)[Tiles<D>::LOADS],
+                                           int gwave) {
+    // This wave's part of the tile starts gofs elements into dst.  Derived
+    // afresh at every call (the empty asm hides its origin), each load's LDS
+    // address is one scalar add, rather than a value the compiler keeps in a
+    // register of its own for every buffer and load.
+    int gofs = gwave * (512 * Tiles<D>::LOADS);
+    __asm__ volatile("" : "+s"(gofs));
 #pragma unroll
-    for (int i = 0; i < T::LOADS; i++) {
-        const int n = gwave * T::LOADS + i;  // wave-uniform
-        const int r = RPI * n + lane / CPR;
-        const int swz = KIND == 0 ? T::swz_k(r) : (KIND == 1 ? T::swz_v(r) : T::swz_vt(r));
-        const uint32_t row = (uint32_t)(KIND == 2 ? r : (r < last_row ? r : last_row));
-        const uint32_t off = row * rs_bytes + 16u * (uint32_t)(slot ^ swz);
-        __builtin_amdgcn_global_load_lds((const char*)tile + off, (lds_void*)(dst + 512 * n), 16, 0, 0);
+    for (int i = 0; i < Tiles<D>::LOADS; i++) {
+        uint32_t o = off[i];
+        __asm__ volatile("" : "+v"(o));  // keeps the 32-bit offset form (uniform base + lane offset)
+        __builtin_amdgcn_global_load_lds(tile + o, (lds_void*)(dst + gofs + 512 * i), 16, 0, 0);
     }
 }
 
@@ -169,7 +180,7 @@ __device__ __forceinline__ float other_half(float x) {
     return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
 }
 
-template <int D, bool VT>
+template <int D, bool VT, bool RING>
 __global__ __launch_bounds__(THREADS, 1) void step_bf16_kernel(const StepArgs a) {
     using TL = Tiles<D>;
     // Three stage buffers as six distinct arrays: the compiler can then tell
@@ -204,7 +215,7 @@ __global__ __launch_bounds__(THREADS, 1) void step_bf16_kernel(const StepArgs a)
     const int head = grp_id % a.Hq;
     const int widx = grp_id / a.Hq;
     const int kvh = head / a.group;
-    const bool ring = a.works != nullptr;
+    constexpr bool ring = RING;  // chains from the ring tables (always finalized), else one pair each
 
     // This work: its query block, state and chain of key/value blocks.
     int64_t q_off, q_pos0, out_off, lse_off;
@@ -312,6 +323,7 @@ __global__ __launch_bounds__(THREADS, 1) void step_bf16_kernel(const StepArgs a)
         }
     }
     const bool ragged_block = a.Bk % BK != 0;
+    const int ragged_kt = ragged_block ? nkt - 1 : -1;  // a block's part-filled last tile, if any
 
     // This lane's query row, and the keys of the current block it may see as
     // one index range [w_lo, w_hi) (keys sit at k_pos0 + w * pos_stride):
@@ -403,18 +415,53 @@ __global__ __launch_bounds__(THREADS, 1) void step_bf16_kernel(const StepArgs a)
     row_bounds(rl64(cb_kpos, e0));
     const uint32_t k_rs_bytes = (uint32_t)(a.k_row_stride * 2);
     const uint32_t v_rs_bytes = (uint32_t)((VT ? a.vt_row_stride : a.v_row_stride) * 2);
-    auto last_row = [&](int kt) __attribute__((always_inline)) {
-        const int64_t rem = a.Bk - 1 - (int64_t)kt * BK;
-        return rem < BK ? (int)rem : BK;
+    // This wave's chunk offsets within a stage tile (G0 loads K tiles, G1 V
+    // tiles), kept in registers: issuing a load then takes no vector
+    // arithmetic.  A ragged last tile of a block recomputes them with its rows
+    // clamped to the block's last row.
+    uint32_t ld_off[TL::LOADS];
+    {
+        const int lane0 = threadIdx.x & 63;
+#pragma unroll
+        for (int i = 0; i < TL::LOADS; i++) {
+            const int n = gwave * TL::LOADS + i;
+            ld_off[i] = grp == 0 ? tile_chunk_offset<D, 0>(lane0, n, k_rs_bytes, BK)
+                                 : tile_chunk_offset<D, VT ? 2 : 1>(lane0, n, v_rs_bytes, BK);
+        }
+    }
+    const int lr_ragged = (int)((a.Bk - 1) % BK);
+    // Address of a tile of this wave's group's tensor; the load cursor keeps
+    // the address of its tile and moves it by one tile stride within a block.
+    const char* const ld_all = (const char*)(grp == 0 ? k_all : v_all);
+    const int64_t ld_tab = grp == 0 ? cb_koff : cb_voff;  // lane-distributed block offsets
+    const int64_t ld_stride = grp == 0 ? (int64_t)BK * a.k_row_stride * 2
+                                       : (VT ? (int64_t)BK * 2 : (int64_t)BK * a.v_row_stride * 2);
+    auto ld_addr = [&](const Cursor& c) __attribute__((always_inline)) {
+        return ld_all + rl64(ld_tab, c.e) * 2 + (int64_t)c.kt * ld_stride;
     };
-    auto issue_k = [&](const Cursor& c, bf16* dst) __attribute__((always_inline)) {
-        issue_tile<D, 0>(dst, k_all + rl64(cb_koff, c.e) + (int64_t)c.kt * BK * a.k_row_stride, k_rs_bytes,
-                         last_row(c.kt), gwave);
+    const char* ld_base = ld_addr(cl);
+    auto ld_next = [&]() __attribute__((always_inline)) {  // the load cursor to the next tile (there is one)
+        const int e_was = cl.e;
+        cur_next(cl);
+        if (cl.e != e_was) ld_base = ld_addr(cl);
+        else ld_base += ld_stride;
     };
-    auto issue_v = [&](const Cursor& c, bf16* dst) __attribute__((always_inline)) {
-        if (VT) issue_tile<D, 2>(dst, v_all + rl64(cb_voff, c.e) + (int64_t)c.kt * BK, v_rs_bytes, 0, gwave);
-        else issue_tile<D, 1>(dst, v_all + rl64(cb_voff, c.e) + (int64_t)c.kt * BK * a.v_row_stride, v_rs_bytes,
-                              last_row(c.kt), gwave);
+    auto issue_stage = [&](bf16* dst, const char* base, int kt) __attribute__((always_inline)) {
+        if (!(VT && grp == 1) && kt == ragged_kt) {
+            uint32_t o[TL::LOADS];
+            const int lane1 = fresh_lane();
+#pragma unroll
+            for (int i = 0; i < TL::LOADS; i++) {
+                const int n = gwave * TL::LOADS + i;
+                o[i] = grp == 0 ? tile_chunk_offset<D, 0>(lane1, n, k_rs_bytes, lr_ragged)
+                                : tile_chunk_offset<D, 1>(lane1, n, v_rs_bytes, lr_ragged);
+            }
+            issue_tile<D>(dst, base, o, gwave);
+            __asm__ volatile("; ragged tile issued" ::: "memory");
+        } else {
+            issue_tile<D>(dst, base, ld_off, gwave);
+            __asm__ volatile("; tile issued" ::: "memory");
+        }
     };
 
     f32x16 s[2];        // S^T of the current tile, 32 keys each (M phase -> V phase)
@@ -453,10 +500,10 @@ __global__ __launch_bounds__(THREADS, 1) void step_bf16_kernel(const StepArgs a)
         for (int db = 0; db < D / 32; db++)
             v_off[db] = vrow * D + 8 * ((4 * db + 2 * g16 + ((j16 & 3) >> 1)) ^ TL::swz_v(vrow)) + 4 * (j16 & 1);
     }
+    auto k_frag = [&](const bf16* ks, int n) __attribute__((always_inline)) {
+        return *(const bf16x8*)(ks + k_off[n >> 1] + 32 * D * (n & 1));
+    };
     auto m_phase = [&](const bf16* ks, const bf16* vs) __attribute__((always_inline)) {
-        auto k_frag = [&](int n) __attribute__((always_inline)) {
-            return *(const bf16x8*)(ks + k_off[n >> 1] + 32 * D * (n & 1));
-        };
         auto v_frag = [&](int n) __attribute__((always_inline)) {
             const int q = n / (D / 32), db = n % (D / 32);
             if (VT) {
@@ -472,7 +519,7 @@ __global__ __launch_bounds__(THREADS, 1) void step_bf16_kernel(const StepArgs a)
 #pragma unroll
         for (int i = 0; i < AHEAD; i++) {
             va[i] = v_frag(i);
-            ka[i] = k_frag(i);
+            ka[i] = k_frag(ks, i);
         }
         s[0] = f32x16{};
         s[1] = f32x16{};
@@ -482,60 +529,94 @@ __global__ __launch_bounds__(THREADS, 1) void step_bf16_kernel(const StepArgs a)
             o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i % AHEAD], pb[q >> 1][q & 1], o[db], 0, 0, 0);
             if (i + AHEAD < NS) va[i % AHEAD] = v_frag(i + AHEAD);
             s[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[i % AHEAD], qf[i >> 1], s[i & 1], 0, 0, 0);
-            if (i + AHEAD < NS) ka[i % AHEAD] = k_frag(i + AHEAD);
+            if (i + AHEAD < NS) ka[i % AHEAD] = k_frag(ks, i + AHEAD);
         }
     };
 
     // ---- V phase: mask, max, online-softmax update, P ----
-    auto v_phase = [&](int kt) __attribute__((always_inline)) {
-        const bool full = kt >= cc_flo && kt <= cc_fhi && !(ragged_block && kt == nkt - 1);
-        if (!full) {
-            // Register i of s[kb] holds tile key 32 kb + 8 (i/4) + 4 half + i%4;
-            // the allowed keys shifted by -4 half leave a constant to compare.
-            const int x_lo = w_lo - kt * BK - 4 * half, x_hi = w_hi - kt * BK - 4 * half;
+    // ks is the tile's K stage buffer, intact through this phase (the next
+    // load into it is issued two phases later).
+    auto v_phase = [&](int kt, const bf16* ks) __attribute__((always_inline)) {
+        const bool full = kt >= cc_flo && kt <= cc_fhi && kt != ragged_kt;
+        auto mask = [&]() __attribute__((always_inline)) {
+            if (!full) {
+                // Register i of s[kb] holds tile key 32 kb + 8 (i/4) + 4 half + i%4;
+                // the allowed keys shifted by -4 half leave a constant to compare.
+                const int x_lo = w_lo - kt * BK - 4 * half, x_hi = w_hi - kt * BK - 4 * half;
+#pragma unroll
+                for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+                    for (int i = 0; i < 16; i++) {
+                        const int x = 32 * kb + 8 * (i / 4) + (i % 4);
+                        if (x < x_lo || x >= x_hi) s[kb][i] = -INFINITY;
+                    }
+            }
+        };
+        mask();
+        // Row maximum (four independent chains of three-way maxima) and the
+        // lazy re-reference: the accumulators move to a new reference only
+        // when the maximum has grown by more than kLazyRescale (log2 units).
+        auto rebase = [&]() __attribute__((always_inline)) {
+            float m4[4];
+#pragma unroll
+            for (int c = 0; c < 4; c++) {
+                const f32x16& sv = s[c / 2];
+                const int i = 8 * (c % 2);
+                float t = fmaxf(fmaxf(sv[i], sv[i + 1]), sv[i + 2]);
+                t = fmaxf(fmaxf(t, sv[i + 3]), sv[i + 4]);
+                t = fmaxf(fmaxf(t, sv[i + 5]), sv[i + 6]);
+                m4[c] = fmaxf(t, sv[i + 7]);
+            }
+            float mt = fmaxf(fmaxf(fmaxf(m4[0], m4[1]), m4[2]), m4[3]);
+            mt = fmaxf(mt, other_half(mt));
+            const float mnew = fmaxf(mx, mt);
+            const float mnc = mnew * a.c2;
+            const bool need = mnc > mrc + kLazyRescale;  // false while the row has no key
+            if (__ballot(need)) {
+                const float alpha = need ? __builtin_amdgcn_exp2f(mrc - mnc) : 1.f;
+                if (need) mrc = mnc;
+                lsum *= alpha;
+#pragma unroll
+                for (int db = 0; db < D / 32; db++) o[db] *= alpha;
+            }
+            mx = mnew;
+        };
+        // P = 2^(c2 s - reference) in bf16 for the next PV, and this lane's
+        // (fp32) sum of it.
+        auto probs = [&]() __attribute__((always_inline)) {
+            const float mref = mrc == -INFINITY ? 0.f : mrc;
+            float ps[4];
 #pragma unroll
             for (int kb = 0; kb < 2; kb++)
 #pragma unroll
                 for (int i = 0; i < 16; i++) {
-                    const int x = 32 * kb + 8 * (i / 4) + (i % 4);
-                    if (x < x_lo || x >= x_hi) s[kb][i] = -INFINITY;
+                    const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][i], a.c2, -mref));
+                    ps[i % 4] = (kb == 0 && i < 4) ? p : ps[i % 4] + p;
+                    pb[kb][i / 8][i % 8] = (bf16)p;
                 }
+            return (ps[0] + ps[1]) + (ps[2] + ps[3]);
+        };
+        // A state written back for a later step holds the exact row maximum,
+        // so every tile of a step takes the maximum.  The ring chains end in a
+        // fused finalize, which needs only a reference that keeps P bounded:
+        // P is taken against the current one, and the tile goes back through
+        // the maximum only if a row has no reference yet or its sum of P
+        // exceeds 2^(kLazyRescale + 6) (which bounds every P of the tile; NaN
+        // sums go back as well).  P overwrites S, so going back recomputes S
+        // from the K tile (same MFMA order, same values).
+        if (!RING) rebase();
+        float lt = probs();
+        if (RING && __ballot(!(lt <= kTileSumMax) || mrc == -INFINITY)) {
+            s[0] = f32x16{};
+            s[1] = f32x16{};
+#pragma unroll
+            for (int i = 0; i < NS; i++)
+                s[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_frag(ks, i), qf[i >> 1], s[i & 1], 0, 0, 0);
+            mask();
+            rebase();
+            lt = probs();
         }
-        // Row maximum: four independent chains of three-way maxima.
-        float m4[4];
-#pragma unroll
-        for (int c = 0; c < 4; c++) {
-            const f32x16& sv = s[c / 2];
-            const int i = 8 * (c % 2);
-            float t = fmaxf(fmaxf(sv[i], sv[i + 1]), sv[i + 2]);
-            t = fmaxf(fmaxf(t, sv[i + 3]), sv[i + 4]);
-            t = fmaxf(fmaxf(t, sv[i + 5]), sv[i + 6]);
-            m4[c] = fmaxf(t, sv[i + 7]);
-        }
-        float mt = fmaxf(fmaxf(fmaxf(m4[0], m4[1]), m4[2]), m4[3]);
-        mt = fmaxf(mt, other_half(mt));
-        const float mnew = fmaxf(mx, mt);
-        const float mnc = mnew * a.c2;
-        const bool need = mnc > mrc + kLazyRescale;  // false while the row has no key
-        if (__ballot(need)) {
-            const float alpha = need ? __builtin_amdgcn_exp2f(mrc - mnc) : 1.f;
-            if (need) mrc = mnc;
-            lsum *= alpha;
-#pragma unroll
-            for (int db = 0; db < D / 32; db++) o[db] *= alpha;
-        }
-        mx = mnew;
-        const float mref = mrc == -INFINITY ? 0.f : mrc;
-        float ps[4];
-#pragma unroll
-        for (int kb = 0; kb < 2; kb++)
-#pragma unroll
-            for (int i = 0; i < 16; i++) {
-                const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][i], a.c2, -mref));
-                ps[i % 4] = (kb == 0 && i < 4) ? p : ps[i % 4] + p;
-                pb[kb][i / 8][i % 8] = (bf16)p;
-            }
-        lsum += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+        lsum += lt;
 #pragma unroll
         for (int kb = 0; kb < 2; kb++) {
             pin(pb[kb][0]);
@@ -574,20 +655,20 @@ __global__ __launch_bounds__(THREADS, 1) void step_bf16_kernel(const StepArgs a)
         __builtin_amdgcn_s_setprio(0);
         // Past the last tile the batch re-reads the last tile into a buffer
         // no later phase reads: every V phase issues exactly one batch.
-        if (j + 2 < nT) cur_next(cl);  // tile j + 2 (past the end: the last tile again)
+        if (j + 2 < nT) ld_next();  // tile j + 2 (past the end: the last tile again)
         // (The two distinct empty asm statements stop the compiler from
         // merging the last load of both branches into one whose LDS target
         // it can no longer tell apart from the buffers read later, which
         // would make it wait for that load before every LDS read.)
         if (grp == 0) {
-            issue_k(cl, k_next2);
+            issue_stage(k_next2, ld_base, cl.kt);
             __asm__ volatile("; K stage issued" ::: "memory");
         } else {
-            issue_v(cl, vc);
+            issue_stage(vc, ld_base, cl.kt);
             __asm__ volatile("; V stage issued" ::: "memory");
         }
         if (j < nT) {
-            v_phase(cc.kt);
+            v_phase(cc.kt, kc);
             if (j + 1 < nT) {  // the compute cursor moves on to tile j + 1
                 const int e_was = cc.e;
                 cur_next(cc);
@@ -614,14 +695,15 @@ __global__ __launch_bounds__(THREADS, 1) void step_bf16_kernel(const StepArgs a)
         // Stages 0-2: K_0, K_1 by G0; V_0, V_1 by G1; stage 0's V (tile -1)
         // is a zeroed buffer.
         const Cursor c0 = cl;
-        if (nT > 1) cur_next(cl);  // tile 1 (or tile 0 again)
+        const char* const base0 = ld_base;
+        if (nT > 1) ld_next();  // tile 1 (or tile 0 again)
         if (grp == 0) {
-            issue_k(c0, k_buf0);
-            issue_k(cl, k_buf1);
+            issue_stage(k_buf0, base0, c0.kt);
+            issue_stage(k_buf1, ld_base, cl.kt);
             __asm__ volatile("; K stages issued" ::: "memory");
         } else {
-            issue_v(c0, v_buf1);
-            issue_v(cl, v_buf2);
+            issue_stage(v_buf1, base0, c0.kt);
+            issue_stage(v_buf2, ld_base, cl.kt);
             __asm__ volatile("; V stages issued" ::: "memory");
         }
         for (int i = threadIdx.x; i < TL::ELEMS / 8; i += THREADS) ((bf16x8*)v_buf0)[i] = bf16x8{};
@@ -686,13 +768,18 @@ hipError_t launch_step_bf16(const StepArgs& a, hipStream_t stream) {
     const int64_t nwg = (int64_t)a.n_qtiles * a.Hq * a.n_pairs;
     if (nwg == 0) return hipSuccess;
     const dim3 grid((unsigned)nwg), block(THREADS);
-    if (a.vt) {
-        if (a.d == 128) step_bf16_kernel<128, true><<<grid, block, 0, stream>>>(a);
-        else if (a.d == 64) step_bf16_kernel<64, true><<<grid, block, 0, stream>>>(a);
+    if (a.works) {  // the one-launch ring reads the packed V^T
+        if (!a.vt) return hipErrorInvalidValue;
+        if (a.d == 128) step_bf16_kernel<128, true, true><<<grid, block, 0, stream>>>(a);
+        else if (a.d == 64) step_bf16_kernel<64, true, true><<<grid, block, 0, stream>>>(a);
+        else return hipErrorInvalidValue;
+    } else if (a.vt) {
+        if (a.d == 128) step_bf16_kernel<128, true, false><<<grid, block, 0, stream>>>(a);
+        else if (a.d == 64) step_bf16_kernel<64, true, false><<<grid, block, 0, stream>>>(a);
         else return hipErrorInvalidValue;
     } else {
-        if (a.d == 128) step_bf16_kernel<128, false><<<grid, block, 0, stream>>>(a);
-        else if (a.d == 64) step_bf16_kernel<64, false><<<grid, block, 0, stream>>>(a);
+        if (a.d == 128) step_bf16_kernel<128, false, false><<<grid, block, 0, stream>>>(a);
+        else if (a.d == 64) step_bf16_kernel<64, false, false><<<grid, block, 0, stream>>>(a);
         else return hipErrorInvalidValue;
     }
     return hipGetLastError();
