@@ -185,6 +185,32 @@ def test_bf16_forward_small(ra, case):
     assert torch.equal(out_bf, out.to(torch.bfloat16))
 
 
+def test_bf16_ring_late_score_jumps(ra):
+    """Scores that jump far above a row's running reference late in its chain:
+    under a causal ring, device i visits blocks i, i-1, ..., 0, so keys of
+    block 0 scaled by 8 raise the row maximum by tens of log2 units at the end
+    of every chain, and one key on a query's own direction raises it by
+    hundreds (2^(jump) would overflow fp32).  The one-launch ring takes P
+    against the current reference and must fall back to the maximum (with S
+    recomputed from the K tile) on exactly such tiles."""
+    T, N, H, d = 1024, 4, 2, 128
+    qh, kh, vh = W.random_qkv(T, H, H, d, "bf16", 4242)
+    kf = kh.float()
+    B = T // N
+    kf[:B] *= 8.0
+    kf[B // 2, 0] = (qh[T - 1, 0].float() * 24.0)  # a very large score for the last query row of head 0
+    kh = kf.to(torch.bfloat16)
+    _say("bf16 late score jumps", T, N, H, d)
+    q, k, v = _dev(qh, kh, vh)
+    out, lse = ra.forward(q, k, v, n_blocks=N, causal=True, out_dtype=torch.float32, return_lse=True)
+    ref = oracle.forward(qh, kh, vh, n_blocks=N, mask=oracle.MASK_CAUSAL)
+    assert torch.isfinite(out).all() and torch.isfinite(lse).all()
+    _check_bf16(out.cpu().double().numpy(), ref["out"], "out")
+    lse_err = np.abs(lse.cpu().double().numpy() - ref["lse"])
+    _say("lse max err", float(lse_err.max()), "max |lse|", float(np.abs(ref["lse"]).max()))
+    assert lse_err.max() <= 1e-3
+
+
 def test_bf16_packed_qkv_views(ra):
     T, H, d = 1024, 2, 128
     qh, kh, vh = W.random_qkv(T, H, H, d, "bf16", 77, packed=True)
