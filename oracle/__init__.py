@@ -79,6 +79,10 @@ def _load():
         lib.ro_tile_tallies.restype = ci
         lib.ro_allowed_pairs.argtypes = [i64, i64, ci, ci, i64, vp, i64, vp]
         lib.ro_allowed_pairs.restype = ci
+        lib.ro_backward.argtypes = [vp, vp, vp, vp, ci, ci, i64, i64, i64, i64,
+                                    i64, i64, i64, i64, i64, i64, i64, i64, dbl, ci, ci, i64, i64,
+                                    vp, i64, vp, vp, vp]
+        lib.ro_backward.restype = ci
         _lib = lib
     return _lib
 
@@ -255,3 +259,34 @@ def allowed_pairs(T: int, n_blocks: int, *, layout: int = LAYOUT_CONTIGUOUS, mas
     if rc != 0:
         raise ValueError("oracle rejected the arguments (code %d)" % rc)
     return int(out[0])
+
+
+def backward(q, k, v, dout, *, n_blocks: int, layout: int = LAYOUT_CONTIGUOUS, mask: int = MASK_NONE,
+             max_ring_passes: Optional[int] = None, cu_seqlens=None, scale: Optional[float] = None):
+    """Gradients (dq, dk, dv) of ``forward``'s output with respect to q, k, v
+    for the output gradient ``dout`` ([T, Hq, d], float32 or bfloat16), as
+    float64 arrays [T, Hq, d], [T, Hkv, d], [T, Hkv, d].  The arithmetic is in
+    ``ring_oracle.c`` (``ro_backward``)."""
+    for name, x in (("q", q), ("k", k), ("v", v), ("dout", dout)):
+        _check_view(x, name)
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share a dtype")
+    T, Hq, d = q.shape
+    Hkv = k.shape[1]
+    if k.shape != (T, Hkv, d) or v.shape != (T, Hkv, d) or dout.shape != (T, Hq, d):
+        raise ValueError("k, v must be [T, Hkv, d] and dout [T, Hq, d]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    P = n_blocks if max_ring_passes is None else int(max_ring_passes)
+    cu, n_docs = _cu(cu_seqlens)
+    dq = np.zeros((T, Hq, d))
+    dk = np.zeros((T, Hkv, d))
+    dv = np.zeros((T, Hkv, d))
+    rc = _load().ro_backward(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _dtype_code(q), _dtype_code(dout), T, Hq, Hkv, d,
+        q.stride(0), q.stride(1), k.stride(0), k.stride(1), v.stride(0), v.stride(1),
+        dout.stride(0), dout.stride(1), float(scale), int(mask), int(layout), int(n_blocks), P,
+        _ptr(cu), n_docs, _ptr(dq), _ptr(dk), _ptr(dv))
+    if rc != 0:
+        raise ValueError("oracle rejected the arguments (code %d)" % rc)
+    return dq, dk, dv

@@ -359,3 +359,96 @@ int ro_allowed_pairs(int64_t T, int64_t n_blocks, int layout, int mask, int64_t 
     *pairs = total;
     return RO_OK;
 }
+
+/*
+ * Gradients of the ring forward above with respect to q, k and v, given the
+ * gradient dout of its output (GitHub issue "A ring attention with flash
+ * attention kernel implementation": the backward pass of ring attention
+ * yields the gradients of full attention, and the saved lse is what lets the
+ * backward recompute the probabilities).  For one query row t of head h
+ * (KV head g) with allowed keys A(t), P_j = exp(s_j - M) / L and
+ * out = sum_j P_j v_j, so by the chain rule
+ *   dv_j     += P_j dout
+ *   dP_j      = dout . v_j
+ *   dS_j      = P_j (dP_j - D),   D = sum_j P_j dP_j = dout . out
+ *   dq       += scale sum_j dS_j k_j
+ *   dk_j     += scale dS_j q
+ * (the softmax Jacobian is diag(P) - P P^T).  Rows with no allowed key give
+ * no gradient.  Outputs are fp64 arrays dq [T, Hq, d], dk and dv [T, Hkv, d]
+ * (dense, overwritten); the work is split over KV heads so that the dk / dv
+ * sums of one head stay in one thread.
+ */
+int ro_backward(const void* q, const void* k, const void* v, const void* dout, int dtype, int dout_dtype,
+                int64_t T, int64_t Hq, int64_t Hkv, int64_t d,
+                int64_t q_st, int64_t q_sh, int64_t k_st, int64_t k_sh,
+                int64_t v_st, int64_t v_sh, int64_t o_st, int64_t o_sh,
+                double scale, int mask, int layout, int64_t n_blocks, int64_t max_ring_passes,
+                const int32_t* cu_seqlens, int64_t n_docs,
+                double* dq, double* dk, double* dv) {
+    if (T < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv || d < 1 || n_blocks < 1 || max_ring_passes < 1)
+        return RO_BAD_ARG;
+    if (T % n_blocks) return RO_BAD_ARG;
+    if (mask == RO_MASK_DOC_CAUSAL && (!cu_seqlens || n_docs < 1 || cu_seqlens[0] != 0 ||
+                                       cu_seqlens[n_docs] != T))
+        return RO_BAD_ARG;
+    ro_view qv = {q, dtype, q_st, q_sh}, kv = {k, dtype, k_st, k_sh}, vv = {v, dtype, v_st, v_sh};
+    ro_view ov = {dout, dout_dtype, o_st, o_sh};
+    ro_ring ring = {T, n_blocks, max_ring_passes < n_blocks ? max_ring_passes : n_blocks, layout};
+    int32_t* doc_of = NULL;
+    if (mask == RO_MASK_DOC_CAUSAL) {
+        doc_of = make_doc_of(cu_seqlens, n_docs, T);
+        if (!doc_of) return RO_NO_MEM;
+    }
+    memset(dq, 0, sizeof(double) * (size_t)(T * Hq * d));
+    memset(dk, 0, sizeof(double) * (size_t)(T * Hkv * d));
+    memset(dv, 0, sizeof(double) * (size_t)(T * Hkv * d));
+    int64_t group = Hq / Hkv;
+    int status = RO_OK;
+#pragma omp parallel
+    {
+        int64_t* idx = (int64_t*)malloc(sizeof(int64_t) * (size_t)(T > 0 ? T : 1));
+        double* sbuf = (double*)malloc(sizeof(double) * (size_t)(T > 0 ? T : 1));
+        double* Obuf = (double*)malloc(sizeof(double) * (size_t)d);
+        double* obuf = (double*)malloc(sizeof(double) * (size_t)d);
+        if (!idx || !sbuf || !Obuf || !obuf) {
+#pragma omp atomic write
+            status = RO_NO_MEM;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t g = 0; g < Hkv; g++)
+                for (int64_t h = g * group; h < (g + 1) * group; h++)
+                    for (int64_t t = 0; t < T; t++) {
+                        int64_t n = 0;
+                        for (int64_t tk = 0; tk < T; tk++)
+                            if (mask_allows(mask, doc_of, t, tk) && ring_visible(&ring, t, tk)) idx[n++] = tk;
+                        if (n == 0) continue;
+                        double lse_r, m_r, l_r;
+                        attend_one(&qv, t, h, &kv, &vv, g, d, scale, idx, n, sbuf, obuf, &lse_r, &m_r, &l_r,
+                                   Obuf);
+                        double D = 0.0;
+                        for (int64_t c = 0; c < d; c++) D += view_at(&ov, t, h, c) * obuf[c];
+                        double* dqr = dq + (t * Hq + h) * d;
+                        for (int64_t a = 0; a < n; a++) {
+                            int64_t j = idx[a];
+                            double p = exp(sbuf[a] - m_r) / l_r;
+                            double dp = 0.0;
+                            for (int64_t c = 0; c < d; c++) dp += view_at(&ov, t, h, c) * view_at(&vv, j, g, c);
+                            double ds = p * (dp - D);
+                            double* dkr = dk + (j * Hkv + g) * d;
+                            double* dvr = dv + (j * Hkv + g) * d;
+                            for (int64_t c = 0; c < d; c++) {
+                                dqr[c] += scale * ds * view_at(&kv, j, g, c);
+                                dkr[c] += scale * ds * view_at(&qv, t, h, c);
+                                dvr[c] += p * view_at(&ov, t, h, c);
+                            }
+                        }
+                    }
+        }
+        free(idx);
+        free(sbuf);
+        free(Obuf);
+        free(obuf);
+    }
+    free(doc_of);
+    return status;
+}

@@ -26,6 +26,37 @@ MUTANTS = {
 }
 
 
+# Mistakes in the backward, caught by its own pins.
+MUTANTS_BWD = {
+    "bwd_softmax_jacobian_diagonal_only": ("double ds = p * (dp - D);", "double ds = p * dp;"),
+    "bwd_dk_without_scale": ("dkr[c] += scale * ds * view_at(&qv, t, h, c);", "dkr[c] += ds * view_at(&qv, t, h, c);"),
+    "bwd_dv_uses_dp": ("dvr[c] += p * view_at(&ov, t, h, c);", "dvr[c] += dp * view_at(&ov, t, h, c);"),
+    "bwd_dq_uses_value": ("dqr[c] += scale * ds * view_at(&kv, j, g, c);", "dqr[c] += scale * ds * view_at(&vv, j, g, c);"),
+    "bwd_D_from_state": ("D += view_at(&ov, t, h, c) * obuf[c];", "D += view_at(&ov, t, h, c) * Obuf[c];"),
+}
+
+
+def _build_mutant(tmp_path, name, before, after):
+    src = open(SRC).read()
+    assert before in src, "mutation site vanished: update the mutant table"
+    c_path = tmp_path / (name + ".c")
+    c_path.write_text(src.replace(before, after, 1))
+    so = tmp_path / ("lib_%s.so" % name)
+    subprocess.check_call(["gcc", "-O2", "-fopenmp", "-shared", "-fPIC", "-std=c99", str(c_path),
+                           "-o", str(so), "-lm"])
+    return so
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS_BWD))
+def test_backward_pins_catch_planted_mistake(name, tmp_path):
+    so = _build_mutant(tmp_path, name, *MUTANTS_BWD[name])
+    env = dict(os.environ, RING_ORACLE_LIB=str(so), OMP_NUM_THREADS="4")
+    r = subprocess.run([sys.executable, "-m", "pytest", os.path.join(ROOT, "tests", "test_oracle_backward_pins.py"),
+                        "-q", "-x", "-p", "no:cacheprovider"], env=env, capture_output=True, text=True,
+                       cwd=ROOT, timeout=600)
+    assert r.returncode != 0, "planted mistake %r passed every pin:\n%s" % (name, r.stdout[-2000:])
+
+
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_pins_catch_planted_mistake(name, tmp_path):
     src = open(SRC).read()
