@@ -166,6 +166,38 @@ ra_status ring_attn_forward(const ra_tensor* q, const ra_tensor* k, const ra_ten
                             int32_t n_docs, float scale, int prefetch, void* workspace,
                             size_t workspace_bytes, ra_stats* stats, void* stream);
 
+/* Bytes of device workspace ring_attn_backward needs for these shapes. */
+size_t ring_attn_backward_workspace_size(const ra_tensor* q, int32_t n_blocks, int32_t n_docs);
+
+/*
+ * Gradients of ring_attn_forward's output for a given output gradient
+ * (GitHub issue "A ring attention with flash attention kernel
+ * implementation": the backward pass produces the gradients of full
+ * attention and reuses the forward's lse).  With P_tj = exp(scale q_t.k_j -
+ * lse_t) over the pairs the forward attends (its mask and its
+ * max_ring_passes) and D_t = dout_t . out_t:
+ *   dS_tj = P_tj (dout_t . v_j - D_t),
+ *   dq_t = scale sum_j dS_tj k_j,  dk_j = scale sum_t dS_tj q_t,
+ *   dv_j = sum_t P_tj dout_t
+ * (the chain rule through the row softmax); a grouped kv head sums over the
+ * query heads that read it.  No atomics: the results do not depend on
+ * scheduling.
+ *   q, k, v, n_blocks, layout, mask_mode, max_ring_passes, cu_seqlens_host,
+ *     n_docs, scale: as given to ring_attn_forward.  bf16 inputs with
+ *     head_dim 64 or 128 only (RA_E_UNSUPPORTED otherwise).
+ *   out: the forward's output [T, Hq, d] view, bf16 or f32 (16-byte aligned
+ *     rows); dout: [T, Hq, d] bf16 view.
+ *   lse: the forward's lse, [Hq, T] fp32 (natural log).
+ *   dq [T, Hq, d], dk / dv [T, Hkv, d]: contiguous, 16-byte aligned,
+ *     grad_dtype (fp32 or bf16), every element written.
+ *   workspace: ring_attn_backward_workspace_size bytes, 256-byte aligned.
+ */
+ra_status ring_attn_backward(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v, const ra_tensor* out,
+                             const ra_tensor* dout, const float* lse, void* dq, void* dk, void* dv,
+                             ra_dtype grad_dtype, int32_t n_blocks, ra_layout layout, ra_mask mask_mode,
+                             int32_t max_ring_passes, const int32_t* cu_seqlens_host, int32_t n_docs, float scale,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
 /*
  * Host-only planning (no GPU work): fills `stats` with the tallies and the
  * allowed-pair count that ring_attn_forward would produce for these shapes,

@@ -8,9 +8,9 @@ missing library raises instead of falling back to anything else.
 Entry points (same names as the C ABI):
   ring_attn_step, ring_attn_finalize, ring_attn_merge,
   ring_attn_forward_workspace_size, ring_attn_forward, ring_attn_plan,
-  ring_attn_tile_shape
-plus the conveniences ``forward`` and ``forward_qkvpacked`` that allocate the
-output, lse and workspace with torch.
+  ring_attn_tile_shape, ring_attn_backward_workspace_size, ring_attn_backward
+plus the conveniences ``forward``, ``forward_qkvpacked`` and ``backward`` that
+allocate outputs, lse, gradients and workspace with torch.
 """
 from __future__ import annotations
 
@@ -77,12 +77,16 @@ def load_library():
     lib.ring_attn_forward_workspace_size.restype = _sz
     lib.ring_attn_forward.argtypes = [P(RaTensor), P(RaTensor), P(RaTensor), _vp, _int, _vp, _i32, _int, _int,
                                       _i32, _vp, _i32, _f32, _int, _vp, _sz, P(RaStats), _vp]
+    lib.ring_attn_backward_workspace_size.argtypes = [P(RaTensor), _i32, _i32]
+    lib.ring_attn_backward_workspace_size.restype = _sz
+    lib.ring_attn_backward.argtypes = [P(RaTensor), P(RaTensor), P(RaTensor), P(RaTensor), P(RaTensor), _vp, _vp,
+                                       _vp, _vp, _int, _i32, _int, _int, _i32, _vp, _i32, _f32, _vp, _sz, _vp]
     lib.ring_attn_plan.argtypes = [_i64, _i32, _int, _int, _i32, _vp, _i32, _int, _i64, P(RaStats)]
     lib.ring_attn_tile_shape.argtypes = [_int, _i64, P(_i32), P(_i32)]
     lib.ring_attn_status_string.argtypes = [_int]
     lib.ring_attn_status_string.restype = ctypes.c_char_p
     for fn in ("ring_attn_step", "ring_attn_finalize", "ring_attn_merge", "ring_attn_forward",
-               "ring_attn_plan", "ring_attn_tile_shape"):
+               "ring_attn_plan", "ring_attn_tile_shape", "ring_attn_backward"):
         getattr(lib, fn).restype = _int
     _lib = lib
     return lib
@@ -224,6 +228,40 @@ def ring_attn_forward(q, k, v, out, lse, *, n_blocks: int, layout: int, mask_mod
     return stats.as_dict() if want_stats else None
 
 
+def ring_attn_backward_workspace_size(q, n_blocks: int, n_docs: int = 0) -> int:
+    qt = _tensor(q, "q")
+    return int(load_library().ring_attn_backward_workspace_size(ctypes.byref(qt), int(n_blocks), int(n_docs)))
+
+
+def ring_attn_backward(q, k, v, out, dout, lse, dq, dk, dv, *, n_blocks: int, layout: int, mask_mode: int,
+                       max_ring_passes: int, cu_seqlens_host=None, scale: float, workspace: torch.Tensor,
+                       stream=None):
+    """Gradients of the ring forward: dq [T, Hq, d], dk / dv [T, Hkv, d] (contiguous, fp32 or bf16, written
+    in full) from the forward's out [T, Hq, d] and lse [Hq, T] and the output gradient dout [T, Hq, d]."""
+    qt, kt, vt = _tensor(q, "q"), _tensor(k, "k"), _tensor(v, "v")
+    ot, gt = _tensor(out, "out"), _tensor(dout, "dout")
+    _gpu(lse, "lse")
+    if lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != (q.shape[1], q.shape[0]):
+        raise ValueError("lse must be contiguous float32 [Hq, T]")
+    for x, name, shape in ((dq, "dq", q.shape), (dk, "dk", k.shape), (dv, "dv", k.shape)):
+        _gpu(x, name)
+        if not x.is_contiguous() or tuple(x.shape) != tuple(shape):
+            raise ValueError("%s must be contiguous with shape %s" % (name, tuple(shape)))
+    if not (dq.dtype == dk.dtype == dv.dtype):
+        raise ValueError("dq, dk, dv must share a dtype")
+    _gpu(workspace, "workspace")
+    cu_ptr, n_docs, cu_keep = None, 0, None
+    if cu_seqlens_host is not None:
+        cu_keep = torch.as_tensor(cu_seqlens_host).to(device="cpu", dtype=torch.int32).contiguous()
+        cu_ptr, n_docs = cu_keep.data_ptr(), cu_keep.numel() - 1
+    st = load_library().ring_attn_backward(
+        ctypes.byref(qt), ctypes.byref(kt), ctypes.byref(vt), ctypes.byref(ot), ctypes.byref(gt), lse.data_ptr(),
+        dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), _dtype_code(dq.dtype), int(n_blocks), int(layout),
+        int(mask_mode), int(max_ring_passes), cu_ptr, n_docs, float(scale), workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("ring_attn_backward", st)
+
+
 def ring_attn_plan(T: int, n_blocks: int, *, layout: int, mask_mode: int, max_ring_passes: int,
                    cu_seqlens_host=None, dtype: torch.dtype, head_dim: int) -> dict:
     """Host-only: tallies and allowed-pair count the forward would produce."""
@@ -281,6 +319,35 @@ def forward_qkvpacked(qkv, **kw):
     return forward(qkv[:, 0], qkv[:, 1], qkv[:, 2], **kw)
 
 
+def backward(q, k, v, out, lse, dout, *, n_blocks: int, layout: str = "contiguous", causal: bool = False,
+             cu_seqlens=None, max_ring_passes: Optional[int] = None, scale: Optional[float] = None,
+             grad_dtype: torch.dtype = torch.float32, workspace: Optional[torch.Tensor] = None):
+    """(dq, dk, dv) of ``forward(q, k, v, ...)`` for the output gradient dout, given that call's out and lse
+    (return_lse=True) and the same ring arguments."""
+    T, Hq, d = q.shape
+    mask = RA_MASK_NONE
+    if causal:
+        mask = RA_MASK_CAUSAL
+    if cu_seqlens is not None:
+        mask = RA_MASK_DOC_CAUSAL
+        cu_seqlens = torch.as_tensor(cu_seqlens).to(device="cpu", dtype=torch.int32)
+    n_docs = 0 if cu_seqlens is None else cu_seqlens.numel() - 1
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    P = n_blocks if max_ring_passes is None else max_ring_passes
+    dq = torch.empty(T, Hq, d, device=q.device, dtype=grad_dtype)
+    dk = torch.empty(k.shape, device=q.device, dtype=grad_dtype)
+    dv = torch.empty(k.shape, device=q.device, dtype=grad_dtype)
+    ws_bytes = ring_attn_backward_workspace_size(q, n_blocks, n_docs)
+    if workspace is None or workspace.numel() * workspace.element_size() < ws_bytes:
+        workspace = torch.empty(ws_bytes, device=q.device, dtype=torch.uint8)
+    ring_attn_backward(q, k, v, out, dout, lse, dq, dk, dv, n_blocks=n_blocks, layout=_LAYOUTS[layout],
+                       mask_mode=mask, max_ring_passes=P, cu_seqlens_host=cu_seqlens, scale=scale,
+                       workspace=workspace)
+    return dq, dk, dv
+
+
 __all__ = ["ring_attn_step", "ring_attn_finalize", "ring_attn_merge", "ring_attn_forward_workspace_size",
-           "ring_attn_forward", "ring_attn_plan", "ring_attn_tile_shape", "forward", "forward_qkvpacked",
+           "ring_attn_forward", "ring_attn_plan", "ring_attn_tile_shape", "ring_attn_backward_workspace_size",
+           "ring_attn_backward", "forward", "forward_qkvpacked", "backward",
            "load_library", "RingAttnError"]

@@ -135,6 +135,35 @@ Workspace carve(void* base, int64_t T, int64_t N, int64_t Hq, int64_t Hkv, int64
     return w;
 }
 
+struct BwdWorkspace {
+    float* Dsum = nullptr;          // [Hq, T]
+    int32_t* cu = nullptr;
+    BwdWork* works = nullptr;       // N
+    int64_t* partners = nullptr;    // N x N
+    BwdWork* rworks = nullptr;      // N
+    int64_t* rpartners = nullptr;   // N x N
+    size_t total = 0;
+};
+
+BwdWorkspace carve_bwd(void* base, int64_t T, int64_t N, int64_t Hq, int64_t n_docs) {
+    BwdWorkspace w;
+    size_t off = 0;
+    char* b = (char*)base;
+    auto take = [&](size_t bytes) {
+        char* p = b ? b + off : nullptr;
+        off += align_up(bytes);
+        return p;
+    };
+    w.Dsum = (float*)take(sizeof(float) * (size_t)(T * Hq));
+    w.cu = (int32_t*)take(sizeof(int32_t) * (size_t)(n_docs + 1));
+    w.works = (BwdWork*)take(sizeof(BwdWork) * (size_t)N);
+    w.partners = (int64_t*)take(sizeof(int64_t) * (size_t)(N * N));
+    w.rworks = (BwdWork*)take(sizeof(BwdWork) * (size_t)N);
+    w.rpartners = (int64_t*)take(sizeof(int64_t) * (size_t)(N * N));
+    w.total = off;
+    return w;
+}
+
 }  // namespace
 }  // namespace ra
 
@@ -575,6 +604,156 @@ ra_status ring_attn_forward(const ra_tensor* q, const ra_tensor* k, const ra_ten
         stats->tile_q = tq;
         stats->tile_k = tk;
     }
+    return RA_OK;
+}
+
+size_t ring_attn_backward_workspace_size(const ra_tensor* q, int32_t n_blocks, int32_t n_docs) {
+    if (!q || n_blocks < 1 || n_docs < 0 || q->n_tok < 0 || q->n_head < 1) return 0;
+    if (q->n_tok % n_blocks) return 0;
+    return carve_bwd(nullptr, q->n_tok, n_blocks, q->n_head, n_docs).total;
+}
+
+ra_status ring_attn_backward(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v, const ra_tensor* out,
+                             const ra_tensor* dout, const float* lse, void* dq, void* dk, void* dv,
+                             ra_dtype grad_dtype, int32_t n_blocks, ra_layout layout, ra_mask mask_mode,
+                             int32_t max_ring_passes, const int32_t* cu_seqlens_host, int32_t n_docs, float scale,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+    // ---- arguments ----
+    if (!tensor_ok(q) || !tensor_ok(k) || !tensor_ok(v) || !tensor_ok(out) || !tensor_ok(dout)) return RA_E_ARG;
+    if (!lse || !dq || !dk || !dv || !valid_dtype(grad_dtype)) return RA_E_ARG;
+    if (q->dtype != k->dtype || q->dtype != v->dtype || dout->dtype != q->dtype) return RA_E_ARG;
+    const int64_t T = q->n_tok, Hq = q->n_head, Hkv = k->n_head, d = q->head_dim;
+    if (k->n_tok != T || v->n_tok != T || v->n_head != Hkv || k->head_dim != d || v->head_dim != d) return RA_E_ARG;
+    if (out->n_tok != T || out->n_head != Hq || out->head_dim != d) return RA_E_ARG;
+    if (dout->n_tok != T || dout->n_head != Hq || dout->head_dim != d) return RA_E_ARG;
+    if (Hq % Hkv) return RA_E_ARG;
+    if (n_blocks < 1 || T % n_blocks || max_ring_passes < 1 || !scale_ok(scale)) return RA_E_ARG;
+    if (layout != RA_LAYOUT_CONTIGUOUS && layout != RA_LAYOUT_STRIPED) return RA_E_ARG;
+    if (mask_mode < RA_MASK_NONE || mask_mode > RA_MASK_DOC_CAUSAL) return RA_E_ARG;
+    if (mask_mode == RA_MASK_DOC_CAUSAL) {
+        if (!cu_seqlens_host || n_docs < 1 || cu_seqlens_host[0] != 0 || cu_seqlens_host[n_docs] != T)
+            return RA_E_ARG;
+        for (int32_t i = 0; i < n_docs; i++)
+            if (cu_seqlens_host[i + 1] < cu_seqlens_host[i]) return RA_E_ARG;
+        if (layout == RA_LAYOUT_STRIPED) return RA_E_UNSUPPORTED;
+    } else {
+        n_docs = 0;
+    }
+    // Matrix-core backward only: bf16 inputs, head_dim 64 or 128, 16-byte rows.
+    if (q->dtype != RA_BF16 || (d != 64 && d != 128)) return RA_E_UNSUPPORTED;
+    if (!bf16_aligned(q) || !bf16_aligned(k) || !bf16_aligned(v) || !bf16_aligned(dout)) return RA_E_UNSUPPORTED;
+    if ((uintptr_t)out->data % 16 || out->stride_tok % (out->dtype == RA_BF16 ? 8 : 4) ||
+        out->stride_head % (out->dtype == RA_BF16 ? 8 : 4))
+        return RA_E_UNSUPPORTED;
+    if ((uintptr_t)dq % 16 || (uintptr_t)dk % 16 || (uintptr_t)dv % 16) return RA_E_UNSUPPORTED;
+    const int64_t N = n_blocks, B = T / N;
+    const int64_t n_qtiles = (B + bwd_tile_q() - 1) / bwd_tile_q();
+    const int64_t n_ktiles = (B + bwd_tile_k() - 1) / bwd_tile_k();
+    if (N * Hq * n_qtiles * 256 > INT32_MAX || N * Hkv * n_ktiles * 256 > INT32_MAX) return RA_E_UNSUPPORTED;
+    BwdWorkspace ws = carve_bwd(workspace, T, N, Hq, n_docs);
+    if (!workspace || workspace_bytes < ws.total) return RA_E_WORKSPACE;
+    if ((uintptr_t)workspace % kAlign) return RA_E_WORKSPACE;
+    if (T == 0) return RA_OK;
+
+    // ---- ring visits: device i's key blocks (ring order) and block j's visitors ----
+    Ring r;
+    r.T = T;
+    r.N = N;
+    r.B = B;
+    r.layout = layout;
+    r.mask = mask_mode;
+    r.passes = std::min<int64_t>(max_ring_passes, N);
+    r.cu = cu_seqlens_host;
+    r.n_docs = n_docs;
+    const Plan plan = make_plan(r, bwd_tile_q(), bwd_tile_k());
+    const bool striped = layout == RA_LAYOUT_STRIPED;
+    auto pos0 = [&](int64_t blk) { return striped ? blk : blk * B; };
+    std::vector<std::vector<int64_t>> fwd((size_t)N), rev((size_t)N);
+    for (int64_t s = 0; s < r.passes; s++)
+        for (const StepPair& sp : plan.steps[s]) {
+            fwd[sp.i].push_back(pos0(sp.j));
+            rev[sp.j].push_back(pos0(sp.i));
+        }
+    std::vector<BwdWork> works, rworks;
+    std::vector<int64_t> partners, rpartners;
+    auto flatten = [&](std::vector<std::vector<int64_t>>& lists, std::vector<BwdWork>& wv, std::vector<int64_t>& pv) {
+        // Blocks with the most partners first (the longest workgroups start early).
+        std::vector<int64_t> order((size_t)N);
+        for (int64_t i = 0; i < N; i++) order[i] = i;
+        std::stable_sort(order.begin(), order.end(),
+                         [&](int64_t x, int64_t y) { return lists[x].size() > lists[y].size(); });
+        for (int64_t i : order) {
+            BwdWork w;
+            w.pos0 = pos0(i);
+            w.first = (int32_t)pv.size();
+            w.count = (int32_t)lists[i].size();
+            wv.push_back(w);
+            pv.insert(pv.end(), lists[i].begin(), lists[i].end());
+        }
+    };
+    flatten(fwd, works, partners);
+    flatten(rev, rworks, rpartners);
+
+    hipStream_t st = (hipStream_t)stream;
+    if (n_docs > 0 && hipMemcpyAsync(ws.cu, cu_seqlens_host, sizeof(int32_t) * (size_t)(n_docs + 1),
+                                     hipMemcpyHostToDevice, st) != hipSuccess)
+        return RA_E_HIP;
+    if (hipMemcpyAsync(ws.works, works.data(), sizeof(BwdWork) * works.size(), hipMemcpyHostToDevice, st) !=
+            hipSuccess ||
+        hipMemcpyAsync(ws.rworks, rworks.data(), sizeof(BwdWork) * rworks.size(), hipMemcpyHostToDevice, st) !=
+            hipSuccess)
+        return RA_E_HIP;
+    if (!partners.empty() && (hipMemcpyAsync(ws.partners, partners.data(), sizeof(int64_t) * partners.size(),
+                                             hipMemcpyHostToDevice, st) != hipSuccess ||
+                              hipMemcpyAsync(ws.rpartners, rpartners.data(), sizeof(int64_t) * rpartners.size(),
+                                             hipMemcpyHostToDevice, st) != hipSuccess))
+        return RA_E_HIP;
+
+    BwdArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.q = q->data;
+    a.k = k->data;
+    a.v = v->data;
+    a.out = out->data;
+    a.dout = dout->data;
+    a.q_st = q->stride_tok;
+    a.q_sh = q->stride_head;
+    a.k_st = k->stride_tok;
+    a.k_sh = k->stride_head;
+    a.v_st = v->stride_tok;
+    a.v_sh = v->stride_head;
+    a.out_st = out->stride_tok;
+    a.out_sh = out->stride_head;
+    a.do_st = dout->stride_tok;
+    a.do_sh = dout->stride_head;
+    a.lse = lse;
+    a.Dsum = ws.Dsum;
+    a.dq = dq;
+    a.dk = dk;
+    a.dv = dv;
+    a.out_bf16 = out->dtype == RA_BF16;
+    a.grad_bf16 = grad_dtype == RA_BF16;
+    a.T = T;
+    a.B = B;
+    a.pos_stride = striped ? N : 1;
+    a.Hq = (int32_t)Hq;
+    a.Hkv = (int32_t)Hkv;
+    a.group = (int32_t)(Hq / Hkv);
+    a.d = (int32_t)d;
+    a.mask = mask_mode;
+    a.scale = scale;
+    a.c2 = scale * 1.4426950408889634f;
+    a.cu = ws.cu;
+    a.n_docs = n_docs;
+    a.n_qtiles = (int32_t)n_qtiles;
+    a.n_ktiles = (int32_t)n_ktiles;
+    a.n_works = (int32_t)works.size();
+    a.n_rworks = (int32_t)rworks.size();
+    a.works = ws.works;
+    a.partners = ws.partners;
+    a.rworks = ws.rworks;
+    a.rpartners = ws.rpartners;
+    if (launch_backward(a, st) != hipSuccess) return RA_E_HIP;
     return RA_OK;
 }
 

@@ -1,0 +1,172 @@
+"""GPU parity of the ring backward (ring_attn_backward through the C ABI)
+against the fp64 oracle's gradients on the same seeded inputs.
+
+The GPU path takes the forward's own out and lse (bf16 inputs, fp32
+accumulation, P and dS rounded to bf16 as matrix-core operands); the oracle
+recomputes everything in fp64.  Tolerance (fp32 gradients compared with the
+oracle): max |diff| <= 2e-2 and mean |diff| <= 1e-2, the forward's bf16 bar.
+bf16 gradients are the round-to-nearest-even of the fp32 ones, bit for bit.
+
+Full sizes: dout is zero outside a seeded sample of (head, token) rows, so
+every gradient is exactly those rows' terms, which the oracle computes at
+any length; dq must vanish exactly on every other row.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+BF16_MAX, BF16_MEAN = 2e-2, 1e-2
+
+
+@pytest.fixture(scope="module")
+def ra():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import ring_attention_step_amd as mod
+    mod.load_library()
+    return mod
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+
+
+def _check(got, ref, what):
+    diff = np.abs(got - ref)
+    _say(what, "max", float(diff.max()), "mean", float(diff.mean()), "max|ref|", float(np.abs(ref).max()))
+    assert diff.max() <= BF16_MAX and diff.mean() <= BF16_MEAN, (what, diff.max(), diff.mean())
+
+
+BWD_SMALL = [
+    # T, N, Hq, Hkv, d, layout, mask, P, docs, forward out dtype
+    (888, 3, 4, 2, 128, 0, 1, 3, None, "bf16"),     # B = 296: ragged tiles on both sides
+    (888, 3, 4, 4, 128, 0, 0, 3, None, "bf16"),
+    (888, 3, 4, 1, 128, 1, 1, 3, None, "f32"),      # striped, MQA
+    (1200, 4, 2, 2, 64, 0, 1, 4, None, "bf16"),
+    (1200, 4, 4, 2, 64, 1, 1, 2, None, "bf16"),     # striped with a pass limit
+    (1024, 4, 2, 2, 128, 0, 0, 1, None, "bf16"),    # own block only
+    (960, 4, 2, 2, 128, 0, 2, 4, [0, 100, 101, 400, 700, 960], "bf16"),
+    (2048, 4, 2, 1, 128, 0, 2, 2, "random", "f32"),
+    (256, 1, 2, 2, 128, 0, 1, 1, None, "bf16"),     # one virtual device
+    (520, 8, 2, 2, 128, 1, 1, 8, None, "bf16"),     # B = 65: 1-row ragged tails
+]
+
+
+def _fwd_bwd(ra, q, k, v, dout, *, N, lay, mask, P, docs, out_dtype, grad_dtype=torch.float32):
+    out, lse = ra.forward(q, k, v, n_blocks=N, layout=lay, causal=mask == 1, cu_seqlens=docs, max_ring_passes=P,
+                          out_dtype=out_dtype, return_lse=True)
+    return ra.backward(q, k, v, out, lse, dout, n_blocks=N, layout=lay, causal=mask == 1, cu_seqlens=docs,
+                       max_ring_passes=P, grad_dtype=grad_dtype)
+
+
+@pytest.mark.parametrize("case", range(len(BWD_SMALL)))
+def test_bf16_backward_small(ra, case):
+    T, N, Hq, Hkv, d, layout, mask, P, docs, odt = BWD_SMALL[case]
+    if docs == "random":
+        docs = W.random_doc_cu_seqlens(T, 16, 900, seed=case).tolist()
+    _say("bf16 backward small", BWD_SMALL[case])
+    qh, kh, vh = W.random_qkv(T, Hq, Hkv, d, "bf16", 2000 + case)
+    gh = W.random_dout(T, Hq, d, "bf16", 2000 + case)
+    q, k, v, g = (x.cuda() for x in (qh, kh, vh, gh))
+    lay = "striped" if layout == 1 else "contiguous"
+    kw = dict(N=N, lay=lay, mask=mask, P=P, docs=docs, out_dtype=torch.bfloat16 if odt == "bf16" else torch.float32)
+    dq, dk, dv = _fwd_bwd(ra, q, k, v, g, **kw)
+    ref = oracle.backward(qh, kh, vh, gh, n_blocks=N, layout=layout, mask=mask, max_ring_passes=P, cu_seqlens=docs)
+    for name, got, r in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
+        _check(got.cpu().double().numpy(), r, name)
+    # bf16 gradients: the same values rounded to nearest even
+    bq, bk, bv = _fwd_bwd(ra, q, k, v, g, grad_dtype=torch.bfloat16, **kw)
+    for got, f in zip((bq, bk, bv), (dq, dk, dv)):
+        assert got.dtype == torch.bfloat16 and torch.equal(got, f.to(torch.bfloat16))
+
+
+def test_bf16_backward_packed_qkv_views(ra):
+    """Strided q / k / v views of one [T, 3, H, d] tensor give the gradients of
+    contiguous copies, bit for bit."""
+    T, H, d, N = 1024, 2, 128, 4
+    qh, kh, vh = W.random_qkv(T, H, H, d, "bf16", 77)
+    gh = W.random_dout(T, H, d, "bf16", 77)
+    _say("bf16 backward packed views", T, H, d, N)
+    qkv = torch.stack([qh, kh, vh], dim=1).cuda()  # [T, 3, H, d]
+    g = gh.cuda()
+    kw = dict(N=N, lay="contiguous", mask=1, P=N, docs=None, out_dtype=torch.bfloat16)
+    a = _fwd_bwd(ra, qkv[:, 0], qkv[:, 1], qkv[:, 2], g, **kw)
+    b = _fwd_bwd(ra, qkv[:, 0].contiguous(), qkv[:, 1].contiguous(), qkv[:, 2].contiguous(), g, **kw)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_bf16_backward_is_deterministic(ra):
+    T, Hq, Hkv, d, N = 1536, 4, 2, 128, 3
+    qh, kh, vh = W.random_qkv(T, Hq, Hkv, d, "bf16", 91)
+    gh = W.random_dout(T, Hq, d, "bf16", 91)
+    q, k, v, g = (x.cuda() for x in (qh, kh, vh, gh))
+    _say("bf16 backward determinism", T, Hq, Hkv, d, N)
+    kw = dict(N=N, lay="striped", mask=1, P=N, docs=None, out_dtype=torch.bfloat16)
+    a = _fwd_bwd(ra, q, k, v, g, **kw)
+    b = _fwd_bwd(ra, q, k, v, g, **kw)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def _sample_pairs(w, rng, heads, n_per_head):
+    B = w.block
+    pairs = set()
+    for h in heads:
+        toks = [0, 1, B - 1, B, w.T - 1, w.T // 2] + list(rng.integers(0, w.T, size=n_per_head))
+        pairs.update((int(h), int(t)) for t in toks)
+    pairs = sorted(pairs)
+    return np.array([p[0] for p in pairs]), np.array([p[1] for p in pairs])
+
+
+@pytest.mark.parametrize("name", ["causal32k_h32_d128_8blk", "gqa_striped64k_h32kv8_d128_16blk",
+                                  "varlen_packed128k_h32_d128_8blk_p4"])
+def test_long_workload_sparse_dout(ra, name):
+    w = W.WORKLOADS[name]
+    _say(name, "generating inputs")
+    x = W.make_inputs(w)
+    if w.packed:
+        qkv = x["qkv"].cuda()
+        q, k, v = qkv[:, 0], qkv[:, 1], qkv[:, 2]
+    else:
+        q, k, v = (x[n].cuda() for n in ("q", "k", "v"))
+    cu = x.get("cu_seqlens")
+    group = w.Hq // w.Hkv
+    rng = np.random.default_rng(w.seed + 100)
+    # one query head in each of two kv heads
+    kv_sel = sorted(rng.choice(w.Hkv, size=2, replace=False).tolist())
+    q_sel = [g * group + int(rng.integers(0, group)) for g in kv_sel]
+    heads, toks = _sample_pairs(w, rng, q_sel, 26)
+    full = W.random_dout(w.T, w.Hq, w.d, "bf16", w.seed)
+    dout = torch.zeros_like(full)
+    dout[toks, heads] = full[toks, heads]
+    lay = "striped" if w.layout else "contiguous"
+    _say(name, "forward + backward on", len(toks), "rows of heads", q_sel)
+    dq, dk, dv = _fwd_bwd(ra, q, k, v, dout.cuda(), N=w.n_blocks, lay=lay, mask=w.mask, P=w.max_ring_passes,
+                          docs=cu, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    # oracle on the selected heads only, each query head with its own kv head
+    sub_q = x["q"][:, q_sel]
+    sub_k = x["k"][:, kv_sel]
+    sub_v = x["v"][:, kv_sel]
+    sub_g = dout[:, q_sel].contiguous()
+    idx = {h: n for n, h in enumerate(q_sel)}
+    _say(name, "oracle")
+    ref_dq, ref_dk, ref_dv = oracle.backward(sub_q, sub_k, sub_v, sub_g, n_blocks=w.n_blocks, layout=w.layout,
+                                             mask=w.mask, max_ring_passes=w.max_ring_passes, cu_seqlens=cu,
+                                             scale=w.scale, rows=(np.array([idx[int(h)] for h in heads]), toks),
+                                             rows_dkdv=True)
+    _check(dq.cpu()[toks, heads].double().numpy(), ref_dq, name + " dq rows")
+    _check(dk.cpu()[:, kv_sel].double().numpy(), ref_dk, name + " dk")
+    _check(dv.cpu()[:, kv_sel].double().numpy(), ref_dv, name + " dv")
+    # every other row and kv head: exactly zero
+    dq_rest = dq.clone()
+    dq_rest[toks, heads] = 0
+    assert not dq_rest.any()
+    others = [g for g in range(w.Hkv) if g not in kv_sel]
+    assert not dk[:, others].any() and not dv[:, others].any()

@@ -32,7 +32,7 @@ def test_header_declares_the_boundary():
     names = _declared_functions()
     for fn in ("ring_attn_step", "ring_attn_finalize", "ring_attn_merge", "ring_attn_forward",
                "ring_attn_forward_workspace_size", "ring_attn_plan", "ring_attn_tile_shape",
-               "ring_attn_status_string"):
+               "ring_attn_status_string", "ring_attn_backward", "ring_attn_backward_workspace_size"):
         assert fn in names
 
 
@@ -186,3 +186,44 @@ def test_workspace_size_grows_with_prefetch(lib):
     b = lib.ring_attn_forward_workspace_size(ctypes.byref(q), ctypes.byref(k), 8, 0, 1)
     state = 4096 * 32 * 128 * 4 + 2 * 4096 * 32 * 4
     assert a >= state and b >= a + 2 * 2 * 4096 * 8 * 128 * 2
+
+
+def test_backward_refuses_bad_arguments_before_any_gpu_work(lib):
+    q, k, v = _fake(64, 4, 128), _fake(64, 2, 128), _fake(64, 2, 128)
+    out, dout = _fake(64, 4, 128), _fake(64, 4, 128)
+    lse, g, ws = ctypes.c_void_p(1 << 24), ctypes.c_void_p(1 << 25), ctypes.c_void_p(1 << 26)
+    R = ctypes.byref
+
+    def bwd(qq=q, kk=k, vv=v, oo=out, gg=dout, ll=lse, dq=g, n_blocks=4, layout=0, mask=1, P=4, cu=None,
+            n_docs=0, scale=0.1, ws_bytes=1 << 40, grad=ra.RA_F32):
+        return lib.ring_attn_backward(R(qq), R(kk), R(vv), R(oo), R(gg), ll, dq, g, g, grad, n_blocks, layout,
+                                      mask, P, cu, n_docs, scale, ws, ws_bytes, None)
+
+    assert bwd(n_blocks=5) == ra.RA_E_ARG             # 64 % 5
+    assert bwd(P=0) == ra.RA_E_ARG
+    assert bwd(scale=-1.0) == ra.RA_E_ARG
+    assert bwd(ll=None) == ra.RA_E_ARG
+    assert bwd(dq=None) == ra.RA_E_ARG
+    assert bwd(gg=_fake(64, 2, 128)) == ra.RA_E_ARG   # dout heads != q heads
+    assert bwd(oo=_fake(32, 4, 128)) == ra.RA_E_ARG
+    assert bwd(kk=_fake(64, 3, 128)) == ra.RA_E_ARG
+    assert bwd(mask=2) == ra.RA_E_ARG                 # no cu_seqlens
+    assert bwd(grad=7) == ra.RA_E_ARG
+    f32 = dict(qq=_fake(64, 4, 16, ra.RA_F32), kk=_fake(64, 2, 16, ra.RA_F32), vv=_fake(64, 2, 16, ra.RA_F32),
+               oo=_fake(64, 4, 16, ra.RA_F32), gg=_fake(64, 4, 16, ra.RA_F32))
+    assert bwd(**f32) == ra.RA_E_UNSUPPORTED          # fp32 inputs: no backward kernel
+    assert bwd(qq=_fake(64, 4, 96), kk=_fake(64, 2, 96), vv=_fake(64, 2, 96), oo=_fake(64, 4, 96),
+               gg=_fake(64, 4, 96)) == ra.RA_E_UNSUPPORTED
+    assert bwd(qq=_fake(64, 4, 128, ptr=(1 << 20) + 2)) == ra.RA_E_UNSUPPORTED
+    assert bwd(dq=ctypes.c_void_p((1 << 25) + 8)) == ra.RA_E_UNSUPPORTED
+    assert bwd(ws_bytes=16) == ra.RA_E_WORKSPACE
+    cu = (ctypes.c_int32 * 3)(0, 10, 64)
+    assert bwd(mask=2, cu=cu, n_docs=2, layout=1) == ra.RA_E_UNSUPPORTED
+
+
+def test_backward_workspace_size(lib):
+    q = _fake(4096, 32, 128)
+    n = lib.ring_attn_backward_workspace_size(ctypes.byref(q), 8, 0)
+    assert n >= 4096 * 32 * 4 + 2 * 8 * 8 * 8
+    assert lib.ring_attn_backward_workspace_size(ctypes.byref(q), 3, 0) == 0   # 4096 % 3
+    assert lib.ring_attn_backward_workspace_size(ctypes.byref(q), 8, 1000) > n

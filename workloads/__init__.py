@@ -143,5 +143,11 @@ def random_qkv(T: int, Hq: int, Hkv: int, d: int, dtype: str, seed: int, packed:
     return q, k, v
 
 
+def random_dout(T: int, Hq: int, d: int, dtype: str, seed: int):
+    """Seeded N(0,1) output gradient [T, Hq, d] (its own stream, seed + 7919)."""
+    g = torch.Generator().manual_seed(seed + 7919)
+    return _to_dtype(torch.randn(T, Hq, d, generator=g), dtype)
+
+
 def random_doc_cu_seqlens(T: int, lo: int, hi: int, seed: int) -> torch.Tensor:
     return torch.from_numpy(doc_cu_seqlens(seed, T, lo, hi))
