@@ -83,6 +83,10 @@ def _load():
                                     i64, i64, i64, i64, i64, i64, i64, i64, dbl, ci, ci, i64, i64,
                                     vp, i64, vp, vp, vp]
         lib.ro_backward.restype = ci
+        lib.ro_backward_rows.argtypes = [vp, vp, vp, vp, ci, ci, i64, i64, i64, i64,
+                                         i64, i64, i64, i64, i64, i64, i64, i64, dbl, ci, ci, i64, i64,
+                                         vp, i64, vp, vp, i64, vp, vp, vp]
+        lib.ro_backward_rows.restype = ci
         _lib = lib
     return _lib
 
@@ -262,11 +266,19 @@ def allowed_pairs(T: int, n_blocks: int, *, layout: int = LAYOUT_CONTIGUOUS, mas
 
 
 def backward(q, k, v, dout, *, n_blocks: int, layout: int = LAYOUT_CONTIGUOUS, mask: int = MASK_NONE,
-             max_ring_passes: Optional[int] = None, cu_seqlens=None, scale: Optional[float] = None):
+             max_ring_passes: Optional[int] = None, cu_seqlens=None, scale: Optional[float] = None,
+             rows: Optional[Sequence] = None, rows_dkdv: bool = False):
     """Gradients (dq, dk, dv) of ``forward``'s output with respect to q, k, v
     for the output gradient ``dout`` ([T, Hq, d], float32 or bfloat16), as
     float64 arrays [T, Hq, d], [T, Hkv, d], [T, Hkv, d].  The arithmetic is in
-    ``ring_oracle.c`` (``ro_backward``)."""
+    ``ring_oracle.c`` (``ro_backward``).
+
+    With ``rows`` = (heads, tokens) index arrays of equal length n (distinct
+    pairs), only those query rows' terms are computed (``ro_backward_rows``):
+    their dq as an [n, d] array (each equal to the matching row of the full
+    dq), and with ``rows_dkdv`` also (dq_rows, dk, dv) where dk / dv sum those
+    rows' terms only -- the full dk / dv whenever dout vanishes on every other
+    row."""
     for name, x in (("q", q), ("k", k), ("v", v), ("dout", dout)):
         _check_view(x, name)
     if not (q.dtype == k.dtype == v.dtype):
@@ -279,6 +291,24 @@ def backward(q, k, v, dout, *, n_blocks: int, layout: int = LAYOUT_CONTIGUOUS, m
         scale = 1.0 / math.sqrt(d)
     P = n_blocks if max_ring_passes is None else int(max_ring_passes)
     cu, n_docs = _cu(cu_seqlens)
+    if rows is not None:
+        row_head = np.ascontiguousarray(np.asarray(rows[0]), dtype=np.int64)
+        row_tok = np.ascontiguousarray(np.asarray(rows[1]), dtype=np.int64)
+        if row_head.shape != row_tok.shape or row_head.ndim != 1:
+            raise ValueError("rows must be two index arrays of equal length")
+        if len(set(zip(row_head.tolist(), row_tok.tolist()))) != row_head.size:
+            raise ValueError("rows must be distinct (head, token) pairs")
+        out = np.zeros((row_head.size, d))
+        dk = np.zeros((T, Hkv, d)) if rows_dkdv else None
+        dv = np.zeros((T, Hkv, d)) if rows_dkdv else None
+        rc = _load().ro_backward_rows(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _dtype_code(q), _dtype_code(dout), T, Hq, Hkv, d,
+            q.stride(0), q.stride(1), k.stride(0), k.stride(1), v.stride(0), v.stride(1),
+            dout.stride(0), dout.stride(1), float(scale), int(mask), int(layout), int(n_blocks), P,
+            _ptr(cu), n_docs, _ptr(row_head), _ptr(row_tok), row_head.size, _ptr(out), _ptr(dk), _ptr(dv))
+        if rc != 0:
+            raise ValueError("oracle rejected the arguments (code %d)" % rc)
+        return (out, dk, dv) if rows_dkdv else out
     dq = np.zeros((T, Hq, d))
     dk = np.zeros((T, Hkv, d))
     dv = np.zeros((T, Hkv, d))

@@ -374,10 +374,61 @@ int ro_allowed_pairs(int64_t T, int64_t n_blocks, int layout, int mask, int64_t 
  *   dq       += scale sum_j dS_j k_j
  *   dk_j     += scale dS_j q
  * (the softmax Jacobian is diag(P) - P P^T).  Rows with no allowed key give
- * no gradient.  Outputs are fp64 arrays dq [T, Hq, d], dk and dv [T, Hkv, d]
- * (dense, overwritten); the work is split over KV heads so that the dk / dv
- * sums of one head stay in one thread.
+ * no gradient.  backward_row adds one row's terms: dq_row always, dk / dv
+ * when non-null.
  */
+typedef struct {
+    const ro_view *q, *k, *v, *dout;
+    const ro_ring* ring;
+    const int32_t* doc_of;
+    int mask;
+    int64_t T, Hkv, d;
+    double scale;
+} ro_bwd_ctx;
+
+static void backward_row(const ro_bwd_ctx* c, int64_t t, int64_t h, int64_t g, int64_t* idx, double* sbuf,
+                         double* Obuf, double* obuf, double* dq_row, double* dk, double* dv) {
+    const int64_t T = c->T, d = c->d, Hkv = c->Hkv;
+    int64_t n = 0;
+    for (int64_t tk = 0; tk < T; tk++)
+        if (mask_allows(c->mask, c->doc_of, t, tk) && ring_visible(c->ring, t, tk)) idx[n++] = tk;
+    if (n == 0) return;
+    double lse_r, m_r, l_r;
+    attend_one(c->q, t, h, c->k, c->v, g, d, c->scale, idx, n, sbuf, obuf, &lse_r, &m_r, &l_r, Obuf);
+    double D = 0.0;
+    for (int64_t x = 0; x < d; x++) D += view_at(c->dout, t, h, x) * obuf[x];
+    for (int64_t a = 0; a < n; a++) {
+        int64_t j = idx[a];
+        double p = exp(sbuf[a] - m_r) / l_r;
+        double dp = 0.0;
+        for (int64_t x = 0; x < d; x++) dp += view_at(c->dout, t, h, x) * view_at(c->v, j, g, x);
+        double ds = p * (dp - D);
+        for (int64_t x = 0; x < d; x++) dq_row[x] += c->scale * ds * view_at(c->k, j, g, x);
+        if (dk) {
+            double* dkr = dk + (j * Hkv + g) * d;
+            double* dvr = dv + (j * Hkv + g) * d;
+            for (int64_t x = 0; x < d; x++) {
+                dkr[x] += c->scale * ds * view_at(c->q, t, h, x);
+                dvr[x] += p * view_at(c->dout, t, h, x);
+            }
+        }
+    }
+}
+
+static int bwd_check(int64_t T, int64_t Hq, int64_t Hkv, int64_t d, int mask, int64_t n_blocks,
+                     int64_t max_ring_passes, const int32_t* cu_seqlens, int64_t n_docs) {
+    if (T < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv || d < 1 || n_blocks < 1 || max_ring_passes < 1)
+        return RO_BAD_ARG;
+    if (T % n_blocks) return RO_BAD_ARG;
+    if (mask == RO_MASK_DOC_CAUSAL && (!cu_seqlens || n_docs < 1 || cu_seqlens[0] != 0 ||
+                                       cu_seqlens[n_docs] != T))
+        return RO_BAD_ARG;
+    return RO_OK;
+}
+
+/* Full gradients: fp64 arrays dq [T, Hq, d], dk and dv [T, Hkv, d] (dense,
+ * overwritten); the work is split over KV heads so that the dk / dv sums of
+ * one head stay in one thread. */
 int ro_backward(const void* q, const void* k, const void* v, const void* dout, int dtype, int dout_dtype,
                 int64_t T, int64_t Hq, int64_t Hkv, int64_t d,
                 int64_t q_st, int64_t q_sh, int64_t k_st, int64_t k_sh,
@@ -385,12 +436,8 @@ int ro_backward(const void* q, const void* k, const void* v, const void* dout, i
                 double scale, int mask, int layout, int64_t n_blocks, int64_t max_ring_passes,
                 const int32_t* cu_seqlens, int64_t n_docs,
                 double* dq, double* dk, double* dv) {
-    if (T < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv || d < 1 || n_blocks < 1 || max_ring_passes < 1)
-        return RO_BAD_ARG;
-    if (T % n_blocks) return RO_BAD_ARG;
-    if (mask == RO_MASK_DOC_CAUSAL && (!cu_seqlens || n_docs < 1 || cu_seqlens[0] != 0 ||
-                                       cu_seqlens[n_docs] != T))
-        return RO_BAD_ARG;
+    int rc = bwd_check(T, Hq, Hkv, d, mask, n_blocks, max_ring_passes, cu_seqlens, n_docs);
+    if (rc != RO_OK) return rc;
     ro_view qv = {q, dtype, q_st, q_sh}, kv = {k, dtype, k_st, k_sh}, vv = {v, dtype, v_st, v_sh};
     ro_view ov = {dout, dout_dtype, o_st, o_sh};
     ro_ring ring = {T, n_blocks, max_ring_passes < n_blocks ? max_ring_passes : n_blocks, layout};
@@ -399,6 +446,7 @@ int ro_backward(const void* q, const void* k, const void* v, const void* dout, i
         doc_of = make_doc_of(cu_seqlens, n_docs, T);
         if (!doc_of) return RO_NO_MEM;
     }
+    ro_bwd_ctx c = {&qv, &kv, &vv, &ov, &ring, doc_of, mask, T, Hkv, d, scale};
     memset(dq, 0, sizeof(double) * (size_t)(T * Hq * d));
     memset(dk, 0, sizeof(double) * (size_t)(T * Hkv * d));
     memset(dv, 0, sizeof(double) * (size_t)(T * Hkv * d));
@@ -417,32 +465,68 @@ int ro_backward(const void* q, const void* k, const void* v, const void* dout, i
 #pragma omp for schedule(dynamic, 1)
             for (int64_t g = 0; g < Hkv; g++)
                 for (int64_t h = g * group; h < (g + 1) * group; h++)
-                    for (int64_t t = 0; t < T; t++) {
-                        int64_t n = 0;
-                        for (int64_t tk = 0; tk < T; tk++)
-                            if (mask_allows(mask, doc_of, t, tk) && ring_visible(&ring, t, tk)) idx[n++] = tk;
-                        if (n == 0) continue;
-                        double lse_r, m_r, l_r;
-                        attend_one(&qv, t, h, &kv, &vv, g, d, scale, idx, n, sbuf, obuf, &lse_r, &m_r, &l_r,
-                                   Obuf);
-                        double D = 0.0;
-                        for (int64_t c = 0; c < d; c++) D += view_at(&ov, t, h, c) * obuf[c];
-                        double* dqr = dq + (t * Hq + h) * d;
-                        for (int64_t a = 0; a < n; a++) {
-                            int64_t j = idx[a];
-                            double p = exp(sbuf[a] - m_r) / l_r;
-                            double dp = 0.0;
-                            for (int64_t c = 0; c < d; c++) dp += view_at(&ov, t, h, c) * view_at(&vv, j, g, c);
-                            double ds = p * (dp - D);
-                            double* dkr = dk + (j * Hkv + g) * d;
-                            double* dvr = dv + (j * Hkv + g) * d;
-                            for (int64_t c = 0; c < d; c++) {
-                                dqr[c] += scale * ds * view_at(&kv, j, g, c);
-                                dkr[c] += scale * ds * view_at(&qv, t, h, c);
-                                dvr[c] += p * view_at(&ov, t, h, c);
-                            }
-                        }
-                    }
+                    for (int64_t t = 0; t < T; t++)
+                        backward_row(&c, t, h, g, idx, sbuf, Obuf, obuf, dq + (t * Hq + h) * d, dk, dv);
+        }
+        free(idx);
+        free(sbuf);
+        free(Obuf);
+        free(obuf);
+    }
+    free(doc_of);
+    return status;
+}
+
+/* The terms of selected query rows only: row r is query head row_head[r] at
+ * token row_tok[r] (each (head, token) listed once).  dq_rows [n_rows, d]
+ * gets those rows' dq (a row's dq depends on that row alone, so these equal
+ * the full gradients' rows); dk / dv, when non-null, [T, Hkv, d], get the
+ * sums of those rows' terms only, which are the full gradients when dout is
+ * zero on every other row.  dk / dv are summed serially in row order. */
+int ro_backward_rows(const void* q, const void* k, const void* v, const void* dout, int dtype, int dout_dtype,
+                        int64_t T, int64_t Hq, int64_t Hkv, int64_t d,
+                        int64_t q_st, int64_t q_sh, int64_t k_st, int64_t k_sh,
+                        int64_t v_st, int64_t v_sh, int64_t o_st, int64_t o_sh,
+                        double scale, int mask, int layout, int64_t n_blocks, int64_t max_ring_passes,
+                        const int32_t* cu_seqlens, int64_t n_docs,
+                        const int64_t* row_head, const int64_t* row_tok, int64_t n_rows, double* dq_rows,
+                        double* dk, double* dv) {
+    int rc = bwd_check(T, Hq, Hkv, d, mask, n_blocks, max_ring_passes, cu_seqlens, n_docs);
+    if (rc != RO_OK) return rc;
+    for (int64_t r = 0; r < n_rows; r++)
+        if (row_head[r] < 0 || row_head[r] >= Hq || row_tok[r] < 0 || row_tok[r] >= T) return RO_BAD_ARG;
+    ro_view qv = {q, dtype, q_st, q_sh}, kv = {k, dtype, k_st, k_sh}, vv = {v, dtype, v_st, v_sh};
+    ro_view ov = {dout, dout_dtype, o_st, o_sh};
+    ro_ring ring = {T, n_blocks, max_ring_passes < n_blocks ? max_ring_passes : n_blocks, layout};
+    int32_t* doc_of = NULL;
+    if (mask == RO_MASK_DOC_CAUSAL) {
+        doc_of = make_doc_of(cu_seqlens, n_docs, T);
+        if (!doc_of) return RO_NO_MEM;
+    }
+    ro_bwd_ctx c = {&qv, &kv, &vv, &ov, &ring, doc_of, mask, T, Hkv, d, scale};
+    memset(dq_rows, 0, sizeof(double) * (size_t)(n_rows * d));
+    if (dk) memset(dk, 0, sizeof(double) * (size_t)(T * Hkv * d));
+    if (dv) memset(dv, 0, sizeof(double) * (size_t)(T * Hkv * d));
+    if (!dk != !dv) {
+        free(doc_of);
+        return RO_BAD_ARG;
+    }
+    int64_t group = Hq / Hkv;
+    int status = RO_OK;
+#pragma omp parallel if (!dk)
+    {
+        int64_t* idx = (int64_t*)malloc(sizeof(int64_t) * (size_t)(T > 0 ? T : 1));
+        double* sbuf = (double*)malloc(sizeof(double) * (size_t)(T > 0 ? T : 1));
+        double* Obuf = (double*)malloc(sizeof(double) * (size_t)d);
+        double* obuf = (double*)malloc(sizeof(double) * (size_t)d);
+        if (!idx || !sbuf || !Obuf || !obuf) {
+#pragma omp atomic write
+            status = RO_NO_MEM;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t r = 0; r < n_rows; r++)
+                backward_row(&c, row_tok[r], row_head[r], row_head[r] / group, idx, sbuf, Obuf, obuf,
+                             dq_rows + r * d, dk, dv);
         }
         free(idx);
         free(sbuf);

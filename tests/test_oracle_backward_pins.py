@@ -126,3 +126,42 @@ def test_bf16_inputs_decode_exactly():
     b = oracle.backward(q.float(), k.float(), v.float(), do.float(), n_blocks=4, mask=oracle.MASK_CAUSAL)
     for x, y in zip(a, b):
         assert np.array_equal(x, y)
+
+
+@pytest.mark.parametrize("case", range(len(CASES)))
+def test_dq_rows_equal_full_rows(case):
+    """The sampled-row entry returns exactly the full backward's dq rows (a
+    row's dq depends on that row alone)."""
+    T, N, Hq, Hkv, d, layout, mask, P, docs = CASES[case]
+    q, k, v, dout = _inputs(T, Hq, Hkv, d, 70 + case)
+    kw = dict(n_blocks=N, layout=layout, mask=mask, max_ring_passes=P, cu_seqlens=docs)
+    dq, _, _ = oracle.backward(q, k, v, dout, **kw)
+    rng = np.random.default_rng(case)
+    heads, toks = rng.integers(0, Hq, 9), rng.integers(0, T, 9)
+    pairs = sorted(set(zip(heads.tolist(), toks.tolist())))
+    heads, toks = np.array([p[0] for p in pairs]), np.array([p[1] for p in pairs])
+    got = oracle.backward(q, k, v, dout, rows=(heads, toks), **kw)
+    assert got.shape == (len(pairs), d)
+    assert np.array_equal(got, dq[toks, heads])
+
+
+@pytest.mark.parametrize("case", range(len(CASES)))
+def test_row_terms_equal_full_gradients_of_a_sparse_dout(case):
+    """dout zero outside a few rows: the rows entry's dk / dv (those rows'
+    terms only) equal the full backward's, and its dq rows equal the full dq
+    rows; the full dq is zero on every other row."""
+    T, N, Hq, Hkv, d, layout, mask, P, docs = CASES[case]
+    q, k, v, dout = _inputs(T, Hq, Hkv, d, 90 + case)
+    rng = np.random.default_rng(10 + case)
+    pairs = sorted(set(zip(rng.integers(0, Hq, 6).tolist(), rng.integers(0, T, 6).tolist())))
+    heads, toks = np.array([p[0] for p in pairs]), np.array([p[1] for p in pairs])
+    sparse = torch.zeros_like(dout)
+    sparse[toks, heads] = dout[toks, heads]
+    kw = dict(n_blocks=N, layout=layout, mask=mask, max_ring_passes=P, cu_seqlens=docs)
+    dq, dk, dv = oracle.backward(q, k, v, sparse, **kw)
+    dq_r, dk_r, dv_r = oracle.backward(q, k, v, sparse, rows=(heads, toks), rows_dkdv=True, **kw)
+    assert np.allclose(dk_r, dk, rtol=0, atol=1e-12) and np.allclose(dv_r, dv, rtol=0, atol=1e-12)
+    assert np.array_equal(dq_r, dq[toks, heads])
+    rest = np.ones((T, Hq), bool)
+    rest[toks, heads] = False
+    assert not dq[rest].any()

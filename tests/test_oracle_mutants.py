@@ -29,10 +29,12 @@ MUTANTS = {
 # Mistakes in the backward, caught by its own pins.
 MUTANTS_BWD = {
     "bwd_softmax_jacobian_diagonal_only": ("double ds = p * (dp - D);", "double ds = p * dp;"),
-    "bwd_dk_without_scale": ("dkr[c] += scale * ds * view_at(&qv, t, h, c);", "dkr[c] += ds * view_at(&qv, t, h, c);"),
-    "bwd_dv_uses_dp": ("dvr[c] += p * view_at(&ov, t, h, c);", "dvr[c] += dp * view_at(&ov, t, h, c);"),
-    "bwd_dq_uses_value": ("dqr[c] += scale * ds * view_at(&kv, j, g, c);", "dqr[c] += scale * ds * view_at(&vv, j, g, c);"),
-    "bwd_D_from_state": ("D += view_at(&ov, t, h, c) * obuf[c];", "D += view_at(&ov, t, h, c) * Obuf[c];"),
+    "bwd_dk_without_scale": ("dkr[x] += c->scale * ds * view_at(c->q, t, h, x);",
+                             "dkr[x] += ds * view_at(c->q, t, h, x);"),
+    "bwd_dv_uses_dp": ("dvr[x] += p * view_at(c->dout, t, h, x);", "dvr[x] += dp * view_at(c->dout, t, h, x);"),
+    "bwd_dq_uses_value": ("dq_row[x] += c->scale * ds * view_at(c->k, j, g, x);",
+                          "dq_row[x] += c->scale * ds * view_at(c->v, j, g, x);"),
+    "bwd_D_from_state": ("D += view_at(c->dout, t, h, x) * obuf[x];", "D += view_at(c->dout, t, h, x) * Obuf[x];"),
 }
 
 
