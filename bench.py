@@ -1,7 +1,7 @@
 """Benchmark of the one-GPU ring-attention forward.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--prefetch]
-                    [--no-cpu-baseline]
+                    [--backward] [--no-cpu-baseline]
 
 A step is one ring_attn_forward call: every ring step of every virtual device
 plus the fused finalize, on synthetic bf16 inputs already resident in HBM.
@@ -14,6 +14,11 @@ Default workload: 32768 tokens, 32 heads, d = 128, 8 contiguous ring blocks of
 4096, causal mask, scale 1/sqrt(128).  Throughput is causal-adjusted: FLOP =
 4 * d * Hq * (allowed (query, key) pairs), i.e. only the two contractions over
 pairs the mask lets through.  Prints one JSON line.
+
+--backward times ring_attn_backward instead (the D = dout.out prep, the dq
+kernel and the dk/dv kernel), with the forward's out and lse and a seeded
+dout resident in HBM; FLOP = 10 * d * Hq * allowed pairs (the five
+contractions of the backward: S, dP, dV, dK, dQ), fp32 gradients.
 """
 from __future__ import annotations
 
@@ -32,6 +37,7 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak (AMD published figure)
 DEFAULT_WORKLOAD = "causal32k_h32_d128_8blk"
 KERNEL = "step_bf16_kernel<128, true, true>"
+BWD_KERNEL = "bwd_dkdv_kernel<128>"
 KERNEL_SOURCES = ["ring_attention_step_amd/csrc/step_bf16.hip", "ring_attention_step_amd/csrc/plan.h",
                   "ring_attention_step_amd/csrc/kernels.h"]
 
@@ -95,6 +101,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--prefetch", action="store_true")
+    ap.add_argument("--backward", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="instead of the benchmark, run a plain device copy of BYTES bytes 5 times "
@@ -144,6 +151,8 @@ def main():
     ws = torch.empty(ra.ring_attn_forward_workspace_size(q, k, w.n_blocks, n_docs, args.prefetch), device=dev,
                      dtype=torch.uint8)
     stream = torch.cuda.current_stream()
+    if args.backward:
+        return bench_backward(args, ra, W, w, x, q, k, v, cu, out, lse, plan, stream)
 
     def step():
         ra.ring_attn_forward(q, k, v, out, lse, n_blocks=w.n_blocks, layout=w.layout, mask_mode=w.mask,
@@ -201,34 +210,127 @@ def main():
     print(json.dumps(res), flush=True)
 
 
-def cpu_baseline_for(w, x):
+def bench_backward(args, ra, W, w, x, q, k, v, cu, out, lse, plan, stream):
+    import torch
+
+    dev = q.device
+    n_docs = 0 if cu is None else cu.numel() - 1
+    ws_f = torch.empty(ra.ring_attn_forward_workspace_size(q, k, w.n_blocks, n_docs, False), device=dev,
+                       dtype=torch.uint8)
+    ra.ring_attn_forward(q, k, v, out, lse, n_blocks=w.n_blocks, layout=w.layout, mask_mode=w.mask,
+                         max_ring_passes=w.max_ring_passes, cu_seqlens_host=cu, scale=w.scale, prefetch=False,
+                         workspace=ws_f, stream=stream)
+    del ws_f
+    dout = W.random_dout(w.T, w.Hq, w.d, "bf16", w.seed).to(dev)
+    dq = torch.empty(w.T, w.Hq, w.d, device=dev, dtype=torch.float32)
+    dk = torch.empty(w.T, w.Hkv, w.d, device=dev, dtype=torch.float32)
+    dv = torch.empty_like(dk)
+    ws = torch.empty(ra.ring_attn_backward_workspace_size(q, w.n_blocks, n_docs), device=dev, dtype=torch.uint8)
+    flop = 10.0 * w.d * w.Hq * plan["allowed_pairs"]
+
+    def step():
+        ra.ring_attn_backward(q, k, v, out, dout, lse, dq, dk, dv, n_blocks=w.n_blocks, layout=w.layout,
+                              mask_mode=w.mask, max_ring_passes=w.max_ring_passes, cu_seqlens_host=cu,
+                              scale=w.scale, workspace=ws, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_event = ev0.elapsed_time(ev1) / args.steps
+    ms_wall = wall * 1e3 / args.steps
+    value = flop / (ms_wall * 1e-3) / 1e12
+    achieved = flop / (ms_event * 1e-3) / 1e12
+    res = {
+        "metric": "causal-adjusted attention backward TFLOP/s and % bf16 MFMA peak, ring bwd, 1 GPU",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_wall, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "pass": "backward", "tokens": w.T, "q_heads": w.Hq, "kv_heads": w.Hkv,
+                   "head_dim": w.d, "ring_blocks": w.n_blocks, "layout": ["contiguous", "striped"][w.layout],
+                   "mask": ["none", "causal", "doc-causal"][w.mask], "max_ring_passes": w.max_ring_passes,
+                   "grad_dtype": "f32", "flop_per_step": flop, "allowed_pairs_per_head": plan["allowed_pairs"]},
+        "pct_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        # the three backward kernels together, event-timed on the launch stream
+        "roofline": {"bound": "mfma", "kernel": "bwd_prep + bwd_dq_kernel<128> + " + BWD_KERNEL,
+                     "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "event_ms_per_step": round(ms_event, 4),
+                     "timing": "hip events on the launch stream around the timed backward calls"},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_backward(w, x, dout.cpu())
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline_backward(w, x, dout):
+    """The fp64 oracle's backward, untuned, on a bounded sample: dout kept on
+    n_tok evenly spaced tokens of one head (zero elsewhere), that head and its
+    kv head only; every term of those rows (dq rows, their dk / dv sums)."""
     import numpy as np
 
-    def pairs_fn(toks):
-        # allowed keys of each sampled row under this workload's mask and ring
-        tot = 0
-        N, B, P = w.n_blocks, w.block, min(w.max_ring_passes, w.n_blocks)
-        cu = x.get("cu_seqlens")
-        for t in toks:
-            t = int(t)
-            lo, hi = 0, w.T - 1
-            if w.mask:
-                hi = t
-            if w.mask == 2:
-                c = cu.numpy()
-                lo = int(c[np.searchsorted(c, t, side="right") - 1])
-            bi = t % N if w.layout == 1 else t // B
-            for s in range(P):
-                j = (bi - s) % N
-                if w.layout == 1:
-                    keys = np.arange(B) * N + j
-                    tot += int(((keys >= lo) & (keys <= hi)).sum())
-                else:
-                    a, b = max(lo, j * B), min(hi, j * B + B - 1)
-                    tot += max(0, b - a + 1)
-        return tot
+    import oracle
 
-    return cpu_baseline(w, x, pairs_fn)
+    n_tok = int(os.environ.get("RING_BENCH_CPU_BWD_TOKENS", "1024"))
+    toks = np.linspace(0, w.T - 1, n_tok).astype(np.int64)
+    h, g = 0, 0
+    sub_g = dout.new_zeros(dout.shape[0], 1, dout.shape[2])
+    sub_g[toks, 0] = dout[toks, h]
+    t0 = time.perf_counter()
+    oracle.backward(x["q"][:, [h]], x["k"][:, [g]], x["v"][:, [g]], sub_g, n_blocks=w.n_blocks, layout=w.layout,
+                    mask=w.mask, max_ring_passes=w.max_ring_passes, cu_seqlens=x.get("cu_seqlens"), scale=w.scale,
+                    rows=(np.zeros(n_tok, np.int64), toks), rows_dkdv=True)
+    dt = time.perf_counter() - t0
+    pairs = _pairs_of_rows(w, x, toks)
+    return {"value": 10.0 * w.d * pairs / dt / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+            "sample": "backward terms of %d query rows (head 0, evenly spaced tokens, full key sets) of %s "
+                      "in %.1f s, single thread (dk/dv sums are serial)" % (n_tok, w.name, dt)}
+
+
+def cpu_baseline_for(w, x):
+    return cpu_baseline(w, x, lambda toks: _pairs_of_rows(w, x, toks))
+
+
+def _pairs_of_rows(w, x, toks):
+    """Allowed keys of each listed query token under the workload's mask and ring, summed."""
+    import numpy as np
+
+    tot = 0
+    N, B, P = w.n_blocks, w.block, min(w.max_ring_passes, w.n_blocks)
+    cu = x.get("cu_seqlens")
+    for t in toks:
+        t = int(t)
+        lo, hi = 0, w.T - 1
+        if w.mask:
+            hi = t
+        if w.mask == 2:
+            c = cu.numpy()
+            lo = int(c[np.searchsorted(c, t, side="right") - 1])
+        bi = t % N if w.layout == 1 else t // B
+        for s in range(P):
+            j = (bi - s) % N
+            if w.layout == 1:
+                keys = np.arange(B) * N + j
+                tot += int(((keys >= lo) & (keys <= hi)).sum())
+            else:
+                a, b = max(lo, j * B), min(hi, j * B + B - 1)
+                tot += max(0, b - a + 1)
+    return tot
 
 
 if __name__ == "__main__":

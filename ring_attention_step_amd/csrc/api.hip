@@ -136,7 +136,8 @@ Workspace carve(void* base, int64_t T, int64_t N, int64_t Hq, int64_t Hkv, int64
 }
 
 struct BwdWorkspace {
-    float* Dsum = nullptr;          // [Hq, T]
+    float* Lse2 = nullptr;          // [Hq, T] + kBwdPad floats of padding (tiles may read past a block)
+    float* Dsum = nullptr;          // [Hq, T] + kBwdPad, right after Lse2 in the same allocation
     int32_t* cu = nullptr;
     BwdWork* works = nullptr;       // N
     int64_t* partners = nullptr;    // N x N
@@ -154,7 +155,9 @@ BwdWorkspace carve_bwd(void* base, int64_t T, int64_t N, int64_t Hq, int64_t n_d
         off += align_up(bytes);
         return p;
     };
-    w.Dsum = (float*)take(sizeof(float) * (size_t)(T * Hq));
+    const size_t plane = align_up(sizeof(float) * (size_t)(T * Hq + kBwdPad));
+    w.Lse2 = (float*)take(2 * plane);
+    w.Dsum = w.Lse2 ? (float*)((char*)w.Lse2 + plane) : nullptr;
     w.cu = (int32_t*)take(sizeof(int32_t) * (size_t)(n_docs + 1));
     w.works = (BwdWork*)take(sizeof(BwdWork) * (size_t)N);
     w.partners = (int64_t*)take(sizeof(int64_t) * (size_t)(N * N));
@@ -639,13 +642,22 @@ ra_status ring_attn_backward(const ra_tensor* q, const ra_tensor* k, const ra_te
     } else {
         n_docs = 0;
     }
-    // Matrix-core backward only: bf16 inputs, head_dim 64 or 128, 16-byte rows.
+    // Matrix-core backward only: bf16 inputs, head_dim 64 or 128, 16-byte rows,
+    // at most one ring block per lane of a wave (the per-block tables).
     if (q->dtype != RA_BF16 || (d != 64 && d != 128)) return RA_E_UNSUPPORTED;
+    if (n_blocks > kMaxRingChain) return RA_E_UNSUPPORTED;
     if (!bf16_aligned(q) || !bf16_aligned(k) || !bf16_aligned(v) || !bf16_aligned(dout)) return RA_E_UNSUPPORTED;
     if ((uintptr_t)out->data % 16 || out->stride_tok % (out->dtype == RA_BF16 ? 8 : 4) ||
         out->stride_head % (out->dtype == RA_BF16 ? 8 : 4))
         return RA_E_UNSUPPORTED;
     if ((uintptr_t)dq % 16 || (uintptr_t)dk % 16 || (uintptr_t)dv % 16) return RA_E_UNSUPPORTED;
+    {
+        // 64-row tiles are addressed with 32-bit byte offsets from their first row.
+        const int64_t rm = layout == RA_LAYOUT_STRIPED ? n_blocks : 1;
+        if (!bf16_tile_addressable(rm * q->stride_tok) || !bf16_tile_addressable(rm * k->stride_tok) ||
+            !bf16_tile_addressable(rm * v->stride_tok) || !bf16_tile_addressable(rm * dout->stride_tok))
+            return RA_E_UNSUPPORTED;
+    }
     const int64_t N = n_blocks, B = T / N;
     const int64_t n_qtiles = (B + bwd_tile_q() - 1) / bwd_tile_q();
     const int64_t n_ktiles = (B + bwd_tile_k() - 1) / bwd_tile_k();
@@ -685,6 +697,7 @@ ra_status ring_attn_backward(const ra_tensor* q, const ra_tensor* k, const ra_te
         for (int64_t i : order) {
             BwdWork w;
             w.pos0 = pos0(i);
+            w.loc0 = i * B;
             w.first = (int32_t)pv.size();
             w.count = (int32_t)lists[i].size();
             wv.push_back(w);
@@ -727,6 +740,7 @@ ra_status ring_attn_backward(const ra_tensor* q, const ra_tensor* k, const ra_te
     a.do_st = dout->stride_tok;
     a.do_sh = dout->stride_head;
     a.lse = lse;
+    a.Lse2 = ws.Lse2;
     a.Dsum = ws.Dsum;
     a.dq = dq;
     a.dk = dk;

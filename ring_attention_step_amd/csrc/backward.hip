@@ -12,20 +12,30 @@
 // forward's softmax).
 //
 // Three kernels, no atomics:
-//  * bwd_prep: D_t for every (head, row).
-//  * bwd_dq: one workgroup per (virtual device, head, 128-row query tile),
-//    walking the device's visited key/value blocks in ring order (the
-//    forward's chain tables) in 32-key tiles.  Per wave (32 query rows),
-//    with S^T = K Q^T so that one query row sits in each lane:
+//  * bwd_prep: D_t and lse_t log2(e) for every (head, row), stored in
+//    block-local row order (block b's rows at b B .. b B + B - 1), so that
+//    the rows of any tile of a block are contiguous in both layouts.
+//  * bwd_dq: one workgroup (8 waves x 32 query rows) per (virtual device,
+//    head, 256-row query tile), its q and dout rows held in registers,
+//    walking the device's visited key/value blocks in ring order in 64-key
+//    tiles streamed through LDS.  Per wave, with S^T = K Q^T so that one
+//    query row sits in each lane:
 //      S^T = K Q^T, dP^T = V dout^T, dS^T = P^T (dP^T - D), dq^T += K^T dS^T,
 //    the last through transposing LDS reads of the K tile.
-//  * bwd_dkdv: one workgroup per (key/value block, KV head, 128-key tile),
-//    walking the query blocks that visit the block, every query head of the
-//    KV head's group, in 32-row query tiles.  Per wave (32 keys), with
+//  * bwd_dkdv: one workgroup (4 waves x 32 keys) per (key/value block, KV
+//    head, 128-key tile), its keys and values held in registers, walking the
+//    query blocks that visit the block, every query head of the KV head's
+//    group, in 64-row query tiles streamed through LDS.  Per wave, with
 //    S = Q K^T so that one key sits in each lane:
 //      S = Q K^T, dP = dout V^T, dS = P (dP - D),
 //      dv^T += dout^T P, dk^T += q^T dS,
 //    the last two through transposing reads of the dout and q tiles.
+// Both stream their tiles through a three-stage LDS ring filled by direct
+// global -> LDS loads issued two tiles ahead; a tile's loads have two tiles
+// of compute to land.  Tiles that the mask skips entirely are never loaded:
+// per block the non-skipped tiles form one contiguous range (causal: a
+// skipped prefix or suffix; doc-causal: both), found before the walk.
+//
 // The lane layouts of the 32x32x16 bf16 MFMA are those of the forward
 // kernel: accumulator register i of lane l holds row 8 (i/4) + 4 (l/32) + i%4
 // and column l % 32; an A operand holds row l % 32 and k = 8 (l/32) .. + 7;
@@ -34,6 +44,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <type_traits>
 
 #include "kernels.h"
 #include "plan.h"
@@ -47,23 +58,49 @@ typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int BW_WAVES = 4;
-constexpr int BW_THREADS = 64 * BW_WAVES;
-constexpr int BW_TQ = 32 * BW_WAVES;  // query rows per dq workgroup
-constexpr int BW_TK = 32 * BW_WAVES;  // keys per dk/dv workgroup
-constexpr int BW_T = 32;              // the tile streamed per iteration (keys for dq, queries for dk/dv)
+template <int I>
+using ic = std::integral_constant<int, I>;
 
-// A [32 rows][D] bf16 tile in LDS, 16-byte chunks XOR-swizzled per row:
-// logical chunk c of row r at slot c ^ (r & (D/8 - 1)).
+constexpr int DQ_WAVES = 8;                // dq: two waves per SIMD
+constexpr int DQ_THREADS = 64 * DQ_WAVES;
+constexpr int KV_WAVES = 4;                // dk/dv: one wave per SIMD (its 32 keys' dK and dV
+constexpr int KV_THREADS = 64 * KV_WAVES;  //   accumulators alone take 128 registers)
+constexpr int BW_TQ = 32 * DQ_WAVES;       // query rows per dq workgroup
+constexpr int BW_TK = 32 * KV_WAVES;       // keys per dk/dv workgroup
+constexpr int BW_T = 64;                   // rows of a streamed tile (keys for dq, queries for dk/dv)
+constexpr float kLog2e = 1.4426950408889634f;
+static_assert(kBwdPad >= 64, "a 64-row tile may read 63 rows past the last block");
+
+// A [64 rows][D] bf16 tile in LDS, 16-byte chunks XOR-swizzled per row:
+// logical chunk c of row r at slot c ^ (r & (D/8 - 1)).  Row reads (16 rows
+// of one chunk column per pass) and transposing reads both spread over the
+// banks.
 template <int D>
-__device__ __forceinline__ int swz(int r) {
+__device__ __forceinline__ constexpr int swz(int r) {
     return r & (D / 8 - 1);
 }
 
 __device__ __forceinline__ i16x4 lds_read_tr(const bf16* p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p));
+}
+
+// s_waitcnt vmcnt(N): all but this wave's N most recent vector-memory loads
+// have landed; through the builtin so the compiler's own bookkeeping sees it.
+template <int N>
+__device__ __forceinline__ void wait_loads_but() {
+    static_assert(N >= 0 && N < 16, "vmcnt field");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
+
+// Workgroup barrier that waits for this wave's LDS traffic only: the direct
+// stage loads stay in flight across it (each is waited for explicitly
+// before the barrier that hands its buffer to the readers).
+__device__ __forceinline__ void phase_barrier() {
+    __builtin_amdgcn_sched_barrier(0);
+    __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
 }
 
 // Document end (start of the next document) of global position t.
@@ -76,30 +113,43 @@ __device__ __forceinline__ int64_t doc_end(const int32_t* cu, int64_t n_docs, in
     return cu[lo + 1];
 }
 
-// Cooperative copy of rows [r0, r0 + 32) of a [rows][D] bf16 matrix (row
-// stride rs elements) into a swizzled LDS tile; rows at or past n_rows copy
-// row n_rows - 1 (callers mask them), and n_rows == 0 copies zeros.
+// Byte offset, from the tile's first row, of the global 16-byte chunk that
+// lands in LDS slot s = 64 n + lane of a [64][D] tile (row s / (D/8), slot
+// column s % (D/8), logical chunk slot ^ swz(row)); rows past last_row
+// re-read last_row (callers mask them).
 template <int D>
-__device__ __forceinline__ void load_tile(bf16* dst, const bf16* src, int64_t rs, int64_t r0, int64_t n_rows) {
+__device__ __forceinline__ uint32_t chunk_offset(int lane, int n, uint32_t rs_bytes, int last_row) {
     constexpr int CH = D / 8;
-    for (int x = threadIdx.x; x < BW_T * CH; x += BW_THREADS) {
-        const int r = x / CH, c = x % CH;
-        int64_t row = r0 + r;
-        if (row > n_rows - 1) row = n_rows - 1;
-        u32x4 val = u32x4{0, 0, 0, 0};
-        if (row >= 0) val = *(const u32x4*)(src + row * rs + 8 * c);
-        *(u32x4*)(dst + r * D + 8 * (c ^ swz<D>(r))) = val;
+    const int s = 64 * n + lane;
+    const int r = s / CH;
+    const uint32_t row = (uint32_t)(r < last_row ? r : last_row);
+    return row * rs_bytes + 16u * (uint32_t)((s % CH) ^ swz<D>(r));
+}
+
+// Issue this wave's NL direct loads of one tile (16 bytes per lane each):
+// load i writes the 1 KB block of slots 64 (base_n + i) .. + 63.
+template <int NL>
+__device__ __forceinline__ void issue_loads(bf16* dst, int base_n, const char* tile, const uint32_t (&off)[NL]) {
+    int gofs = base_n * 512;
+    __asm__ volatile("" : "+s"(gofs));
+#pragma unroll
+    for (int i = 0; i < NL; i++) {
+        uint32_t o = off[i];
+        __asm__ volatile("" : "+v"(o));  // keeps the uniform-base + 32-bit lane offset form
+        __builtin_amdgcn_global_load_lds(tile + o, (lds_void*)(dst + gofs + 512 * i), 16, 0, 0);
     }
 }
 
 // MFMA operand offsets (elements) into a swizzled [rows][D] tile:
 //  row operand (A or B) of row 32 rb + col, dims 16 kc + 8 half .. + 7;
-//  transposing pair for rows 16 q + vrow (+8), dims 32 db + 16 g + 4 (j % 4).
+//  transposing pair for rows 16 q + vrow (+8), dims 32 db + 16 g + 4 (j % 4),
+//  which gives lane l dim 32 db + l % 32 and, as its 8 k values, the rows
+//  16 q + 4 half + 0..3 and 16 q + 8 + 4 half + 0..3 (accumulator order).
 template <int D>
 struct TileOps {
-    int row_off[D / 16];   // + 32 rb D for row block rb
-    int tr_off0[D / 32];   // rows 16 q + vrow      (+ 16 q D)
-    int tr_off1[D / 32];   // rows 16 q + vrow + 8  (+ 16 q D)
+    int row_off[D / 16];
+    int tr_off0[D / 32];
+    int tr_off1[D / 32];
     __device__ TileOps(int lane) {
         const int col = lane & 31, half = lane >> 5;
 #pragma unroll
@@ -115,8 +165,6 @@ struct TileOps {
     __device__ __forceinline__ bf16x8 row(const bf16* t, int rb, int kc) const {
         return *(const bf16x8*)(t + row_off[kc] + 32 * D * rb);
     }
-    // Transposed operand of 16-row chunk q, dim block db (its k index runs
-    // over the rows in accumulator order: 16 q + 4 half + 0..3, then + 8).
     __device__ __forceinline__ bf16x8 tr(const bf16* t, int q, int db) const {
         const i16x4 r1 = lds_read_tr(t + tr_off0[db] + 16 * q * D);
         const i16x4 r2 = lds_read_tr(t + tr_off1[db] + 16 * q * D);
@@ -128,7 +176,7 @@ __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// Accumulator register order -> bf16 B operand pair (16-row chunks 2 h, 2 h + 1).
+// Accumulator register order -> bf16 operand pair (16-row chunks 2 h, 2 h + 1).
 __device__ __forceinline__ void acc_to_b(const f32x16& acc, bf16x8& b0, bf16x8& b1) {
 #pragma unroll
     for (int i = 0; i < 8; i++) {
@@ -137,19 +185,30 @@ __device__ __forceinline__ void acc_to_b(const f32x16& acc, bf16x8& b0, bf16x8& 
     }
 }
 
-// ---- D = rowsum(dout * out) ----
+// ---- D = rowsum(dout * out), lse log2(e) ----
 // d / 8 lanes per (token, head) row, 8 elements each, reduced by shuffles.
+// Outputs in block-local order: row u of block b (token pos(b, u)) at
+// h T + b B + u; lse = -inf (a row with no key) becomes +inf, so that every
+// P of the row is exp2(-inf) = 0.
 __global__ void bwd_prep_kernel(const BwdArgs a) {
     const int lanes = a.d / 8;
     const int64_t n = (int64_t)a.T * a.Hq;
+    // The padding after both arrays (tiles of a block's last rows read up to
+    // 63 rows past it): finite values.
+    if (blockIdx.x == 0 && threadIdx.x < kBwdPad) {
+        a.Dsum[n + threadIdx.x] = 0.f;
+        a.Lse2[n + threadIdx.x] = INFINITY;
+    }
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t x0 = (int64_t)blockIdx.x * blockDim.x; x0 < n * lanes; x0 += stride) {
         const int64_t x = x0 + threadIdx.x;
         const int64_t row = x / lanes;
         const int c = (int)(x % lanes);
         float s = 0.f;
+        int64_t t = 0, h = 0;
         if (row < n) {
-            const int64_t t = row / a.Hq, h = row % a.Hq;
+            t = row / a.Hq;
+            h = row % a.Hq;
             const bf16x8 gv = *(const bf16x8*)((const bf16*)a.dout + t * a.do_st + h * a.do_sh + 8 * c);
             const int64_t oe = t * a.out_st + h * a.out_sh + 8 * c;
             if (a.out_bf16) {
@@ -166,19 +225,38 @@ __global__ void bwd_prep_kernel(const BwdArgs a) {
             }
         }
         for (int w = 1; w < lanes; w <<= 1) s += __shfl_xor(s, w, 64);
-        if (row < n && c == 0) a.Dsum[(row % a.Hq) * a.T + row / a.Hq] = s;
+        if (row < n && c == 0) {
+            const int64_t loc = a.pos_stride == 1 ? t : (t % a.pos_stride) * a.B + t / a.pos_stride;
+            const float l = a.lse[h * a.T + t];
+            a.Dsum[h * a.T + loc] = s;
+            a.Lse2[h * a.T + loc] = l == -INFINITY ? INFINITY : l * kLog2e;
+        }
     }
+}
+
+// Non-skipped streamed tiles of a block: [lo, hi] (hi < lo when none).
+template <typename Cls3>
+__device__ __forceinline__ void tile_range(int n_tiles, Cls3 cls, int& lo, int& hi) {
+    lo = 0;
+    hi = n_tiles - 1;
+    while (lo <= hi && cls(lo) == kSkip) lo++;
+    while (hi >= lo && cls(hi) == kSkip) hi--;
 }
 
 // ---- dq ----
 template <int D>
-__global__ __launch_bounds__(BW_THREADS, 2) void bwd_dq_kernel(const BwdArgs a) {
-    __shared__ __attribute__((aligned(16))) bf16 k_t[BW_T * D];
-    __shared__ __attribute__((aligned(16))) bf16 v_t[BW_T * D];
+__global__ __launch_bounds__(DQ_THREADS, 1) void bwd_dq_kernel(const BwdArgs a) {
+    constexpr int TE = BW_T * D;              // elements of one [64][D] tile
+    constexpr int NL = 2 * (TE / 512 / DQ_WAVES);  // loads per wave per stage: K tile, then V tile
+    // Three stages, one array each (K tile, then V tile): the compiler can
+    // then tell the direct loads into one stage from the reads of another.
+    __shared__ bf16 st0[2 * TE], st1[2 * TE], st2[2 * TE];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int half = lane >> 5, col = lane & 31;
-    const int qt = blockIdx.x % a.n_qtiles;
+    // Workgroups of one (device, head) run their q-tiles last first (the
+    // causal ones with the most keys start early).
+    const int qt = a.n_qtiles - 1 - (int)(blockIdx.x % a.n_qtiles);
     const int head = (blockIdx.x / a.n_qtiles) % a.Hq;
     const int widx = blockIdx.x / (a.n_qtiles * a.Hq);
     const int kvh = head / a.group;
@@ -186,13 +264,13 @@ __global__ __launch_bounds__(BW_THREADS, 2) void bwd_dq_kernel(const BwdArgs a) 
     const int64_t B = a.B, ps = a.pos_stride;
     const int64_t u = (int64_t)qt * BW_TQ + wave * 32 + col;  // this lane's query row (local)
     const bool row_ok = u < B;
-    const int64_t t_row = w.pos0 + (row_ok ? u : B - 1) * ps;  // its global position = token row
-    const float lse_row = a.lse[head * a.T + t_row];
-    const float lse2 = (row_ok && lse_row != -INFINITY) ? lse_row * 1.4426950408889634f : INFINITY;
-    const float drow = row_ok ? a.Dsum[head * a.T + t_row] : 0.f;
+    const int64_t ur = row_ok ? u : B - 1;
+    const int64_t t_row = w.pos0 + ur * ps;  // its global position = token row
+    const float lse2 = row_ok ? a.Lse2[head * a.T + w.loc0 + ur] : INFINITY;
+    const float drow = row_ok ? a.Dsum[head * a.T + w.loc0 + ur] : 0.f;
     const int64_t ds_row = a.mask == kMaskDoc ? doc_start(a.cu, a.n_docs, t_row) : 0;
 
-    // This wave's query and dout rows as B operands (row u, dims 16 kc + 8 half .. + 7).
+    // This wave's q and dout rows as B operands (row u, dims 16 kc + 8 half .. + 7).
     bf16x8 qf[D / 16], gf[D / 16];
     {
         const bf16* qp = (const bf16*)a.q + t_row * a.q_st + head * a.q_sh + 8 * half;
@@ -213,55 +291,184 @@ __global__ __launch_bounds__(BW_THREADS, 2) void bwd_dq_kernel(const BwdArgs a) 
     const int64_t ds_min = a.mask == kMaskDoc ? doc_start(a.cu, a.n_docs, t_min) : 0;
     const int64_t ds_max = a.mask == kMaskDoc ? doc_start(a.cu, a.n_docs, t_max) : 0;
     const int nkt = (int)((B + BW_T - 1) / BW_T);
+    auto cls_of = [&](int64_t kp, int kt) __attribute__((always_inline)) {
+        const int64_t w0 = (int64_t)kt * BW_T, w1 = (B < w0 + BW_T ? B : w0 + BW_T) - 1;
+        return classify(a.mask, t_min, t_max, ds_min, ds_max, kp + w0 * ps, kp + w1 * ps);
+    };
+    // The chain table, one visited block per lane (lane e < count holds
+    // block e): its first position, non-skipped key tiles [lo, hi] and fully
+    // visible ones [flo, fhi] (contiguous, between the partial tiles).  The
+    // loop reads it with readlane and so issues no memory loads besides the
+    // stage loads (a load waited for inside the loop would also wait for
+    // every stage load issued before it).
+    int tb_lo = 0, tb_hi = -1, tb_flo = 0, tb_fhi = -1;
+    int64_t tb_kp = 0;
+    if (lane < w.count) {
+        tb_kp = a.partners[w.first + lane];
+        tile_range(nkt, [&](int x) { return cls_of(tb_kp, x); }, tb_lo, tb_hi);
+        tb_flo = tb_lo;
+        tb_fhi = tb_hi;
+        while (tb_flo <= tb_fhi && cls_of(tb_kp, tb_flo) != kFull) tb_flo++;
+        while (tb_fhi >= tb_flo && cls_of(tb_kp, tb_fhi) != kFull) tb_fhi--;
+    }
+    auto rl32 = [&](int x, int e) __attribute__((always_inline)) { return __builtin_amdgcn_readlane(x, e); };
+    auto rl64 = [&](int64_t x, int e) __attribute__((always_inline)) {
+        const uint32_t lo32 = __builtin_amdgcn_readlane((int)(uint32_t)x, e);
+        const uint32_t hi32 = __builtin_amdgcn_readlane((int)(uint32_t)((uint64_t)x >> 32), e);
+        return (int64_t)(((uint64_t)hi32 << 32) | lo32);
+    };
+    // Streamed tiles: every non-skipped key tile of every visited block.
+    struct Cursor {
+        int e, kt, hi;
+        int64_t kp;  // position of the block's row 0
+    };
+    auto cur_next = [&](Cursor& c) __attribute__((always_inline)) {
+        int e = c.e, kt = c.kt + 1, hi = c.hi;
+        while (kt > hi && e + 1 < w.count) {
+            e++;
+            kt = rl32(tb_lo, e);
+            hi = rl32(tb_hi, e);
+        }
+        if (kt <= hi) c = Cursor{e, kt, hi, rl64(tb_kp, e)};
+    };
+    int nT = 0;
+    for (int e = 0; e < w.count; e++) nT += rl32(tb_hi, e) - rl32(tb_lo, e) + 1;
 
-    for (int e = 0; e < w.count; e++) {
-        const int64_t kp = a.partners[w.first + e];  // position of the key block's row 0
-        // This row's allowed keys of the block: local indices [w_lo, w_hi).
-        int64_t w_lo = 0, w_hi = row_ok ? B : 0;
+    // This row's allowed keys of the block at kp: local indices [w_lo, w_hi).
+    int64_t w_lo = 0, w_hi = 0;
+    auto row_bounds = [&](int64_t kp) __attribute__((always_inline)) {
+        w_lo = 0;
+        w_hi = row_ok ? B : 0;
         if (a.mask != kMaskNone) {
             const int64_t lim = t_row - kp;
             const int64_t last = lim < 0 ? -1 : lim / ps;
             if (last + 1 < w_hi) w_hi = last + 1;
             if (a.mask == kMaskDoc && ds_row - kp > 0) w_lo = ds_row - kp;
         }
-        const bf16* kb = (const bf16*)a.k + kp * a.k_st + kvh * a.k_sh;
-        const bf16* vb = (const bf16*)a.v + kp * a.v_st + kvh * a.v_sh;
-        for (int kt = 0; kt < nkt; kt++) {
-            const int64_t w0 = (int64_t)kt * BW_T, w1 = (B < w0 + BW_T ? B : w0 + BW_T) - 1;
-            const Cls cls = classify(a.mask, t_min, t_max, ds_min, ds_max, kp + w0 * ps, kp + w1 * ps);
-            if (cls == kSkip) continue;
-            __syncthreads();
-            load_tile<D>(k_t, kb, ps * a.k_st, w0, B);
-            load_tile<D>(v_t, vb, ps * a.v_st, w0, B);
-            __syncthreads();
-            // S^T and dP^T: the tile's 32 keys (rows) x this wave's 32 query rows (columns).
+    };
+
+    // Chunk offsets of this wave's loads (K: loads 0 .. NL/2-1 of the tile's
+    // K part, V likewise), recomputed for a ragged last tile.
+    const uint32_t k_rs = (uint32_t)(ps * a.k_st * 2), v_rs = (uint32_t)(ps * a.v_st * 2);
+    const int last_full = BW_T - 1, last_ragged = (int)((B - 1) % BW_T);
+    const int ragged_kt = B % BW_T ? nkt - 1 : -1;
+    // Both offset sets stay in registers and a ragged tile selects its own
+    // (no branch around the loads).
+    uint32_t off_k[NL / 2], off_v[NL / 2], rag_k[NL / 2], rag_v[NL / 2];
+#pragma unroll
+    for (int i = 0; i < NL / 2; i++) {
+        off_k[i] = chunk_offset<D>(lane, wave * (NL / 2) + i, k_rs, last_full);
+        off_v[i] = chunk_offset<D>(lane, wave * (NL / 2) + i, v_rs, last_full);
+        rag_k[i] = chunk_offset<D>(lane, wave * (NL / 2) + i, k_rs, last_ragged);
+        rag_v[i] = chunk_offset<D>(lane, wave * (NL / 2) + i, v_rs, last_ragged);
+    }
+    const char* const k_head = (const char*)((const bf16*)a.k + kvh * a.k_sh);
+    const char* const v_head = (const char*)((const bf16*)a.v + kvh * a.v_sh);
+    auto issue = [&](bf16* ks, bf16* vs, const Cursor& c) __attribute__((always_inline)) {
+        const int64_t row0 = c.kp + (int64_t)c.kt * BW_T * ps;  // token of the tile's first key
+        const bool rag = c.kt == ragged_kt;
+        uint32_t ok[NL / 2], ov[NL / 2];
+#pragma unroll
+        for (int i = 0; i < NL / 2; i++) {
+            ok[i] = rag ? rag_k[i] : off_k[i];
+            ov[i] = rag ? rag_v[i] : off_v[i];
+        }
+        issue_loads<NL / 2>(ks, wave * (NL / 2), k_head + row0 * a.k_st * 2, ok);
+        issue_loads<NL / 2>(vs, wave * (NL / 2), v_head + row0 * a.v_st * 2, ov);
+        __asm__ volatile("; tile issued" ::: "memory");
+    };
+
+    int cc_flo = 0, cc_fhi = -1;  // fully visible tiles of the compute cursor's block
+    auto compute = [&](const bf16* ks, const bf16* vs, const Cursor& c) __attribute__((always_inline)) {
+        const int64_t w0 = (int64_t)c.kt * BW_T;
+        const bool full = c.kt != ragged_kt && c.kt >= cc_flo && c.kt <= cc_fhi;
+        // Allowed keys shifted by -4 half, relative to the tile (|x| <= B + 4).
+        const int x_lo = (int)(w_lo - w0) - 4 * half, x_hi = (int)(w_hi - w0) - 4 * half;
+#pragma unroll
+        for (int kb = 0; kb < 2; kb++) {
+            // S^T and dP^T: keys 32 kb .. + 31 of the tile (rows) x this wave's rows.
             f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
             for (int kc = 0; kc < D / 16; kc++) {
-                s = mfma(ops.row(k_t, 0, kc), qf[kc], s);
-                dp = mfma(ops.row(v_t, 0, kc), gf[kc], dp);
+                s = mfma(ops.row(ks, kb, kc), qf[kc], s);
+                dp = mfma(ops.row(vs, kb, kc), gf[kc], dp);
             }
-            // dS^T = P^T (dP^T - D); register i holds key w0 + 8 (i/4) + 4 half + i%4.
-            const bool full = cls == kFull && w1 - w0 + 1 == BW_T;
-            const int64_t x_lo = w_lo - w0 - 4 * half, x_hi = w_hi - w0 - 4 * half;
+            // dS^T = P^T (dP^T - D); register i holds key 32 kb + 8 (i/4) + 4 half + i%4.
+            // A masked key's exponent becomes -inf (P = 0, dS = 0): selects,
+            // so that no per-element branch is formed around the exp2.
             f32x16 dsv;
 #pragma unroll
             for (int i = 0; i < 16; i++) {
-                const int x = 8 * (i / 4) + (i % 4);
-                float p = __builtin_amdgcn_exp2f(fmaf(s[i], a.c2, -lse2));
-                if (!full && (x < x_lo || x >= x_hi)) p = 0.f;
-                dsv[i] = p * (dp[i] - drow);
+                const int x = 32 * kb + 8 * (i / 4) + (i % 4);
+                float arg = fmaf(s[i], a.c2, -lse2);
+                if (!full) arg = (x >= x_lo) & (x < x_hi) ? arg : -INFINITY;
+                dsv[i] = __builtin_amdgcn_exp2f(arg) * (dp[i] - drow);
             }
             bf16x8 b0, b1;
             acc_to_b(dsv, b0, b1);
-            // dq^T += K^T dS^T over the tile's two 16-key chunks.
+            // dq^T += K^T dS^T over the two 16-key chunks of this half.
 #pragma unroll
             for (int db = 0; db < D / 32; db++) {
-                dq[db] = mfma(ops.tr(k_t, 0, db), b0, dq[db]);
-                dq[db] = mfma(ops.tr(k_t, 1, db), b1, dq[db]);
+                dq[db] = mfma(ops.tr(ks, 2 * kb, db), b0, dq[db]);
+                dq[db] = mfma(ops.tr(ks, 2 * kb + 1, db), b1, dq[db]);
             }
+            __builtin_amdgcn_sched_barrier(0);  // one half's S / dP live at a time
         }
+    };
+
+    // ---- pipeline: tile j in stage j % 3, issued two tiles ahead ----
+    Cursor cl{-1, 0, -1, 0};
+    cur_next(cl);
+    Cursor cc = cl;
+    auto enter_block = [&](const Cursor& c) __attribute__((always_inline)) {
+        row_bounds(c.kp);
+        cc_flo = rl32(tb_flo, c.e);
+        cc_fhi = rl32(tb_fhi, c.e);
+    };
+    if (nT > 0) enter_block(cc);
+    auto iteration = [&](int j, auto slot) __attribute__((always_inline)) {
+        constexpr int S = decltype(slot)::value;  // j % 3
+        bf16* const kc = S == 0 ? st0 : (S == 1 ? st1 : st2);
+        bf16* const vc = kc + TE;
+        bf16* const kn = S == 0 ? st2 : (S == 1 ? st0 : st1);  // stage j + 2 (= j - 1)
+        bf16* const vn = kn + TE;
+        // Tile j + 2 (past the end: the last tile again, into a stage no
+        // later iteration reads), so that every iteration issues NL loads.
+        if (j + 2 < nT) cur_next(cl);
+        issue(kn, vn, cl);
+        compute(kc, vc, cc);
+        if (j + 1 < nT) {
+            const int e_was = cc.e;
+            cur_next(cc);
+            if (cc.e != e_was) enter_block(cc);
+        }
+        wait_loads_but<NL>();  // tile j + 1 has landed
+        phase_barrier();
+    };
+    if (nT > 0) {
+        wait_loads_but<0>();  // q / dout rows in registers: the waits below count stage loads only
+        const Cursor c0 = cl;
+        if (nT > 1) cur_next(cl);
+        issue(st0, st0 + TE, c0);
+        issue(st1, st1 + TE, cl);
+        wait_loads_but<NL>();
+        phase_barrier();
+        // Whole triples of tiles in the loop, the rest after it: the loop
+        // body is straight-line code, so at every point the compiler knows
+        // exactly which stage's loads are still in flight (a conditional
+        // iteration inside the loop would give it paths on which the stage
+        // about to be read had just been issued, and a wait for all loads).
+        int j = 0;
+        for (; j + 3 <= nT; j += 3) {
+            iteration(j, ic<0>{});
+            iteration(j + 1, ic<1>{});
+            iteration(j + 2, ic<2>{});
+        }
+        if (j < nT) iteration(j, ic<0>{});
+        if (j + 1 < nT) iteration(j + 1, ic<1>{});
+        wait_loads_but<0>();  // no load may land in LDS after the workgroup ends
     }
+
     if (!row_ok) return;
     char* ob = (char*)a.dq;
     const int64_t oe = (t_row * a.Hq + head) * D + 4 * half;
@@ -279,15 +486,15 @@ __global__ __launch_bounds__(BW_THREADS, 2) void bwd_dq_kernel(const BwdArgs a) 
 
 // ---- dk, dv ----
 template <int D>
-__global__ __launch_bounds__(BW_THREADS, 1) void bwd_dkdv_kernel(const BwdArgs a) {
-    // This workgroup's keys and values (one swizzled 32-row tile per wave),
-    // and the current query tile: q, dout, and per row lse * log2(e) and D.
-    __shared__ __attribute__((aligned(16))) bf16 k_all[BW_TK * D];
-    __shared__ __attribute__((aligned(16))) bf16 v_all[BW_TK * D];
-    __shared__ __attribute__((aligned(16))) bf16 q_t[BW_T * D];
-    __shared__ __attribute__((aligned(16))) bf16 g_t[BW_T * D];
-    __shared__ __attribute__((aligned(16))) float lse_t[BW_T];
-    __shared__ __attribute__((aligned(16))) float d_t[BW_T];
+__global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(const BwdArgs a) {
+    constexpr int TE = BW_T * D;
+    constexpr int NQ = TE / 512 / KV_WAVES;  // loads per wave per stage for each of q and dout
+    constexpr int NL = 2 * NQ + 1;  // + this wave's copy of the tile's lse2 / D rows
+    // Three stages, one array each: the q tile, the dout tile, then per wave
+    // lse2 of the tile's 64 rows and their D (1 KB, the upper half a
+    // duplicate written by lanes 32..63).
+    constexpr int SE = 2 * TE + KV_WAVES * 512;  // elements of one stage
+    __shared__ __attribute__((aligned(16))) bf16 st0[SE], st1[SE], st2[SE];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int half = lane >> 5, col = lane & 31;
@@ -302,17 +509,18 @@ __global__ __launch_bounds__(BW_THREADS, 1) void bwd_dkdv_kernel(const BwdArgs a
     const int64_t p_key = w.pos0 + (key_ok ? wk : B - 1) * ps;  // its global position = token row
     const int64_t de_key = a.mask == kMaskDoc ? doc_end(a.cu, a.n_docs, p_key) : 0;
 
+    // This wave's keys and values as B operands (key wk, dims 16 kc + 8 half .. + 7).
+    bf16x8 kf[D / 16], vf[D / 16];
     {
-        const bf16* kb = (const bf16*)a.k + w.pos0 * a.k_st + kvh * a.k_sh;
-        const bf16* vb = (const bf16*)a.v + w.pos0 * a.v_st + kvh * a.v_sh;
-        for (int ti = 0; ti < BW_WAVES; ti++) {
-            load_tile<D>(k_all + ti * BW_T * D, kb, ps * a.k_st, wk0 + ti * BW_T, B);
-            load_tile<D>(v_all + ti * BW_T * D, vb, ps * a.v_st, wk0 + ti * BW_T, B);
+        const bf16* kp = (const bf16*)a.k + p_key * a.k_st + kvh * a.k_sh + 8 * half;
+        const bf16* vp = (const bf16*)a.v + p_key * a.v_st + kvh * a.v_sh + 8 * half;
+#pragma unroll
+        for (int kc = 0; kc < D / 16; kc++) {
+            kf[kc] = *(const bf16x8*)(kp + 16 * kc);
+            vf[kc] = *(const bf16x8*)(vp + 16 * kc);
         }
     }
     const TileOps<D> ops(lane);
-    const bf16* k_w = k_all + wave * BW_T * D;
-    const bf16* v_w = v_all + wave * BW_T * D;
     f32x16 dk[D / 32], dv[D / 32];
 #pragma unroll
     for (int db = 0; db < D / 32; db++) dk[db] = dv[db] = f32x16{};
@@ -320,75 +528,227 @@ __global__ __launch_bounds__(BW_THREADS, 1) void bwd_dkdv_kernel(const BwdArgs a
     const int64_t wl = (B < wk0 + BW_TK ? B : wk0 + BW_TK) - 1;  // last key of the workgroup
     const int64_t tk_min = w.pos0 + wk0 * ps, tk_max = w.pos0 + wl * ps;
     const int nqt = (int)((B + BW_T - 1) / BW_T);
-    for (int e = 0; e < w.count; e++) {
-        const int64_t qp = a.rpartners[w.first + e];  // position of the query block's row 0
-        // This key's allowed query rows of the block: local indices [u_lo, u_hi).
-        int64_t u_lo = 0, u_hi = key_ok ? B : 0;
-        if (a.mask != kMaskNone) {
-            const int64_t rel = p_key - qp;  // a query must not precede the key
-            const int64_t first = rel <= 0 ? 0 : (rel + ps - 1) / ps;
-            u_lo = first;
-            if (a.mask == kMaskDoc && de_key - qp < u_hi) u_hi = de_key - qp;
-        }
-        for (int hq = kvh * a.group; hq < (kvh + 1) * a.group; hq++) {
-            const bf16* qb = (const bf16*)a.q + qp * a.q_st + hq * a.q_sh;
-            const bf16* gb = (const bf16*)a.dout + qp * a.do_st + hq * a.do_sh;
-            for (int qt = 0; qt < nqt; qt++) {
-                const int64_t u0 = (int64_t)qt * BW_T, u1 = (B < u0 + BW_T ? B : u0 + BW_T) - 1;
-                const int64_t t0 = qp + u0 * ps, t1 = qp + u1 * ps;
-                const int64_t ds0 = a.mask == kMaskDoc ? doc_start(a.cu, a.n_docs, t0) : 0;
-                const int64_t ds1 = a.mask == kMaskDoc ? doc_start(a.cu, a.n_docs, t1) : 0;
-                const Cls cls = classify(a.mask, t0, t1, ds0, ds1, tk_min, tk_max);
-                if (cls == kSkip) continue;
-                __syncthreads();
-                load_tile<D>(q_t, qb, ps * a.q_st, u0, B);
-                load_tile<D>(g_t, gb, ps * a.do_st, u0, B);
-                if (threadIdx.x < BW_T) {
-                    const int64_t uu = u0 + threadIdx.x;
-                    const int64_t tt = qp + (uu < B ? uu : B - 1) * ps;
-                    const float l = a.lse[hq * a.T + tt];
-                    lse_t[threadIdx.x] = l == -INFINITY ? INFINITY : l * 1.4426950408889634f;
-                    d_t[threadIdx.x] = a.Dsum[hq * a.T + tt];
-                }
-                __syncthreads();
-                // S and dP: the tile's 32 query rows (rows) x this wave's 32 keys (columns).
-                f32x16 s = f32x16{}, dp = f32x16{};
-#pragma unroll
-                for (int kc = 0; kc < D / 16; kc++) {
-                    s = mfma(ops.row(q_t, 0, kc), ops.row(k_w, 0, kc), s);
-                    dp = mfma(ops.row(g_t, 0, kc), ops.row(v_w, 0, kc), dp);
-                }
-                // Register i holds query row u0 + 8 (i/4) + 4 half + i%4.
-                const bool full = cls == kFull && u1 - u0 + 1 == BW_T;
-                const int64_t x_lo = u_lo - u0 - 4 * half, x_hi = u_hi - u0 - 4 * half;
-                f32x16 pv, dsv;
-#pragma unroll
-                for (int g4 = 0; g4 < 4; g4++) {
-                    const f32x4 l4 = *(const f32x4*)(lse_t + 8 * g4 + 4 * half);
-                    const f32x4 d4 = *(const f32x4*)(d_t + 8 * g4 + 4 * half);
-#pragma unroll
-                    for (int r = 0; r < 4; r++) {
-                        const int i = 4 * g4 + r, x = 8 * g4 + r;
-                        float p = __builtin_amdgcn_exp2f(fmaf(s[i], a.c2, -l4[r]));
-                        if (!full && (x < x_lo || x >= x_hi)) p = 0.f;
-                        pv[i] = p;
-                        dsv[i] = p * (dp[i] - d4[r]);
-                    }
-                }
-                bf16x8 p0, p1, s0, s1;
-                acc_to_b(pv, p0, p1);
-                acc_to_b(dsv, s0, s1);
-                // dv^T += dout^T P and dk^T += q^T dS over the tile's two 16-row chunks.
-#pragma unroll
-                for (int db = 0; db < D / 32; db++) {
-                    dv[db] = mfma(ops.tr(g_t, 0, db), p0, dv[db]);
-                    dv[db] = mfma(ops.tr(g_t, 1, db), p1, dv[db]);
-                    dk[db] = mfma(ops.tr(q_t, 0, db), s0, dk[db]);
-                    dk[db] = mfma(ops.tr(q_t, 1, db), s1, dk[db]);
-                }
+    auto cls_of = [&](int64_t qp, int qt) __attribute__((always_inline)) {
+        const int64_t u0 = (int64_t)qt * BW_T, u1 = (B < u0 + BW_T ? B : u0 + BW_T) - 1;
+        const int64_t t0 = qp + u0 * ps, t1 = qp + u1 * ps;
+        const int64_t ds0 = a.mask == kMaskDoc ? doc_start(a.cu, a.n_docs, t0) : 0;
+        const int64_t ds1 = a.mask == kMaskDoc ? doc_start(a.cu, a.n_docs, t1) : 0;
+        return classify(a.mask, t0, t1, ds0, ds1, tk_min, tk_max);
+    };
+    // The table of visiting query blocks, one per lane (lane e < count
+    // holds block e): its first position, non-skipped query tiles [lo, hi]
+    // and fully visible ones [flo, fhi]; read with readlane in the loop,
+    // which then issues no memory loads besides the stage loads.
+    int tb_lo = 0, tb_hi = -1, tb_flo = 0, tb_fhi = -1;
+    int64_t tb_qp = 0;
+    if (lane < w.count) {
+        tb_qp = a.rpartners[w.first + lane];
+        tile_range(nqt, [&](int x) { return cls_of(tb_qp, x); }, tb_lo, tb_hi);
+        tb_flo = tb_lo;
+        tb_fhi = tb_hi;
+        while (tb_flo <= tb_fhi && cls_of(tb_qp, tb_flo) != kFull) tb_flo++;
+        while (tb_fhi >= tb_flo && cls_of(tb_qp, tb_fhi) != kFull) tb_fhi--;
+    }
+    auto rl32 = [&](int x, int e) __attribute__((always_inline)) { return __builtin_amdgcn_readlane(x, e); };
+    auto rl64 = [&](int64_t x, int e) __attribute__((always_inline)) {
+        const uint32_t lo32 = __builtin_amdgcn_readlane((int)(uint32_t)x, e);
+        const uint32_t hi32 = __builtin_amdgcn_readlane((int)(uint32_t)((uint64_t)x >> 32), e);
+        return (int64_t)(((uint64_t)hi32 << 32) | lo32);
+    };
+    // Streamed tiles: for every visiting query block, every query head of
+    // the group, its non-skipped query tiles.
+    struct Cursor {
+        int e, h, qt, lo, hi;
+        int64_t qp;  // position of the query block's row 0
+    };
+    auto enter = [&](Cursor& c, int e) __attribute__((always_inline)) {
+        c.e = e;
+        c.h = 0;
+        c.qp = rl64(tb_qp, e);
+        c.lo = rl32(tb_lo, e);
+        c.hi = rl32(tb_hi, e);
+        c.qt = c.lo;
+    };
+    // The next tile after c (c unchanged when there is none).
+    auto cur_next = [&](Cursor& c) __attribute__((always_inline)) {
+        Cursor n = c;
+        n.qt++;
+        while (n.qt > n.hi) {
+            if (n.h + 1 < a.group && n.lo <= n.hi) {
+                n.h++;
+                n.qt = n.lo;
+            } else if (n.e + 1 < w.count) {
+                enter(n, n.e + 1);
+            } else {
+                return;
             }
         }
+        c = n;
+    };
+    int nT = 0;
+    for (int e = 0; e < w.count; e++) {
+        const int lo = rl32(tb_lo, e), hi = rl32(tb_hi, e);
+        if (hi >= lo) nT += a.group * (hi - lo + 1);
     }
+
+    // This key's allowed query rows of the block at qp: local indices [u_lo, u_hi).
+    int64_t u_lo = 0, u_hi = 0;
+    auto key_bounds = [&](int64_t qp) __attribute__((always_inline)) {
+        u_lo = 0;
+        u_hi = key_ok ? B : 0;
+        if (a.mask != kMaskNone) {
+            const int64_t rel = p_key - qp;  // a query must not precede the key
+            u_lo = rel <= 0 ? 0 : (rel + ps - 1) / ps;
+            if (a.mask == kMaskDoc && de_key - qp < u_hi) u_hi = de_key - qp;
+        }
+    };
+
+    // Load offsets: q / dout chunks (NQ loads each), and the lse2 / D rows
+    // (lanes 0..15: lse2 rows 4 l .. 4 l + 3; lanes 16..31: D rows; lanes
+    // 32..63 repeat lanes 0..31).
+    const uint32_t q_rs = (uint32_t)(ps * a.q_st * 2), g_rs = (uint32_t)(ps * a.do_st * 2);
+    const int last_full = BW_T - 1, last_ragged = (int)((B - 1) % BW_T);
+    const int ragged_qt = B % BW_T ? nqt - 1 : -1;
+    // Both offset sets stay in registers and a ragged tile selects its own.
+    uint32_t off_q[NQ], off_g[NQ], rag_q[NQ], rag_g[NQ], off_l[1];
+#pragma unroll
+    for (int i = 0; i < NQ; i++) {
+        off_q[i] = chunk_offset<D>(lane, wave * NQ + i, q_rs, last_full);
+        off_g[i] = chunk_offset<D>(lane, wave * NQ + i, g_rs, last_full);
+        rag_q[i] = chunk_offset<D>(lane, wave * NQ + i, q_rs, last_ragged);
+        rag_g[i] = chunk_offset<D>(lane, wave * NQ + i, g_rs, last_ragged);
+    }
+    {
+        const int l32 = lane & 31;
+        // Lse2 and Dsum sit in one allocation, Dsum a fixed number of floats after Lse2.
+        const int64_t dd = a.Dsum - a.Lse2;
+        off_l[0] = (uint32_t)(4 * (l32 < 16 ? 4 * l32 : dd + 4 * (l32 - 16)));
+    }
+    auto issue = [&](bf16* qs, bf16* gs, float* ls, const Cursor& c) __attribute__((always_inline)) {
+        const int hq = kvh * a.group + c.h;
+        const int64_t u0 = (int64_t)c.qt * BW_T;
+        const int64_t row0 = c.qp + u0 * ps;  // token of the tile's first row
+        const char* qb = (const char*)((const bf16*)a.q + row0 * a.q_st + hq * a.q_sh);
+        const char* gb = (const char*)((const bf16*)a.dout + row0 * a.do_st + hq * a.do_sh);
+        const int64_t qloc = ps == 1 ? c.qp : c.qp * B;  // block-local index of row 0 (striped: block = qp)
+        const char* lb = (const char*)(a.Lse2 + hq * a.T + qloc + u0);
+        const bool rag = c.qt == ragged_qt;
+        uint32_t oq[NQ], og[NQ];
+#pragma unroll
+        for (int i = 0; i < NQ; i++) {
+            oq[i] = rag ? rag_q[i] : off_q[i];
+            og[i] = rag ? rag_g[i] : off_g[i];
+        }
+        issue_loads<NQ>(qs, wave * NQ, qb, oq);
+        issue_loads<NQ>(gs, wave * NQ, gb, og);
+        issue_loads<1>((bf16*)ls, wave, lb, off_l);
+        __asm__ volatile("; tile issued" ::: "memory");
+    };
+
+    int cc_flo = 0, cc_fhi = -1;  // fully visible tiles of the compute cursor's block
+    auto compute = [&](const bf16* qs, const bf16* gs, const float* ls, const Cursor& c)
+                       __attribute__((always_inline)) {
+        const int64_t u0 = (int64_t)c.qt * BW_T;
+        const bool full = c.qt != ragged_qt && c.qt >= cc_flo && c.qt <= cc_fhi;
+        const float* lw = ls + wave * 256;
+#pragma unroll
+        for (int sb = 0; sb < 2; sb++) {
+            // S and dP: tile rows 32 sb .. + 31 x this wave's 32 keys.
+            f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+            for (int kc = 0; kc < D / 16; kc++) {
+                s = mfma(ops.row(qs, sb, kc), kf[kc], s);
+                dp = mfma(ops.row(gs, sb, kc), vf[kc], dp);
+            }
+            // Register i holds tile row 32 sb + 8 (i/4) + 4 half + i%4.  A
+            // masked row's exponent becomes -inf (P = 0, dS = 0; its D is
+            // finite: rows past a block read the next rows or zeroed padding).
+            const int x_lo = (int)(u_lo - u0) - 4 * half, x_hi = (int)(u_hi - u0) - 4 * half;
+            f32x16 pv, dsv;
+#pragma unroll
+            for (int g4 = 0; g4 < 4; g4++) {
+                const int r0 = 32 * sb + 8 * g4 + 4 * half;
+                const f32x4 l4 = *(const f32x4*)(lw + r0);
+                const f32x4 d4 = *(const f32x4*)(lw + 64 + r0);
+#pragma unroll
+                for (int r = 0; r < 4; r++) {
+                    const int i = 4 * g4 + r, x = 32 * sb + 8 * g4 + r;
+                    float arg = fmaf(s[i], a.c2, -l4[r]);
+                    if (!full) arg = (x >= x_lo) & (x < x_hi) ? arg : -INFINITY;
+                    const float p = __builtin_amdgcn_exp2f(arg);
+                    pv[i] = p;
+                    dsv[i] = p * (dp[i] - d4[r]);
+                }
+            }
+            bf16x8 p0, p1, s0, s1;
+            acc_to_b(pv, p0, p1);
+            acc_to_b(dsv, s0, s1);
+            // dv^T += dout^T P and dk^T += q^T dS over the two 16-row chunks of this half.
+#pragma unroll
+            for (int db = 0; db < D / 32; db++) {
+                dv[db] = mfma(ops.tr(gs, 2 * sb, db), p0, dv[db]);
+                dv[db] = mfma(ops.tr(gs, 2 * sb + 1, db), p1, dv[db]);
+                dk[db] = mfma(ops.tr(qs, 2 * sb, db), s0, dk[db]);
+                dk[db] = mfma(ops.tr(qs, 2 * sb + 1, db), s1, dk[db]);
+            }
+        }
+    };
+
+    Cursor cl{0, 0, 0, 0, -1, 0};
+    if (w.count > 0) {
+        enter(cl, 0);
+        if (cl.hi < cl.lo) cur_next(cl);  // empty first block: step onto the first real tile
+    }
+    Cursor cc = cl;
+    auto enter_block = [&](const Cursor& c) __attribute__((always_inline)) {
+        key_bounds(c.qp);
+        cc_flo = rl32(tb_flo, c.e);
+        cc_fhi = rl32(tb_fhi, c.e);
+    };
+    if (nT > 0) enter_block(cc);
+    auto iteration = [&](int j, auto slot) __attribute__((always_inline)) {
+        constexpr int S = decltype(slot)::value;
+        bf16* const qc = S == 0 ? st0 : (S == 1 ? st1 : st2);
+        bf16* const gc = qc + TE;
+        float* const lc = (float*)(qc + 2 * TE);
+        bf16* const qn = S == 0 ? st2 : (S == 1 ? st0 : st1);
+        bf16* const gn = qn + TE;
+        float* const ln = (float*)(qn + 2 * TE);
+        if (j + 2 < nT) cur_next(cl);
+        issue(qn, gn, ln, cl);
+        compute(qc, gc, lc, cc);
+        if (j + 1 < nT) {
+            const int e_was = cc.e;
+            cur_next(cc);
+            if (cc.e != e_was) enter_block(cc);
+        }
+        wait_loads_but<NL>();
+        phase_barrier();
+    };
+    if (nT > 0) {
+        wait_loads_but<0>();
+        const Cursor c0 = cl;
+        if (nT > 1) cur_next(cl);
+        issue(st0, st0 + TE, (float*)(st0 + 2 * TE), c0);
+        issue(st1, st1 + TE, (float*)(st1 + 2 * TE), cl);
+        wait_loads_but<NL>();
+        phase_barrier();
+        // Whole triples of tiles in the loop, the rest after it: the loop
+        // body is straight-line code, so at every point the compiler knows
+        // exactly which stage's loads are still in flight (a conditional
+        // iteration inside the loop would give it paths on which the stage
+        // about to be read had just been issued, and a wait for all loads).
+        int j = 0;
+        for (; j + 3 <= nT; j += 3) {
+            iteration(j, ic<0>{});
+            iteration(j + 1, ic<1>{});
+            iteration(j + 2, ic<2>{});
+        }
+        if (j < nT) iteration(j, ic<0>{});
+        if (j + 1 < nT) iteration(j + 1, ic<1>{});
+        wait_loads_but<0>();
+    }
+
     if (!key_ok) return;
     char* kb = (char*)a.dk;
     char* vb = (char*)a.dv;
@@ -425,13 +785,13 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t stream) {
     const int64_t ndq = (int64_t)a.n_works * a.Hq * a.n_qtiles;
     const int64_t ndk = (int64_t)a.n_rworks * a.Hkv * a.n_ktiles;
     if (ndq > 0) {
-        if (a.d == 128) bwd_dq_kernel<128><<<(unsigned)ndq, BW_THREADS, 0, stream>>>(a);
-        else if (a.d == 64) bwd_dq_kernel<64><<<(unsigned)ndq, BW_THREADS, 0, stream>>>(a);
+        if (a.d == 128) bwd_dq_kernel<128><<<(unsigned)ndq, DQ_THREADS, 0, stream>>>(a);
+        else if (a.d == 64) bwd_dq_kernel<64><<<(unsigned)ndq, DQ_THREADS, 0, stream>>>(a);
         else return hipErrorInvalidValue;
     }
     if (ndk > 0) {
-        if (a.d == 128) bwd_dkdv_kernel<128><<<(unsigned)ndk, BW_THREADS, 0, stream>>>(a);
-        else if (a.d == 64) bwd_dkdv_kernel<64><<<(unsigned)ndk, BW_THREADS, 0, stream>>>(a);
+        if (a.d == 128) bwd_dkdv_kernel<128><<<(unsigned)ndk, KV_THREADS, 0, stream>>>(a);
+        else if (a.d == 64) bwd_dkdv_kernel<64><<<(unsigned)ndk, KV_THREADS, 0, stream>>>(a);
         else return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -96,6 +96,7 @@ hipError_t launch_empty_rows(void* out, int out_bf16, int64_t out_off, int64_t o
 // global token positions (striped blocks are strided views).
 struct BwdWork {                   // one ring block and the blocks paired with it
     int64_t pos0;                  // global position of its local row 0
+    int64_t loc0;                  // block index * rows per block (block-local row order)
     int32_t first, count;          // partner positions: partners[first .. first + count)
 };
 struct BwdArgs {
@@ -106,7 +107,8 @@ struct BwdArgs {
     const void* dout;              // bf16 [T, Hq, d] view
     int64_t q_st, q_sh, k_st, k_sh, v_st, v_sh, out_st, out_sh, do_st, do_sh;  // element strides
     const float* lse;              // [Hq, T], natural log
-    float* Dsum;                   // [Hq, T] workspace: dout . out per row
+    float* Lse2;                   // workspace [Hq, T] (+ pad): lse * log2(e) in block-local row order
+    float* Dsum;                   // workspace [Hq, T] (+ pad), same order: dout . out; Dsum - Lse2 < 2^30
     void* dq;                      // [T, Hq, d] contiguous, f32 or bf16 (grad_bf16)
     void* dk;                      // [T, Hkv, d] contiguous
     void* dv;
@@ -123,6 +125,7 @@ struct BwdArgs {
     const BwdWork* rworks;         // per key block: the query blocks that visit it
     const int64_t* rpartners;
 };
+constexpr int kBwdPad = 256;       // floats of padding after Lse2 and after Dsum
 int bwd_tile_q();
 int bwd_tile_k();
 hipError_t launch_backward(const BwdArgs& a, hipStream_t stream);

@@ -216,6 +216,9 @@ def test_backward_refuses_bad_arguments_before_any_gpu_work(lib):
                gg=_fake(64, 4, 96)) == ra.RA_E_UNSUPPORTED
     assert bwd(qq=_fake(64, 4, 128, ptr=(1 << 20) + 2)) == ra.RA_E_UNSUPPORTED
     assert bwd(dq=ctypes.c_void_p((1 << 25) + 8)) == ra.RA_E_UNSUPPORTED
+    big = dict(qq=_fake(128, 4, 128), kk=_fake(128, 2, 128), vv=_fake(128, 2, 128), oo=_fake(128, 4, 128),
+               gg=_fake(128, 4, 128))
+    assert bwd(n_blocks=128, P=1, **big) == ra.RA_E_UNSUPPORTED  # more ring blocks than lanes
     assert bwd(ws_bytes=16) == ra.RA_E_WORKSPACE
     cu = (ctypes.c_int32 * 3)(0, 10, 64)
     assert bwd(mask=2, cu=cu, n_docs=2, layout=1) == ra.RA_E_UNSUPPORTED
