@@ -22,14 +22,17 @@
 //    query row sits in each lane:
 //      S^T = K Q^T, dP^T = V dout^T, dS^T = P^T (dP^T - D), dq^T += K^T dS^T,
 //    the last through transposing LDS reads of the K tile.
-//  * bwd_dkdv: one workgroup (4 waves x 32 keys) per (key/value block, KV
-//    head, 128-key tile), its keys and values held in registers, walking the
-//    query blocks that visit the block, every query head of the KV head's
-//    group, in 64-row query tiles streamed through LDS.  Per wave, with
-//    S = Q K^T so that one key sits in each lane:
-//      S = Q K^T, dP = dout V^T, dS = P (dP - D),
-//      dv^T += dout^T P, dk^T += q^T dS,
-//    the last two through transposing reads of the dout and q tiles.
+//  * bwd_dkdv: one workgroup (8 waves) per (key/value block, KV head,
+//    128-key tile), walking the query blocks that visit the block, every
+//    query head of the KV head's group, in 64-row query tiles streamed
+//    through LDS.  Each 32 keys have two waves, their keys (and values) held
+//    in registers, with S = Q K^T so that one key sits in each lane:
+//      dV wave:  S = Q K^T, P, dv^T += dout^T P;
+//      dK wave:  S = Q K^T, dP = dout V^T, dS = P (dP - D), dk^T += q^T dS,
+//    the last products through transposing reads of the dout and q tiles.
+//    S is computed twice (1.25x the matrix-core work of one wave doing
+//    both), but each wave holds one set of 32 x d accumulators, so two
+//    waves fit per SIMD and hide each other's latency.
 // Both stream their tiles through a three-stage LDS ring filled by direct
 // global -> LDS loads issued two tiles ahead; a tile's loads have two tiles
 // of compute to land.  Tiles that the mask skips entirely are never loaded:
@@ -65,10 +68,10 @@ using ic = std::integral_constant<int, I>;
 
 constexpr int DQ_WAVES = 8;                // dq: two waves per SIMD
 constexpr int DQ_THREADS = 64 * DQ_WAVES;
-constexpr int KV_WAVES = 4;                // dk/dv: one wave per SIMD (its 32 keys' dK and dV
-constexpr int KV_THREADS = 64 * KV_WAVES;  //   accumulators alone take 128 registers)
+constexpr int KV_WAVES = 8;                // dk/dv: two waves per 32 keys (dV, dK), two per SIMD
+constexpr int KV_THREADS = 64 * KV_WAVES;
 constexpr int BW_TQ = 32 * DQ_WAVES;       // query rows per dq workgroup
-constexpr int BW_TK = 32 * KV_WAVES;       // keys per dk/dv workgroup
+constexpr int BW_TK = 32 * (KV_WAVES / 2); // keys per dk/dv workgroup
 constexpr int BW_T = 64;                   // rows of a streamed tile (keys for dq, queries for dk/dv)
 constexpr float kLog2e = 1.4426950408889634f;
 static_assert(kBwdPad >= 64, "a 64-row tile may read 63 rows past the last block");
@@ -148,8 +151,7 @@ __device__ __forceinline__ void issue_loads(bf16* dst, int base_n, const char* t
 template <int D>
 struct TileOps {
     int row_off[D / 16];
-    int tr_off0[D / 32];
-    int tr_off1[D / 32];
+    int tr_off[D / 32];
     __device__ TileOps(int lane) {
         const int col = lane & 31, half = lane >> 5;
 #pragma unroll
@@ -158,19 +160,23 @@ struct TileOps {
 #pragma unroll
         for (int db = 0; db < D / 32; db++) {
             const int chunk = 4 * db + 2 * g16 + ((j16 & 3) >> 1);
-            tr_off0[db] = vrow * D + 8 * (chunk ^ swz<D>(vrow)) + 4 * (j16 & 1);
-            tr_off1[db] = (vrow + 8) * D + 8 * (chunk ^ swz<D>(vrow + 8)) + 4 * (j16 & 1);
+            tr_off[db] = vrow * D + 8 * (chunk ^ swz<D>(vrow)) + 4 * (j16 & 1);
         }
     }
+    // Rows vrow + 8 (vrow < 8): their swizzle differs from row vrow's by 8
+    // (D = 128) or not at all (D = 64), so their chunk moves by +-8 slots,
+    // the sign set by bit 3 of the chunk, that is by bit 1 of db.
+    static constexpr int tr_plus8(int db) { return 8 * D + (D == 128 ? ((db & 2) ? -64 : 64) : 0); }
     __device__ __forceinline__ bf16x8 row(const bf16* t, int rb, int kc) const {
         return *(const bf16x8*)(t + row_off[kc] + 32 * D * rb);
     }
     __device__ __forceinline__ bf16x8 tr(const bf16* t, int q, int db) const {
-        const i16x4 r1 = lds_read_tr(t + tr_off0[db] + 16 * q * D);
-        const i16x4 r2 = lds_read_tr(t + tr_off1[db] + 16 * q * D);
+        const i16x4 r1 = lds_read_tr(t + tr_off[db] + 16 * q * D);
+        const i16x4 r2 = lds_read_tr(t + tr_off[db] + tr_plus8(db) + 16 * q * D);
         return __builtin_bit_cast(bf16x8, __builtin_shufflevector(r1, r2, 0, 1, 2, 3, 4, 5, 6, 7));
     }
 };
+static_assert(TileOps<128>::tr_plus8(0) == 8 * 128 + 64 && TileOps<128>::tr_plus8(3) == 8 * 128 - 64, "");
 
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -262,13 +268,14 @@ __global__ __launch_bounds__(DQ_THREADS, 1) void bwd_dq_kernel(const BwdArgs a) 
     const int kvh = head / a.group;
     const BwdWork w = a.works[widx];
     const int64_t B = a.B, ps = a.pos_stride;
-    const int64_t u = (int64_t)qt * BW_TQ + wave * 32 + col;  // this lane's query row (local)
+    // Per-lane mask state in 32 bits (positions and indices stay below 2^31).
+    const int u = qt * BW_TQ + wave * 32 + col;  // this lane's query row (local)
     const bool row_ok = u < B;
     const int64_t ur = row_ok ? u : B - 1;
     const int64_t t_row = w.pos0 + ur * ps;  // its global position = token row
     const float lse2 = row_ok ? a.Lse2[head * a.T + w.loc0 + ur] : INFINITY;
     const float drow = row_ok ? a.Dsum[head * a.T + w.loc0 + ur] : 0.f;
-    const int64_t ds_row = a.mask == kMaskDoc ? doc_start(a.cu, a.n_docs, t_row) : 0;
+    const int ds_row = a.mask == kMaskDoc ? (int)doc_start(a.cu, a.n_docs, t_row) : 0;
 
     // This wave's q and dout rows as B operands (row u, dims 16 kc + 8 half .. + 7).
     bf16x8 qf[D / 16], gf[D / 16];
@@ -335,15 +342,19 @@ __global__ __launch_bounds__(DQ_THREADS, 1) void bwd_dq_kernel(const BwdArgs a) 
     for (int e = 0; e < w.count; e++) nT += rl32(tb_hi, e) - rl32(tb_lo, e) + 1;
 
     // This row's allowed keys of the block at kp: local indices [w_lo, w_hi).
-    int64_t w_lo = 0, w_hi = 0;
+    // A key must not follow the row: w ps + kp <= u ps + pos0, that is
+    // w <= u + floor((pos0 - kp) / ps), the last term per block (both row-0
+    // positions lie below ps when striped) and computed in scalar code.
+    int w_lo = 0, w_hi = 0;
     auto row_bounds = [&](int64_t kp) __attribute__((always_inline)) {
         w_lo = 0;
-        w_hi = row_ok ? B : 0;
+        w_hi = row_ok ? (int)B : 0;
         if (a.mask != kMaskNone) {
-            const int64_t lim = t_row - kp;
-            const int64_t last = lim < 0 ? -1 : lim / ps;
-            if (last + 1 < w_hi) w_hi = last + 1;
-            if (a.mask == kMaskDoc && ds_row - kp > 0) w_lo = ds_row - kp;
+            const int dd = (int)(w.pos0 - kp);
+            const int shift = ps == 1 ? dd : (dd >= 0 ? 0 : -1);  // floor(dd / ps), |dd| < ps when striped
+            const int last = u + shift;
+            if (last + 1 < w_hi) w_hi = last + 1 < 0 ? 0 : last + 1;
+            if (a.mask == kMaskDoc && ds_row - (int)kp > 0) w_lo = ds_row - (int)kp;
         }
     };
 
@@ -352,15 +363,13 @@ __global__ __launch_bounds__(DQ_THREADS, 1) void bwd_dq_kernel(const BwdArgs a) 
     const uint32_t k_rs = (uint32_t)(ps * a.k_st * 2), v_rs = (uint32_t)(ps * a.v_st * 2);
     const int last_full = BW_T - 1, last_ragged = (int)((B - 1) % BW_T);
     const int ragged_kt = B % BW_T ? nkt - 1 : -1;
-    // Both offset sets stay in registers and a ragged tile selects its own
-    // (no branch around the loads).
-    uint32_t off_k[NL / 2], off_v[NL / 2], rag_k[NL / 2], rag_v[NL / 2];
+    // Offsets of a full tile stay in registers; a ragged tile's are computed
+    // when it is issued, and selected without a branch around the loads.
+    uint32_t off_k[NL / 2], off_v[NL / 2];
 #pragma unroll
     for (int i = 0; i < NL / 2; i++) {
         off_k[i] = chunk_offset<D>(lane, wave * (NL / 2) + i, k_rs, last_full);
         off_v[i] = chunk_offset<D>(lane, wave * (NL / 2) + i, v_rs, last_full);
-        rag_k[i] = chunk_offset<D>(lane, wave * (NL / 2) + i, k_rs, last_ragged);
-        rag_v[i] = chunk_offset<D>(lane, wave * (NL / 2) + i, v_rs, last_ragged);
     }
     const char* const k_head = (const char*)((const bf16*)a.k + kvh * a.k_sh);
     const char* const v_head = (const char*)((const bf16*)a.v + kvh * a.v_sh);
@@ -370,8 +379,8 @@ __global__ __launch_bounds__(DQ_THREADS, 1) void bwd_dq_kernel(const BwdArgs a) 
         uint32_t ok[NL / 2], ov[NL / 2];
 #pragma unroll
         for (int i = 0; i < NL / 2; i++) {
-            ok[i] = rag ? rag_k[i] : off_k[i];
-            ov[i] = rag ? rag_v[i] : off_v[i];
+            ok[i] = rag ? chunk_offset<D>(lane, wave * (NL / 2) + i, k_rs, last_ragged) : off_k[i];
+            ov[i] = rag ? chunk_offset<D>(lane, wave * (NL / 2) + i, v_rs, last_ragged) : off_v[i];
         }
         issue_loads<NL / 2>(ks, wave * (NL / 2), k_head + row0 * a.k_st * 2, ok);
         issue_loads<NL / 2>(vs, wave * (NL / 2), v_head + row0 * a.v_st * 2, ov);
@@ -383,7 +392,7 @@ __global__ __launch_bounds__(DQ_THREADS, 1) void bwd_dq_kernel(const BwdArgs a) 
         const int64_t w0 = (int64_t)c.kt * BW_T;
         const bool full = c.kt != ragged_kt && c.kt >= cc_flo && c.kt <= cc_fhi;
         // Allowed keys shifted by -4 half, relative to the tile (|x| <= B + 4).
-        const int x_lo = (int)(w_lo - w0) - 4 * half, x_hi = (int)(w_hi - w0) - 4 * half;
+        const int x_lo = w_lo - (int)w0 - 4 * half, x_hi = w_hi - (int)w0 - 4 * half;
 #pragma unroll
         for (int kb = 0; kb < 2; kb++) {
             // S^T and dP^T: keys 32 kb .. + 31 of the tile (rows) x this wave's rows.
@@ -401,7 +410,7 @@ __global__ __launch_bounds__(DQ_THREADS, 1) void bwd_dq_kernel(const BwdArgs a) 
             for (int i = 0; i < 16; i++) {
                 const int x = 32 * kb + 8 * (i / 4) + (i % 4);
                 float arg = fmaf(s[i], a.c2, -lse2);
-                if (!full) arg = (x >= x_lo) & (x < x_hi) ? arg : -INFINITY;
+                if (!full) arg = ((x >= x_lo) & (x < x_hi)) ? arg : -INFINITY;
                 dsv[i] = __builtin_amdgcn_exp2f(arg) * (dp[i] - drow);
             }
             bf16x8 b0, b1;
@@ -490,13 +499,22 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(const BwdArgs a
     constexpr int TE = BW_T * D;
     constexpr int NQ = TE / 512 / KV_WAVES;  // loads per wave per stage for each of q and dout
     constexpr int NL = 2 * NQ + 1;  // + this wave's copy of the tile's lse2 / D rows
-    // Three stages, one array each: the q tile, the dout tile, then per wave
-    // lse2 of the tile's 64 rows and their D (1 KB, the upper half a
-    // duplicate written by lanes 32..63).
-    constexpr int SE = 2 * TE + KV_WAVES * 512;  // elements of one stage
+    // Three stages, one array each: the q tile, the dout tile, then lse2 of
+    // the tile's 64 rows and their D (1 KB, the upper half a duplicate
+    // written by lanes 32..63).  Every wave loads that last KB (the same
+    // bytes): each wave then issues the same number of loads per stage, and
+    // its reads need no per-wave offset (with one, the compiler loses track
+    // of which stage they read and waits for every load in flight).
+    constexpr int SE = 2 * TE + 512;  // elements of one stage
     __shared__ __attribute__((aligned(16))) bf16 st0[SE], st1[SE], st2[SE];
+    // P of the current tile, handed from each dV wave to its dK partner:
+    // [32-key group][half][4-register group][lane] 4 floats (accumulator
+    // order), so that each 16-byte access of a wave is contiguous.
+    __shared__ __attribute__((aligned(16))) float p_lds[KV_WAVES / 2][2][4][64 * 4];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int role = wave >> 2;  // 0: dV, 1: dK
+    const int kw = wave & 3;     // which 32 keys of the workgroup
     const int half = lane >> 5, col = lane & 31;
     const int kt = blockIdx.x % a.n_ktiles;
     const int kvh = (blockIdx.x / a.n_ktiles) % a.Hkv;
@@ -504,26 +522,25 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(const BwdArgs a
     const BwdWork w = a.rworks[ridx];
     const int64_t B = a.B, ps = a.pos_stride;
     const int64_t wk0 = (int64_t)kt * BW_TK;
-    const int64_t wk = wk0 + wave * 32 + col;  // this lane's key (local)
+    // Per-lane mask state in 32 bits (positions and indices stay below 2^31).
+    const int wk = (int)wk0 + kw * 32 + col;  // this lane's key (local)
     const bool key_ok = wk < B;
     const int64_t p_key = w.pos0 + (key_ok ? wk : B - 1) * ps;  // its global position = token row
-    const int64_t de_key = a.mask == kMaskDoc ? doc_end(a.cu, a.n_docs, p_key) : 0;
+    const int de_key = a.mask == kMaskDoc ? (int)doc_end(a.cu, a.n_docs, p_key) : 0;
 
-    // This wave's keys and values as B operands (key wk, dims 16 kc + 8 half .. + 7).
-    bf16x8 kf[D / 16], vf[D / 16];
+    // This wave's B operand rows (key wk, dims 16 kc + 8 half .. + 7): keys
+    // for the dV wave (S = q K^T), values for the dK wave (dP = dout V^T).
+    bf16x8 opf[D / 16];
     {
-        const bf16* kp = (const bf16*)a.k + p_key * a.k_st + kvh * a.k_sh + 8 * half;
-        const bf16* vp = (const bf16*)a.v + p_key * a.v_st + kvh * a.v_sh + 8 * half;
+        const bf16* op = role ? (const bf16*)a.v + p_key * a.v_st + kvh * a.v_sh
+                              : (const bf16*)a.k + p_key * a.k_st + kvh * a.k_sh;
 #pragma unroll
-        for (int kc = 0; kc < D / 16; kc++) {
-            kf[kc] = *(const bf16x8*)(kp + 16 * kc);
-            vf[kc] = *(const bf16x8*)(vp + 16 * kc);
-        }
+        for (int kc = 0; kc < D / 16; kc++) opf[kc] = *(const bf16x8*)(op + 8 * half + 16 * kc);
     }
     const TileOps<D> ops(lane);
-    f32x16 dk[D / 32], dv[D / 32];
+    f32x16 acc[D / 32];  // dV^T (dV wave) or dK^T / scale (dK wave)
 #pragma unroll
-    for (int db = 0; db < D / 32; db++) dk[db] = dv[db] = f32x16{};
+    for (int db = 0; db < D / 32; db++) acc[db] = f32x16{};
 
     const int64_t wl = (B < wk0 + BW_TK ? B : wk0 + BW_TK) - 1;  // last key of the workgroup
     const int64_t tk_min = w.pos0 + wk0 * ps, tk_max = w.pos0 + wl * ps;
@@ -592,31 +609,35 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(const BwdArgs a
     }
 
     // This key's allowed query rows of the block at qp: local indices [u_lo, u_hi).
-    int64_t u_lo = 0, u_hi = 0;
+    // A query must not precede the key: u ps + qp >= wk ps + pos0, that is
+    // u >= wk + ceil((pos0 - qp) / ps), where the last term is per block (both
+    // row-0 positions lie below ps when striped) and computed in scalar code.
+    int u_lo = 0, u_hi = 0;
     auto key_bounds = [&](int64_t qp) __attribute__((always_inline)) {
         u_lo = 0;
-        u_hi = key_ok ? B : 0;
+        u_hi = key_ok ? (int)B : 0;
         if (a.mask != kMaskNone) {
-            const int64_t rel = p_key - qp;  // a query must not precede the key
-            u_lo = rel <= 0 ? 0 : (rel + ps - 1) / ps;
-            if (a.mask == kMaskDoc && de_key - qp < u_hi) u_hi = de_key - qp;
+            const int dd = (int)(w.pos0 - qp);
+            const int shift = ps == 1 ? dd : (dd > 0 ? 1 : 0);  // ceil(dd / ps), |dd| < ps when striped
+            const int lo = wk + shift;
+            u_lo = lo < 0 ? 0 : lo;
+            if (a.mask == kMaskDoc && de_key - (int)qp < u_hi) u_hi = de_key - (int)qp;
         }
     };
 
     // Load offsets: q / dout chunks (NQ loads each), and the lse2 / D rows
     // (lanes 0..15: lse2 rows 4 l .. 4 l + 3; lanes 16..31: D rows; lanes
-    // 32..63 repeat lanes 0..31).
+    // 32..63 repeat lanes 0..31), the same for every wave.
     const uint32_t q_rs = (uint32_t)(ps * a.q_st * 2), g_rs = (uint32_t)(ps * a.do_st * 2);
     const int last_full = BW_T - 1, last_ragged = (int)((B - 1) % BW_T);
     const int ragged_qt = B % BW_T ? nqt - 1 : -1;
-    // Both offset sets stay in registers and a ragged tile selects its own.
-    uint32_t off_q[NQ], off_g[NQ], rag_q[NQ], rag_g[NQ], off_l[1];
+    // Offsets of a full tile stay in registers; a ragged tile's are computed
+    // when it is issued, and selected without a branch around the loads.
+    uint32_t off_q[NQ], off_g[NQ], off_l[1];
 #pragma unroll
     for (int i = 0; i < NQ; i++) {
         off_q[i] = chunk_offset<D>(lane, wave * NQ + i, q_rs, last_full);
         off_g[i] = chunk_offset<D>(lane, wave * NQ + i, g_rs, last_full);
-        rag_q[i] = chunk_offset<D>(lane, wave * NQ + i, q_rs, last_ragged);
-        rag_g[i] = chunk_offset<D>(lane, wave * NQ + i, g_rs, last_ragged);
     }
     {
         const int l32 = lane & 31;
@@ -636,62 +657,119 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(const BwdArgs a
         uint32_t oq[NQ], og[NQ];
 #pragma unroll
         for (int i = 0; i < NQ; i++) {
-            oq[i] = rag ? rag_q[i] : off_q[i];
-            og[i] = rag ? rag_g[i] : off_g[i];
+            oq[i] = rag ? chunk_offset<D>(lane, wave * NQ + i, q_rs, last_ragged) : off_q[i];
+            og[i] = rag ? chunk_offset<D>(lane, wave * NQ + i, g_rs, last_ragged) : off_g[i];
         }
         issue_loads<NQ>(qs, wave * NQ, qb, oq);
         issue_loads<NQ>(gs, wave * NQ, gb, og);
-        issue_loads<1>((bf16*)ls, wave, lb, off_l);
+        issue_loads<1>((bf16*)ls, 0, lb, off_l);
         __asm__ volatile("; tile issued" ::: "memory");
     };
 
     int cc_flo = 0, cc_fhi = -1;  // fully visible tiles of the compute cursor's block
+    // A tile in two phases with a workgroup barrier between them; the waves
+    // of one 32-key group (dV wave, dK wave) share a SIMD, and in each phase
+    // one of them carries the softmax arithmetic while the other mostly
+    // runs the matrix core.
+    //  phase 1  dV wave: S = q K^T, P (to LDS, and kept as bf16);  dK wave: dP = dout V^T
+    //  phase 2  dV wave: dv^T += dout^T P;  dK wave: P from LDS, dS = P (dP - D), dk^T += q^T dS
+    // Register i of S / dP / P holds tile row 32 sb + 8 (i/4) + 4 half + i%4.
+    float* const p_mine = &p_lds[kw][0][0][lane * 4];  // + (4 sb + q4) * 256
+    // Both roles run the same matrix-core instruction stream on role-selected
+    // operands (so the accumulators stay in place); role-specific work is
+    // vector arithmetic only.  x[sb] carries phase 1's product of half sb to
+    // phase 2: the dK wave's dP, or the dV wave's P as bf16 operands (first
+    // 8 registers).
+    f32x16 x[2];
+    auto b16 = [&](int sb, int h) __attribute__((always_inline)) {
+        return __builtin_bit_cast(bf16x8, f32x4{x[sb][4 * h], x[sb][4 * h + 1], x[sb][4 * h + 2], x[sb][4 * h + 3]});
+    };
+    auto set_b16 = [&](int sb, int h, bf16x8 v) __attribute__((always_inline)) {
+        const f32x4 y = __builtin_bit_cast(f32x4, v);
+#pragma unroll
+        for (int e = 0; e < 4; e++) x[sb][4 * h + e] = y[e];
+    };
+    const int row_src = role ? TE : 0;  // phase 1 rows: q (dV wave) or dout (dK wave)
+    const int tr_src = role ? 0 : TE;   // phase 2 columns: dout (dV wave) or q (dK wave)
+    auto phase1_mfma = [&](const bf16* qs) __attribute__((always_inline)) {
+        // S = q K^T (dV wave) or dP = dout V^T (dK wave), both halves.
+#pragma unroll
+        for (int sb = 0; sb < 2; sb++) {
+            x[sb] = f32x16{};
+#pragma unroll
+            for (int kc = 0; kc < D / 16; kc++) x[sb] = mfma(ops.row(qs + row_src, sb, kc), opf[kc], x[sb]);
+        }
+    };
+    auto phase1_p = [&](const float* lw, int64_t u0, auto full_t) __attribute__((always_inline)) {
+        constexpr bool FULL = decltype(full_t)::value;
+        {
+            // P (a masked row's exponent becomes -inf), to LDS for the dK
+            // wave and kept as bf16 operands.
+            const int x_lo = u_lo - (int)u0 - 4 * half, x_hi = u_hi - (int)u0 - 4 * half;
+#pragma unroll
+            for (int sb = 0; sb < 2; sb++) {
+                f32x16 pv;
+#pragma unroll
+                for (int g4 = 0; g4 < 4; g4++) {
+                    const f32x4 l4 = *(const f32x4*)(lw + 32 * sb + 8 * g4 + 4 * half);
+#pragma unroll
+                    for (int r = 0; r < 4; r++) {
+                        const int i = 4 * g4 + r, xr = 32 * sb + 8 * g4 + r;
+                        float arg = fmaf(x[sb][i], a.c2, -l4[r]);
+                        if (!FULL) arg = ((xr >= x_lo) & (xr < x_hi)) ? arg : -INFINITY;
+                        pv[i] = __builtin_amdgcn_exp2f(arg);
+                    }
+                }
+#pragma unroll
+                for (int q4 = 0; q4 < 4; q4++)
+                    *(f32x4*)(p_mine + (4 * sb + q4) * 256) =
+                        f32x4{pv[4 * q4], pv[4 * q4 + 1], pv[4 * q4 + 2], pv[4 * q4 + 3]};
+                bf16x8 b0, b1;
+                acc_to_b(pv, b0, b1);
+                set_b16(sb, 0, b0);
+                set_b16(sb, 1, b1);
+            }
+        }
+    };
+    auto phase2 = [&](const bf16* qs, const float* lw) __attribute__((always_inline)) {
+#pragma unroll
+        for (int sb = 0; sb < 2; sb++) {
+            if (__builtin_amdgcn_readfirstlane(role) == 1) {
+                // dS = P (dP - D); a masked row has P = 0 and a finite D
+                // (rows past a block read the next rows or zeroed padding).
+                f32x16 dsv;
+#pragma unroll
+                for (int g4 = 0; g4 < 4; g4++) {
+                    const f32x4 d4 = *(const f32x4*)(lw + 64 + 32 * sb + 8 * g4 + 4 * half);
+                    const f32x4 p4 = *(const f32x4*)(p_mine + (4 * sb + g4) * 256);
+#pragma unroll
+                    for (int r = 0; r < 4; r++) dsv[4 * g4 + r] = p4[r] * (x[sb][4 * g4 + r] - d4[r]);
+                }
+                bf16x8 e0, e1;
+                acc_to_b(dsv, e0, e1);
+                set_b16(sb, 0, e0);
+                set_b16(sb, 1, e1);
+            }
+            // dv^T += dout^T P (dV wave) or dk^T += q^T dS (dK wave).
+#pragma unroll
+            for (int db = 0; db < D / 32; db++) {
+                acc[db] = mfma(ops.tr(qs + tr_src, 2 * sb, db), b16(sb, 0), acc[db]);
+                acc[db] = mfma(ops.tr(qs + tr_src, 2 * sb + 1, db), b16(sb, 1), acc[db]);
+            }
+        }
+    };
     auto compute = [&](const bf16* qs, const bf16* gs, const float* ls, const Cursor& c)
                        __attribute__((always_inline)) {
         const int64_t u0 = (int64_t)c.qt * BW_T;
         const bool full = c.qt != ragged_qt && c.qt >= cc_flo && c.qt <= cc_fhi;
-        const float* lw = ls + wave * 256;
-#pragma unroll
-        for (int sb = 0; sb < 2; sb++) {
-            // S and dP: tile rows 32 sb .. + 31 x this wave's 32 keys.
-            f32x16 s = f32x16{}, dp = f32x16{};
-#pragma unroll
-            for (int kc = 0; kc < D / 16; kc++) {
-                s = mfma(ops.row(qs, sb, kc), kf[kc], s);
-                dp = mfma(ops.row(gs, sb, kc), vf[kc], dp);
-            }
-            // Register i holds tile row 32 sb + 8 (i/4) + 4 half + i%4.  A
-            // masked row's exponent becomes -inf (P = 0, dS = 0; its D is
-            // finite: rows past a block read the next rows or zeroed padding).
-            const int x_lo = (int)(u_lo - u0) - 4 * half, x_hi = (int)(u_hi - u0) - 4 * half;
-            f32x16 pv, dsv;
-#pragma unroll
-            for (int g4 = 0; g4 < 4; g4++) {
-                const int r0 = 32 * sb + 8 * g4 + 4 * half;
-                const f32x4 l4 = *(const f32x4*)(lw + r0);
-                const f32x4 d4 = *(const f32x4*)(lw + 64 + r0);
-#pragma unroll
-                for (int r = 0; r < 4; r++) {
-                    const int i = 4 * g4 + r, x = 32 * sb + 8 * g4 + r;
-                    float arg = fmaf(s[i], a.c2, -l4[r]);
-                    if (!full) arg = (x >= x_lo) & (x < x_hi) ? arg : -INFINITY;
-                    const float p = __builtin_amdgcn_exp2f(arg);
-                    pv[i] = p;
-                    dsv[i] = p * (dp[i] - d4[r]);
-                }
-            }
-            bf16x8 p0, p1, s0, s1;
-            acc_to_b(pv, p0, p1);
-            acc_to_b(dsv, s0, s1);
-            // dv^T += dout^T P and dk^T += q^T dS over the two 16-row chunks of this half.
-#pragma unroll
-            for (int db = 0; db < D / 32; db++) {
-                dv[db] = mfma(ops.tr(gs, 2 * sb, db), p0, dv[db]);
-                dv[db] = mfma(ops.tr(gs, 2 * sb + 1, db), p1, dv[db]);
-                dk[db] = mfma(ops.tr(qs, 2 * sb, db), s0, dk[db]);
-                dk[db] = mfma(ops.tr(qs, 2 * sb + 1, db), s1, dk[db]);
-            }
+        const float* lw = ls;
+        phase1_mfma(qs);
+        if (__builtin_amdgcn_readfirstlane(role) == 0) {
+            if (__builtin_amdgcn_readfirstlane((int)full)) phase1_p(lw, u0, std::true_type{});
+            else phase1_p(lw, u0, std::false_type{});
         }
+        phase_barrier();  // P of this tile is in LDS
+        phase2(qs, lw);
     };
 
     Cursor cl{0, 0, 0, 0, -1, 0};
@@ -750,24 +828,18 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(const BwdArgs a
     }
 
     if (!key_ok) return;
-    char* kb = (char*)a.dk;
-    char* vb = (char*)a.dv;
+    const float mul = role ? a.scale : 1.f;
+    char* ob = (char*)(role ? a.dk : a.dv);
     const int64_t oe = (p_key * a.Hkv + kvh) * D + 4 * half;
 #pragma unroll
     for (int db = 0; db < D / 32; db++)
 #pragma unroll
         for (int g = 0; g < 4; g++) {
             const int64_t e = oe + 32 * db + 8 * g;
-            const float k0 = dk[db][4 * g] * a.scale, k1 = dk[db][4 * g + 1] * a.scale;
-            const float k2 = dk[db][4 * g + 2] * a.scale, k3 = dk[db][4 * g + 3] * a.scale;
-            const float v0 = dv[db][4 * g], v1 = dv[db][4 * g + 1], v2 = dv[db][4 * g + 2], v3 = dv[db][4 * g + 3];
-            if (a.grad_bf16) {
-                *(bf16x4*)(kb + 2 * e) = bf16x4{(bf16)k0, (bf16)k1, (bf16)k2, (bf16)k3};
-                *(bf16x4*)(vb + 2 * e) = bf16x4{(bf16)v0, (bf16)v1, (bf16)v2, (bf16)v3};
-            } else {
-                *(f32x4*)(kb + 4 * e) = f32x4{k0, k1, k2, k3};
-                *(f32x4*)(vb + 4 * e) = f32x4{v0, v1, v2, v3};
-            }
+            const float x0 = acc[db][4 * g] * mul, x1 = acc[db][4 * g + 1] * mul;
+            const float x2 = acc[db][4 * g + 2] * mul, x3 = acc[db][4 * g + 3] * mul;
+            if (a.grad_bf16) *(bf16x4*)(ob + 2 * e) = bf16x4{(bf16)x0, (bf16)x1, (bf16)x2, (bf16)x3};
+            else *(f32x4*)(ob + 4 * e) = f32x4{x0, x1, x2, x3};
         }
 }
 
