@@ -184,7 +184,8 @@ size_t ring_attn_backward_workspace_size(const ra_tensor* q, int32_t n_blocks, i
  * scheduling.
  *   q, k, v, n_blocks, layout, mask_mode, max_ring_passes, cu_seqlens_host,
  *     n_docs, scale: as given to ring_attn_forward.  bf16 inputs with
- *     head_dim 64 or 128 and n_blocks <= 64 only (RA_E_UNSUPPORTED otherwise).
+ *     head_dim 64 or 128, n_blocks <= 64, T < 2^31 and T / n_blocks < 2^21
+ *     only (RA_E_UNSUPPORTED otherwise).
  *   out: the forward's output [T, Hq, d] view, bf16 or f32 (16-byte aligned
  *     rows); dout: [T, Hq, d] bf16 view.
  *   lse: the forward's lse, [Hq, T] fp32 (natural log).

@@ -647,6 +647,7 @@ ra_status ring_attn_backward(const ra_tensor* q, const ra_tensor* k, const ra_te
     if (q->dtype != RA_BF16 || (d != 64 && d != 128)) return RA_E_UNSUPPORTED;
     if (n_blocks > kMaxRingChain) return RA_E_UNSUPPORTED;
     if (T >= ((int64_t)1 << 31)) return RA_E_UNSUPPORTED;  // per-lane positions are 32-bit
+    if (T / n_blocks >= ((int64_t)1 << 21)) return RA_E_UNSUPPORTED;  // 64-row tile indices fit 15 bits
     if (!bf16_aligned(q) || !bf16_aligned(k) || !bf16_aligned(v) || !bf16_aligned(dout)) return RA_E_UNSUPPORTED;
     if ((uintptr_t)out->data % 16 || out->stride_tok % (out->dtype == RA_BF16 ? 8 : 4) ||
         out->stride_head % (out->dtype == RA_BF16 ? 8 : 4))

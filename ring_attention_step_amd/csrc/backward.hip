@@ -77,12 +77,19 @@ constexpr float kLog2e = 1.4426950408889634f;
 static_assert(kBwdPad >= 64, "a 64-row tile may read 63 rows past the last block");
 
 // A [64 rows][D] bf16 tile in LDS, 16-byte chunks XOR-swizzled per row:
-// logical chunk c of row r at slot c ^ (r & (D/8 - 1)).  Row reads (16 rows
-// of one chunk column per pass) and transposing reads both spread over the
-// banks.
+// logical chunk c of row r at slot c ^ swz(r).  Both kinds of operand read
+// are free of bank conflicts (measured with the LDS bank-conflict counter):
+//  row reads: 16 lanes read one chunk column of 16 consecutive rows, which
+//    swz spreads over 16 distinct slots;
+//  transposing reads: 32 lanes read 64 bytes (4 chunks) of each of 4 rows
+//    4j .. 4j + 3, which swz moves to 4 different 64-byte quarters of the
+//    256-byte bank window (D = 128: by 4 (r & 3); D = 64, where two
+//    rows share the window, by 4 ((r >> 1) & 1) and the row's half).
+// (r & (D/8 - 1), the plain choice, costs the transposing reads 6 conflict
+// cycles each.)  Rows r and r + 8 (r < 8) differ by XOR 2.
 template <int D>
 __device__ __forceinline__ constexpr int swz(int r) {
-    return r & (D / 8 - 1);
+    return D == 128 ? ((4 * (r & 3)) ^ ((r >> 2) & 3)) & 15 : ((4 * ((r >> 1) & 1)) ^ ((r >> 2) & 3)) & 7;
 }
 
 __device__ __forceinline__ i16x4 lds_read_tr(const bf16* p) {
@@ -152,6 +159,7 @@ template <int D>
 struct TileOps {
     int row_off[D / 16];
     int tr_off[D / 32];
+    int tr_d8;  // rows vrow + 8 relative to rows vrow (the same for every db)
     __device__ TileOps(int lane) {
         const int col = lane & 31, half = lane >> 5;
 #pragma unroll
@@ -162,21 +170,19 @@ struct TileOps {
             const int chunk = 4 * db + 2 * g16 + ((j16 & 3) >> 1);
             tr_off[db] = vrow * D + 8 * (chunk ^ swz<D>(vrow)) + 4 * (j16 & 1);
         }
+        // swz(vrow + 8) = swz(vrow) ^ 2 with bit 1 of swz(vrow) clear, so
+        // the chunk moves by 2 slots, down when bit 1 of the chunk (g16) is set.
+        tr_d8 = 8 * D + (g16 ? -16 : 16);
     }
-    // Rows vrow + 8 (vrow < 8): their swizzle differs from row vrow's by 8
-    // (D = 128) or not at all (D = 64), so their chunk moves by +-8 slots,
-    // the sign set by bit 3 of the chunk, that is by bit 1 of db.
-    static constexpr int tr_plus8(int db) { return 8 * D + (D == 128 ? ((db & 2) ? -64 : 64) : 0); }
     __device__ __forceinline__ bf16x8 row(const bf16* t, int rb, int kc) const {
         return *(const bf16x8*)(t + row_off[kc] + 32 * D * rb);
     }
     __device__ __forceinline__ bf16x8 tr(const bf16* t, int q, int db) const {
         const i16x4 r1 = lds_read_tr(t + tr_off[db] + 16 * q * D);
-        const i16x4 r2 = lds_read_tr(t + tr_off[db] + tr_plus8(db) + 16 * q * D);
+        const i16x4 r2 = lds_read_tr(t + tr_off[db] + tr_d8 + 16 * q * D);
         return __builtin_bit_cast(bf16x8, __builtin_shufflevector(r1, r2, 0, 1, 2, 3, 4, 5, 6, 7));
     }
 };
-static_assert(TileOps<128>::tr_plus8(0) == 8 * 128 + 64 && TileOps<128>::tr_plus8(3) == 8 * 128 - 64, "");
 
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -308,22 +314,20 @@ __global__ __launch_bounds__(DQ_THREADS, 1) void bwd_dq_kernel(const BwdArgs a) 
     // loop reads it with readlane and so issues no memory loads besides the
     // stage loads (a load waited for inside the loop would also wait for
     // every stage load issued before it).
-    int tb_lo = 0, tb_hi = -1, tb_flo = 0, tb_fhi = -1;
-    int64_t tb_kp = 0;
+    // (Positions fit 32 bits; the fully visible range is packed as two
+    // 16-bit fields, fhi + 1 above flo: tile indices stay below 2^15.)
+    int tb_lo = 0, tb_hi = -1, tb_full = 0;
+    int tb_kp = 0;
     if (lane < w.count) {
-        tb_kp = a.partners[w.first + lane];
-        tile_range(nkt, [&](int x) { return cls_of(tb_kp, x); }, tb_lo, tb_hi);
-        tb_flo = tb_lo;
-        tb_fhi = tb_hi;
-        while (tb_flo <= tb_fhi && cls_of(tb_kp, tb_flo) != kFull) tb_flo++;
-        while (tb_fhi >= tb_flo && cls_of(tb_kp, tb_fhi) != kFull) tb_fhi--;
+        const int64_t kp = a.partners[w.first + lane];
+        tb_kp = (int)kp;
+        tile_range(nkt, [&](int x) { return cls_of(kp, x); }, tb_lo, tb_hi);
+        int flo = tb_lo, fhi = tb_hi;
+        while (flo <= fhi && cls_of(kp, flo) != kFull) flo++;
+        while (fhi >= flo && cls_of(kp, fhi) != kFull) fhi--;
+        tb_full = flo | ((fhi + 1) << 16);
     }
     auto rl32 = [&](int x, int e) __attribute__((always_inline)) { return __builtin_amdgcn_readlane(x, e); };
-    auto rl64 = [&](int64_t x, int e) __attribute__((always_inline)) {
-        const uint32_t lo32 = __builtin_amdgcn_readlane((int)(uint32_t)x, e);
-        const uint32_t hi32 = __builtin_amdgcn_readlane((int)(uint32_t)((uint64_t)x >> 32), e);
-        return (int64_t)(((uint64_t)hi32 << 32) | lo32);
-    };
     // Streamed tiles: every non-skipped key tile of every visited block.
     struct Cursor {
         int e, kt, hi;
@@ -336,7 +340,7 @@ __global__ __launch_bounds__(DQ_THREADS, 1) void bwd_dq_kernel(const BwdArgs a) 
             kt = rl32(tb_lo, e);
             hi = rl32(tb_hi, e);
         }
-        if (kt <= hi) c = Cursor{e, kt, hi, rl64(tb_kp, e)};
+        if (kt <= hi) c = Cursor{e, kt, hi, (int64_t)rl32(tb_kp, e)};
     };
     int nT = 0;
     for (int e = 0; e < w.count; e++) nT += rl32(tb_hi, e) - rl32(tb_lo, e) + 1;
@@ -404,24 +408,30 @@ __global__ __launch_bounds__(DQ_THREADS, 1) void bwd_dq_kernel(const BwdArgs a) 
             }
             // dS^T = P^T (dP^T - D); register i holds key 32 kb + 8 (i/4) + 4 half + i%4.
             // A masked key's exponent becomes -inf (P = 0, dS = 0): selects,
-            // so that no per-element branch is formed around the exp2.
-            f32x16 dsv;
-#pragma unroll
-            for (int i = 0; i < 16; i++) {
-                const int x = 32 * kb + 8 * (i / 4) + (i % 4);
-                float arg = fmaf(s[i], a.c2, -lse2);
-                if (!full) arg = ((x >= x_lo) & (x < x_hi)) ? arg : -INFINITY;
-                dsv[i] = __builtin_amdgcn_exp2f(arg) * (dp[i] - drow);
-            }
+            // so that no per-element branch is formed around the exp2.  Fully
+            // visible tiles take a copy without the mask (the branch holds
+            // vector work only, so the accumulators stay in place).
             bf16x8 b0, b1;
-            acc_to_b(dsv, b0, b1);
+            auto softmax = [&](auto full_t) __attribute__((always_inline)) {
+                constexpr bool FULL = decltype(full_t)::value;
+                f32x16 dsv;
+#pragma unroll
+                for (int i = 0; i < 16; i++) {
+                    const int x = 32 * kb + 8 * (i / 4) + (i % 4);
+                    float arg = fmaf(s[i], a.c2, -lse2);
+                    if (!FULL) arg = ((x >= x_lo) & (x < x_hi)) ? arg : -INFINITY;
+                    dsv[i] = __builtin_amdgcn_exp2f(arg) * (dp[i] - drow);
+                }
+                acc_to_b(dsv, b0, b1);
+            };
+            if (__builtin_amdgcn_readfirstlane((int)full)) softmax(std::true_type{});
+            else softmax(std::false_type{});
             // dq^T += K^T dS^T over the two 16-key chunks of this half.
 #pragma unroll
             for (int db = 0; db < D / 32; db++) {
                 dq[db] = mfma(ops.tr(ks, 2 * kb, db), b0, dq[db]);
                 dq[db] = mfma(ops.tr(ks, 2 * kb + 1, db), b1, dq[db]);
             }
-            __builtin_amdgcn_sched_barrier(0);  // one half's S / dP live at a time
         }
     };
 
@@ -431,8 +441,9 @@ __global__ __launch_bounds__(DQ_THREADS, 1) void bwd_dq_kernel(const BwdArgs a) 
     Cursor cc = cl;
     auto enter_block = [&](const Cursor& c) __attribute__((always_inline)) {
         row_bounds(c.kp);
-        cc_flo = rl32(tb_flo, c.e);
-        cc_fhi = rl32(tb_fhi, c.e);
+        const int f = rl32(tb_full, c.e);
+        cc_flo = f & 0xffff;
+        cc_fhi = (f >> 16) - 1;
     };
     if (nT > 0) enter_block(cc);
     auto iteration = [&](int j, auto slot) __attribute__((always_inline)) {
