@@ -246,6 +246,22 @@ __global__ void bwd_prep_kernel(const BwdArgs a) {
     }
 }
 
+// Workgroup b of a grid of groups x per_group workgroups -> (group, index in
+// group).  Consecutive workgroup ids are dispatched to the 8 XCDs in turn;
+// when the group count is a multiple of 8 every group is kept on one XCD
+// (XCD b % 8 takes groups b % 8, b % 8 + 8, ...), else plain row order.
+__device__ __forceinline__ void xcd_map(int b, int nwg, int per_group, int& group, int& idx) {
+    const int n_groups = nwg / per_group;
+    if (n_groups % 8 == 0) {
+        const int r = b / 8;
+        group = b % 8 + 8 * (r / per_group);
+        idx = r % per_group;
+    } else {
+        group = b / per_group;
+        idx = b % per_group;
+    }
+}
+
 // Non-skipped streamed tiles of a block: [lo, hi] (hi < lo when none).
 template <typename Cls3>
 __device__ __forceinline__ void tile_range(int n_tiles, Cls3 cls, int& lo, int& hi) {
@@ -266,11 +282,17 @@ __global__ __launch_bounds__(DQ_THREADS, 1) void bwd_dq_kernel(const BwdArgs a) 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int half = lane >> 5, col = lane & 31;
-    // Workgroups of one (device, head) run their q-tiles last first (the
-    // causal ones with the most keys start early).
-    const int qt = a.n_qtiles - 1 - (int)(blockIdx.x % a.n_qtiles);
-    const int head = (blockIdx.x / a.n_qtiles) % a.Hq;
-    const int widx = blockIdx.x / (a.n_qtiles * a.Hq);
+    // Workgroup -> (device, head, q-tile): the q-tiles of one (device, head)
+    // group share every K/V tile they stream, so they run on one XCD (whose
+    // L2 then serves the re-reads); consecutive workgroup ids go to the 8
+    // XCDs in turn, so groups are dealt to the XCDs round robin.  Within a
+    // group the q-tiles run last first (under causal masks they have the
+    // most keys).
+    int grp_id, qi;
+    xcd_map(blockIdx.x, gridDim.x, a.n_qtiles, grp_id, qi);
+    const int qt = a.n_qtiles - 1 - qi;
+    const int head = grp_id % a.Hq;
+    const int widx = grp_id / a.Hq;
     const int kvh = head / a.group;
     const BwdWork w = a.works[widx];
     const int64_t B = a.B, ps = a.pos_stride;
@@ -527,9 +549,13 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(const BwdArgs a
     const int role = wave >> 2;  // 0: dV, 1: dK
     const int kw = wave & 3;     // which 32 keys of the workgroup
     const int half = lane >> 5, col = lane & 31;
-    const int kt = blockIdx.x % a.n_ktiles;
-    const int kvh = (blockIdx.x / a.n_ktiles) % a.Hkv;
-    const int ridx = blockIdx.x / (a.n_ktiles * a.Hkv);
+    // Workgroup -> (key block, kv head, key tile), the key tiles of one
+    // (block, kv head) group on one XCD, as for dq; they run first to last
+    // (under causal masks the first keys have the most queries).
+    int grp_id, kt;
+    xcd_map(blockIdx.x, gridDim.x, a.n_ktiles, grp_id, kt);
+    const int kvh = grp_id % a.Hkv;
+    const int ridx = grp_id / a.Hkv;
     const BwdWork w = a.rworks[ridx];
     const int64_t B = a.B, ps = a.pos_stride;
     const int64_t wk0 = (int64_t)kt * BW_TK;
