@@ -40,6 +40,8 @@ KERNEL = "step_bf16_kernel<128, true, true>"
 BWD_KERNEL = "bwd_dkdv_kernel<128>"
 KERNEL_SOURCES = ["ring_attention_step_amd/csrc/step_bf16.hip", "ring_attention_step_amd/csrc/plan.h",
                   "ring_attention_step_amd/csrc/kernels.h"]
+BWD_KERNEL_SOURCES = ["ring_attention_step_amd/csrc/backward.hip", "ring_attention_step_amd/csrc/plan.h",
+                      "ring_attention_step_amd/csrc/kernels.h"]
 
 
 def _code_only(text: str) -> str:
@@ -49,23 +51,24 @@ def _code_only(text: str) -> str:
     return " ".join(text.split())
 
 
-def kernel_source_sha() -> str:
+def kernel_source_sha(sources=KERNEL_SOURCES) -> str:
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in sources:
         with open(os.path.join(ROOT, p)) as f:
             h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 
-def traffic_from_profile(workload: str, prefetch: bool):
+def traffic_from_profile(workload: str, prefetch: bool, backward: bool = False):
     """HBM bytes per launch of the dominant kernel from the committed rocprofv3
     counter summary, or None when it is missing or the kernel changed since."""
-    path = os.path.join(ROOT, "profiles", "traffic_%s%s.json" % (workload, "_prefetch" if prefetch else ""))
+    name = "traffic_%s%s%s.json" % ("bwd_" if backward else "", workload, "_prefetch" if prefetch else "")
+    path = os.path.join(ROOT, "profiles", name)
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("kernel_src_sha") != kernel_source_sha():
+    if rec.get("kernel_src_sha") != kernel_source_sha(BWD_KERNEL_SOURCES if backward else KERNEL_SOURCES):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -266,10 +269,14 @@ def bench_backward(args, ra, W, w, x, q, k, v, cu, out, lse, plan, stream):
                    "mask": ["none", "causal", "doc-causal"][w.mask], "max_ring_passes": w.max_ring_passes,
                    "grad_dtype": "f32", "flop_per_step": flop, "allowed_pairs_per_head": plan["allowed_pairs"]},
         "pct_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
-        # the three backward kernels together, event-timed on the launch stream
+        # the three backward kernels together, event-timed on the launch stream;
+        # traffic: HBM bytes per launch of the dominant one (dk/dv) from the
+        # committed counter record
         "roofline": {"bound": "mfma", "kernel": "bwd_prep + bwd_dq_kernel<128> + " + BWD_KERNEL,
                      "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic_from_profile(w.name, False, backward=True),
+                     "traffic_kernel": BWD_KERNEL,
                      "event_ms_per_step": round(ms_event, 4),
                      "timing": "hip events on the launch stream around the timed backward calls"},
     }

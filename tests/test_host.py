@@ -219,6 +219,12 @@ def test_backward_refuses_bad_arguments_before_any_gpu_work(lib):
     big = dict(qq=_fake(128, 4, 128), kk=_fake(128, 2, 128), vv=_fake(128, 2, 128), oo=_fake(128, 4, 128),
                gg=_fake(128, 4, 128))
     assert bwd(n_blocks=128, P=1, **big) == ra.RA_E_UNSUPPORTED  # more ring blocks than lanes
+    huge = dict(qq=_fake(1 << 31, 4, 128), kk=_fake(1 << 31, 2, 128), vv=_fake(1 << 31, 2, 128),
+                oo=_fake(1 << 31, 4, 128), gg=_fake(1 << 31, 4, 128))
+    assert bwd(n_blocks=64, P=1, **huge) == ra.RA_E_UNSUPPORTED  # positions beyond 32 bits
+    long_blk = dict(qq=_fake(1 << 21, 4, 128), kk=_fake(1 << 21, 2, 128), vv=_fake(1 << 21, 2, 128),
+                    oo=_fake(1 << 21, 4, 128), gg=_fake(1 << 21, 4, 128))
+    assert bwd(n_blocks=1, P=1, **long_blk) == ra.RA_E_UNSUPPORTED  # 2^21 rows in one block
     assert bwd(ws_bytes=16) == ra.RA_E_WORKSPACE
     cu = (ctypes.c_int32 * 3)(0, 10, 64)
     assert bwd(mask=2, cu=cu, n_docs=2, layout=1) == ra.RA_E_UNSUPPORTED
