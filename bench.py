@@ -40,7 +40,8 @@ KERNEL = "step_bf16_kernel<128, true, true>"
 BWD_KERNEL = "bwd_dkdv_kernel<128>"
 KERNEL_SOURCES = ["ring_attention_step_amd/csrc/step_bf16.hip", "ring_attention_step_amd/csrc/plan.h",
                   "ring_attention_step_amd/csrc/kernels.h"]
-BWD_KERNEL_SOURCES = ["ring_attention_step_amd/csrc/backward.hip", "ring_attention_step_amd/csrc/plan.h",
+BWD_KERNEL_SOURCES = ["ring_attention_step_amd/csrc/backward.hip", "ring_attention_step_amd/csrc/bwd_kernels.h",
+                      "ring_attention_step_amd/csrc/plan.h",
                       "ring_attention_step_amd/csrc/kernels.h"]
 
 

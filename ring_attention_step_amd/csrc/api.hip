@@ -8,6 +8,7 @@
 #include <mutex>
 #include <vector>
 
+#include "bwd_kernels.h"
 #include "kernels.h"
 #include "plan.h"
 #include "ring_attn.h"

@@ -49,6 +49,7 @@
 #include <cstdint>
 #include <type_traits>
 
+#include "bwd_kernels.h"
 #include "kernels.h"
 #include "plan.h"
 
