@@ -29,8 +29,10 @@
  *  - Query head h reads key/value head h / (Hq / Hkv) (grouped-query
  *    attention, named on the flash-attention scrape page).
  *  - Scores are scale * q.k; scale must be finite and > 0.
- *  - Supported: bf16 inputs with head_dim 64 or 128 (matrix-core path, fp32
- *    accumulation); f32 inputs with head_dim 1..128 (exact fp32 path).
+ *  - Supported: 16-bit inputs (bf16 or fp16, the two data types the
+ *    flash-attention scrape page lists) with head_dim 64 or 128 (matrix-core
+ *    path, fp32 accumulation); f32 inputs with head_dim 1..128 (exact fp32
+ *    path).
  */
 #ifndef RING_ATTN_H
 #define RING_ATTN_H
@@ -50,7 +52,9 @@ typedef enum {
     RA_E_WORKSPACE = 4     /* workspace missing or smaller than ring_attn_forward_workspace_size */
 } ra_status;
 
-typedef enum { RA_F32 = 0, RA_BF16 = 1 } ra_dtype;
+/* Element types.  16-bit values round to nearest even wherever the library
+ * writes them (P before the P.V product, 16-bit outputs and gradients). */
+typedef enum { RA_F32 = 0, RA_BF16 = 1, RA_F16 = 2 } ra_dtype;
 
 /* Masks act on global token positions t (query) and t' (key):
  *  NONE: every key; CAUSAL: t' <= t; DOC_CAUSAL: t' <= t and both in the same
@@ -111,7 +115,7 @@ ra_status ring_attn_step(const ra_tensor* q_blk, const ra_tensor* k_blk, const r
  * accumulated weighted values by the accumulated weights at the end).
  *   O [Hq, Bq, d], m/l [Hq, Bq] fp32 contiguous; out is written at
  *   out + u*out_stride_tok + h*out_stride_head (+ c), dtype out_dtype
- *   (bf16 rounds to nearest even); lse nullable, [Hq, Bq] contiguous.
+ *   (16-bit types round to nearest even); lse nullable, [Hq, Bq] contiguous.
  */
 ra_status ring_attn_finalize(const float* O, const float* m, const float* l, int64_t Hq, int64_t Bq,
                              int64_t d, void* out, ra_dtype out_dtype, int64_t out_stride_tok,
@@ -139,7 +143,7 @@ size_t ring_attn_forward_workspace_size(const ra_tensor* q, const ra_tensor* k, 
  * ring blocks (virtual devices) by `layout`; for s = 0 .. min(P, N) - 1 every
  * virtual device i runs one step against block (i - s) mod N, with P =
  * max_ring_passes (GitHub issue: the maximum number of ring passes; one pass
- * is one step).  Pairs the mask skips entirely are not run.  bf16 inputs
+ * is one step).  Pairs the mask skips entirely are not run.  16-bit inputs
  * without prefetch: one launch runs the whole ring, every query tile of
  * every virtual device taking its device's steps in ring order with the
  * state kept on chip, then writing its normalised output.  Otherwise one
@@ -147,15 +151,15 @@ size_t ring_attn_forward_workspace_size(const ra_tensor* q, const ra_tensor* k, 
  * through the workspace between steps, and a device's last active step
  * writes its normalised output.
  *   q [T, Hq, d], k/v [T, Hkv, d] (views allowed, e.g. of a packed qkv).
- *   out: [T, Hq, d] contiguous, out_dtype (RA_F32 always allowed; RA_BF16 for
- *     bf16 inputs).  lse: nullable, [Hq, T] fp32 (natural log).
+ *   out: [T, Hq, d] contiguous, out_dtype (RA_F32 always allowed; for 16-bit
+ *     inputs also their own type).  lse: nullable, [Hq, T] fp32 (natural log).
  *   cu_seqlens_host: HOST pointer, n_docs + 1 entries, needed for DOC_CAUSAL
  *     (contiguous layout only); copied into the workspace.
  *   prefetch != 0: one launch per step; every step's key/value blocks are
  *     first copied, on a side stream, into a double buffer in the workspace
  *     while the previous step computes (the ring's transfer of the next
  *     block, modelled on one GPU).  For fp32 inputs the results are
- *     bit-identical to prefetch = 0; for bf16 they agree to bf16 rounding
+ *     bit-identical to prefetch = 0; for 16-bit inputs they agree to 16-bit rounding
  *     (the state hand-off changes the reference P is rounded against).
  *   stats: nullable HOST pointer; when given the call synchronises `stream`
  *     and fills it.
@@ -183,14 +187,14 @@ size_t ring_attn_backward_workspace_size(const ra_tensor* q, int32_t n_blocks, i
  * query heads that read it.  No atomics: the results do not depend on
  * scheduling.
  *   q, k, v, n_blocks, layout, mask_mode, max_ring_passes, cu_seqlens_host,
- *     n_docs, scale: as given to ring_attn_forward.  bf16 inputs with
- *     head_dim 64 or 128, n_blocks <= 64, T < 2^31 and T / n_blocks < 2^21
+ *     n_docs, scale: as given to ring_attn_forward.  16-bit inputs (bf16 or
+ *     fp16, all the same type) with head_dim 64 or 128, n_blocks <= 64, T < 2^31 and T / n_blocks < 2^21
  *     only (RA_E_UNSUPPORTED otherwise).
- *   out: the forward's output [T, Hq, d] view, bf16 or f32 (16-byte aligned
- *     rows); dout: [T, Hq, d] bf16 view.
+ *   out: the forward's output [T, Hq, d] view, f32 or the inputs' type
+ *     (16-byte aligned rows); dout: [T, Hq, d] view of the inputs' type.
  *   lse: the forward's lse, [Hq, T] fp32 (natural log).
  *   dq [T, Hq, d], dk / dv [T, Hkv, d]: contiguous, 16-byte aligned,
- *     grad_dtype (fp32 or bf16), every element written.
+ *     grad_dtype (fp32 or the inputs' type), every element written.
  *   workspace: ring_attn_backward_workspace_size bytes, 256-byte aligned.
  */
 ra_status ring_attn_backward(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v, const ra_tensor* out,

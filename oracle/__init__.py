@@ -96,7 +96,13 @@ def _dtype_code(x: torch.Tensor) -> int:
         return _F32
     if x.dtype == torch.bfloat16:
         return _BF16
-    raise TypeError("oracle takes float32 or bfloat16 tensors, got %s" % x.dtype)
+    raise TypeError("oracle takes float32, bfloat16 or float16 tensors, got %s" % x.dtype)
+
+
+def _widen(x: torch.Tensor) -> torch.Tensor:
+    """fp16 inputs as fp32 tensors: every binary16 value is exactly a binary32
+    value, so the fp64 decode downstream sees the same numbers."""
+    return x.float() if isinstance(x, torch.Tensor) and x.dtype == torch.float16 else x
 
 
 def _check_view(x: torch.Tensor, name: str):
@@ -131,6 +137,9 @@ def forward(q, k, v, *, n_blocks: int, layout: int = LAYOUT_CONTIGUOUS, mask: in
     With ``rows`` = (heads, tokens) index arrays of equal length n: out/O are
     [n, d] and lse/m/l are [n].
     """
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share a dtype")
+    q, k, v = _widen(q), _widen(k), _widen(v)
     for name, x in (("q", q), ("k", k), ("v", v)):
         _check_view(x, name)
     if not (q.dtype == k.dtype == v.dtype):
@@ -172,6 +181,7 @@ def block(q_blk, k_blk, v_blk, q_pos, k_pos, *, mask: int = MASK_NONE, cu_seqlen
           doc_T: Optional[int] = None, scale: Optional[float] = None):
     """One query block against one key/value block at explicit global positions.
     Returns dict(out, O: [Hq, nq, d]; lse, m, l: [Hq, nq])."""
+    q_blk, k_blk, v_blk = _widen(q_blk), _widen(k_blk), _widen(v_blk)
     for name, x in (("q_blk", q_blk), ("k_blk", k_blk), ("v_blk", v_blk)):
         _check_view(x, name)
     nq, Hq, d = q_blk.shape
@@ -269,7 +279,7 @@ def backward(q, k, v, dout, *, n_blocks: int, layout: int = LAYOUT_CONTIGUOUS, m
              max_ring_passes: Optional[int] = None, cu_seqlens=None, scale: Optional[float] = None,
              rows: Optional[Sequence] = None, rows_dkdv: bool = False):
     """Gradients (dq, dk, dv) of ``forward``'s output with respect to q, k, v
-    for the output gradient ``dout`` ([T, Hq, d], float32 or bfloat16), as
+    for the output gradient ``dout`` ([T, Hq, d], float32, bfloat16 or float16), as
     float64 arrays [T, Hq, d], [T, Hkv, d], [T, Hkv, d].  The arithmetic is in
     ``ring_oracle.c`` (``ro_backward``).
 
@@ -279,6 +289,9 @@ def backward(q, k, v, dout, *, n_blocks: int, layout: int = LAYOUT_CONTIGUOUS, m
     dq), and with ``rows_dkdv`` also (dq_rows, dk, dv) where dk / dv sum those
     rows' terms only -- the full dk / dv whenever dout vanishes on every other
     row."""
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share a dtype")
+    q, k, v, dout = _widen(q), _widen(k), _widen(v), _widen(dout)
     for name, x in (("q", q), ("k", k), ("v", v), ("dout", dout)):
         _check_view(x, name)
     if not (q.dtype == k.dtype == v.dtype):

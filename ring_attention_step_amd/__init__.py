@@ -25,7 +25,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libring_attn.so")
 
 RA_OK, RA_E_ARG, RA_E_UNSUPPORTED, RA_E_HIP, RA_E_WORKSPACE = range(5)
-RA_F32, RA_BF16 = 0, 1
+RA_F32, RA_BF16, RA_F16 = 0, 1, 2
 RA_MASK_NONE, RA_MASK_CAUSAL, RA_MASK_DOC_CAUSAL = 0, 1, 2
 RA_LAYOUT_CONTIGUOUS, RA_LAYOUT_STRIPED = 0, 1
 
@@ -102,7 +102,9 @@ def _dtype_code(dt: torch.dtype) -> int:
         return RA_F32
     if dt == torch.bfloat16:
         return RA_BF16
-    raise TypeError("ring attention takes float32 or bfloat16 tensors, got %s" % dt)
+    if dt == torch.float16:
+        return RA_F16
+    raise TypeError("ring attention takes float32, bfloat16 or float16 tensors, got %s" % dt)
 
 
 def _gpu(x: torch.Tensor, name: str):

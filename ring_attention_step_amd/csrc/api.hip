@@ -19,9 +19,12 @@ namespace {
 constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
-size_t elem_size(ra_dtype t) { return t == RA_BF16 ? 2 : 4; }
+// 16-bit element types (bf16, fp16) run on the matrix-core kernels.
+bool is16(int t) { return t == RA_BF16 || t == RA_F16; }
 
-bool valid_dtype(int t) { return t == RA_F32 || t == RA_BF16; }
+size_t elem_size(ra_dtype t) { return is16(t) ? 2 : 4; }
+
+bool valid_dtype(int t) { return t == RA_F32 || is16(t); }
 
 bool tensor_ok(const ra_tensor* x) {
     return x && x->data && valid_dtype(x->dtype) && x->n_tok >= 0 && x->n_head >= 1 && x->head_dim >= 1 &&
@@ -30,7 +33,7 @@ bool tensor_ok(const ra_tensor* x) {
 
 // Which kernel serves (dtype, head_dim); RA_OK when one does.
 ra_status kernel_for(ra_dtype dt, int64_t d, int* tq, int* tk) {
-    if (dt == RA_BF16) {
+    if (is16(dt)) {
         if (d != 64 && d != 128) return RA_E_UNSUPPORTED;
         *tq = kBf16TileQ;
         *tk = kBf16TileK;
@@ -46,7 +49,7 @@ ra_status kernel_for(ra_dtype dt, int64_t d, int* tq, int* tk) {
 }
 
 // The matrix-core kernel reads 16-byte vectors: base pointers and strides
-// must keep every row of 8 bf16 aligned.
+// must keep every row of 8 16-bit elements aligned.
 bool bf16_aligned(const ra_tensor* x) {
     return ((uintptr_t)x->data % 16 == 0) && x->stride_tok % 8 == 0 && x->stride_head % 8 == 0;
 }
@@ -60,7 +63,7 @@ bool bf16_tile_addressable(int64_t row_stride_elems) {
 bool scale_ok(float s) { return std::isfinite(s) && s > 0.f; }
 
 hipError_t launch(const StepArgs& a, ra_dtype dt, hipStream_t st) {
-    return dt == RA_BF16 ? launch_step_bf16(a, st) : launch_step_f32(a, st);
+    return is16(dt) ? launch_step_bf16(a, st) : launch_step_f32(a, st);
 }
 
 // Side stream + events used by the prefetch path, created once per device.
@@ -116,20 +119,20 @@ Workspace carve(void* base, int64_t T, int64_t N, int64_t Hq, int64_t Hkv, int64
     };
     const int64_t B = N > 0 ? T / N : 0;
     const size_t es = elem_size(dt);
-    const size_t vt_bytes = dt == RA_BF16 ? (size_t)N * Hkv * d * vt_padded_keys(B) * 2 : 0;
+    const size_t vt_bytes = is16(dt) ? (size_t)N * Hkv * d * vt_padded_keys(B) * 2 : 0;
     w.counters = (unsigned long long*)take(4 * sizeof(unsigned long long));
     w.cu = (int32_t*)take(sizeof(int32_t) * (size_t)(n_docs + 1));
     w.O = (float*)take(sizeof(float) * (size_t)(T * Hq * d));
     w.m = (float*)take(sizeof(float) * (size_t)(T * Hq));
     w.l = (float*)take(sizeof(float) * (size_t)(T * Hq));
-    if (dt == RA_BF16) {
+    if (is16(dt)) {
         w.vt = take(vt_bytes);
         w.works = (RingWork*)take(sizeof(RingWork) * (size_t)N);
         w.entries = (RingEntry*)take(sizeof(RingEntry) * (size_t)N * (size_t)N);
     }
     if (prefetch) {
         w.k_half = 2 * (size_t)T * Hkv * d * es;
-        const size_t v_half = dt == RA_BF16 ? 2 * vt_bytes : w.k_half;
+        const size_t v_half = is16(dt) ? 2 * vt_bytes : w.k_half;
         w.kv = take(w.k_half + v_half);
     }
     w.total = off;
@@ -213,7 +216,7 @@ ra_status ring_attn_step(const ra_tensor* q_blk, const ra_tensor* k_blk, const r
     int tq = 0, tk = 0;
     ra_status ks = kernel_for(q_blk->dtype, d, &tq, &tk);
     if (ks != RA_OK) return ks;
-    if (q_blk->dtype == RA_BF16 && (!bf16_aligned(q_blk) || !bf16_aligned(k_blk) || !bf16_aligned(v_blk) ||
+    if (is16(q_blk->dtype) && (!bf16_aligned(q_blk) || !bf16_aligned(k_blk) || !bf16_aligned(v_blk) ||
                                     !bf16_tile_addressable(k_blk->stride_tok) ||
                                     !bf16_tile_addressable(v_blk->stride_tok)))
         return RA_E_UNSUPPORTED;
@@ -239,6 +242,7 @@ ra_status ring_attn_step(const ra_tensor* q_blk, const ra_tensor* k_blk, const r
     a.Hq = (int32_t)Hq;
     a.group = (int32_t)(Hq / k_blk->n_head);
     a.d = (int32_t)d;
+    a.f16 = q_blk->dtype == RA_F16;
     a.mask = mask_mode;
     a.scale = scale;
     a.c2 = scale * 1.4426950408889634f;
@@ -264,7 +268,7 @@ ra_status ring_attn_finalize(const float* O, const float* m, const float* l, int
                              float* lse, void* stream) {
     if (!O || !m || !l || !out || Hq < 1 || Bq < 0 || d < 1 || !valid_dtype(out_dtype)) return RA_E_ARG;
     if (out_stride_tok < 0 || out_stride_head < 0) return RA_E_ARG;
-    if (launch_finalize(O, m, l, Hq, Bq, d, out, out_dtype == RA_BF16, out_stride_tok, out_stride_head, lse,
+    if (launch_finalize(O, m, l, Hq, Bq, d, out, (int)out_dtype, out_stride_tok, out_stride_head, lse,
                         (hipStream_t)stream) != hipSuccess)
         return RA_E_HIP;
     return RA_OK;
@@ -274,7 +278,7 @@ ra_status ring_attn_merge(void* out_acc, float* lse_acc, const void* out_blk, co
                           ra_dtype dtype, int64_t Hq, int64_t rows, int64_t d, void* stream) {
     if (!out_acc || !lse_acc || !out_blk || !lse_blk || !valid_dtype(dtype) || Hq < 1 || rows < 0 || d < 1)
         return RA_E_ARG;
-    if (launch_merge(out_acc, lse_acc, out_blk, lse_blk, dtype == RA_BF16, Hq, rows, d, (hipStream_t)stream) !=
+    if (launch_merge(out_acc, lse_acc, out_blk, lse_blk, (int)dtype, Hq, rows, d, (hipStream_t)stream) !=
         hipSuccess)
         return RA_E_HIP;
     return RA_OK;
@@ -350,18 +354,18 @@ ra_status ring_attn_forward(const ra_tensor* q, const ra_tensor* k, const ra_ten
     } else {
         n_docs = 0;
     }
-    if (out_dtype == RA_BF16 && q->dtype != RA_BF16) return RA_E_UNSUPPORTED;
+    if (is16(out_dtype) && out_dtype != q->dtype) return RA_E_UNSUPPORTED;
     int tq = 0, tk = 0;
     ra_status ks = kernel_for(q->dtype, d, &tq, &tk);
     if (ks != RA_OK) return ks;
     const int64_t row_mult = layout == RA_LAYOUT_STRIPED ? n_blocks : 1;
-    if (q->dtype == RA_BF16 && (!bf16_aligned(q) || !bf16_aligned(k) || !bf16_aligned(v) ||
+    if (is16(q->dtype) && (!bf16_aligned(q) || !bf16_aligned(k) || !bf16_aligned(v) ||
                                 !bf16_tile_addressable(row_mult * k->stride_tok) ||
                                 !bf16_tile_addressable(row_mult * v->stride_tok) ||
                                 vt_padded_keys(T / n_blocks) * 2 * d >= ((int64_t)1 << 31)))  // V^T tile rows
         return RA_E_UNSUPPORTED;
     if (prefetch && (k->stride_head != d || v->stride_head != d)) return RA_E_UNSUPPORTED;
-    if (q->dtype == RA_BF16 && (uintptr_t)out % 16) return RA_E_UNSUPPORTED;
+    if (is16(q->dtype) && (uintptr_t)out % 16) return RA_E_UNSUPPORTED;
     const int64_t N = n_blocks, B = T / N;
     const int64_t n_qtiles = (B + tq - 1) / tq;
     if (n_qtiles * Hq * kMaxPairs > INT32_MAX) return RA_E_UNSUPPORTED;
@@ -407,7 +411,8 @@ ra_status ring_attn_forward(const ra_tensor* q, const ra_tensor* k, const ra_ten
     base.c2 = scale * 1.4426950408889634f;
     base.cu = ws.cu;
     base.n_docs = n_docs;
-    base.out_bf16 = out_dtype == RA_BF16;
+    base.f16 = q->dtype == RA_F16;
+    base.out16 = is16(out_dtype);
     base.out = out;
     base.out_row_stride = (striped ? N : 1) * out_tok;
     base.out_head_stride = d;
@@ -421,7 +426,7 @@ ra_status ring_attn_forward(const ra_tensor* q, const ra_tensor* k, const ra_ten
     base.q_head_stride = q->stride_head;
 
     const size_t es = elem_size(q->dtype);
-    const bool use_vt = q->dtype == RA_BF16;
+    const bool use_vt = is16(q->dtype);
     const int64_t Bp = vt_padded_keys(B);
     const int64_t vt_blk = Hkv * d * Bp;    // elements of one packed V^T block
     const int64_t blk_elems = B * Hkv * d;  // one contiguous prefetched K (or V) block
@@ -588,7 +593,7 @@ ra_status ring_attn_forward(const ra_tensor* q, const ra_tensor* k, const ra_ten
     }
     for (int32_t i : plan.empty_devices) {
         const int64_t o_off = striped ? i * out_tok : i * B * out_tok;
-        if (launch_empty_rows(out, out_dtype == RA_BF16, o_off, base.out_row_stride, d, lse, striped ? i : i * B,
+        if (launch_empty_rows(out, (int)out_dtype, o_off, base.out_row_stride, d, lse, striped ? i : i * B,
                               base.lse_row_stride, T, B, Hq, d, st) != hipSuccess)
             return RA_E_HIP;
     }
@@ -643,15 +648,18 @@ ra_status ring_attn_backward(const ra_tensor* q, const ra_tensor* k, const ra_te
     } else {
         n_docs = 0;
     }
-    // Matrix-core backward only: bf16 inputs, head_dim 64 or 128, 16-byte rows,
-    // at most one ring block per lane of a wave (the per-block tables).
-    if (q->dtype != RA_BF16 || (d != 64 && d != 128)) return RA_E_UNSUPPORTED;
+    // Matrix-core backward only: 16-bit inputs, head_dim 64 or 128, 16-byte
+    // rows, at most one ring block per lane of a wave (the per-block tables);
+    // a 16-bit out or gradient has the inputs' type.
+    if (!is16(q->dtype) || (d != 64 && d != 128)) return RA_E_UNSUPPORTED;
+    if ((is16(out->dtype) && out->dtype != q->dtype) || (is16(grad_dtype) && grad_dtype != q->dtype))
+        return RA_E_UNSUPPORTED;
     if (n_blocks > kMaxRingChain) return RA_E_UNSUPPORTED;
     if (T >= ((int64_t)1 << 31)) return RA_E_UNSUPPORTED;  // per-lane positions are 32-bit
     if (T / n_blocks >= ((int64_t)1 << 21)) return RA_E_UNSUPPORTED;  // 64-row tile indices fit 15 bits
     if (!bf16_aligned(q) || !bf16_aligned(k) || !bf16_aligned(v) || !bf16_aligned(dout)) return RA_E_UNSUPPORTED;
-    if ((uintptr_t)out->data % 16 || out->stride_tok % (out->dtype == RA_BF16 ? 8 : 4) ||
-        out->stride_head % (out->dtype == RA_BF16 ? 8 : 4))
+    if ((uintptr_t)out->data % 16 || out->stride_tok % (is16(out->dtype) ? 8 : 4) ||
+        out->stride_head % (is16(out->dtype) ? 8 : 4))
         return RA_E_UNSUPPORTED;
     if ((uintptr_t)dq % 16 || (uintptr_t)dk % 16 || (uintptr_t)dv % 16) return RA_E_UNSUPPORTED;
     {
@@ -748,8 +756,9 @@ ra_status ring_attn_backward(const ra_tensor* q, const ra_tensor* k, const ra_te
     a.dq = dq;
     a.dk = dk;
     a.dv = dv;
-    a.out_bf16 = out->dtype == RA_BF16;
-    a.grad_bf16 = grad_dtype == RA_BF16;
+    a.f16 = q->dtype == RA_F16;
+    a.out16 = is16(out->dtype);
+    a.grad16 = is16(grad_dtype);
     a.T = T;
     a.B = B;
     a.pos_stride = striped ? N : 1;

@@ -1,5 +1,5 @@
-// Backward of the ring forward on the matrix cores (bf16 inputs, fp32
-// accumulation): the gradients dq, dk, dv of out = ring attention(q, k, v)
+// Backward of the ring forward on the matrix cores (16-bit inputs, bf16 or
+// fp16 -- the kernels' E --, fp32 accumulation): the gradients dq, dk, dv of out = ring attention(q, k, v)
 // for a given dout, from the forward's saved lse.
 //
 // For a query row t and an allowed key j (the forward's masks and ring
@@ -59,6 +59,8 @@ namespace {
 typedef __bf16 bf16;
 typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16;
+typedef f16 f16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -185,16 +187,34 @@ struct TileOps {
     }
 };
 
+// 16-bit operands are held as raw values in the bf16 vector type; E (bf16 or
+// fp16) picks the matrix-core instruction and the conversions.
+template <typename E>
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    if constexpr (std::is_same<E, f16>::value)
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c,
+                                                      0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// Accumulator register order -> bf16 operand pair (16-row chunks 2 h, 2 h + 1).
+template <typename E>
+__device__ __forceinline__ bf16 to16(float x) {  // round to E (nearest even)
+    return __builtin_bit_cast(bf16, (E)x);
+}
+
+template <typename E>
+__device__ __forceinline__ float from16(bf16 x) {
+    return (float)__builtin_bit_cast(E, x);
+}
+
+// Accumulator register order -> 16-bit operand pair (16-row chunks 2 h, 2 h + 1).
+template <typename E>
 __device__ __forceinline__ void acc_to_b(const f32x16& acc, bf16x8& b0, bf16x8& b1) {
 #pragma unroll
     for (int i = 0; i < 8; i++) {
-        b0[i] = (bf16)acc[i];
-        b1[i] = (bf16)acc[8 + i];
+        b0[i] = to16<E>(acc[i]);
+        b1[i] = to16<E>(acc[8 + i]);
     }
 }
 
@@ -203,6 +223,7 @@ __device__ __forceinline__ void acc_to_b(const f32x16& acc, bf16x8& b0, bf16x8& 
 // Outputs in block-local order: row u of block b (token pos(b, u)) at
 // h T + b B + u; lse = -inf (a row with no key) becomes +inf, so that every
 // P of the row is exp2(-inf) = 0.
+template <typename E>
 __global__ void bwd_prep_kernel(const BwdArgs a) {
     const int lanes = a.d / 8;
     const int64_t n = (int64_t)a.T * a.Hq;
@@ -224,17 +245,17 @@ __global__ void bwd_prep_kernel(const BwdArgs a) {
             h = row % a.Hq;
             const bf16x8 gv = *(const bf16x8*)((const bf16*)a.dout + t * a.do_st + h * a.do_sh + 8 * c);
             const int64_t oe = t * a.out_st + h * a.out_sh + 8 * c;
-            if (a.out_bf16) {
+            if (a.out16) {
                 const bf16x8 ov = *(const bf16x8*)((const bf16*)a.out + oe);
 #pragma unroll
-                for (int e = 0; e < 8; e++) s = fmaf((float)ov[e], (float)gv[e], s);
+                for (int e = 0; e < 8; e++) s = fmaf(from16<E>(ov[e]), from16<E>(gv[e]), s);
             } else {
                 const f32x4 o0 = *(const f32x4*)((const float*)a.out + oe);
                 const f32x4 o1 = *(const f32x4*)((const float*)a.out + oe + 4);
 #pragma unroll
-                for (int e = 0; e < 4; e++) s = fmaf(o0[e], (float)gv[e], s);
+                for (int e = 0; e < 4; e++) s = fmaf(o0[e], from16<E>(gv[e]), s);
 #pragma unroll
-                for (int e = 0; e < 4; e++) s = fmaf(o1[e], (float)gv[4 + e], s);
+                for (int e = 0; e < 4; e++) s = fmaf(o1[e], from16<E>(gv[4 + e]), s);
             }
         }
         for (int w = 1; w < lanes; w <<= 1) s += __shfl_xor(s, w, 64);
@@ -273,7 +294,7 @@ __device__ __forceinline__ void tile_range(int n_tiles, Cls3 cls, int& lo, int& 
 }
 
 // ---- dq ----
-template <int D>
+template <typename E, int D>
 __global__ __launch_bounds__(DQ_THREADS, 1) void bwd_dq_kernel(const BwdArgs a) {
     constexpr int TE = BW_T * D;              // elements of one [64][D] tile
     constexpr int NL = 2 * (TE / 512 / DQ_WAVES);  // loads per wave per stage: K tile, then V tile
@@ -426,8 +447,8 @@ __global__ __launch_bounds__(DQ_THREADS, 1) void bwd_dq_kernel(const BwdArgs a) 
             f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
             for (int kc = 0; kc < D / 16; kc++) {
-                s = mfma(ops.row(ks, kb, kc), qf[kc], s);
-                dp = mfma(ops.row(vs, kb, kc), gf[kc], dp);
+                s = mfma<E>(ops.row(ks, kb, kc), qf[kc], s);
+                dp = mfma<E>(ops.row(vs, kb, kc), gf[kc], dp);
             }
             // dS^T = P^T (dP^T - D); register i holds key 32 kb + 8 (i/4) + 4 half + i%4.
             // A masked key's exponent becomes -inf (P = 0, dS = 0): selects,
@@ -445,15 +466,15 @@ __global__ __launch_bounds__(DQ_THREADS, 1) void bwd_dq_kernel(const BwdArgs a) 
                     if (!FULL) arg = ((x >= x_lo) & (x < x_hi)) ? arg : -INFINITY;
                     dsv[i] = __builtin_amdgcn_exp2f(arg) * (dp[i] - drow);
                 }
-                acc_to_b(dsv, b0, b1);
+                acc_to_b<E>(dsv, b0, b1);
             };
             if (__builtin_amdgcn_readfirstlane((int)full)) softmax(std::true_type{});
             else softmax(std::false_type{});
             // dq^T += K^T dS^T over the two 16-key chunks of this half.
 #pragma unroll
             for (int db = 0; db < D / 32; db++) {
-                dq[db] = mfma(ops.tr(ks, 2 * kb, db), b0, dq[db]);
-                dq[db] = mfma(ops.tr(ks, 2 * kb + 1, db), b1, dq[db]);
+                dq[db] = mfma<E>(ops.tr(ks, 2 * kb, db), b0, dq[db]);
+                dq[db] = mfma<E>(ops.tr(ks, 2 * kb + 1, db), b1, dq[db]);
             }
         }
     };
@@ -522,13 +543,13 @@ __global__ __launch_bounds__(DQ_THREADS, 1) void bwd_dq_kernel(const BwdArgs a) 
             const int64_t e = oe + 32 * db + 8 * g;
             const float x0 = dq[db][4 * g] * a.scale, x1 = dq[db][4 * g + 1] * a.scale;
             const float x2 = dq[db][4 * g + 2] * a.scale, x3 = dq[db][4 * g + 3] * a.scale;
-            if (a.grad_bf16) *(bf16x4*)(ob + 2 * e) = bf16x4{(bf16)x0, (bf16)x1, (bf16)x2, (bf16)x3};
+            if (a.grad16) *(bf16x4*)(ob + 2 * e) = bf16x4{to16<E>(x0), to16<E>(x1), to16<E>(x2), to16<E>(x3)};
             else *(f32x4*)(ob + 4 * e) = f32x4{x0, x1, x2, x3};
         }
 }
 
 // ---- dk, dv ----
-template <int D>
+template <typename E, int D>
 __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(const BwdArgs a) {
     constexpr int TE = BW_T * D;
     constexpr int NQ = TE / 512 / KV_WAVES;  // loads per wave per stage for each of q and dout
@@ -735,7 +756,7 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(const BwdArgs a
         for (int sb = 0; sb < 2; sb++) {
             x[sb] = f32x16{};
 #pragma unroll
-            for (int kc = 0; kc < D / 16; kc++) x[sb] = mfma(ops.row(qs + row_src, sb, kc), opf[kc], x[sb]);
+            for (int kc = 0; kc < D / 16; kc++) x[sb] = mfma<E>(ops.row(qs + row_src, sb, kc), opf[kc], x[sb]);
         }
     };
     auto phase1_p = [&](const float* lw, int64_t u0, auto full_t) __attribute__((always_inline)) {
@@ -763,7 +784,7 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(const BwdArgs a
                     *(f32x4*)(p_mine + (4 * sb + q4) * 256) =
                         f32x4{pv[4 * q4], pv[4 * q4 + 1], pv[4 * q4 + 2], pv[4 * q4 + 3]};
                 bf16x8 b0, b1;
-                acc_to_b(pv, b0, b1);
+                acc_to_b<E>(pv, b0, b1);
                 set_b16(sb, 0, b0);
                 set_b16(sb, 1, b1);
             }
@@ -784,15 +805,15 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(const BwdArgs a
                     for (int r = 0; r < 4; r++) dsv[4 * g4 + r] = p4[r] * (x[sb][4 * g4 + r] - d4[r]);
                 }
                 bf16x8 e0, e1;
-                acc_to_b(dsv, e0, e1);
+                acc_to_b<E>(dsv, e0, e1);
                 set_b16(sb, 0, e0);
                 set_b16(sb, 1, e1);
             }
             // dv^T += dout^T P (dV wave) or dk^T += q^T dS (dK wave).
 #pragma unroll
             for (int db = 0; db < D / 32; db++) {
-                acc[db] = mfma(ops.tr(qs + tr_src, 2 * sb, db), b16(sb, 0), acc[db]);
-                acc[db] = mfma(ops.tr(qs + tr_src, 2 * sb + 1, db), b16(sb, 1), acc[db]);
+                acc[db] = mfma<E>(ops.tr(qs + tr_src, 2 * sb, db), b16(sb, 0), acc[db]);
+                acc[db] = mfma<E>(ops.tr(qs + tr_src, 2 * sb + 1, db), b16(sb, 1), acc[db]);
             }
         }
     };
@@ -876,9 +897,31 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(const BwdArgs a
             const int64_t e = oe + 32 * db + 8 * g;
             const float x0 = acc[db][4 * g] * mul, x1 = acc[db][4 * g + 1] * mul;
             const float x2 = acc[db][4 * g + 2] * mul, x3 = acc[db][4 * g + 3] * mul;
-            if (a.grad_bf16) *(bf16x4*)(ob + 2 * e) = bf16x4{(bf16)x0, (bf16)x1, (bf16)x2, (bf16)x3};
+            if (a.grad16) *(bf16x4*)(ob + 2 * e) = bf16x4{to16<E>(x0), to16<E>(x1), to16<E>(x2), to16<E>(x3)};
             else *(f32x4*)(ob + 4 * e) = f32x4{x0, x1, x2, x3};
         }
+}
+
+template <typename E>
+hipError_t launch_backward16(const BwdArgs& a, hipStream_t stream) {
+    if (a.T > 0) {
+        const int64_t threads = (int64_t)a.T * a.Hq * (a.d / 8);
+        const int blocks = (int)((threads + 255) / 256 < 8192 ? (threads + 255) / 256 : 8192);
+        bwd_prep_kernel<E><<<blocks, 256, 0, stream>>>(a);
+    }
+    const int64_t ndq = (int64_t)a.n_works * a.Hq * a.n_qtiles;
+    const int64_t ndk = (int64_t)a.n_rworks * a.Hkv * a.n_ktiles;
+    if (ndq > 0) {
+        if (a.d == 128) bwd_dq_kernel<E, 128><<<(unsigned)ndq, DQ_THREADS, 0, stream>>>(a);
+        else if (a.d == 64) bwd_dq_kernel<E, 64><<<(unsigned)ndq, DQ_THREADS, 0, stream>>>(a);
+        else return hipErrorInvalidValue;
+    }
+    if (ndk > 0) {
+        if (a.d == 128) bwd_dkdv_kernel<E, 128><<<(unsigned)ndk, KV_THREADS, 0, stream>>>(a);
+        else if (a.d == 64) bwd_dkdv_kernel<E, 64><<<(unsigned)ndk, KV_THREADS, 0, stream>>>(a);
+        else return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
 }
 
 }  // namespace
@@ -887,24 +930,7 @@ int bwd_tile_q() { return BW_TQ; }
 int bwd_tile_k() { return BW_TK; }
 
 hipError_t launch_backward(const BwdArgs& a, hipStream_t stream) {
-    if (a.T > 0) {
-        const int64_t threads = (int64_t)a.T * a.Hq * (a.d / 8);
-        const int blocks = (int)((threads + 255) / 256 < 8192 ? (threads + 255) / 256 : 8192);
-        bwd_prep_kernel<<<blocks, 256, 0, stream>>>(a);
-    }
-    const int64_t ndq = (int64_t)a.n_works * a.Hq * a.n_qtiles;
-    const int64_t ndk = (int64_t)a.n_rworks * a.Hkv * a.n_ktiles;
-    if (ndq > 0) {
-        if (a.d == 128) bwd_dq_kernel<128><<<(unsigned)ndq, DQ_THREADS, 0, stream>>>(a);
-        else if (a.d == 64) bwd_dq_kernel<64><<<(unsigned)ndq, DQ_THREADS, 0, stream>>>(a);
-        else return hipErrorInvalidValue;
-    }
-    if (ndk > 0) {
-        if (a.d == 128) bwd_dkdv_kernel<128><<<(unsigned)ndk, KV_THREADS, 0, stream>>>(a);
-        else if (a.d == 64) bwd_dkdv_kernel<64><<<(unsigned)ndk, KV_THREADS, 0, stream>>>(a);
-        else return hipErrorInvalidValue;
-    }
-    return hipGetLastError();
+    return a.f16 ? launch_backward16<f16>(a, stream) : launch_backward16<bf16>(a, stream);
 }
 
 }  // namespace ra

@@ -6,7 +6,7 @@
 
 namespace ra {
 
-// Backward of the ring (bf16 inputs, matrix cores).  Rows of every tensor are
+// Backward of the ring (16-bit inputs, bf16 or fp16; matrix cores).  Rows of every tensor are
 // global token positions (striped blocks are strided views).
 struct BwdWork {                   // one ring block and the blocks paired with it
     int64_t pos0;                  // global position of its local row 0
@@ -14,19 +14,19 @@ struct BwdWork {                   // one ring block and the blocks paired with 
     int32_t first, count;          // partner positions: partners[first .. first + count)
 };
 struct BwdArgs {
-    const void* q;                 // bf16 [T, Hq, d] view
-    const void* k;                 // bf16 [T, Hkv, d] view
+    const void* q;                 // 16-bit [T, Hq, d] view
+    const void* k;                 // 16-bit [T, Hkv, d] view
     const void* v;
-    const void* out;               // forward output [T, Hq, d], bf16 or f32 (out_bf16)
-    const void* dout;              // bf16 [T, Hq, d] view
+    const void* out;               // forward output [T, Hq, d], 16-bit or f32 (out16)
+    const void* dout;              // 16-bit [T, Hq, d] view
     int64_t q_st, q_sh, k_st, k_sh, v_st, v_sh, out_st, out_sh, do_st, do_sh;  // element strides
     const float* lse;              // [Hq, T], natural log
     float* Lse2;                   // workspace [Hq, T] (+ pad): lse * log2(e) in block-local row order
     float* Dsum;                   // workspace [Hq, T] (+ pad), same order: dout . out; Dsum - Lse2 < 2^30
-    void* dq;                      // [T, Hq, d] contiguous, f32 or bf16 (grad_bf16)
+    void* dq;                      // [T, Hq, d] contiguous, f32 or 16-bit (grad16)
     void* dk;                      // [T, Hkv, d] contiguous
     void* dv;
-    int32_t out_bf16, grad_bf16;
+    int32_t out16, grad16;
     int64_t T, B, pos_stride;      // tokens; rows per block; position step between local rows
     int32_t Hq, Hkv, group, d, mask;
     float scale, c2;               // scale and scale * log2(e)
@@ -38,6 +38,7 @@ struct BwdArgs {
     const int64_t* partners;
     const BwdWork* rworks;         // per key block: the query blocks that visit it
     const int64_t* rpartners;
+    int32_t f16;                   // 16-bit values are fp16, else bf16 (picks the kernels)
 };
 constexpr int kBwdPad = 256;       // floats of padding after Lse2 and after Dsum
 int bwd_tile_q();

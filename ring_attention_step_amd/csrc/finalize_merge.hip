@@ -17,31 +17,36 @@ namespace ra {
 namespace {
 
 typedef __bf16 bf16;
+typedef _Float16 f16;
 
-__device__ __forceinline__ float load_val(const void* p, int bf, int64_t i) {
-    return bf ? (float)((const bf16*)p)[i] : ((const float*)p)[i];
+// Element kinds: 0 fp32, 1 bf16, 2 fp16 (16-bit stores round to nearest even).
+__device__ __forceinline__ float load_val(const void* p, int kind, int64_t i) {
+    if (kind == 1) return (float)((const bf16*)p)[i];
+    if (kind == 2) return (float)((const f16*)p)[i];
+    return ((const float*)p)[i];
 }
-__device__ __forceinline__ void store_val(void* p, int bf, int64_t i, float x) {
-    if (bf) ((bf16*)p)[i] = (bf16)x;
+__device__ __forceinline__ void store_val(void* p, int kind, int64_t i, float x) {
+    if (kind == 1) ((bf16*)p)[i] = (bf16)x;
+    else if (kind == 2) ((f16*)p)[i] = (f16)x;
     else ((float*)p)[i] = x;
 }
 
 __global__ __launch_bounds__(256) void finalize_kernel(const float* O, const float* m, const float* l,
                                                         int64_t Hq, int64_t Bq, int64_t d, void* out,
-                                                        int out_bf16, int64_t ost, int64_t osh, float* lse) {
+                                                        int out_kind, int64_t ost, int64_t osh, float* lse) {
     const int lane = threadIdx.x & 63;
     const int64_t rows = Hq * Bq;
     for (int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); r < rows; r += (int64_t)gridDim.x * 4) {
         const int64_t h = r / Bq, u = r % Bq;
         const float lr = l[r];
         const float inv = lr > 0.f ? 1.f / lr : 0.f;
-        for (int64_t c = lane; c < d; c += 64) store_val(out, out_bf16, u * ost + h * osh + c, O[r * d + c] * inv);
+        for (int64_t c = lane; c < d; c += 64) store_val(out, out_kind, u * ost + h * osh + c, O[r * d + c] * inv);
         if (lane == 0 && lse) lse[r] = lr > 0.f ? m[r] + logf(lr) : -INFINITY;
     }
 }
 
 __global__ __launch_bounds__(256) void merge_kernel(void* out_acc, float* lse_acc, const void* out_blk,
-                                                     const float* lse_blk, int bf, int64_t Hq, int64_t rows,
+                                                     const float* lse_blk, int kind, int64_t Hq, int64_t rows,
                                                      int64_t d) {
     const int lane = threadIdx.x & 63;
     const int64_t n = Hq * rows;
@@ -60,8 +65,8 @@ __global__ __launch_bounds__(256) void merge_kernel(void* out_acc, float* lse_ac
         }
         const int64_t base = (u * Hq + h) * d;
         for (int64_t c = lane; c < d; c += 64) {
-            const float x = wa * load_val(out_acc, bf, base + c) + wb * load_val(out_blk, bf, base + c);
-            store_val(out_acc, bf, base + c, big == -INFINITY ? 0.f : x);
+            const float x = wa * load_val(out_acc, kind, base + c) + wb * load_val(out_blk, kind, base + c);
+            store_val(out_acc, kind, base + c, big == -INFINITY ? 0.f : x);
         }
         if (lane == 0) lse_acc[r] = lse;
     }
@@ -72,13 +77,13 @@ __global__ void fill_u64_kernel(unsigned long long* p, int64_t n) {
         p[i] = 0ull;
 }
 
-__global__ __launch_bounds__(256) void empty_rows_kernel(void* out, int out_bf16, int64_t out_off, int64_t ors,
+__global__ __launch_bounds__(256) void empty_rows_kernel(void* out, int out_kind, int64_t out_off, int64_t ors,
                                                           int64_t ohs, float* lse, int64_t lse_off, int64_t lrs,
                                                           int64_t lhs, int64_t rows, int64_t Hq, int64_t d) {
     const int64_t n = rows * Hq * d;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
         const int64_t c = i % d, h = (i / d) % Hq, u = i / (d * Hq);
-        store_val(out, out_bf16, out_off + u * ors + h * ohs + c, 0.f);
+        store_val(out, out_kind, out_off + u * ors + h * ohs + c, 0.f);
         if (c == 0 && lse) lse[lse_off + h * lhs + u * lrs] = -INFINITY;
     }
 }
@@ -93,16 +98,16 @@ unsigned grid_for(int64_t work, int64_t per_block) {
 }  // namespace
 
 hipError_t launch_finalize(const float* O, const float* m, const float* l, int64_t Hq, int64_t Bq, int64_t d,
-                           void* out, int out_bf16, int64_t ost, int64_t osh, float* lse, hipStream_t stream) {
+                           void* out, int out_kind, int64_t ost, int64_t osh, float* lse, hipStream_t stream) {
     if (Hq * Bq == 0) return hipSuccess;
-    finalize_kernel<<<grid_for(Hq * Bq, 4), 256, 0, stream>>>(O, m, l, Hq, Bq, d, out, out_bf16, ost, osh, lse);
+    finalize_kernel<<<grid_for(Hq * Bq, 4), 256, 0, stream>>>(O, m, l, Hq, Bq, d, out, out_kind, ost, osh, lse);
     return hipGetLastError();
 }
 
-hipError_t launch_merge(void* out_acc, float* lse_acc, const void* out_blk, const float* lse_blk, int bf16_,
+hipError_t launch_merge(void* out_acc, float* lse_acc, const void* out_blk, const float* lse_blk, int kind,
                         int64_t Hq, int64_t rows, int64_t d, hipStream_t stream) {
     if (Hq * rows == 0) return hipSuccess;
-    merge_kernel<<<grid_for(Hq * rows, 4), 256, 0, stream>>>(out_acc, lse_acc, out_blk, lse_blk, bf16_, Hq, rows, d);
+    merge_kernel<<<grid_for(Hq * rows, 4), 256, 0, stream>>>(out_acc, lse_acc, out_blk, lse_blk, kind, Hq, rows, d);
     return hipGetLastError();
 }
 
@@ -112,11 +117,11 @@ hipError_t launch_fill_u64(unsigned long long* p, int64_t n, hipStream_t stream)
     return hipGetLastError();
 }
 
-hipError_t launch_empty_rows(void* out, int out_bf16, int64_t out_off, int64_t ors, int64_t ohs, float* lse,
+hipError_t launch_empty_rows(void* out, int out_kind, int64_t out_off, int64_t ors, int64_t ohs, float* lse,
                              int64_t lse_off, int64_t lrs, int64_t lhs, int64_t rows, int64_t Hq, int64_t d,
                              hipStream_t stream) {
     if (rows * Hq * d == 0) return hipSuccess;
-    empty_rows_kernel<<<grid_for(rows * Hq * d, 256), 256, 0, stream>>>(out, out_bf16, out_off, ors, ohs, lse,
+    empty_rows_kernel<<<grid_for(rows * Hq * d, 256), 256, 0, stream>>>(out, out_kind, out_off, ors, ohs, lse,
                                                                          lse_off, lrs, lhs, rows, Hq, d);
     return hipGetLastError();
 }

@@ -42,7 +42,7 @@ struct StepArgs {
     int64_t q_row_stride, q_head_stride;   // elements, per local row / head
     int64_t k_row_stride, k_head_stride;
     int64_t v_row_stride, v_head_stride;
-    const void* vt;                        // packed V^T (bf16 matrix-core path) or null
+    const void* vt;                        // packed V^T (16-bit matrix-core path) or null
     int64_t vt_row_stride, vt_head_stride; // elements per dim row / per head of a packed block
     int64_t Bq, Bk;                        // rows in the query block / key block
     int64_t pos_stride;                    // position step between local rows
@@ -53,7 +53,7 @@ struct StepArgs {
     float c2;                              // scale * log2(e)
     const int32_t* cu;                     // device cu_seqlens (doc-causal)
     int32_t n_docs;
-    int32_t out_bf16;
+    int32_t out16;                         // out in the inputs' 16-bit type (else fp32)
     void* out;
     int64_t out_row_stride, out_head_stride;
     float* lse;                            // nullable
@@ -65,6 +65,7 @@ struct StepArgs {
     // RingWork entries (pairs[] is unused), each finalised at its end.
     const RingWork* works;
     const RingEntry* entries;
+    int32_t f16;                           // 16-bit inputs are fp16, else bf16 (picks the kernel)
 };
 
 // Kernel tile shapes (query rows x key columns per workgroup tile).
@@ -74,10 +75,11 @@ constexpr int kF32TileQ = 64, kF32TileK = 64;
 hipError_t launch_step_bf16(const StepArgs& a, hipStream_t stream);
 hipError_t launch_step_f32(const StepArgs& a, hipStream_t stream);
 hipError_t launch_finalize(const float* O, const float* m, const float* l, int64_t Hq, int64_t Bq,
-                           int64_t d, void* out, int out_bf16, int64_t out_stride_tok,
+                           int64_t d, void* out, int out_kind, int64_t out_stride_tok,
                            int64_t out_stride_head, float* lse, hipStream_t stream);
 hipError_t launch_merge(void* out_acc, float* lse_acc, const void* out_blk, const float* lse_blk,
-                        int bf16, int64_t Hq, int64_t rows, int64_t d, hipStream_t stream);
+                        int kind, int64_t Hq, int64_t rows, int64_t d, hipStream_t stream);
+// out_kind / kind: element type of out (0 fp32, 1 bf16, 2 fp16).
 hipError_t launch_fill_u64(unsigned long long* p, int64_t n, hipStream_t stream);
 
 // Packed V^T of the ring blocks: vt[j][g][c][p] (p < Bp = B rounded up to the
@@ -87,7 +89,7 @@ hipError_t launch_fill_u64(unsigned long long* p, int64_t n, hipStream_t stream)
 int64_t vt_padded_keys(int64_t B);
 hipError_t launch_pack_vt(const void* v, int64_t v_stride_tok, int64_t v_stride_head, int64_t N, int64_t B,
                           int striped, int64_t Hkv, int64_t d, void* vt, hipStream_t stream);
-hipError_t launch_empty_rows(void* out, int out_bf16, int64_t out_off, int64_t out_row_stride,
+hipError_t launch_empty_rows(void* out, int out_kind, int64_t out_off, int64_t out_row_stride,
                              int64_t out_head_stride, float* lse, int64_t lse_off,
                              int64_t lse_row_stride, int64_t lse_head_stride, int64_t rows,
                              int64_t Hq, int64_t d, hipStream_t stream);

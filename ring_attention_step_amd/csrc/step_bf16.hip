@@ -1,4 +1,7 @@
-// One ring step on the gfx950 matrix cores: bf16 Q, K, V; fp32 accumulation.
+// One ring step on the gfx950 matrix cores: 16-bit Q, K, V (bf16 or fp16,
+// the kernel's E); fp32 accumulation.  Operands are held as raw 16-bit values
+// (the bf16 vector type is only their container); E picks the MFMA and the
+// rounding of P and of a 16-bit output.
 //
 // A workgroup owns tile_q = 256 query rows of one head of one (query block,
 // key/value block) pair: 8 waves of 32 rows.  Waves w and w + 4 share a SIMD
@@ -22,9 +25,9 @@
 //                    simulation" gist applied to a whole tile (Zhihu article,
 //                    local vs. global softmax): tile max, rescale of the state
 //                    when the max grows, P = exp2(S*c - m*c), c = scale*log2 e.
-//                    Row sums add up P in fp32, before its bf16 rounding.
+//                    Row sums add up P in fp32, before its 16-bit rounding.
 //   O^T += V^T P^T   4 x D/32 MFMA 32x32x16 (dims x queries); P converted to
-//                    bf16 straight from the S^T accumulators (its lane layout
+//                    E straight from the S^T accumulators (its lane layout
 //                    is already the B operand).
 // The O rescale is lazy: it is applied only when some row's maximum grows by
 // more than 8 in log2 units (P stays <= 256), and one final rescale to the
@@ -61,6 +64,8 @@ namespace {
 typedef __bf16 bf16;
 typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16;
+typedef f16 f16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -75,6 +80,23 @@ static_assert(BK == 64, "the lane layouts below assume 64-key tiles");
 
 template <int I>
 using ic = std::integral_constant<int, I>;
+
+// C += A B on the 32x32x16 matrix core for element type E (operands as 16-bit
+// containers, reinterpreted without conversion).
+template <typename E>
+__device__ __forceinline__ f32x16 mma(bf16x8 a, bf16x8 b, f32x16 c) {
+    if constexpr (std::is_same<E, f16>::value)
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c,
+                                                      0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// x rounded to E (nearest even), in the 16-bit container.
+template <typename E>
+__device__ __forceinline__ bf16 to16(float x) {
+    return __builtin_bit_cast(bf16, (E)x);
+}
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -180,7 +202,7 @@ __device__ __forceinline__ float other_half(float x) {
     return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
 }
 
-template <int D, bool VT, bool RING>
+template <typename E, int D, bool VT, bool RING>
 __global__ __launch_bounds__(THREADS, 1) void step_bf16_kernel(const StepArgs a) {
     using TL = Tiles<D>;
     // Three stage buffers as six distinct arrays: the compiler can then tell
@@ -526,9 +548,9 @@ __global__ __launch_bounds__(THREADS, 1) void step_bf16_kernel(const StepArgs a)
 #pragma unroll
         for (int i = 0; i < NS; i++) {
             const int q = i / (D / 32), db = i % (D / 32);
-            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i % AHEAD], pb[q >> 1][q & 1], o[db], 0, 0, 0);
+            o[db] = mma<E>(va[i % AHEAD], pb[q >> 1][q & 1], o[db]);
             if (i + AHEAD < NS) va[i % AHEAD] = v_frag(i + AHEAD);
-            s[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[i % AHEAD], qf[i >> 1], s[i & 1], 0, 0, 0);
+            s[i & 1] = mma<E>(ka[i % AHEAD], qf[i >> 1], s[i & 1]);
             if (i + AHEAD < NS) ka[i % AHEAD] = k_frag(ks, i + AHEAD);
         }
     };
@@ -592,7 +614,7 @@ __global__ __launch_bounds__(THREADS, 1) void step_bf16_kernel(const StepArgs a)
                 for (int i = 0; i < 16; i++) {
                     const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][i], a.c2, -mref));
                     ps[i % 4] = (kb == 0 && i < 4) ? p : ps[i % 4] + p;
-                    pb[kb][i / 8][i % 8] = (bf16)p;
+                    pb[kb][i / 8][i % 8] = to16<E>(p);
                 }
             return (ps[0] + ps[1]) + (ps[2] + ps[3]);
         };
@@ -611,7 +633,7 @@ __global__ __launch_bounds__(THREADS, 1) void step_bf16_kernel(const StepArgs a)
             s[1] = f32x16{};
 #pragma unroll
             for (int i = 0; i < NS; i++)
-                s[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_frag(ks, i), qf[i >> 1], s[i & 1], 0, 0, 0);
+                s[i & 1] = mma<E>(k_frag(ks, i), qf[i >> 1], s[i & 1]);
             mask();
             rebase();
             lt = probs();
@@ -741,7 +763,7 @@ __global__ __launch_bounds__(THREADS, 1) void step_bf16_kernel(const StepArgs a)
                 const int64_t e = oe + 32 * db + 8 * g;
                 const float x0 = o[db][4 * g] * inv, x1 = o[db][4 * g + 1] * inv;
                 const float x2 = o[db][4 * g + 2] * inv, x3 = o[db][4 * g + 3] * inv;
-                if (a.out_bf16) *(bf16x4*)(ob + 2 * e) = bf16x4{(bf16)x0, (bf16)x1, (bf16)x2, (bf16)x3};
+                if (a.out16) *(bf16x4*)(ob + 2 * e) = bf16x4{to16<E>(x0), to16<E>(x1), to16<E>(x2), to16<E>(x3)};
                 else *(f32x4*)(ob + 4 * e) = f32x4{x0, x1, x2, x3};
             }
         if (half == 0 && a.lse)
@@ -762,27 +784,32 @@ __global__ __launch_bounds__(THREADS, 1) void step_bf16_kernel(const StepArgs a)
     }
 }
 
-}  // namespace
-
-hipError_t launch_step_bf16(const StepArgs& a, hipStream_t stream) {
+template <typename E>
+hipError_t launch_step16(const StepArgs& a, hipStream_t stream) {
     const int64_t nwg = (int64_t)a.n_qtiles * a.Hq * a.n_pairs;
     if (nwg == 0) return hipSuccess;
     const dim3 grid((unsigned)nwg), block(THREADS);
     if (a.works) {  // the one-launch ring reads the packed V^T
         if (!a.vt) return hipErrorInvalidValue;
-        if (a.d == 128) step_bf16_kernel<128, true, true><<<grid, block, 0, stream>>>(a);
-        else if (a.d == 64) step_bf16_kernel<64, true, true><<<grid, block, 0, stream>>>(a);
+        if (a.d == 128) step_bf16_kernel<E, 128, true, true><<<grid, block, 0, stream>>>(a);
+        else if (a.d == 64) step_bf16_kernel<E, 64, true, true><<<grid, block, 0, stream>>>(a);
         else return hipErrorInvalidValue;
     } else if (a.vt) {
-        if (a.d == 128) step_bf16_kernel<128, true, false><<<grid, block, 0, stream>>>(a);
-        else if (a.d == 64) step_bf16_kernel<64, true, false><<<grid, block, 0, stream>>>(a);
+        if (a.d == 128) step_bf16_kernel<E, 128, true, false><<<grid, block, 0, stream>>>(a);
+        else if (a.d == 64) step_bf16_kernel<E, 64, true, false><<<grid, block, 0, stream>>>(a);
         else return hipErrorInvalidValue;
     } else {
-        if (a.d == 128) step_bf16_kernel<128, false, false><<<grid, block, 0, stream>>>(a);
-        else if (a.d == 64) step_bf16_kernel<64, false, false><<<grid, block, 0, stream>>>(a);
+        if (a.d == 128) step_bf16_kernel<E, 128, false, false><<<grid, block, 0, stream>>>(a);
+        else if (a.d == 64) step_bf16_kernel<E, 64, false, false><<<grid, block, 0, stream>>>(a);
         else return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_step_bf16(const StepArgs& a, hipStream_t stream) {
+    return a.f16 ? launch_step16<f16>(a, stream) : launch_step16<bf16>(a, stream);
 }
 
 }  // namespace ra

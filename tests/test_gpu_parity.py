@@ -2,8 +2,11 @@
 seeded inputs.  Tolerances (fp32 outputs compared with the oracle):
   fp32 inputs: max |diff| <= 1e-5;
   bf16 inputs (fp32 accumulation): max |diff| <= 2e-2 and mean |diff| <= 1e-2;
+  fp16 inputs: the bf16 bounds scaled by the ratio of the two unit roundoffs
+    (2^-11 / 2^-8 = 1/8): max |diff| <= 2.5e-3 and mean |diff| <= 1.25e-3;
   tallies: exact.
 """
+import dataclasses
 import math
 
 import numpy as np
@@ -17,6 +20,8 @@ pytestmark = pytest.mark.gpu
 
 F32_TOL = 1e-5
 BF16_MAX, BF16_MEAN = 2e-2, 1e-2
+TOL16 = {"bf16": (BF16_MAX, BF16_MEAN), "f16": (BF16_MAX / 8, BF16_MEAN / 8)}
+TORCH16 = {"bf16": torch.bfloat16, "f16": torch.float16}
 
 
 @pytest.fixture(scope="module")
@@ -36,10 +41,11 @@ def _dev(*xs):
     return [x.cuda() for x in xs]
 
 
-def _check_bf16(out, ref, what):
+def _check_bf16(out, ref, what, dt="bf16"):
     diff = np.abs(out - ref)
-    _say(what, "max", float(diff.max()), "mean", float(diff.mean()))
-    assert diff.max() <= BF16_MAX and diff.mean() <= BF16_MEAN, (what, diff.max(), diff.mean())
+    _say(what, dt, "max", float(diff.max()), "mean", float(diff.mean()))
+    tmax, tmean = TOL16[dt]
+    assert diff.max() <= tmax and diff.mean() <= tmean, (what, dt, diff.max(), diff.mean())
 
 
 # ---------------------------------------------------------------------------
@@ -161,28 +167,29 @@ SMALL = [
 ]
 
 
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
 @pytest.mark.parametrize("case", range(len(SMALL)))
-def test_bf16_forward_small(ra, case):
+def test_16bit_forward_small(ra, case, dt):
     T, N, Hq, Hkv, d, layout, mask, P, docs = SMALL[case]
     if docs == "random":
         docs = W.random_doc_cu_seqlens(T, 16, 900, seed=case).tolist()
-    _say("bf16 small", SMALL[case])
-    qh, kh, vh = W.random_qkv(T, Hq, Hkv, d, "bf16", 1000 + case)
+    _say(dt, "small", SMALL[case])
+    qh, kh, vh = W.random_qkv(T, Hq, Hkv, d, dt, 1000 + case)
     q, k, v = _dev(qh, kh, vh)
     lay = "striped" if layout == 1 else "contiguous"
     out, lse, st = ra.forward(q, k, v, n_blocks=N, layout=lay, causal=mask == 1, cu_seqlens=docs,
                               max_ring_passes=P, out_dtype=torch.float32, return_lse=True, return_stats=True)
     ref = oracle.forward(qh, kh, vh, n_blocks=N, layout=layout, mask=mask, max_ring_passes=P, cu_seqlens=docs)
-    _check_bf16(out.cpu().double().numpy(), ref["out"], "out")
+    _check_bf16(out.cpu().double().numpy(), ref["out"], "out", dt)
     assert np.abs(lse.cpu().double().numpy() - ref["lse"]).max() <= 1e-3
     tal = oracle.tallies(T, N, layout=layout, mask=mask, max_ring_passes=P, cu_seqlens=docs,
                          tile_q=st["tile_q"], tile_k=st["tile_k"])
     for key, val in tal.items():
         assert st[key] == val, key
-    # bf16 output is the round-to-nearest-even of the fp32 one, bit for bit
-    out_bf = ra.forward(q, k, v, n_blocks=N, layout=lay, causal=mask == 1, cu_seqlens=docs, max_ring_passes=P)
-    assert out_bf.dtype == torch.bfloat16
-    assert torch.equal(out_bf, out.to(torch.bfloat16))
+    # 16-bit output is the round-to-nearest-even of the fp32 one, bit for bit
+    out16 = ra.forward(q, k, v, n_blocks=N, layout=lay, causal=mask == 1, cu_seqlens=docs, max_ring_passes=P)
+    assert out16.dtype == TORCH16[dt]
+    assert torch.equal(out16, out.to(TORCH16[dt]))
 
 
 def test_bf16_ring_late_score_jumps(ra):
@@ -220,28 +227,29 @@ def test_bf16_packed_qkv_views(ra):
     _check_bf16(out.cpu().double().numpy(), ref["out"], "packed")
 
 
-def test_bf16_prefetch_matches_one_launch_ring(ra):
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_16bit_prefetch_matches_one_launch_ring(ra, dt):
     """The side-stream prefetch path (one launch per ring step, state through
     HBM between steps) and the default one-launch ring (state in registers)
     round differently, so both are held to the oracle and to each other."""
     for layout, docs in (("contiguous", None), ("striped", None), ("contiguous", [0, 300, 301, 1024])):
-        qkv = W.random_qkv(1024, 4, 2, 128, "bf16", 5, packed=False)
+        qkv = W.random_qkv(1024, 4, 2, 128, dt, 5, packed=False)
         q, k, v = _dev(*qkv)
         kw = dict(n_blocks=4, layout=layout, causal=docs is None, cu_seqlens=docs, return_lse=True,
                   out_dtype=torch.float32)
         a, la = ra.forward(q, k, v, prefetch=False, **kw)
         b, lb = ra.forward(q, k, v, prefetch=True, **kw)
         torch.cuda.synchronize()
-        _say("prefetch", layout, docs is not None)
+        _say("prefetch", dt, layout, docs is not None)
         lay = oracle.LAYOUT_STRIPED if layout == "striped" else oracle.LAYOUT_CONTIGUOUS
         mask = oracle.MASK_CAUSAL if docs is None else oracle.MASK_DOC_CAUSAL
         ref = oracle.forward(*qkv, n_blocks=4, layout=lay, mask=mask, cu_seqlens=docs)
         for x, lx in ((a, la), (b, lb)):
-            _check_bf16(x.cpu().double().numpy(), ref["out"], "prefetch")
+            _check_bf16(x.cpu().double().numpy(), ref["out"], "prefetch", dt)
             assert np.abs(lx.cpu().double().numpy() - ref["lse"]).max() <= 1e-3
-        # The two paths differ in where P is rounded to bf16 (relative to the
-        # running reference maximum, which a state hand-off resets): they
-        # agree to bf16 level, not bitwise.
+        # The two paths differ in where P is rounded to 16 bits (relative to
+        # the running reference maximum, which a state hand-off resets): they
+        # agree to that rounding level, not bitwise.
         dif = (a - b).abs()
         assert dif.max().item() <= 1e-2 and dif.mean().item() <= 5e-4
         assert (la - lb).abs().max().item() <= 1e-3
@@ -292,11 +300,12 @@ def test_bf16_shuffled_step_order_within_tolerance(ra):
     _check_bf16(out.cpu().double().numpy(), ref["out"], "shuffled")
 
 
-def test_bf16_step_api_striped_positions(ra):
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_16bit_step_api_striped_positions(ra, dt):
     """ring_attn_step on striped blocks given as strided views, positions
     q_offset + u * N; the state must equal the oracle's block state."""
     T, N, Hq, d = 1024, 4, 2, 128
-    qh, kh, vh = W.random_qkv(T, Hq, Hq, d, "bf16", 11)
+    qh, kh, vh = W.random_qkv(T, Hq, Hq, d, dt, 11)
     q, k, v = _dev(qh, kh, vh)
     i, j = 1, 3
     B = T // N
@@ -311,8 +320,38 @@ def test_bf16_step_api_striped_positions(ra):
     ok = ref["l"] > 0
     assert np.array_equal(got_l > 0, ok)
     out = (O.cpu().double().numpy() / np.where(ok, got_l, 1)[..., None])
-    _check_bf16(out[ok], ref["out"][ok], "striped step")
+    _check_bf16(out[ok], ref["out"][ok], "striped step", dt)
     assert np.abs(m.cpu().double().numpy()[ok] - ref["m"][ok]).max() <= 1e-3
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_16bit_finalize_and_merge_round_the_fp32_results(ra, dt):
+    """ring_attn_finalize / ring_attn_merge with a 16-bit out: the finalized
+    output is the fp32 one rounded to nearest even, and so is the merge of two
+    16-bit partial outputs (the merge computes in fp32 either way)."""
+    g = torch.Generator().manual_seed(12)
+    Hq, B, d = 2, 300, 128
+    O = torch.randn(Hq, B, d, generator=g).cuda()
+    m = torch.randn(Hq, B, generator=g).cuda()
+    l = (torch.rand(Hq, B, generator=g) + 0.5).cuda()
+    l[0, :7] = 0  # rows that saw no key: out 0, lse -inf
+    o32 = torch.empty(B, Hq, d, device="cuda")
+    o16 = torch.empty(B, Hq, d, device="cuda", dtype=TORCH16[dt])
+    lse = torch.empty(Hq, B, device="cuda")
+    ra.ring_attn_finalize(O, m, l, o32, lse)
+    ra.ring_attn_finalize(O, m, l, o16)
+    assert torch.equal(o16, o32.to(TORCH16[dt]))
+    assert torch.isinf(lse[0, :7]).all() and not o32[:7, 0].any()
+    # merge (o16, lse) with a second partial result
+    ob = torch.randn(B, Hq, d, generator=g).to(TORCH16[dt]).cuda()
+    lb = torch.randn(Hq, B, generator=g).cuda()
+    acc16, lacc16 = o16.clone(), lse.clone()
+    acc32, lacc32 = o16.float(), lse.clone()
+    ra.ring_attn_merge(acc16, lacc16, ob, lb)
+    ra.ring_attn_merge(acc32, lacc32, ob.float(), lb)
+    torch.cuda.synchronize()
+    assert torch.equal(lacc16, lacc32)
+    assert torch.equal(acc16, acc32.to(TORCH16[dt]))
 
 
 # ---------------------------------------------------------------------------
@@ -328,10 +367,12 @@ def _sample_rows(w, rng, n=48):
     return np.asarray(heads), np.asarray(toks)
 
 
-@pytest.mark.parametrize("name", ["causal32k_h32_d128_8blk", "gqa_striped64k_h32kv8_d128_16blk",
-                                  "varlen_packed128k_h32_d128_8blk_p4"])
-def test_long_workload_sampled_rows(ra, name):
-    w = W.WORKLOADS[name]
+@pytest.mark.parametrize("name,dt", [("causal32k_h32_d128_8blk", "bf16"),
+                                     ("gqa_striped64k_h32kv8_d128_16blk", "bf16"),
+                                     ("varlen_packed128k_h32_d128_8blk_p4", "bf16"),
+                                     ("causal32k_h32_d128_8blk", "f16")])
+def test_long_workload_sampled_rows(ra, name, dt):
+    w = dataclasses.replace(W.WORKLOADS[name], dtype=dt)
     _say(name, "generating inputs")
     x = W.make_inputs(w)
     if w.packed:
@@ -360,7 +401,7 @@ def test_long_workload_sampled_rows(ra, name):
                          max_ring_passes=w.max_ring_passes, cu_seqlens=cu, scale=w.scale,
                          rows=(np.array([idx[int(h)] for h in heads]), toks))
     got = out.cpu()[toks, heads].double().numpy()
-    _check_bf16(got, ref["out"], name)
+    _check_bf16(got, ref["out"], name, dt)
     assert np.abs(lse.cpu()[heads, toks].double().numpy() - ref["lse"]).max() <= 1e-3
     tal = oracle.tallies(w.T, w.n_blocks, layout=w.layout, mask=w.mask, max_ring_passes=w.max_ring_passes,
                          cu_seqlens=cu, tile_q=st["tile_q"], tile_k=st["tile_k"])

@@ -4,13 +4,17 @@ against the fp64 oracle's gradients on the same seeded inputs.
 The GPU path takes the forward's own out and lse (bf16 inputs, fp32
 accumulation, P and dS rounded to bf16 as matrix-core operands); the oracle
 recomputes everything in fp64.  Tolerance (fp32 gradients compared with the
-oracle): max |diff| <= 2e-2 and mean |diff| <= 1e-2, the forward's bf16 bar.
-bf16 gradients are the round-to-nearest-even of the fp32 ones, bit for bit.
+oracle): max |diff| <= 2e-2 and mean |diff| <= 1e-2, the forward's bf16 bar;
+for fp16 inputs those bounds times 2^-11 / 2^-8 = 1/8 (the ratio of the unit
+roundoffs).  16-bit gradients are the round-to-nearest-even of the fp32
+ones, bit for bit.
 
 Full sizes: dout is zero outside a seeded sample of (head, token) rows, so
 every gradient is exactly those rows' terms, which the oracle computes at
 any length; dq must vanish exactly on every other row.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -21,6 +25,8 @@ import workloads as W
 pytestmark = pytest.mark.gpu
 
 BF16_MAX, BF16_MEAN = 2e-2, 1e-2
+TOL16 = {"bf16": (BF16_MAX, BF16_MEAN), "f16": (BF16_MAX / 8, BF16_MEAN / 8)}
+TORCH16 = {"bf16": torch.bfloat16, "f16": torch.float16}
 
 
 @pytest.fixture(scope="module")
@@ -36,10 +42,11 @@ def _say(*a):
     print("[case]", *a, flush=True)
 
 
-def _check(got, ref, what):
+def _check(got, ref, what, dt="bf16"):
     diff = np.abs(got - ref)
-    _say(what, "max", float(diff.max()), "mean", float(diff.mean()), "max|ref|", float(np.abs(ref).max()))
-    assert diff.max() <= BF16_MAX and diff.mean() <= BF16_MEAN, (what, diff.max(), diff.mean())
+    _say(what, dt, "max", float(diff.max()), "mean", float(diff.mean()), "max|ref|", float(np.abs(ref).max()))
+    tmax, tmean = TOL16[dt]
+    assert diff.max() <= tmax and diff.mean() <= tmean, (what, dt, diff.max(), diff.mean())
 
 
 BWD_SMALL = [
@@ -64,25 +71,27 @@ def _fwd_bwd(ra, q, k, v, dout, *, N, lay, mask, P, docs, out_dtype, grad_dtype=
                        max_ring_passes=P, grad_dtype=grad_dtype)
 
 
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
 @pytest.mark.parametrize("case", range(len(BWD_SMALL)))
-def test_bf16_backward_small(ra, case):
+def test_16bit_backward_small(ra, case, dt):
     T, N, Hq, Hkv, d, layout, mask, P, docs, odt = BWD_SMALL[case]
     if docs == "random":
         docs = W.random_doc_cu_seqlens(T, 16, 900, seed=case).tolist()
-    _say("bf16 backward small", BWD_SMALL[case])
-    qh, kh, vh = W.random_qkv(T, Hq, Hkv, d, "bf16", 2000 + case)
-    gh = W.random_dout(T, Hq, d, "bf16", 2000 + case)
+    _say(dt, "backward small", BWD_SMALL[case])
+    t16 = TORCH16[dt]
+    qh, kh, vh = W.random_qkv(T, Hq, Hkv, d, dt, 2000 + case)
+    gh = W.random_dout(T, Hq, d, dt, 2000 + case)
     q, k, v, g = (x.cuda() for x in (qh, kh, vh, gh))
     lay = "striped" if layout == 1 else "contiguous"
-    kw = dict(N=N, lay=lay, mask=mask, P=P, docs=docs, out_dtype=torch.bfloat16 if odt == "bf16" else torch.float32)
+    kw = dict(N=N, lay=lay, mask=mask, P=P, docs=docs, out_dtype=t16 if odt == "bf16" else torch.float32)
     dq, dk, dv = _fwd_bwd(ra, q, k, v, g, **kw)
     ref = oracle.backward(qh, kh, vh, gh, n_blocks=N, layout=layout, mask=mask, max_ring_passes=P, cu_seqlens=docs)
     for name, got, r in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
-        _check(got.cpu().double().numpy(), r, name)
-    # bf16 gradients: the same values rounded to nearest even
-    bq, bk, bv = _fwd_bwd(ra, q, k, v, g, grad_dtype=torch.bfloat16, **kw)
+        _check(got.cpu().double().numpy(), r, name, dt)
+    # 16-bit gradients: the same values rounded to nearest even
+    bq, bk, bv = _fwd_bwd(ra, q, k, v, g, grad_dtype=t16, **kw)
     for got, f in zip((bq, bk, bv), (dq, dk, dv)):
-        assert got.dtype == torch.bfloat16 and torch.equal(got, f.to(torch.bfloat16))
+        assert got.dtype == t16 and torch.equal(got, f.to(t16))
 
 
 def test_bf16_backward_packed_qkv_views(ra):
@@ -124,10 +133,12 @@ def _sample_pairs(w, rng, heads, n_per_head):
     return np.array([p[0] for p in pairs]), np.array([p[1] for p in pairs])
 
 
-@pytest.mark.parametrize("name", ["causal32k_h32_d128_8blk", "gqa_striped64k_h32kv8_d128_16blk",
-                                  "varlen_packed128k_h32_d128_8blk_p4"])
-def test_long_workload_sparse_dout(ra, name):
-    w = W.WORKLOADS[name]
+@pytest.mark.parametrize("name,dt", [("causal32k_h32_d128_8blk", "bf16"),
+                                     ("gqa_striped64k_h32kv8_d128_16blk", "bf16"),
+                                     ("varlen_packed128k_h32_d128_8blk_p4", "bf16"),
+                                     ("causal32k_h32_d128_8blk", "f16")])
+def test_long_workload_sparse_dout(ra, name, dt):
+    w = dataclasses.replace(W.WORKLOADS[name], dtype=dt)
     _say(name, "generating inputs")
     x = W.make_inputs(w)
     if w.packed:
@@ -142,13 +153,13 @@ def test_long_workload_sparse_dout(ra, name):
     kv_sel = sorted(rng.choice(w.Hkv, size=2, replace=False).tolist())
     q_sel = [g * group + int(rng.integers(0, group)) for g in kv_sel]
     heads, toks = _sample_pairs(w, rng, q_sel, 26)
-    full = W.random_dout(w.T, w.Hq, w.d, "bf16", w.seed)
+    full = W.random_dout(w.T, w.Hq, w.d, dt, w.seed)
     dout = torch.zeros_like(full)
     dout[toks, heads] = full[toks, heads]
     lay = "striped" if w.layout else "contiguous"
     _say(name, "forward + backward on", len(toks), "rows of heads", q_sel)
     dq, dk, dv = _fwd_bwd(ra, q, k, v, dout.cuda(), N=w.n_blocks, lay=lay, mask=w.mask, P=w.max_ring_passes,
-                          docs=cu, out_dtype=torch.bfloat16)
+                          docs=cu, out_dtype=TORCH16[dt])
     torch.cuda.synchronize()
     # oracle on the selected heads only, each query head with its own kv head
     sub_q = x["q"][:, q_sel]
@@ -161,9 +172,9 @@ def test_long_workload_sparse_dout(ra, name):
                                              mask=w.mask, max_ring_passes=w.max_ring_passes, cu_seqlens=cu,
                                              scale=w.scale, rows=(np.array([idx[int(h)] for h in heads]), toks),
                                              rows_dkdv=True)
-    _check(dq.cpu()[toks, heads].double().numpy(), ref_dq, name + " dq rows")
-    _check(dk.cpu()[:, kv_sel].double().numpy(), ref_dk, name + " dk")
-    _check(dv.cpu()[:, kv_sel].double().numpy(), ref_dv, name + " dv")
+    _check(dq.cpu()[toks, heads].double().numpy(), ref_dq, name + " dq rows", dt)
+    _check(dk.cpu()[:, kv_sel].double().numpy(), ref_dk, name + " dk", dt)
+    _check(dv.cpu()[:, kv_sel].double().numpy(), ref_dv, name + " dv", dt)
     # every other row and kv head: exactly zero
     dq_rest = dq.clone()
     dq_rest[toks, heads] = 0

@@ -164,6 +164,11 @@ def test_forward_and_step_refuse_bad_arguments_before_any_gpu_work(lib):
     assert fwd(qq=_fake(64, 4, 128, ptr=(1 << 20) + 2)) == ra.RA_E_UNSUPPORTED  # misaligned bf16
     f32 = [_fake(64, 4, 16, ra.RA_F32), _fake(64, 2, 16, ra.RA_F32), _fake(64, 2, 16, ra.RA_F32)]
     assert fwd(*f32, out_dtype=ra.RA_BF16) == ra.RA_E_UNSUPPORTED
+    h16 = [_fake(64, 4, 128, ra.RA_F16), _fake(64, 2, 128, ra.RA_F16), _fake(64, 2, 128, ra.RA_F16)]
+    assert fwd(*h16, out_dtype=ra.RA_BF16) == ra.RA_E_UNSUPPORTED  # 16-bit out must be the inputs' type
+    assert fwd(*h16, out_dtype=ra.RA_F16, ws_bytes=16) == ra.RA_E_WORKSPACE  # fp16 passes the checks
+    assert fwd(h16[0], k, v) == ra.RA_E_ARG           # mixed input types
+    assert fwd(out_dtype=3) == ra.RA_E_ARG
     assert fwd(ws_bytes=16) == ra.RA_E_WORKSPACE
     cu = (ctypes.c_int32 * 3)(0, 10, 64)
     assert fwd(mask=2, cu=cu, n_docs=2, layout=1) == ra.RA_E_UNSUPPORTED
@@ -212,6 +217,12 @@ def test_backward_refuses_bad_arguments_before_any_gpu_work(lib):
     f32 = dict(qq=_fake(64, 4, 16, ra.RA_F32), kk=_fake(64, 2, 16, ra.RA_F32), vv=_fake(64, 2, 16, ra.RA_F32),
                oo=_fake(64, 4, 16, ra.RA_F32), gg=_fake(64, 4, 16, ra.RA_F32))
     assert bwd(**f32) == ra.RA_E_UNSUPPORTED          # fp32 inputs: no backward kernel
+    h16 = dict(qq=_fake(64, 4, 128, ra.RA_F16), kk=_fake(64, 2, 128, ra.RA_F16), vv=_fake(64, 2, 128, ra.RA_F16),
+               gg=_fake(64, 4, 128, ra.RA_F16))
+    assert bwd(grad=ra.RA_BF16, **h16) == ra.RA_E_UNSUPPORTED  # 16-bit gradients take the inputs' type
+    assert bwd(oo=_fake(64, 4, 128, ra.RA_BF16), **h16) == ra.RA_E_UNSUPPORTED  # so does a 16-bit out
+    assert bwd(oo=_fake(64, 4, 128, ra.RA_F16), grad=ra.RA_F16, ws_bytes=16, **h16) == ra.RA_E_WORKSPACE
+    assert bwd(gg=_fake(64, 4, 128, ra.RA_F16)) == ra.RA_E_ARG  # dout type differs from q's
     assert bwd(qq=_fake(64, 4, 96), kk=_fake(64, 2, 96), vv=_fake(64, 2, 96), oo=_fake(64, 4, 96),
                gg=_fake(64, 4, 96)) == ra.RA_E_UNSUPPORTED
     assert bwd(qq=_fake(64, 4, 128, ptr=(1 << 20) + 2)) == ra.RA_E_UNSUPPORTED

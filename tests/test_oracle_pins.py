@@ -160,6 +160,24 @@ def test_bf16_inputs_decode_exactly():
     assert np.abs(r["out"] - ref).max() < 1e-12
 
 
+def test_f16_inputs_decode_exactly():
+    """fp16 values off the bf16 grid (10-bit fractions), subnormal and near
+    the top of the binary16 range reach the oracle unchanged: its result
+    equals fp64 attention on torch's own fp16 -> fp64 conversion."""
+    q, k, v = (x * 0.37 for x in W.random_qkv(32, 2, 2, 8, "f32", 8))
+    q, k, v = q.half(), k.half(), v.half()
+    v[3, 0, 0], v[5, 1, 2], v[9, 0, 7] = 6.0e-8, -3.1e-5, 6.0e4   # subnormal, subnormal, large
+    assert (q.float() != q.float().to(torch.bfloat16).float()).any()
+    r = oracle.forward(q, k, v, n_blocks=4, mask=oracle.MASK_CAUSAL)
+    ref = _sdpa64(q.double(), k.double(), v.double(), is_causal=True)
+    assert np.abs(r["out"] - ref).max() <= 1e-12 * max(1.0, float(np.abs(ref).max()))
+    g = W.random_dout(32, 2, 8, "f16", 8)
+    dq, dk, dv = oracle.backward(q, k, v, g, n_blocks=4, mask=oracle.MASK_CAUSAL)
+    dq32, dk32, dv32 = oracle.backward(q.float(), k.float(), v.float(), g.float(), n_blocks=4,
+                                       mask=oracle.MASK_CAUSAL)
+    assert np.array_equal(dq, dq32) and np.array_equal(dk, dk32) and np.array_equal(dv, dv32)
+
+
 @pytest.mark.parametrize("N", [2, 4, 8])
 def test_striped_causal_full_ring_is_plain_causal(N):
     # The mask is defined on original token order; the striped assignment only

@@ -49,7 +49,7 @@ class Workload:
     mask: int
     layout: int
     max_ring_passes: int
-    dtype: str            # "f32" or "bf16"
+    dtype: str            # "f32", "bf16" or "f16"
     scale: float
     seed: int
     packed: bool = False  # q, k, v are views into one [T, 3, H, d] tensor
@@ -98,6 +98,8 @@ def _to_dtype(x: torch.Tensor, dtype: str) -> torch.Tensor:
         return x.float()
     if dtype == "bf16":
         return x.to(torch.bfloat16)  # round to nearest even
+    if dtype == "f16":
+        return x.to(torch.float16)  # round to nearest even
     raise ValueError(dtype)
 
 
