@@ -69,11 +69,11 @@ def _load():
         i64, vp, dbl, ci = ctypes.c_int64, ctypes.c_void_p, ctypes.c_double, ctypes.c_int
         lib.ro_forward_rows.argtypes = [vp, vp, vp, ci, i64, i64, i64, i64,
                                         i64, i64, i64, i64, i64, i64, dbl, ci, ci, i64, i64,
-                                        vp, i64, i64, vp, vp, vp, vp, vp, vp, vp]
+                                        vp, i64, vp, i64, vp, vp, vp, vp, vp, vp, vp]
         lib.ro_forward_rows.restype = ci
         lib.ro_block_rows.argtypes = [vp, vp, vp, ci, i64, i64, i64, i64, i64,
                                       i64, i64, i64, i64, i64, i64, vp, vp, dbl, ci, vp, i64, i64,
-                                      vp, vp, vp, vp, vp]
+                                      vp, vp, vp, vp, vp, vp]
         lib.ro_block_rows.restype = ci
         lib.ro_tile_tallies.argtypes = [i64, i64, ci, ci, i64, vp, i64, i64, i64, vp]
         lib.ro_tile_tallies.restype = ci
@@ -81,11 +81,11 @@ def _load():
         lib.ro_allowed_pairs.restype = ci
         lib.ro_backward.argtypes = [vp, vp, vp, vp, ci, ci, i64, i64, i64, i64,
                                     i64, i64, i64, i64, i64, i64, i64, i64, dbl, ci, ci, i64, i64,
-                                    vp, i64, vp, vp, vp]
+                                    vp, i64, vp, vp, vp, vp]
         lib.ro_backward.restype = ci
         lib.ro_backward_rows.argtypes = [vp, vp, vp, vp, ci, ci, i64, i64, i64, i64,
                                          i64, i64, i64, i64, i64, i64, i64, i64, dbl, ci, ci, i64, i64,
-                                         vp, i64, vp, vp, i64, vp, vp, vp]
+                                         vp, i64, vp, vp, vp, i64, vp, vp, vp]
         lib.ro_backward_rows.restype = ci
         _lib = lib
     return _lib
@@ -103,6 +103,17 @@ def _widen(x: torch.Tensor) -> torch.Tensor:
     """fp16 inputs as fp32 tensors: every binary16 value is exactly a binary32
     value, so the fp64 decode downstream sees the same numbers."""
     return x.float() if isinstance(x, torch.Tensor) and x.dtype == torch.float16 else x
+
+
+def _key_valid(key_valid, n: int):
+    """A key-padding mask as a contiguous uint8 array of n entries (1 = key
+    takes part), or None."""
+    if key_valid is None:
+        return None
+    kv = np.ascontiguousarray(np.asarray(key_valid).reshape(-1) != 0, dtype=np.uint8)
+    if kv.size != n:
+        raise ValueError("key_valid must have %d entries" % n)
+    return kv
 
 
 def _check_view(x: torch.Tensor, name: str):
@@ -129,9 +140,11 @@ def _cu(cu_seqlens):
 
 def forward(q, k, v, *, n_blocks: int, layout: int = LAYOUT_CONTIGUOUS, mask: int = MASK_NONE,
             max_ring_passes: Optional[int] = None, cu_seqlens=None, scale: Optional[float] = None,
-            rows: Optional[Sequence] = None):
+            rows: Optional[Sequence] = None, key_valid=None):
     """Attention of every (or each listed) query row over the keys the ring lets
     it see.  Returns dict(out, lse, m, l, O) of float64 arrays.
+
+    key_valid: optional [T] key-padding mask (nonzero = the key takes part).
 
     Without ``rows``: out/O are [T, Hq, d] and lse/m/l are [Hq, T].
     With ``rows`` = (heads, tokens) index arrays of equal length n: out/O are
@@ -152,6 +165,7 @@ def forward(q, k, v, *, n_blocks: int, layout: int = LAYOUT_CONTIGUOUS, mask: in
         scale = 1.0 / math.sqrt(d)
     P = n_blocks if max_ring_passes is None else int(max_ring_passes)
     cu, n_docs = _cu(cu_seqlens)
+    kv = _key_valid(key_valid, T)
     full = rows is None
     if full:
         hh, tt = np.meshgrid(np.arange(Hq), np.arange(T), indexing="ij")
@@ -167,7 +181,7 @@ def forward(q, k, v, *, n_blocks: int, layout: int = LAYOUT_CONTIGUOUS, mask: in
     rc = _load().ro_forward_rows(
         _ptr(q), _ptr(k), _ptr(v), _dtype_code(q), T, Hq, Hkv, d,
         q.stride(0), q.stride(1), k.stride(0), k.stride(1), v.stride(0), v.stride(1),
-        float(scale), int(mask), int(layout), int(n_blocks), P, _ptr(cu), n_docs,
+        float(scale), int(mask), int(layout), int(n_blocks), P, _ptr(cu), n_docs, _ptr(kv),
         n, _ptr(row_head), _ptr(row_tok), _ptr(out), _ptr(lse), _ptr(m), _ptr(l), _ptr(O))
     if rc != 0:
         raise ValueError("oracle rejected the arguments (code %d)" % rc)
@@ -178,9 +192,10 @@ def forward(q, k, v, *, n_blocks: int, layout: int = LAYOUT_CONTIGUOUS, mask: in
 
 
 def block(q_blk, k_blk, v_blk, q_pos, k_pos, *, mask: int = MASK_NONE, cu_seqlens=None,
-          doc_T: Optional[int] = None, scale: Optional[float] = None):
+          doc_T: Optional[int] = None, scale: Optional[float] = None, key_valid=None):
     """One query block against one key/value block at explicit global positions.
-    Returns dict(out, O: [Hq, nq, d]; lse, m, l: [Hq, nq])."""
+    Returns dict(out, O: [Hq, nq, d]; lse, m, l: [Hq, nq]).  key_valid:
+    optional key-padding mask of the block's own key rows ([nk])."""
     q_blk, k_blk, v_blk = _widen(q_blk), _widen(k_blk), _widen(v_blk)
     for name, x in (("q_blk", q_blk), ("k_blk", k_blk), ("v_blk", v_blk)):
         _check_view(x, name)
@@ -195,6 +210,7 @@ def block(q_blk, k_blk, v_blk, q_pos, k_pos, *, mask: int = MASK_NONE, cu_seqlen
     cu, n_docs = _cu(cu_seqlens)
     if doc_T is None:
         doc_T = int(cu[-1]) if cu is not None else 0
+    kv = _key_valid(key_valid, nk)  # kept alive across the call
     out = np.zeros((Hq, nq, d))
     O = np.zeros((Hq, nq, d))
     lse, m, l = np.zeros((Hq, nq)), np.zeros((Hq, nq)), np.zeros((Hq, nq))
@@ -202,7 +218,7 @@ def block(q_blk, k_blk, v_blk, q_pos, k_pos, *, mask: int = MASK_NONE, cu_seqlen
         _ptr(q_blk), _ptr(k_blk), _ptr(v_blk), _dtype_code(q_blk), nq, nk, Hq, Hkv, d,
         q_blk.stride(0), q_blk.stride(1), k_blk.stride(0), k_blk.stride(1),
         v_blk.stride(0), v_blk.stride(1), _ptr(qp), _ptr(kp), float(scale), int(mask),
-        _ptr(cu), n_docs, int(doc_T), _ptr(out), _ptr(lse), _ptr(m), _ptr(l), _ptr(O))
+        _ptr(cu), n_docs, int(doc_T), _ptr(kv), _ptr(out), _ptr(lse), _ptr(m), _ptr(l), _ptr(O))
     if rc != 0:
         raise ValueError("oracle rejected the arguments (code %d)" % rc)
     return {"out": out, "O": O, "lse": lse, "m": m, "l": l}
@@ -277,7 +293,7 @@ def allowed_pairs(T: int, n_blocks: int, *, layout: int = LAYOUT_CONTIGUOUS, mas
 
 def backward(q, k, v, dout, *, n_blocks: int, layout: int = LAYOUT_CONTIGUOUS, mask: int = MASK_NONE,
              max_ring_passes: Optional[int] = None, cu_seqlens=None, scale: Optional[float] = None,
-             rows: Optional[Sequence] = None, rows_dkdv: bool = False):
+             rows: Optional[Sequence] = None, rows_dkdv: bool = False, key_valid=None):
     """Gradients (dq, dk, dv) of ``forward``'s output with respect to q, k, v
     for the output gradient ``dout`` ([T, Hq, d], float32, bfloat16 or float16), as
     float64 arrays [T, Hq, d], [T, Hkv, d], [T, Hkv, d].  The arithmetic is in
@@ -288,7 +304,7 @@ def backward(q, k, v, dout, *, n_blocks: int, layout: int = LAYOUT_CONTIGUOUS, m
     their dq as an [n, d] array (each equal to the matching row of the full
     dq), and with ``rows_dkdv`` also (dq_rows, dk, dv) where dk / dv sum those
     rows' terms only -- the full dk / dv whenever dout vanishes on every other
-    row."""
+    row.  key_valid: optional [T] key-padding mask, as for ``forward``."""
     if not (q.dtype == k.dtype == v.dtype):
         raise TypeError("q, k, v must share a dtype")
     q, k, v, dout = _widen(q), _widen(k), _widen(v), _widen(dout)
@@ -304,6 +320,7 @@ def backward(q, k, v, dout, *, n_blocks: int, layout: int = LAYOUT_CONTIGUOUS, m
         scale = 1.0 / math.sqrt(d)
     P = n_blocks if max_ring_passes is None else int(max_ring_passes)
     cu, n_docs = _cu(cu_seqlens)
+    kv = _key_valid(key_valid, T)
     if rows is not None:
         row_head = np.ascontiguousarray(np.asarray(rows[0]), dtype=np.int64)
         row_tok = np.ascontiguousarray(np.asarray(rows[1]), dtype=np.int64)
@@ -318,7 +335,7 @@ def backward(q, k, v, dout, *, n_blocks: int, layout: int = LAYOUT_CONTIGUOUS, m
             _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _dtype_code(q), _dtype_code(dout), T, Hq, Hkv, d,
             q.stride(0), q.stride(1), k.stride(0), k.stride(1), v.stride(0), v.stride(1),
             dout.stride(0), dout.stride(1), float(scale), int(mask), int(layout), int(n_blocks), P,
-            _ptr(cu), n_docs, _ptr(row_head), _ptr(row_tok), row_head.size, _ptr(out), _ptr(dk), _ptr(dv))
+            _ptr(cu), n_docs, _ptr(kv), _ptr(row_head), _ptr(row_tok), row_head.size, _ptr(out), _ptr(dk), _ptr(dv))
         if rc != 0:
             raise ValueError("oracle rejected the arguments (code %d)" % rc)
         return (out, dk, dv) if rows_dkdv else out
@@ -329,7 +346,7 @@ def backward(q, k, v, dout, *, n_blocks: int, layout: int = LAYOUT_CONTIGUOUS, m
         _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _dtype_code(q), _dtype_code(dout), T, Hq, Hkv, d,
         q.stride(0), q.stride(1), k.stride(0), k.stride(1), v.stride(0), v.stride(1),
         dout.stride(0), dout.stride(1), float(scale), int(mask), int(layout), int(n_blocks), P,
-        _ptr(cu), n_docs, _ptr(dq), _ptr(dk), _ptr(dv))
+        _ptr(cu), n_docs, _ptr(kv), _ptr(dq), _ptr(dk), _ptr(dv))
     if rc != 0:
         raise ValueError("oracle rejected the arguments (code %d)" % rc)
     return dq, dk, dv

@@ -37,6 +37,12 @@
  *   doc-causal:  t' <= t and t, t' in the same document, documents given by
  *                cumulative lengths cu_seqlens of shape (n_docs + 1,) (the
  *                flash-attention scrape page's description of cu_seqlens).
+ * and, with a key-padding mask key_valid (one byte per key, nonzero = a real
+ * token), every key with key_valid = 0 is left out as well (GitHub issue "A
+ * ring attention with flash attention kernel implementation": a comment
+ * names the key padding mask beside the causal one).  The whole-sequence
+ * entry points index key_valid by global position t', the block entry point
+ * by the key's row in its block.  The tile tallies below ignore it.
  * Ring visibility with N blocks and P = max ring passes (GitHub issue: the
  * maximum number of ring passes): at step s the device holding query block b
  * holds key block (b - s) mod N (glossary page code), and only steps
@@ -157,7 +163,7 @@ int ro_forward_rows(const void* q, const void* k, const void* v, int dtype,
                     int64_t q_st, int64_t q_sh, int64_t k_st, int64_t k_sh,
                     int64_t v_st, int64_t v_sh, double scale, int mask, int layout,
                     int64_t n_blocks, int64_t max_ring_passes,
-                    const int32_t* cu_seqlens, int64_t n_docs,
+                    const int32_t* cu_seqlens, int64_t n_docs, const uint8_t* key_valid,
                     int64_t n_rows, const int64_t* row_head, const int64_t* row_tok,
                     double* out, double* lse, double* m, double* l, double* O) {
     if (T < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv || d < 1 || n_blocks < 1 || max_ring_passes < 1)
@@ -190,7 +196,9 @@ int ro_forward_rows(const void* q, const void* k, const void* v, int dtype,
                 int64_t h = row_head[r], t = row_tok[r];
                 int64_t n = 0;
                 for (int64_t tk = 0; tk < T; tk++)
-                    if (mask_allows(mask, doc_of, t, tk) && ring_visible(&ring, t, tk)) idx[n++] = tk;
+                    if (mask_allows(mask, doc_of, t, tk) && ring_visible(&ring, t, tk) &&
+                        (!key_valid || key_valid[tk]))
+                        idx[n++] = tk;
                 double lse_r, m_r, l_r;
                 attend_one(&qv, t, h, &kv, &vv, h / group, d, scale, idx, n, sbuf, obuf, &lse_r,
                            &m_r, &l_r, Obuf);
@@ -223,7 +231,7 @@ int ro_block_rows(const void* q, const void* k, const void* v, int dtype,
                   int64_t q_st, int64_t q_sh, int64_t k_st, int64_t k_sh,
                   int64_t v_st, int64_t v_sh, const int64_t* q_pos, const int64_t* k_pos,
                   double scale, int mask, const int32_t* cu_seqlens, int64_t n_docs, int64_t doc_T,
-                  double* out, double* lse, double* m, double* l, double* O) {
+                  const uint8_t* key_valid, double* out, double* lse, double* m, double* l, double* O) {
     if (nq < 0 || nk < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv || d < 1) return RO_BAD_ARG;
     int32_t* doc_of = NULL;
     if (mask == RO_MASK_DOC_CAUSAL) {
@@ -252,7 +260,7 @@ int ro_block_rows(const void* q, const void* k, const void* v, int dtype,
                 int64_t h = r / nq, u = r % nq;
                 int64_t n = 0;
                 for (int64_t w = 0; w < nk; w++)
-                    if (mask_allows(mask, doc_of, q_pos[u], k_pos[w])) idx[n++] = w;
+                    if (mask_allows(mask, doc_of, q_pos[u], k_pos[w]) && (!key_valid || key_valid[w])) idx[n++] = w;
                 double lse_r, m_r, l_r;
                 attend_one(&qv, u, h, &kv, &vv, h / group, d, scale, idx, n, sbuf, obuf, &lse_r, &m_r,
                            &l_r, Obuf);
@@ -381,6 +389,7 @@ typedef struct {
     const ro_view *q, *k, *v, *dout;
     const ro_ring* ring;
     const int32_t* doc_of;
+    const uint8_t* key_valid;  /* nullable, by global position */
     int mask;
     int64_t T, Hkv, d;
     double scale;
@@ -391,7 +400,9 @@ static void backward_row(const ro_bwd_ctx* c, int64_t t, int64_t h, int64_t g, i
     const int64_t T = c->T, d = c->d, Hkv = c->Hkv;
     int64_t n = 0;
     for (int64_t tk = 0; tk < T; tk++)
-        if (mask_allows(c->mask, c->doc_of, t, tk) && ring_visible(c->ring, t, tk)) idx[n++] = tk;
+        if (mask_allows(c->mask, c->doc_of, t, tk) && ring_visible(c->ring, t, tk) &&
+            (!c->key_valid || c->key_valid[tk]))
+            idx[n++] = tk;
     if (n == 0) return;
     double lse_r, m_r, l_r;
     attend_one(c->q, t, h, c->k, c->v, g, d, c->scale, idx, n, sbuf, obuf, &lse_r, &m_r, &l_r, Obuf);
@@ -434,7 +445,7 @@ int ro_backward(const void* q, const void* k, const void* v, const void* dout, i
                 int64_t q_st, int64_t q_sh, int64_t k_st, int64_t k_sh,
                 int64_t v_st, int64_t v_sh, int64_t o_st, int64_t o_sh,
                 double scale, int mask, int layout, int64_t n_blocks, int64_t max_ring_passes,
-                const int32_t* cu_seqlens, int64_t n_docs,
+                const int32_t* cu_seqlens, int64_t n_docs, const uint8_t* key_valid,
                 double* dq, double* dk, double* dv) {
     int rc = bwd_check(T, Hq, Hkv, d, mask, n_blocks, max_ring_passes, cu_seqlens, n_docs);
     if (rc != RO_OK) return rc;
@@ -446,7 +457,7 @@ int ro_backward(const void* q, const void* k, const void* v, const void* dout, i
         doc_of = make_doc_of(cu_seqlens, n_docs, T);
         if (!doc_of) return RO_NO_MEM;
     }
-    ro_bwd_ctx c = {&qv, &kv, &vv, &ov, &ring, doc_of, mask, T, Hkv, d, scale};
+    ro_bwd_ctx c = {&qv, &kv, &vv, &ov, &ring, doc_of, key_valid, mask, T, Hkv, d, scale};
     memset(dq, 0, sizeof(double) * (size_t)(T * Hq * d));
     memset(dk, 0, sizeof(double) * (size_t)(T * Hkv * d));
     memset(dv, 0, sizeof(double) * (size_t)(T * Hkv * d));
@@ -488,7 +499,7 @@ int ro_backward_rows(const void* q, const void* k, const void* v, const void* do
                         int64_t q_st, int64_t q_sh, int64_t k_st, int64_t k_sh,
                         int64_t v_st, int64_t v_sh, int64_t o_st, int64_t o_sh,
                         double scale, int mask, int layout, int64_t n_blocks, int64_t max_ring_passes,
-                        const int32_t* cu_seqlens, int64_t n_docs,
+                        const int32_t* cu_seqlens, int64_t n_docs, const uint8_t* key_valid,
                         const int64_t* row_head, const int64_t* row_tok, int64_t n_rows, double* dq_rows,
                         double* dk, double* dv) {
     int rc = bwd_check(T, Hq, Hkv, d, mask, n_blocks, max_ring_passes, cu_seqlens, n_docs);
@@ -503,7 +514,7 @@ int ro_backward_rows(const void* q, const void* k, const void* v, const void* do
         doc_of = make_doc_of(cu_seqlens, n_docs, T);
         if (!doc_of) return RO_NO_MEM;
     }
-    ro_bwd_ctx c = {&qv, &kv, &vv, &ov, &ring, doc_of, mask, T, Hkv, d, scale};
+    ro_bwd_ctx c = {&qv, &kv, &vv, &ov, &ring, doc_of, key_valid, mask, T, Hkv, d, scale};
     memset(dq_rows, 0, sizeof(double) * (size_t)(n_rows * d));
     if (dk) memset(dk, 0, sizeof(double) * (size_t)(T * Hkv * d));
     if (dv) memset(dv, 0, sizeof(double) * (size_t)(T * Hkv * d));

@@ -88,13 +88,25 @@ AUTOGRAD_CASES = [
 ]
 
 
+def _key_valid(T, seed):
+    """About a third of the keys padded, key 0 among them (so under a causal
+    mask row 0 has no key left)."""
+    kv = torch.rand(T, generator=torch.Generator().manual_seed(seed)) > 0.35
+    kv[0] = False
+    return kv
+
+
+@pytest.mark.parametrize("padded", [False, True])
 @pytest.mark.parametrize("case", range(len(AUTOGRAD_CASES)))
-def test_backward_matches_fp64_autograd(case):
+def test_backward_matches_fp64_autograd(case, padded):
     T, N, Hq, Hkv, d, layout, mask, P, docs = AUTOGRAD_CASES[case]
     q, k, v, do = _inputs(T, Hq, Hkv, d, 50 + case)
+    kv = _key_valid(T, 90 + case) if padded else None
     dq, dk, dv = oracle.backward(q, k, v, do, n_blocks=N, layout=layout, mask=mask, max_ring_passes=P,
-                                 cu_seqlens=docs)
+                                 cu_seqlens=docs, key_valid=kv)
     ok = _allowed(T, N, layout, mask, P, docs)
+    if padded:
+        ok &= kv[None, :]
     qd, kd, vd = (x.double().requires_grad_(True) for x in (q, k, v))
     grp = Hq // Hkv
     outs = []
@@ -111,6 +123,22 @@ def test_backward_matches_fp64_autograd(case):
     for got, want in ((dq, qd.grad), (dk, kd.grad), (dv, vd.grad)):
         want = want.numpy()
         assert np.abs(got - want).max() <= 1e-10 * (1.0 + np.abs(want).max())
+
+
+def test_padded_keys_get_no_gradient_and_no_weight():
+    """A padded key changes nothing: its dk and dv are exactly zero, and dq of
+    every row equals the gradients of the same ring without that key's
+    influence (its k and v replaced by garbage change no other gradient)."""
+    T, N, Hq, Hkv, d = 32, 4, 2, 1, 6
+    q, k, v, do = _inputs(T, Hq, Hkv, d, 77)
+    kv = _key_valid(T, 78)
+    dq, dk, dv = oracle.backward(q, k, v, do, n_blocks=N, mask=1, key_valid=kv)
+    assert not dk[~kv.numpy()].any() and not dv[~kv.numpy()].any()
+    k2, v2 = k.clone(), v.clone()
+    k2[~kv] = 1e3
+    v2[~kv] = -7.0
+    dq2, dk2, dv2 = oracle.backward(q, k2, v2, do, n_blocks=N, mask=1, key_valid=kv)
+    assert np.array_equal(dq, dq2) and np.array_equal(dk, dk2) and np.array_equal(dv, dv2)
 
 
 def test_zero_output_gradient_gives_zero_gradients():

@@ -23,6 +23,9 @@ MUTANTS = {
     "empty_row_lse_zero": ("*lse = -INFINITY;\n        *m_out", "*lse = 0;\n        *m_out"),
     "value_index_transposed": ("w * view_at(v, idx[a], g, c)", "w * view_at(v, idx[a], g, d - 1 - c)"),
     "denominator_missing_term": ("L += w;", "if (a > 0) L += w;"),
+    "key_padding_ignored": ("(!key_valid || key_valid[tk]))\n                        idx[n++] = tk;",
+                            "1)\n                        idx[n++] = tk;"),
+    "block_key_padding_inverted": ("(!key_valid || key_valid[w])", "(!key_valid || !key_valid[w])"),
 }
 
 
@@ -35,6 +38,7 @@ MUTANTS_BWD = {
     "bwd_dq_uses_value": ("dq_row[x] += c->scale * ds * view_at(c->k, j, g, x);",
                           "dq_row[x] += c->scale * ds * view_at(c->v, j, g, x);"),
     "bwd_D_from_state": ("D += view_at(c->dout, t, h, x) * obuf[x];", "D += view_at(c->dout, t, h, x) * Obuf[x];"),
+    "bwd_key_padding_ignored": ("(!c->key_valid || c->key_valid[tk]))", "1)"),
 }
 
 

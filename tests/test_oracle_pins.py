@@ -160,6 +160,39 @@ def test_bf16_inputs_decode_exactly():
     assert np.abs(r["out"] - ref).max() < 1e-12
 
 
+@pytest.mark.parametrize("mask", [0, 1])
+def test_key_padding_equals_sdpa_with_boolean_mask(mask):
+    """Key-padding mask: torch's fp64 attention with the boolean mask
+    (causal and key_valid); rows left with no key give out 0, lse -inf."""
+    T, N, H, d = 48, 4, 2, 8
+    q, k, v = W.random_qkv(T, H, H, d, "f32", 31 + mask)
+    kv = torch.rand(T, generator=torch.Generator().manual_seed(5)) > 0.4
+    kv[0] = False  # under the causal mask, row 0 keeps no key
+    r = oracle.forward(q, k, v, n_blocks=N, mask=mask, key_valid=kv)
+    allowed = kv[None, :].expand(T, T).clone()
+    if mask:
+        allowed &= torch.ones(T, T, dtype=torch.bool).tril()
+    has = allowed.any(dim=1)
+    ref = _sdpa64(q, k, v, mask=allowed)
+    assert np.abs(r["out"][has.numpy()] - ref[has.numpy()]).max() < 1e-12
+    assert not r["out"][~has.numpy()].any() and np.isneginf(r["lse"][:, ~has.numpy()]).all()
+    assert bool((~has).any()) == bool(mask)
+
+
+def test_key_padding_all_valid_is_no_mask_and_drops_keys_exactly():
+    T, N, H, d = 40, 4, 2, 8
+    q, k, v = W.random_qkv(T, H, H, d, "f32", 33)
+    a = oracle.forward(q, k, v, n_blocks=N, mask=1)
+    b = oracle.forward(q, k, v, n_blocks=N, mask=1, key_valid=torch.ones(T, dtype=torch.bool))
+    assert all(np.array_equal(a[x], b[x]) for x in ("out", "lse", "m", "l", "O"))
+    # one block against one block: padding equals removing the padded rows
+    kv = torch.tensor([i % 3 != 1 for i in range(T)])
+    pos = np.arange(T)
+    c = oracle.block(q, k, v, pos, pos, key_valid=kv)
+    e = oracle.block(q, k[kv], v[kv], pos, pos[kv.numpy()])
+    assert np.abs(c["out"] - e["out"]).max() < 1e-13 and np.abs(c["lse"] - e["lse"]).max() < 1e-13
+
+
 def test_f16_inputs_decode_exactly():
     """fp16 values off the bf16 grid (10-bit fractions), subnormal and near
     the top of the binary16 range reach the oracle unchanged: its result
