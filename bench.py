@@ -36,8 +36,8 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak (AMD published figure)
 DEFAULT_WORKLOAD = "causal32k_h32_d128_8blk"
-KERNEL = "step_bf16_kernel<128, true, true>"
-BWD_KERNEL = "bwd_dkdv_kernel<128>"
+KERNEL = "step_bf16_kernel<__bf16, 128, true, true, false>"
+BWD_KERNEL = "bwd_dkdv_kernel<__bf16, 128>"
 KERNEL_SOURCES = ["ring_attention_step_amd/csrc/step_bf16.hip", "ring_attention_step_amd/csrc/plan.h",
                   "ring_attention_step_amd/csrc/kernels.h"]
 BWD_KERNEL_SOURCES = ["ring_attention_step_amd/csrc/backward.hip", "ring_attention_step_amd/csrc/bwd_kernels.h",
@@ -273,7 +273,7 @@ def bench_backward(args, ra, W, w, x, q, k, v, cu, out, lse, plan, stream):
         # the three backward kernels together, event-timed on the launch stream;
         # traffic: HBM bytes per launch of the dominant one (dk/dv) from the
         # committed counter record
-        "roofline": {"bound": "mfma", "kernel": "bwd_prep + bwd_dq_kernel<128> + " + BWD_KERNEL,
+        "roofline": {"bound": "mfma", "kernel": "bwd_prep_kernel<__bf16> + bwd_dq_kernel<__bf16, 128, false> + " + BWD_KERNEL,
                      "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic_from_profile(w.name, False, backward=True),

@@ -100,13 +100,31 @@ typedef struct {
  *     row w at kv_offset + w * pos_stride (pos_stride = 1 for contiguous
  *     blocks, N for striped ones).  DOC_CAUSAL needs pos_stride = 1 and
  *     cu_seqlens (device, n_docs + 1 entries) covering every position used.
+ *   key_bits: nullable device pointer, 8-byte aligned: the key block's
+ *     key-padding mask as ring_attn_pack_key_mask writes it (bit w % 32 of
+ *     word w / 32 set when key row w takes part).  It belongs to the key
+ *     block and travels with it around the ring.  Padded keys leave the
+ *     tile tallies unchanged (they are masked inside the computed tiles).
  *   stats_dev: nullable device int64[3]; the step ADDS its tile counts
  *     {skipped, full, partial} (tile shape as ring_attn_tile_shape reports).
  */
 ra_status ring_attn_step(const ra_tensor* q_blk, const ra_tensor* k_blk, const ra_tensor* v_blk,
                          float* O, float* m, float* l, int first_step, float scale,
                          ra_mask mask_mode, int64_t q_offset, int64_t kv_offset, int64_t pos_stride,
-                         const int32_t* cu_seqlens, int32_t n_docs, int64_t* stats_dev, void* stream);
+                         const int32_t* cu_seqlens, int32_t n_docs, const uint32_t* key_bits,
+                         int64_t* stats_dev, void* stream);
+
+/*
+ * Key-padding mask of one key block as bits: key_bits[w / 32] bit w % 32 =
+ * (key_valid[w * stride] != 0) for w < n_keys; 2 * ceil(n_keys / 64) words
+ * are written (whole 64-key tiles, zero past n_keys).  Both pointers are
+ * device pointers; key_bits 8-byte aligned.  A key-padding mask leaves out
+ * the keys of padding tokens (GitHub issue "A ring attention with flash
+ * attention kernel implementation": a comment names the key padding mask
+ * beside the causal one); it combines with every ra_mask.
+ */
+ra_status ring_attn_pack_key_mask(const uint8_t* key_valid, int64_t n_keys, int64_t stride, uint32_t* key_bits,
+                                  void* stream);
 
 /*
  * Normalise a running state: out[u, h, :] = O[h, u, :] / l[h, u] and
@@ -155,6 +173,10 @@ size_t ring_attn_forward_workspace_size(const ra_tensor* q, const ra_tensor* k, 
  *     inputs also their own type).  lse: nullable, [Hq, T] fp32 (natural log).
  *   cu_seqlens_host: HOST pointer, n_docs + 1 entries, needed for DOC_CAUSAL
  *     (contiguous layout only); copied into the workspace.
+ *   key_valid: nullable device pointer, T bytes: key token t takes part only
+ *     if key_valid[t] != 0 (a key-padding mask, on top of mask_mode; rows
+ *     left with no key get out 0, lse -inf).  Packed into the workspace as
+ *     bits; the tallies in stats ignore it.
  *   prefetch != 0: one launch per step; every step's key/value blocks are
  *     first copied, on a side stream, into a double buffer in the workspace
  *     while the previous step computes (the ring's transfer of the next
@@ -167,7 +189,7 @@ size_t ring_attn_forward_workspace_size(const ra_tensor* q, const ra_tensor* k, 
 ra_status ring_attn_forward(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v, void* out,
                             ra_dtype out_dtype, float* lse, int32_t n_blocks, ra_layout layout,
                             ra_mask mask_mode, int32_t max_ring_passes, const int32_t* cu_seqlens_host,
-                            int32_t n_docs, float scale, int prefetch, void* workspace,
+                            int32_t n_docs, const uint8_t* key_valid, float scale, int prefetch, void* workspace,
                             size_t workspace_bytes, ra_stats* stats, void* stream);
 
 /* Bytes of device workspace ring_attn_backward needs for these shapes. */
@@ -187,9 +209,10 @@ size_t ring_attn_backward_workspace_size(const ra_tensor* q, int32_t n_blocks, i
  * query heads that read it.  No atomics: the results do not depend on
  * scheduling.
  *   q, k, v, n_blocks, layout, mask_mode, max_ring_passes, cu_seqlens_host,
- *     n_docs, scale: as given to ring_attn_forward.  16-bit inputs (bf16 or
- *     fp16, all the same type) with head_dim 64 or 128, n_blocks <= 64, T < 2^31 and T / n_blocks < 2^21
- *     only (RA_E_UNSUPPORTED otherwise).
+ *     n_docs, key_valid, scale: as given to ring_attn_forward.  16-bit
+ *     inputs (bf16 or fp16, all the same type) with head_dim 64 or 128,
+ *     n_blocks <= 64, T < 2^31 and T / n_blocks < 2^21 only
+ *     (RA_E_UNSUPPORTED otherwise).  A padded key gets dk = dv = 0.
  *   out: the forward's output [T, Hq, d] view, f32 or the inputs' type
  *     (16-byte aligned rows); dout: [T, Hq, d] view of the inputs' type.
  *   lse: the forward's lse, [Hq, T] fp32 (natural log).
@@ -200,8 +223,9 @@ size_t ring_attn_backward_workspace_size(const ra_tensor* q, int32_t n_blocks, i
 ra_status ring_attn_backward(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v, const ra_tensor* out,
                              const ra_tensor* dout, const float* lse, void* dq, void* dk, void* dv,
                              ra_dtype grad_dtype, int32_t n_blocks, ra_layout layout, ra_mask mask_mode,
-                             int32_t max_ring_passes, const int32_t* cu_seqlens_host, int32_t n_docs, float scale,
-                             void* workspace, size_t workspace_bytes, void* stream);
+                             int32_t max_ring_passes, const int32_t* cu_seqlens_host, int32_t n_docs,
+                             const uint8_t* key_valid, float scale, void* workspace, size_t workspace_bytes,
+                             void* stream);
 
 /*
  * Host-only planning (no GPU work): fills `stats` with the tallies and the

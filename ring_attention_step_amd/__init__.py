@@ -70,23 +70,24 @@ def load_library():
     lib = ctypes.CDLL(LIB_PATH)
     P = ctypes.POINTER
     lib.ring_attn_step.argtypes = [P(RaTensor), P(RaTensor), P(RaTensor), _vp, _vp, _vp, _int, _f32, _int,
-                                   _i64, _i64, _i64, _vp, _i32, _vp, _vp]
+                                   _i64, _i64, _i64, _vp, _i32, _vp, _vp, _vp]
+    lib.ring_attn_pack_key_mask.argtypes = [_vp, _i64, _i64, _vp, _vp]
     lib.ring_attn_finalize.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, _vp, _int, _i64, _i64, _vp, _vp]
     lib.ring_attn_merge.argtypes = [_vp, _vp, _vp, _vp, _int, _i64, _i64, _i64, _vp]
     lib.ring_attn_forward_workspace_size.argtypes = [P(RaTensor), P(RaTensor), _i32, _i32, _int]
     lib.ring_attn_forward_workspace_size.restype = _sz
     lib.ring_attn_forward.argtypes = [P(RaTensor), P(RaTensor), P(RaTensor), _vp, _int, _vp, _i32, _int, _int,
-                                      _i32, _vp, _i32, _f32, _int, _vp, _sz, P(RaStats), _vp]
+                                      _i32, _vp, _i32, _vp, _f32, _int, _vp, _sz, P(RaStats), _vp]
     lib.ring_attn_backward_workspace_size.argtypes = [P(RaTensor), _i32, _i32]
     lib.ring_attn_backward_workspace_size.restype = _sz
     lib.ring_attn_backward.argtypes = [P(RaTensor), P(RaTensor), P(RaTensor), P(RaTensor), P(RaTensor), _vp, _vp,
-                                       _vp, _vp, _int, _i32, _int, _int, _i32, _vp, _i32, _f32, _vp, _sz, _vp]
+                                       _vp, _vp, _int, _i32, _int, _int, _i32, _vp, _i32, _vp, _f32, _vp, _sz, _vp]
     lib.ring_attn_plan.argtypes = [_i64, _i32, _int, _int, _i32, _vp, _i32, _int, _i64, P(RaStats)]
     lib.ring_attn_tile_shape.argtypes = [_int, _i64, P(_i32), P(_i32)]
     lib.ring_attn_status_string.argtypes = [_int]
     lib.ring_attn_status_string.restype = ctypes.c_char_p
     for fn in ("ring_attn_step", "ring_attn_finalize", "ring_attn_merge", "ring_attn_forward",
-               "ring_attn_plan", "ring_attn_tile_shape", "ring_attn_backward"):
+               "ring_attn_plan", "ring_attn_tile_shape", "ring_attn_backward", "ring_attn_pack_key_mask"):
         getattr(lib, fn).restype = _int
     _lib = lib
     return lib
@@ -141,9 +142,10 @@ def ring_attn_tile_shape(dtype: torch.dtype, head_dim: int):
 
 def ring_attn_step(q_blk, k_blk, v_blk, O, m, l, *, first_step: bool, scale: float, mask_mode: int = RA_MASK_NONE,
                    q_offset: int = 0, kv_offset: int = 0, pos_stride: int = 1, cu_seqlens=None,
-                   stats: Optional[torch.Tensor] = None, stream=None):
+                   key_bits: Optional[torch.Tensor] = None, stats: Optional[torch.Tensor] = None, stream=None):
     """One ring step on the GPU; O [Hq, Bq, d], m / l [Hq, Bq] fp32 are updated in place.
-    cu_seqlens: int32 GPU tensor (doc-causal); stats: int64 GPU tensor of 3 counters (added to)."""
+    cu_seqlens: int32 GPU tensor (doc-causal); key_bits: the key block's padding mask from
+    ring_attn_pack_key_mask; stats: int64 GPU tensor of 3 counters (added to)."""
     qt, kt, vt = _tensor(q_blk, "q_blk"), _tensor(k_blk, "k_blk"), _tensor(v_blk, "v_blk")
     for x, name in ((O, "O"), (m, "m"), (l, "l")):
         _gpu(x, name)
@@ -159,11 +161,39 @@ def ring_attn_step(q_blk, k_blk, v_blk, O, m, l, *, first_step: bool, scale: flo
         _gpu(stats, "stats")
         if stats.dtype != torch.int64 or stats.numel() < 3:
             raise ValueError("stats must hold 3 int64 counters")
+    if key_bits is not None:
+        _gpu(key_bits, "key_bits")
+        if key_bits.dtype != torch.int32 or key_bits.numel() < 2 * ((k_blk.shape[0] + 63) // 64):
+            raise ValueError("key_bits must be the int32 words ring_attn_pack_key_mask writes for the block")
     st = load_library().ring_attn_step(ctypes.byref(qt), ctypes.byref(kt), ctypes.byref(vt), O.data_ptr(),
                                        m.data_ptr(), l.data_ptr(), int(bool(first_step)), float(scale),
                                        int(mask_mode), int(q_offset), int(kv_offset), int(pos_stride),
-                                       _ptr(cu_seqlens), n_docs, _ptr(stats), _stream(stream))
+                                       _ptr(cu_seqlens), n_docs, _ptr(key_bits), _ptr(stats), _stream(stream))
     _check("ring_attn_step", st)
+
+
+def ring_attn_pack_key_mask(key_valid: torch.Tensor, *, stream=None) -> torch.Tensor:
+    """Key-padding mask of one key block ([n] bool / uint8 GPU tensor, may be strided, nonzero = the key
+    takes part) as the int32 bit words ring_attn_step reads (2 * ceil(n / 64) words)."""
+    _gpu(key_valid, "key_valid")
+    if key_valid.dim() != 1 or key_valid.dtype not in (torch.bool, torch.uint8):
+        raise ValueError("key_valid must be a 1-D bool or uint8 tensor")
+    n = key_valid.shape[0]
+    bits = torch.empty(max(2 * ((n + 63) // 64), 2), device=key_valid.device, dtype=torch.int32)
+    _check("ring_attn_pack_key_mask",
+           load_library().ring_attn_pack_key_mask(key_valid.data_ptr(), n, max(key_valid.stride(0), 1),
+                                                  bits.data_ptr(), _stream(stream)))
+    return bits
+
+
+def _key_valid(key_valid, T: int):
+    """A [T] key-padding mask as a contiguous uint8 GPU tensor (or None)."""
+    if key_valid is None:
+        return None
+    _gpu(key_valid, "key_valid")
+    if key_valid.dim() != 1 or key_valid.shape[0] != T or key_valid.dtype not in (torch.bool, torch.uint8):
+        raise ValueError("key_valid must be a [T] bool or uint8 tensor")
+    return key_valid.contiguous().view(torch.uint8)
 
 
 def ring_attn_finalize(O, m, l, out, lse=None, *, stream=None):
@@ -205,7 +235,7 @@ def ring_attn_forward_workspace_size(q, k, n_blocks: int, n_docs: int = 0, prefe
 
 
 def ring_attn_forward(q, k, v, out, lse, *, n_blocks: int, layout: int, mask_mode: int, max_ring_passes: int,
-                      cu_seqlens_host=None, scale: float, prefetch: bool, workspace: torch.Tensor,
+                      cu_seqlens_host=None, key_valid=None, scale: float, prefetch: bool, workspace: torch.Tensor,
                       want_stats: bool = False, stream=None):
     """The whole one-GPU ring; out [T, Hq, d] contiguous; lse [Hq, T] fp32 or None.
     Returns the tallies (dict) when want_stats (this synchronises the stream)."""
@@ -220,10 +250,11 @@ def ring_attn_forward(q, k, v, out, lse, *, n_blocks: int, layout: int, mask_mod
     if cu_seqlens_host is not None:
         cu_keep = torch.as_tensor(cu_seqlens_host).to(device="cpu", dtype=torch.int32).contiguous()
         cu_ptr, n_docs = cu_keep.data_ptr(), cu_keep.numel() - 1
+    kv = _key_valid(key_valid, q.shape[0])
     stats = RaStats()
     st = load_library().ring_attn_forward(
         ctypes.byref(qt), ctypes.byref(kt), ctypes.byref(vt), out.data_ptr(), _dtype_code(out.dtype), _ptr(lse),
-        int(n_blocks), int(layout), int(mask_mode), int(max_ring_passes), cu_ptr, n_docs, float(scale),
+        int(n_blocks), int(layout), int(mask_mode), int(max_ring_passes), cu_ptr, n_docs, _ptr(kv), float(scale),
         int(bool(prefetch)), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
         ctypes.byref(stats) if want_stats else None, _stream(stream))
     _check("ring_attn_forward", st)
@@ -236,8 +267,8 @@ def ring_attn_backward_workspace_size(q, n_blocks: int, n_docs: int = 0) -> int:
 
 
 def ring_attn_backward(q, k, v, out, dout, lse, dq, dk, dv, *, n_blocks: int, layout: int, mask_mode: int,
-                       max_ring_passes: int, cu_seqlens_host=None, scale: float, workspace: torch.Tensor,
-                       stream=None):
+                       max_ring_passes: int, cu_seqlens_host=None, key_valid=None, scale: float,
+                       workspace: torch.Tensor, stream=None):
     """Gradients of the ring forward: dq [T, Hq, d], dk / dv [T, Hkv, d] (contiguous, fp32 or bf16, written
     in full) from the forward's out [T, Hq, d] and lse [Hq, T] and the output gradient dout [T, Hq, d]."""
     qt, kt, vt = _tensor(q, "q"), _tensor(k, "k"), _tensor(v, "v")
@@ -256,10 +287,11 @@ def ring_attn_backward(q, k, v, out, dout, lse, dq, dk, dv, *, n_blocks: int, la
     if cu_seqlens_host is not None:
         cu_keep = torch.as_tensor(cu_seqlens_host).to(device="cpu", dtype=torch.int32).contiguous()
         cu_ptr, n_docs = cu_keep.data_ptr(), cu_keep.numel() - 1
+    kv = _key_valid(key_valid, q.shape[0])
     st = load_library().ring_attn_backward(
         ctypes.byref(qt), ctypes.byref(kt), ctypes.byref(vt), ctypes.byref(ot), ctypes.byref(gt), lse.data_ptr(),
         dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), _dtype_code(dq.dtype), int(n_blocks), int(layout),
-        int(mask_mode), int(max_ring_passes), cu_ptr, n_docs, float(scale), workspace.data_ptr(),
+        int(mask_mode), int(max_ring_passes), cu_ptr, n_docs, _ptr(kv), float(scale), workspace.data_ptr(),
         workspace.numel() * workspace.element_size(), _stream(stream))
     _check("ring_attn_backward", st)
 
@@ -284,9 +316,10 @@ _LAYOUTS = {"contiguous": RA_LAYOUT_CONTIGUOUS, "striped": RA_LAYOUT_STRIPED}
 def forward(q, k, v, *, n_blocks: int, layout: str = "contiguous", causal: bool = False, cu_seqlens=None,
             max_ring_passes: Optional[int] = None, scale: Optional[float] = None, prefetch: bool = False,
             out_dtype: Optional[torch.dtype] = None, return_lse: bool = False, return_stats: bool = False,
-            workspace: Optional[torch.Tensor] = None):
+            key_valid: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
     """Ring attention over q [T, Hq, d], k / v [T, Hkv, d] on one GPU as n_blocks virtual devices.
-    cu_seqlens (documents, implies per-document causal) may be a CPU or GPU int tensor or a list."""
+    cu_seqlens (documents, implies per-document causal) may be a CPU or GPU int tensor or a list;
+    key_valid: optional [T] bool / uint8 GPU tensor, a key-padding mask (False = padded key)."""
     T, Hq, d = q.shape
     mask = RA_MASK_NONE
     if causal:
@@ -304,8 +337,8 @@ def forward(q, k, v, *, n_blocks: int, layout: str = "contiguous", causal: bool 
     if workspace is None or workspace.numel() * workspace.element_size() < ws_bytes:
         workspace = torch.empty(ws_bytes, device=q.device, dtype=torch.uint8)
     stats = ring_attn_forward(q, k, v, out, lse, n_blocks=n_blocks, layout=_LAYOUTS[layout], mask_mode=mask,
-                              max_ring_passes=P, cu_seqlens_host=cu_seqlens, scale=scale, prefetch=prefetch,
-                              workspace=workspace, want_stats=return_stats)
+                              max_ring_passes=P, cu_seqlens_host=cu_seqlens, key_valid=key_valid, scale=scale,
+                              prefetch=prefetch, workspace=workspace, want_stats=return_stats)
     res = [out]
     if return_lse:
         res.append(lse)
@@ -323,7 +356,8 @@ def forward_qkvpacked(qkv, **kw):
 
 def backward(q, k, v, out, lse, dout, *, n_blocks: int, layout: str = "contiguous", causal: bool = False,
              cu_seqlens=None, max_ring_passes: Optional[int] = None, scale: Optional[float] = None,
-             grad_dtype: torch.dtype = torch.float32, workspace: Optional[torch.Tensor] = None):
+             grad_dtype: torch.dtype = torch.float32, key_valid: Optional[torch.Tensor] = None,
+             workspace: Optional[torch.Tensor] = None):
     """(dq, dk, dv) of ``forward(q, k, v, ...)`` for the output gradient dout, given that call's out and lse
     (return_lse=True) and the same ring arguments."""
     T, Hq, d = q.shape
@@ -344,12 +378,12 @@ def backward(q, k, v, out, lse, dout, *, n_blocks: int, layout: str = "contiguou
     if workspace is None or workspace.numel() * workspace.element_size() < ws_bytes:
         workspace = torch.empty(ws_bytes, device=q.device, dtype=torch.uint8)
     ring_attn_backward(q, k, v, out, dout, lse, dq, dk, dv, n_blocks=n_blocks, layout=_LAYOUTS[layout],
-                       mask_mode=mask, max_ring_passes=P, cu_seqlens_host=cu_seqlens, scale=scale,
-                       workspace=workspace)
+                       mask_mode=mask, max_ring_passes=P, cu_seqlens_host=cu_seqlens, key_valid=key_valid,
+                       scale=scale, workspace=workspace)
     return dq, dk, dv
 
 
 __all__ = ["ring_attn_step", "ring_attn_finalize", "ring_attn_merge", "ring_attn_forward_workspace_size",
            "ring_attn_forward", "ring_attn_plan", "ring_attn_tile_shape", "ring_attn_backward_workspace_size",
-           "ring_attn_backward", "forward", "forward_qkvpacked", "backward",
+           "ring_attn_backward", "ring_attn_pack_key_mask", "forward", "forward_qkvpacked", "backward",
            "load_library", "RingAttnError"]

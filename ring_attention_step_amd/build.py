@@ -21,7 +21,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libring_attn.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
-HIP_SOURCES = ["api.hip", "step_bf16.hip", "step_f32.hip", "finalize_merge.hip", "pack_vt.hip", "backward.hip"]
+HIP_SOURCES = ["api.hip", "step_bf16.hip", "step_f32.hip", "finalize_merge.hip", "pack_vt.hip", "key_bits.hip",
+               "backward.hip"]
 CPP_SOURCES = ["plan.cpp"]
 ARCH = "gfx950"
 

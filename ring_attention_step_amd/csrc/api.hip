@@ -62,6 +62,9 @@ bool bf16_tile_addressable(int64_t row_stride_elems) {
 
 bool scale_ok(float s) { return std::isfinite(s) && s > 0.f; }
 
+// 32-bit words of a block's key-padding bits: whole 64-key tiles.
+int64_t key_words(int64_t B) { return 2 * ((B + 63) / 64); }
+
 hipError_t launch(const StepArgs& a, ra_dtype dt, hipStream_t st) {
     return is16(dt) ? launch_step_bf16(a, st) : launch_step_f32(a, st);
 }
@@ -102,6 +105,7 @@ struct Workspace {
     char* vt = nullptr;     // packed V^T of all blocks (bf16 path): [N][Hkv][d][Bp]
     RingWork* works = nullptr;    // one-launch ring forward (bf16): N works
     RingEntry* entries = nullptr; //   and up to N x N chain entries
+    uint32_t* kbits = nullptr;    // key-padding bits of every block: [N][key_words(B)]
     char* kv = nullptr;     // prefetch double buffers: K [2][N][B][Hkv][d], then V (f32) or V^T (bf16)
     size_t k_half = 0;      // bytes of the K double buffer
     size_t total = 0;
@@ -125,6 +129,7 @@ Workspace carve(void* base, int64_t T, int64_t N, int64_t Hq, int64_t Hkv, int64
     w.O = (float*)take(sizeof(float) * (size_t)(T * Hq * d));
     w.m = (float*)take(sizeof(float) * (size_t)(T * Hq));
     w.l = (float*)take(sizeof(float) * (size_t)(T * Hq));
+    w.kbits = (uint32_t*)take(sizeof(uint32_t) * (size_t)(N * key_words(B)));
     if (is16(dt)) {
         w.vt = take(vt_bytes);
         w.works = (RingWork*)take(sizeof(RingWork) * (size_t)N);
@@ -147,6 +152,7 @@ struct BwdWorkspace {
     int64_t* partners = nullptr;    // N x N
     BwdWork* rworks = nullptr;      // N
     int64_t* rpartners = nullptr;   // N x N
+    uint32_t* kbits = nullptr;      // key-padding bits: [N][key_words(B)]
     size_t total = 0;
 };
 
@@ -167,6 +173,7 @@ BwdWorkspace carve_bwd(void* base, int64_t T, int64_t N, int64_t Hq, int64_t n_d
     w.partners = (int64_t*)take(sizeof(int64_t) * (size_t)(N * N));
     w.rworks = (BwdWork*)take(sizeof(BwdWork) * (size_t)N);
     w.rpartners = (int64_t*)take(sizeof(int64_t) * (size_t)(N * N));
+    w.kbits = (uint32_t*)take(sizeof(uint32_t) * (size_t)(N * key_words(N > 0 ? T / N : 0)));
     w.total = off;
     return w;
 }
@@ -189,6 +196,15 @@ const char* ring_attn_status_string(ra_status s) {
     return "unknown status";
 }
 
+ra_status ring_attn_pack_key_mask(const uint8_t* key_valid, int64_t n_keys, int64_t stride, uint32_t* key_bits,
+                                  void* stream) {
+    if (!key_valid || !key_bits || n_keys < 0 || stride < 1 || (uintptr_t)key_bits % 8) return RA_E_ARG;
+    if (launch_pack_key_bits(key_valid, stride, 1, n_keys, 0, key_words(n_keys), key_bits, (hipStream_t)stream) !=
+        hipSuccess)
+        return RA_E_HIP;
+    return RA_OK;
+}
+
 ra_status ring_attn_tile_shape(ra_dtype dtype, int64_t head_dim, int32_t* tile_q, int32_t* tile_k) {
     if (!tile_q || !tile_k) return RA_E_ARG;
     int tq = 0, tk = 0;
@@ -202,7 +218,7 @@ ra_status ring_attn_tile_shape(ra_dtype dtype, int64_t head_dim, int32_t* tile_q
 ra_status ring_attn_step(const ra_tensor* q_blk, const ra_tensor* k_blk, const ra_tensor* v_blk, float* O, float* m,
                          float* l, int first_step, float scale, ra_mask mask_mode, int64_t q_offset,
                          int64_t kv_offset, int64_t pos_stride, const int32_t* cu_seqlens, int32_t n_docs,
-                         int64_t* stats_dev, void* stream) {
+                         const uint32_t* key_bits, int64_t* stats_dev, void* stream) {
     if (!tensor_ok(q_blk) || !tensor_ok(k_blk) || !tensor_ok(v_blk)) return RA_E_ARG;
     if (q_blk->dtype != k_blk->dtype || q_blk->dtype != v_blk->dtype) return RA_E_ARG;
     const int64_t d = q_blk->head_dim;
@@ -213,6 +229,7 @@ ra_status ring_attn_step(const ra_tensor* q_blk, const ra_tensor* k_blk, const r
     if (mask_mode < RA_MASK_NONE || mask_mode > RA_MASK_DOC_CAUSAL) return RA_E_ARG;
     if (mask_mode == RA_MASK_DOC_CAUSAL && (!cu_seqlens || n_docs < 1)) return RA_E_ARG;
     if (mask_mode == RA_MASK_DOC_CAUSAL && pos_stride != 1) return RA_E_UNSUPPORTED;
+    if ((uintptr_t)key_bits % 8) return RA_E_ARG;
     int tq = 0, tk = 0;
     ra_status ks = kernel_for(q_blk->dtype, d, &tq, &tk);
     if (ks != RA_OK) return ks;
@@ -243,6 +260,7 @@ ra_status ring_attn_step(const ra_tensor* q_blk, const ra_tensor* k_blk, const r
     a.group = (int32_t)(Hq / k_blk->n_head);
     a.d = (int32_t)d;
     a.f16 = q_blk->dtype == RA_F16;
+    a.kbits = key_bits;
     a.mask = mask_mode;
     a.scale = scale;
     a.c2 = scale * 1.4426950408889634f;
@@ -334,8 +352,9 @@ ra_status ring_attn_plan(int64_t T, int32_t n_blocks, ra_layout layout, ra_mask 
 
 ra_status ring_attn_forward(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v, void* out,
                             ra_dtype out_dtype, float* lse, int32_t n_blocks, ra_layout layout, ra_mask mask_mode,
-                            int32_t max_ring_passes, const int32_t* cu_seqlens_host, int32_t n_docs, float scale,
-                            int prefetch, void* workspace, size_t workspace_bytes, ra_stats* stats, void* stream) {
+                            int32_t max_ring_passes, const int32_t* cu_seqlens_host, int32_t n_docs,
+                            const uint8_t* key_valid, float scale, int prefetch, void* workspace,
+                            size_t workspace_bytes, ra_stats* stats, void* stream) {
     // ---- arguments ----
     if (!tensor_ok(q) || !tensor_ok(k) || !tensor_ok(v) || !out) return RA_E_ARG;
     if (q->dtype != k->dtype || q->dtype != v->dtype || !valid_dtype(out_dtype)) return RA_E_ARG;
@@ -397,6 +416,9 @@ ra_status ring_attn_forward(const ra_tensor* q, const ra_tensor* k, const ra_ten
     if (n_docs > 0 && hipMemcpyAsync(ws.cu, cu_seqlens_host, sizeof(int32_t) * (size_t)(n_docs + 1),
                                      hipMemcpyHostToDevice, st) != hipSuccess)
         return RA_E_HIP;
+    const int64_t kbw = key_words(B);  // key-padding words per block; block j's at j * kbw
+    if (key_valid && launch_pack_key_bits(key_valid, 1, N, B, striped, kbw, ws.kbits, st) != hipSuccess)
+        return RA_E_HIP;
 
     StepArgs base;
     std::memset(&base, 0, sizeof base);
@@ -412,6 +434,7 @@ ra_status ring_attn_forward(const ra_tensor* q, const ra_tensor* k, const ra_ten
     base.cu = ws.cu;
     base.n_docs = n_docs;
     base.f16 = q->dtype == RA_F16;
+    base.kbits = key_valid ? ws.kbits : nullptr;
     base.out16 = is16(out_dtype);
     base.out = out;
     base.out_row_stride = (striped ? N : 1) * out_tok;
@@ -475,6 +498,7 @@ ra_status ring_attn_forward(const ra_tensor* q, const ra_tensor* k, const ra_ten
                     e.k_off = row_off(j, k->stride_tok);
                     e.vt_off = (int64_t)j * vt_blk;
                     e.k_pos0 = striped ? j : j * B;
+                    e.kb_off = j * kbw;
                     entries.push_back(e);
                 }
             }
@@ -579,6 +603,7 @@ ra_status ring_attn_forward(const ra_tensor* q, const ra_tensor* k, const ra_ten
                 }
                 p.q_pos0 = striped ? sp.i : sp.i * B;
                 p.k_pos0 = striped ? sp.j : sp.j * B;
+                p.kb_off = sp.j * kbw;
                 p.O = ws.O + (size_t)sp.i * Hq * B * d;
                 p.m = ws.m + (size_t)sp.i * Hq * B;
                 p.l = ws.l + (size_t)sp.i * Hq * B;
@@ -625,8 +650,9 @@ size_t ring_attn_backward_workspace_size(const ra_tensor* q, int32_t n_blocks, i
 ra_status ring_attn_backward(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v, const ra_tensor* out,
                              const ra_tensor* dout, const float* lse, void* dq, void* dk, void* dv,
                              ra_dtype grad_dtype, int32_t n_blocks, ra_layout layout, ra_mask mask_mode,
-                             int32_t max_ring_passes, const int32_t* cu_seqlens_host, int32_t n_docs, float scale,
-                             void* workspace, size_t workspace_bytes, void* stream) {
+                             int32_t max_ring_passes, const int32_t* cu_seqlens_host, int32_t n_docs,
+                             const uint8_t* key_valid, float scale, void* workspace, size_t workspace_bytes,
+                             void* stream) {
     // ---- arguments ----
     if (!tensor_ok(q) || !tensor_ok(k) || !tensor_ok(v) || !tensor_ok(out) || !tensor_ok(dout)) return RA_E_ARG;
     if (!lse || !dq || !dk || !dv || !valid_dtype(grad_dtype)) return RA_E_ARG;
@@ -732,9 +758,14 @@ ra_status ring_attn_backward(const ra_tensor* q, const ra_tensor* k, const ra_te
                               hipMemcpyAsync(ws.rpartners, rpartners.data(), sizeof(int64_t) * rpartners.size(),
                                              hipMemcpyHostToDevice, st) != hipSuccess))
         return RA_E_HIP;
+    if (key_valid && launch_pack_key_bits(key_valid, 1, N, B, striped, key_words(B), ws.kbits, st) != hipSuccess)
+        return RA_E_HIP;
 
     BwdArgs a;
     std::memset(&a, 0, sizeof a);
+    a.key_valid = key_valid;
+    a.kbits = key_valid ? ws.kbits : nullptr;
+    a.kb_words = (int32_t)key_words(B);
     a.q = q->data;
     a.k = k->data;
     a.v = v->data;

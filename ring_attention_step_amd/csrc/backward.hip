@@ -294,7 +294,7 @@ __device__ __forceinline__ void tile_range(int n_tiles, Cls3 cls, int& lo, int& 
 }
 
 // ---- dq ----
-template <typename E, int D>
+template <typename E, int D, bool KP>
 __global__ __launch_bounds__(DQ_THREADS, 1) void bwd_dq_kernel(const BwdArgs a) {
     constexpr int TE = BW_T * D;              // elements of one [64][D] tile
     constexpr int NL = 2 * (TE / 512 / DQ_WAVES);  // loads per wave per stage: K tile, then V tile
@@ -436,9 +436,17 @@ __global__ __launch_bounds__(DQ_THREADS, 1) void bwd_dq_kernel(const BwdArgs a) 
     };
 
     int cc_flo = 0, cc_fhi = -1;  // fully visible tiles of the compute cursor's block
+    // Key-padding mask: the compute cursor's block's first bit word, and the
+    // validity word of its tile (all ones without a mask).
+    int kb_cur = 0;
+    uint64_t kw = ~0ull;
+    auto key_word = [&](const Cursor& c) __attribute__((always_inline)) {
+        typedef const __attribute__((address_space(4))) uint64_t* cwp;
+        return *(cwp)(a.kbits + kb_cur + 2 * c.kt);
+    };
     auto compute = [&](const bf16* ks, const bf16* vs, const Cursor& c) __attribute__((always_inline)) {
         const int64_t w0 = (int64_t)c.kt * BW_T;
-        const bool full = c.kt != ragged_kt && c.kt >= cc_flo && c.kt <= cc_fhi;
+        const bool full = c.kt != ragged_kt && c.kt >= cc_flo && c.kt <= cc_fhi && (!KP || kw == ~0ull);
         // Allowed keys shifted by -4 half, relative to the tile (|x| <= B + 4).
         const int x_lo = w_lo - (int)w0 - 4 * half, x_hi = w_hi - (int)w0 - 4 * half;
 #pragma unroll
@@ -456,20 +464,23 @@ __global__ __launch_bounds__(DQ_THREADS, 1) void bwd_dq_kernel(const BwdArgs a) 
             // visible tiles take a copy without the mask (the branch holds
             // vector work only, so the accumulators stay in place).
             bf16x8 b0, b1;
-            auto softmax = [&](auto full_t) __attribute__((always_inline)) {
-                constexpr bool FULL = decltype(full_t)::value;
+            auto softmax = [&](auto full_t, auto padded_t) __attribute__((always_inline)) {
+                constexpr bool FULL = decltype(full_t)::value, PADDED = decltype(padded_t)::value;
+                const uint64_t wl = kw >> (4 * half);  // padded keys: bit x of this half's word
                 f32x16 dsv;
 #pragma unroll
                 for (int i = 0; i < 16; i++) {
                     const int x = 32 * kb + 8 * (i / 4) + (i % 4);
                     float arg = fmaf(s[i], a.c2, -lse2);
                     if (!FULL) arg = ((x >= x_lo) & (x < x_hi)) ? arg : -INFINITY;
+                    if (PADDED) arg = ((wl >> x) & 1) ? arg : -INFINITY;
                     dsv[i] = __builtin_amdgcn_exp2f(arg) * (dp[i] - drow);
                 }
                 acc_to_b<E>(dsv, b0, b1);
             };
-            if (__builtin_amdgcn_readfirstlane((int)full)) softmax(std::true_type{});
-            else softmax(std::false_type{});
+            if (__builtin_amdgcn_readfirstlane((int)full)) softmax(std::true_type{}, std::false_type{});
+            else if (!KP || kw == ~0ull) softmax(std::false_type{}, std::false_type{});
+            else softmax(std::false_type{}, std::true_type{});
             // dq^T += K^T dS^T over the two 16-key chunks of this half.
 #pragma unroll
             for (int db = 0; db < D / 32; db++) {
@@ -488,8 +499,13 @@ __global__ __launch_bounds__(DQ_THREADS, 1) void bwd_dq_kernel(const BwdArgs a) 
         const int f = rl32(tb_full, c.e);
         cc_flo = f & 0xffff;
         cc_fhi = (f >> 16) - 1;
+        // block index: position of row 0 over B (contiguous) or itself (striped)
+        if (KP) kb_cur = (ps == 1 ? (int)((uint32_t)c.kp / (uint32_t)B) : (int)c.kp) * a.kb_words;
     };
-    if (nT > 0) enter_block(cc);
+    if (nT > 0) {
+        enter_block(cc);
+        if (KP) kw = key_word(cc);
+    }
     auto iteration = [&](int j, auto slot) __attribute__((always_inline)) {
         constexpr int S = decltype(slot)::value;  // j % 3
         bf16* const kc = S == 0 ? st0 : (S == 1 ? st1 : st2);
@@ -505,6 +521,7 @@ __global__ __launch_bounds__(DQ_THREADS, 1) void bwd_dq_kernel(const BwdArgs a) 
             const int e_was = cc.e;
             cur_next(cc);
             if (cc.e != e_was) enter_block(cc);
+            if (KP) kw = key_word(cc);  // scalar load, complete at the barrier below
         }
         wait_loads_but<NL>();  // tile j + 1 has landed
         phase_barrier();
@@ -887,6 +904,9 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(const BwdArgs a
     }
 
     if (!key_ok) return;
+    // A padded key gets exact zeros.  Every other key's sums above never
+    // involve a padded key (P comes from the forward's lse, D from its out).
+    const bool padded = a.key_valid && !a.key_valid[p_key];
     const float mul = role ? a.scale : 1.f;
     char* ob = (char*)(role ? a.dk : a.dv);
     const int64_t oe = (p_key * a.Hkv + kvh) * D + 4 * half;
@@ -895,8 +915,9 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(const BwdArgs a
 #pragma unroll
         for (int g = 0; g < 4; g++) {
             const int64_t e = oe + 32 * db + 8 * g;
-            const float x0 = acc[db][4 * g] * mul, x1 = acc[db][4 * g + 1] * mul;
-            const float x2 = acc[db][4 * g + 2] * mul, x3 = acc[db][4 * g + 3] * mul;
+            float x0 = acc[db][4 * g] * mul, x1 = acc[db][4 * g + 1] * mul;
+            float x2 = acc[db][4 * g + 2] * mul, x3 = acc[db][4 * g + 3] * mul;
+            if (padded) x0 = x1 = x2 = x3 = 0.f;
             if (a.grad16) *(bf16x4*)(ob + 2 * e) = bf16x4{to16<E>(x0), to16<E>(x1), to16<E>(x2), to16<E>(x3)};
             else *(f32x4*)(ob + 4 * e) = f32x4{x0, x1, x2, x3};
         }
@@ -912,8 +933,13 @@ hipError_t launch_backward16(const BwdArgs& a, hipStream_t stream) {
     const int64_t ndq = (int64_t)a.n_works * a.Hq * a.n_qtiles;
     const int64_t ndk = (int64_t)a.n_rworks * a.Hkv * a.n_ktiles;
     if (ndq > 0) {
-        if (a.d == 128) bwd_dq_kernel<E, 128><<<(unsigned)ndq, DQ_THREADS, 0, stream>>>(a);
-        else if (a.d == 64) bwd_dq_kernel<E, 64><<<(unsigned)ndq, DQ_THREADS, 0, stream>>>(a);
+        // KP: with a key-padding mask (the unmasked kernel carries none of its code)
+        if (a.kbits) {
+            if (a.d == 128) bwd_dq_kernel<E, 128, true><<<(unsigned)ndq, DQ_THREADS, 0, stream>>>(a);
+            else if (a.d == 64) bwd_dq_kernel<E, 64, true><<<(unsigned)ndq, DQ_THREADS, 0, stream>>>(a);
+            else return hipErrorInvalidValue;
+        } else if (a.d == 128) bwd_dq_kernel<E, 128, false><<<(unsigned)ndq, DQ_THREADS, 0, stream>>>(a);
+        else if (a.d == 64) bwd_dq_kernel<E, 64, false><<<(unsigned)ndq, DQ_THREADS, 0, stream>>>(a);
         else return hipErrorInvalidValue;
     }
     if (ndk > 0) {

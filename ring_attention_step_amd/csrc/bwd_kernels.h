@@ -38,6 +38,12 @@ struct BwdArgs {
     const int64_t* partners;
     const BwdWork* rworks;         // per key block: the query blocks that visit it
     const int64_t* rpartners;
+    // Key-padding mask (both null without one): key_valid[t] != 0 when key
+    // token t takes part; kbits holds the same as bits of whole 64-key tiles,
+    // block j's kb_words words at j * kb_words (block-local rows).
+    const uint8_t* key_valid;
+    const uint32_t* kbits;
+    int32_t kb_words;
     int32_t f16;                   // 16-bit values are fp16, else bf16 (picks the kernels)
 };
 constexpr int kBwdPad = 256;       // floats of padding after Lse2 and after Dsum

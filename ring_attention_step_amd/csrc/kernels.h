@@ -17,6 +17,7 @@ struct PairDesc {
     int64_t vt_off;                // element offset of this key block in the packed V^T
     int32_t load_state;            // state holds earlier steps' keys
     int32_t finalize;              // write out / lse instead of the state
+    int64_t kb_off;                // offset (32-bit words) of the key block's validity bits in kbits
 };
 
 constexpr int kMaxPairs = 16;
@@ -33,6 +34,7 @@ constexpr int kMaxRingChain = 64;  // chain blocks a workgroup can hold (one per
 struct RingEntry {                 // one key/value block of a device's ring, in visiting order
     int64_t k_off, vt_off;         // element offsets of the block in k and in the packed V^T
     int64_t k_pos0;                // global position of its local row 0
+    int64_t kb_off;                // offset (32-bit words) of its validity bits in kbits
 };
 
 struct StepArgs {
@@ -65,6 +67,10 @@ struct StepArgs {
     // RingWork entries (pairs[] is unused), each finalised at its end.
     const RingWork* works;
     const RingEntry* entries;
+    // Key-padding mask (nullable): bit w % 32 of word kb_off + w / 32 is set
+    // when key row w of a block takes part; a block's bits are whole 64-key
+    // tiles (2 words each, 8-byte aligned), zero past its last row.
+    const uint32_t* kbits;
     int32_t f16;                           // 16-bit inputs are fp16, else bf16 (picks the kernel)
 };
 
@@ -81,6 +87,14 @@ hipError_t launch_merge(void* out_acc, float* lse_acc, const void* out_blk, cons
                         int kind, int64_t Hq, int64_t rows, int64_t d, hipStream_t stream);
 // out_kind / kind: element type of out (0 fp32, 1 bf16, 2 fp16).
 hipError_t launch_fill_u64(unsigned long long* p, int64_t n, hipStream_t stream);
+
+// Key-padding bits of ring blocks: for block j < n_blocks and row w < B,
+// bit w % 32 of bits[j * words_per_block + w / 32] = (key_valid[pos] != 0),
+// pos = j + w * n_blocks (striped) or j * B + w; every other bit of the
+// block's words_per_block words is 0.  n_blocks = 1, B = n, striped = 0 and
+// a row stride packs one block given by its own rows.
+hipError_t launch_pack_key_bits(const uint8_t* key_valid, int64_t row_stride, int64_t n_blocks, int64_t B,
+                                int striped, int64_t words_per_block, uint32_t* bits, hipStream_t stream);
 
 // Packed V^T of the ring blocks: vt[j][g][c][p] (p < Bp = B rounded up to the
 // key tile) holds V of key w of block j, kv head g, dim c, where p is w with

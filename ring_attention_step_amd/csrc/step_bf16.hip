@@ -202,7 +202,7 @@ __device__ __forceinline__ float other_half(float x) {
     return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
 }
 
-template <typename E, int D, bool VT, bool RING>
+template <typename E, int D, bool VT, bool RING, bool KP>
 __global__ __launch_bounds__(THREADS, 1) void step_bf16_kernel(const StepArgs a) {
     using TL = Tiles<D>;
     // Three stage buffers as six distinct arrays: the compiler can then tell
@@ -267,15 +267,15 @@ __global__ __launch_bounds__(THREADS, 1) void step_bf16_kernel(const StepArgs a)
     // Key/value block e of the chain: element offsets of its rows in k and
     // v (or the packed V^T), and the global position of its row 0.
     struct Blk {
-        int64_t k_off, v_off, k_pos0;
+        int64_t k_off, v_off, k_pos0, kb_off;
     };
     auto blk = [&](int e) __attribute__((always_inline)) {
         if (ring) {
             const RingEntry& r = a.entries[e_first + e];
-            return Blk{r.k_off, r.vt_off, r.k_pos0};
+            return Blk{r.k_off, r.vt_off, r.k_pos0, r.kb_off};
         }
         const PairDesc& pd = a.pairs[widx];
-        return Blk{pd.k_off, VT ? pd.vt_off : pd.v_off, pd.k_pos0};
+        return Blk{pd.k_off, VT ? pd.vt_off : pd.v_off, pd.k_pos0, pd.kb_off};
     };
 
     const int64_t u0 = (int64_t)qt * BQ;
@@ -298,7 +298,7 @@ __global__ __launch_bounds__(THREADS, 1) void step_bf16_kernel(const StepArgs a)
     // visible ones [flo, fhi] (contiguous too, between the partial tiles at
     // a document start and at the diagonal), offsets and first key position.
     // A cursor reads a block's entry with readlane when it moves on to it.
-    int cb_lo = 0, cb_hi = -1, cb_flo = 0, cb_fhi = -1;
+    int cb_lo = 0, cb_hi = -1, cb_flo = 0, cb_fhi = -1, cb_kb = 0;
     int64_t cb_koff = 0, cb_voff = 0, cb_kpos = 0;
     unsigned cb_nfull = 0, cb_npart = 0;
     if (lane < n_ent) {
@@ -306,6 +306,7 @@ __global__ __launch_bounds__(THREADS, 1) void step_bf16_kernel(const StepArgs a)
         cb_koff = bl.k_off;
         cb_voff = bl.v_off;
         cb_kpos = bl.k_pos0;
+        if (KP) cb_kb = (int)bl.kb_off;
         cb_lo = 0;
         cb_hi = nkt - 1;
         while (cb_lo <= cb_hi && tile_cls(cb_lo, cb_kpos) == kSkip) cb_lo++;
@@ -435,6 +436,14 @@ __global__ __launch_bounds__(THREADS, 1) void step_bf16_kernel(const StepArgs a)
     const int e0 = cc.e < 0 ? 0 : cc.e;
     int cc_flo = rl32(cb_flo, e0), cc_fhi = rl32(cb_fhi, e0);
     row_bounds(rl64(cb_kpos, e0));
+    // Key-padding mask: kw is the validity word of the compute cursor's tile
+    // (all ones without a mask), read with a scalar load one tile ahead.
+    auto key_word = [&](const Cursor& c) __attribute__((always_inline)) {
+        typedef const __attribute__((address_space(4))) uint64_t* cwp;
+        return *(cwp)(a.kbits + rl32(cb_kb, c.e) + 2 * c.kt);
+    };
+    uint64_t kw = ~0ull;
+    if (KP && nT > 0) kw = key_word(cc);
     const uint32_t k_rs_bytes = (uint32_t)(a.k_row_stride * 2);
     const uint32_t v_rs_bytes = (uint32_t)((VT ? a.vt_row_stride : a.v_row_stride) * 2);
     // This wave's chunk offsets within a stage tile (G0 loads K tiles, G1 V
@@ -559,19 +568,30 @@ __global__ __launch_bounds__(THREADS, 1) void step_bf16_kernel(const StepArgs a)
     // ks is the tile's K stage buffer, intact through this phase (the next
     // load into it is issued two phases later).
     auto v_phase = [&](int kt, const bf16* ks) __attribute__((always_inline)) {
-        const bool full = kt >= cc_flo && kt <= cc_fhi && kt != ragged_kt;
+        const bool full = kt >= cc_flo && kt <= cc_fhi && kt != ragged_kt && (!KP || kw == ~0ull);
         auto mask = [&]() __attribute__((always_inline)) {
             if (!full) {
                 // Register i of s[kb] holds tile key 32 kb + 8 (i/4) + 4 half + i%4;
                 // the allowed keys shifted by -4 half leave a constant to compare.
                 const int x_lo = w_lo - kt * BK - 4 * half, x_hi = w_hi - kt * BK - 4 * half;
+                if (!KP || kw == ~0ull) {
 #pragma unroll
-                for (int kb = 0; kb < 2; kb++)
+                    for (int kb = 0; kb < 2; kb++)
 #pragma unroll
-                    for (int i = 0; i < 16; i++) {
-                        const int x = 32 * kb + 8 * (i / 4) + (i % 4);
-                        if (x < x_lo || x >= x_hi) s[kb][i] = -INFINITY;
-                    }
+                        for (int i = 0; i < 16; i++) {
+                            const int x = 32 * kb + 8 * (i / 4) + (i % 4);
+                            if (x < x_lo || x >= x_hi) s[kb][i] = -INFINITY;
+                        }
+                } else {  // padded keys of the tile as well: bit x of this half's word
+                    const uint64_t wl = kw >> (4 * half);
+#pragma unroll
+                    for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+                        for (int i = 0; i < 16; i++) {
+                            const int x = 32 * kb + 8 * (i / 4) + (i % 4);
+                            if (x < x_lo || x >= x_hi || !((wl >> x) & 1)) s[kb][i] = -INFINITY;
+                        }
+                }
             }
         };
         mask();
@@ -690,6 +710,14 @@ __global__ __launch_bounds__(THREADS, 1) void step_bf16_kernel(const StepArgs a)
             __asm__ volatile("; V stage issued" ::: "memory");
         }
         if (j < nT) {
+            // With a key mask, tile j + 1's word is read now, its latency
+            // hidden behind this V phase.
+            uint64_t kw_next = ~0ull;
+            if (KP && j + 1 < nT) {
+                Cursor cn = cc;
+                cur_next(cn);
+                kw_next = key_word(cn);
+            }
             v_phase(cc.kt, kc);
             if (j + 1 < nT) {  // the compute cursor moves on to tile j + 1
                 const int e_was = cc.e;
@@ -700,6 +728,7 @@ __global__ __launch_bounds__(THREADS, 1) void step_bf16_kernel(const StepArgs a)
                     row_bounds(rl64(cb_kpos, cc.e));
                 }
             }
+            kw = kw_next;
         }
         // Everything but this phase's batch has landed: for G0 that is
         // K_{j+1} (stage j+1, read from phase 2j+2 on), for G1 V_{j+1}
@@ -784,23 +813,23 @@ __global__ __launch_bounds__(THREADS, 1) void step_bf16_kernel(const StepArgs a)
     }
 }
 
-template <typename E>
+template <typename E, bool KP>
 hipError_t launch_step16(const StepArgs& a, hipStream_t stream) {
     const int64_t nwg = (int64_t)a.n_qtiles * a.Hq * a.n_pairs;
     if (nwg == 0) return hipSuccess;
     const dim3 grid((unsigned)nwg), block(THREADS);
     if (a.works) {  // the one-launch ring reads the packed V^T
         if (!a.vt) return hipErrorInvalidValue;
-        if (a.d == 128) step_bf16_kernel<E, 128, true, true><<<grid, block, 0, stream>>>(a);
-        else if (a.d == 64) step_bf16_kernel<E, 64, true, true><<<grid, block, 0, stream>>>(a);
+        if (a.d == 128) step_bf16_kernel<E, 128, true, true, KP><<<grid, block, 0, stream>>>(a);
+        else if (a.d == 64) step_bf16_kernel<E, 64, true, true, KP><<<grid, block, 0, stream>>>(a);
         else return hipErrorInvalidValue;
     } else if (a.vt) {
-        if (a.d == 128) step_bf16_kernel<E, 128, true, false><<<grid, block, 0, stream>>>(a);
-        else if (a.d == 64) step_bf16_kernel<E, 64, true, false><<<grid, block, 0, stream>>>(a);
+        if (a.d == 128) step_bf16_kernel<E, 128, true, false, KP><<<grid, block, 0, stream>>>(a);
+        else if (a.d == 64) step_bf16_kernel<E, 64, true, false, KP><<<grid, block, 0, stream>>>(a);
         else return hipErrorInvalidValue;
     } else {
-        if (a.d == 128) step_bf16_kernel<E, 128, false, false><<<grid, block, 0, stream>>>(a);
-        else if (a.d == 64) step_bf16_kernel<E, 64, false, false><<<grid, block, 0, stream>>>(a);
+        if (a.d == 128) step_bf16_kernel<E, 128, false, false, KP><<<grid, block, 0, stream>>>(a);
+        else if (a.d == 64) step_bf16_kernel<E, 64, false, false, KP><<<grid, block, 0, stream>>>(a);
         else return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -809,7 +838,9 @@ hipError_t launch_step16(const StepArgs& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_step_bf16(const StepArgs& a, hipStream_t stream) {
-    return a.f16 ? launch_step16<f16>(a, stream) : launch_step16<bf16>(a, stream);
+    // KP: with a key-padding mask (the unmasked kernels carry none of its code)
+    if (a.kbits) return a.f16 ? launch_step16<f16, true>(a, stream) : launch_step16<bf16, true>(a, stream);
+    return a.f16 ? launch_step16<f16, false>(a, stream) : launch_step16<bf16, false>(a, stream);
 }
 
 }  // namespace ra

@@ -15,6 +15,7 @@ namespace {
 
 constexpr int TQ = kF32TileQ;  // 64 rows = one wave
 constexpr int TK = kF32TileK;  // 64 keys per tile
+static_assert(TK == 64, "one 64-bit key-validity word per key tile");
 
 template <int DP>
 __global__ __launch_bounds__(64) void step_f32_kernel(const StepArgs a) {
@@ -89,6 +90,8 @@ __global__ __launch_bounds__(64) void step_f32_kernel(const StepArgs a) {
         __syncthreads();
         float s[TK];
         float mt = -INFINITY;
+        // Key-padding mask: bit j of the tile's validity word (TK = 64 keys).
+        const uint64_t kw = a.kbits ? *(const uint64_t*)(a.kbits + pd.kb_off + 2 * kt) : ~0ull;
 #pragma unroll
         for (int j = 0; j < TK; j++) {
             float acc = 0.f;
@@ -97,7 +100,7 @@ __global__ __launch_bounds__(64) void step_f32_kernel(const StepArgs a) {
             acc *= a.scale;
             const int64_t w = (int64_t)kt * TK + j;
             const int64_t tk = pd.k_pos0 + w * a.pos_stride;
-            bool ok = w < a.Bk;
+            bool ok = w < a.Bk && ((kw >> j) & 1);
             if (a.mask != kMaskNone) ok = ok && tk <= t;
             if (a.mask == kMaskDoc) ok = ok && tk >= ds;
             s[j] = ok ? acc : -INFINITY;

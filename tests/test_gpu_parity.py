@@ -148,6 +148,19 @@ def test_f32_fully_masked_step_leaves_empty_state(ra):
     assert (out == 0).all() and torch.isneginf(lse).all()
 
 
+def _key_valid(T, seed, frac=0.3):
+    """Seeded key-padding mask: about frac of the keys padded at random, a
+    run of 150 padded keys (whole 64-key tiles with no key left), key 0
+    padded (under causal masks row 0 keeps no key) and the last key kept."""
+    g = torch.Generator().manual_seed(seed)
+    kv = torch.rand(T, generator=g) >= frac
+    start = int(torch.randint(0, max(T - 150, 1), (1,), generator=g))
+    kv[start:start + 150] = False
+    kv[0] = False
+    kv[-1] = True
+    return kv
+
+
 # ---------------------------------------------------------------------------
 # bf16 matrix-core path on small shapes (several tiles, ragged tails)
 # ---------------------------------------------------------------------------
@@ -190,6 +203,94 @@ def test_16bit_forward_small(ra, case, dt):
     out16 = ra.forward(q, k, v, n_blocks=N, layout=lay, causal=mask == 1, cu_seqlens=docs, max_ring_passes=P)
     assert out16.dtype == TORCH16[dt]
     assert torch.equal(out16, out.to(TORCH16[dt]))
+
+
+KP_SMALL = [
+    # T, N, Hq, Hkv, d, layout, mask, P, docs
+    (888, 3, 4, 2, 128, 0, 1, 3, None),       # ragged tiles
+    (888, 3, 4, 1, 128, 1, 1, 3, None),       # striped
+    (1200, 4, 4, 2, 64, 0, 0, 4, None),       # no mask beyond the padding
+    (960, 4, 2, 2, 128, 0, 2, 4, [0, 100, 101, 400, 700, 960]),
+    (1200, 4, 4, 2, 64, 1, 1, 2, None),       # striped with a pass limit
+]
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+@pytest.mark.parametrize("case", range(len(KP_SMALL)))
+def test_16bit_forward_key_padding(ra, case, dt):
+    T, N, Hq, Hkv, d, layout, mask, P, docs = KP_SMALL[case]
+    _say(dt, "key padding", KP_SMALL[case])
+    qh, kh, vh = W.random_qkv(T, Hq, Hkv, d, dt, 3000 + case)
+    kv = _key_valid(T, 3000 + case)
+    q, k, v = _dev(qh, kh, vh)
+    lay = "striped" if layout == 1 else "contiguous"
+    kw = dict(n_blocks=N, layout=lay, causal=mask == 1, cu_seqlens=docs, max_ring_passes=P, out_dtype=torch.float32,
+              return_lse=True)
+    ref = oracle.forward(qh, kh, vh, n_blocks=N, layout=layout, mask=mask, max_ring_passes=P, cu_seqlens=docs,
+                         key_valid=kv)
+    for prefetch in (False, True):
+        out, lse = ra.forward(q, k, v, key_valid=kv.cuda(), prefetch=prefetch, **kw)
+        _check_bf16(out.cpu().double().numpy(), ref["out"], "out prefetch=%d" % prefetch, dt)
+        got_lse = lse.cpu().double().numpy()
+        empty = np.isneginf(ref["lse"])
+        assert np.array_equal(np.isneginf(got_lse), empty)
+        assert np.abs(got_lse[~empty] - ref["lse"][~empty]).max() <= 1e-3
+    # an all-true mask changes nothing, bit for bit
+    a_ = ra.forward(q, k, v, **kw)
+    b_ = ra.forward(q, k, v, key_valid=torch.ones(T, dtype=torch.bool, device="cuda"), **kw)
+    assert torch.equal(a_[0], b_[0]) and torch.equal(a_[1], b_[1])
+
+
+def test_f32_forward_key_padding(ra):
+    T, N, H, d = 512, 4, 2, 40
+    qh, kh, vh = W.random_qkv(T, H, H, d, "f32", 3100)
+    kv = _key_valid(T, 3100)
+    _say("f32 key padding", T, N, H, d)
+    for mask, lay in ((1, "contiguous"), (1, "striped"), (0, "contiguous")):
+        out, lse = ra.forward(*_dev(qh, kh, vh), n_blocks=N, layout=lay, causal=mask == 1, key_valid=kv.cuda(),
+                              return_lse=True)
+        ref = oracle.forward(qh, kh, vh, n_blocks=N, layout=1 if lay == "striped" else 0, mask=mask, key_valid=kv)
+        assert np.abs(out.cpu().double().numpy() - ref["out"]).max() <= F32_TOL
+
+
+def test_pack_key_mask_bits(ra):
+    """Bit words of ring_attn_pack_key_mask, from a strided view, against the
+    definition (bit w % 32 of word w / 32 is key w's flag, zero past n)."""
+    g = torch.Generator().manual_seed(3200)
+    for n in (1, 63, 64, 65, 300):
+        full = torch.rand(3 * n, generator=g) > 0.5
+        view = full.cuda()[1::3]
+        bits = ra.ring_attn_pack_key_mask(view).cpu().numpy().view(np.uint32)
+        flags = full[1::3].numpy()
+        want = np.zeros(2 * ((n + 63) // 64), dtype=np.uint32)
+        for w in range(n):
+            want[w // 32] |= np.uint32(int(flags[w]) << (w % 32))
+        assert np.array_equal(bits, want), n
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_16bit_step_api_key_bits(ra, dt):
+    """ring_attn_step with a key block's packed padding bits (striped block
+    as strided views): the state must equal the oracle's block state."""
+    T, N, Hq, d = 1024, 4, 2, 128
+    qh, kh, vh = W.random_qkv(T, Hq, Hq, d, dt, 3300)
+    kv = _key_valid(T, 3300)
+    q, k, v = _dev(qh, kh, vh)
+    i, j = 2, 1
+    B = T // N
+    O = torch.empty(Hq, B, d, device="cuda")
+    m = torch.empty(Hq, B, device="cuda")
+    l = torch.empty(Hq, B, device="cuda")
+    bits = ra.ring_attn_pack_key_mask(kv.cuda()[j::N])
+    ra.ring_attn_step(q[i::N], k[j::N], v[j::N], O, m, l, first_step=True, scale=1 / math.sqrt(d),
+                      mask_mode=ra.RA_MASK_CAUSAL, q_offset=i, kv_offset=j, pos_stride=N, key_bits=bits)
+    ref = oracle.block(qh[i::N], kh[j::N], vh[j::N], np.arange(B) * N + i, np.arange(B) * N + j,
+                       mask=oracle.MASK_CAUSAL, key_valid=kv[j::N])
+    got_l = l.cpu().double().numpy()
+    ok = ref["l"] > 0
+    assert np.array_equal(got_l > 0, ok)
+    out = (O.cpu().double().numpy() / np.where(ok, got_l, 1)[..., None])
+    _check_bf16(out[ok], ref["out"][ok], "key-bits step", dt)
 
 
 def test_bf16_ring_late_score_jumps(ra):
@@ -367,12 +468,14 @@ def _sample_rows(w, rng, n=48):
     return np.asarray(heads), np.asarray(toks)
 
 
-@pytest.mark.parametrize("name,dt", [("causal32k_h32_d128_8blk", "bf16"),
-                                     ("gqa_striped64k_h32kv8_d128_16blk", "bf16"),
-                                     ("varlen_packed128k_h32_d128_8blk_p4", "bf16"),
-                                     ("causal32k_h32_d128_8blk", "f16")])
-def test_long_workload_sampled_rows(ra, name, dt):
+@pytest.mark.parametrize("name,dt,padded", [("causal32k_h32_d128_8blk", "bf16", False),
+                                            ("gqa_striped64k_h32kv8_d128_16blk", "bf16", False),
+                                            ("varlen_packed128k_h32_d128_8blk_p4", "bf16", False),
+                                            ("causal32k_h32_d128_8blk", "f16", False),
+                                            ("gqa_striped64k_h32kv8_d128_16blk", "bf16", True)])
+def test_long_workload_sampled_rows(ra, name, dt, padded):
     w = dataclasses.replace(W.WORKLOADS[name], dtype=dt)
+    kv = _key_valid(w.T, w.seed, frac=0.1) if padded else None
     _say(name, "generating inputs")
     x = W.make_inputs(w)
     if w.packed:
@@ -384,9 +487,10 @@ def test_long_workload_sampled_rows(ra, name, dt):
     _say(name, "forward")
     out, lse, st = ra.forward(q, k, v, n_blocks=w.n_blocks, layout="striped" if w.layout else "contiguous",
                               causal=w.mask == 1, cu_seqlens=cu, max_ring_passes=w.max_ring_passes,
-                              out_dtype=torch.float32, return_lse=True, return_stats=True)
+                              out_dtype=torch.float32, return_lse=True, return_stats=True,
+                              key_valid=None if kv is None else kv.cuda())
     torch.cuda.synchronize()
-    assert torch.isfinite(out).all() and torch.isfinite(lse).all()
+    assert torch.isfinite(out).all() and (kv is not None or torch.isfinite(lse).all())
     rng = np.random.default_rng(w.seed)
     heads, toks = _sample_rows(w, rng)
     group = w.Hq // w.Hkv
@@ -399,10 +503,13 @@ def test_long_workload_sampled_rows(ra, name, dt):
     _say(name, "oracle on", len(toks), "rows")
     ref = oracle.forward(qs, ks, vs, n_blocks=w.n_blocks, layout=w.layout, mask=w.mask,
                          max_ring_passes=w.max_ring_passes, cu_seqlens=cu, scale=w.scale,
-                         rows=(np.array([idx[int(h)] for h in heads]), toks))
+                         rows=(np.array([idx[int(h)] for h in heads]), toks), key_valid=kv)
     got = out.cpu()[toks, heads].double().numpy()
     _check_bf16(got, ref["out"], name, dt)
-    assert np.abs(lse.cpu()[heads, toks].double().numpy() - ref["lse"]).max() <= 1e-3
+    got_lse = lse.cpu()[heads, toks].double().numpy()
+    empty = np.isneginf(ref["lse"])
+    assert np.array_equal(np.isneginf(got_lse), empty)
+    assert np.abs(got_lse[~empty] - ref["lse"][~empty]).max() <= 1e-3
     tal = oracle.tallies(w.T, w.n_blocks, layout=w.layout, mask=w.mask, max_ring_passes=w.max_ring_passes,
                          cu_seqlens=cu, tile_q=st["tile_q"], tile_k=st["tile_k"])
     for key, val in tal.items():

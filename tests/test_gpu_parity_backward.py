@@ -49,6 +49,74 @@ def _check(got, ref, what, dt="bf16"):
     assert diff.max() <= tmax and diff.mean() <= tmean, (what, dt, diff.max(), diff.mean())
 
 
+U16 = {"bf16": 2.0 ** -8, "f16": 2.0 ** -11}  # unit roundoff of the 16-bit type (8 / 11 significant bits)
+
+
+def _allowed(T, N, layout, mask, P, docs, key_valid=None):
+    """[T, T] allowed (query, key) pairs: ring visibility, mask, key padding."""
+    t = np.arange(T)
+    B = T // N
+    blk = t % N if layout == 1 else t // B
+    ok = (blk[:, None] - blk[None, :]) % N < min(P, N)
+    if mask >= 1:
+        ok &= t[None, :] <= t[:, None]
+    if mask == 2:
+        doc = np.searchsorted(np.asarray(docs[1:]), t, side="right")
+        ok &= doc[:, None] == doc[None, :]
+    if key_valid is not None:
+        ok &= np.asarray(key_valid, dtype=bool)[None, :]
+    return ok
+
+
+def _rounding_bounds(qh, kh, vh, gh, N, layout, mask, P, docs, dt, key_valid=None):
+    """First-order bounds on the 16-bit backward's error, per gradient element.
+    With u the unit roundoff of the 16-bit type and, per (query t, key j),
+    P, dP = dout.v, D = dout.out, dS = P (dP - D) from the fp64 oracle:
+      the kernels round dS to 16 bits (and the dK side may use a 16-bit P),
+      <= 2 u |dS|;  D comes from the forward's 16-bit out, whose error is
+      <= u |out| (its rounding) + u sum_j P |v_j| (the forward's 16-bit P),
+      so |dD| <= u sum_c |dout_c| (|out_c| + (P |v|)_c) and dS moves by P |dD|;
+      dv uses a 16-bit P: <= u P |dout|.
+    Hence |d dq_t| <= scale sum_j w_tj |k_j|, |d dk_j| <= scale sum_t w_tj |q_t|
+    with w = 2 u |dS| + P |dD|, and |d dv_j| <= u sum_t P_tj |dout_t|.  fp32
+    accumulation adds terms of order 2^-24 times the sums, far below these."""
+    T, Hq, d = qh.shape
+    Hkv = kh.shape[1]
+    scale = 1.0 / np.sqrt(d)
+    q, k, v, g = (x.double().numpy() for x in (qh, kh, vh, gh))
+    ref = oracle.forward(qh, kh, vh, n_blocks=N, layout=layout, mask=mask, max_ring_passes=P, cu_seqlens=docs,
+                         key_valid=key_valid)
+    out, lse = ref["out"], ref["lse"]
+    ok = _allowed(T, N, layout, mask, P, docs, key_valid)
+    u = U16[dt]
+    bq, bk, bv = np.zeros((T, Hq, d)), np.zeros((T, Hkv, d)), np.zeros((T, Hkv, d))
+    grp = Hq // Hkv
+    for h in range(Hq):
+        gk = h // grp
+        use = ok & np.isfinite(lse[h])[:, None]
+        s = scale * (q[:, h] @ k[:, gk].T)
+        Pm = np.where(use, np.exp(np.where(use, s - lse[h][:, None], -np.inf)), 0.0)
+        dS = Pm * (g[:, h] @ v[:, gk].T - (g[:, h] * out[:, h]).sum(1)[:, None])
+        dD = u * (np.abs(g[:, h]) * (np.abs(out[:, h]) + Pm @ np.abs(v[:, gk]))).sum(1)[:, None]
+        w = 2 * u * np.abs(dS) + Pm * dD
+        bq[:, h] += scale * (w @ np.abs(k[:, gk]))
+        bk[:, gk] += scale * (w.T @ np.abs(q[:, h]))
+        bv[:, gk] += u * (Pm.T @ np.abs(g[:, h]))
+    return bq, bk, bv
+
+
+def _check_bound(got, ref, bound, what):
+    """err <= bound, widened by 2^-10 of itself and 1e-6 for the fp32 terms
+    (P itself carries ~1e-7 relative error before its 16-bit rounding).  A
+    key that one query reaches has dv = P dout: its error is one rounding of
+    P, so the bound is approached there by construction."""
+    err = np.abs(got - ref)
+    lim = bound * (1 + 2.0 ** -10) + 1e-6
+    ratio = float((err / lim).max())
+    _say(what, "max err", float(err.max()), "max err / bound", ratio)
+    assert (err <= lim).all(), (what, float(err.max()), ratio)
+
+
 BWD_SMALL = [
     # T, N, Hq, Hkv, d, layout, mask, P, docs, forward out dtype
     (888, 3, 4, 2, 128, 0, 1, 3, None, "bf16"),     # B = 296: ragged tiles on both sides
@@ -86,12 +154,63 @@ def test_16bit_backward_small(ra, case, dt):
     kw = dict(N=N, lay=lay, mask=mask, P=P, docs=docs, out_dtype=t16 if odt == "bf16" else torch.float32)
     dq, dk, dv = _fwd_bwd(ra, q, k, v, g, **kw)
     ref = oracle.backward(qh, kh, vh, gh, n_blocks=N, layout=layout, mask=mask, max_ring_passes=P, cu_seqlens=docs)
-    for name, got, r in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
+    bounds = _rounding_bounds(qh, kh, vh, gh, N, layout, mask, P, docs, dt)
+    for name, got, r, bd in zip(("dq", "dk", "dv"), (dq, dk, dv), ref, bounds):
         _check(got.cpu().double().numpy(), r, name, dt)
+        _check_bound(got.cpu().double().numpy(), r, bd, name)
     # 16-bit gradients: the same values rounded to nearest even
     bq, bk, bv = _fwd_bwd(ra, q, k, v, g, grad_dtype=t16, **kw)
     for got, f in zip((bq, bk, bv), (dq, dk, dv)):
         assert got.dtype == t16 and torch.equal(got, f.to(t16))
+
+
+KP_BWD = [
+    # T, N, Hq, Hkv, d, layout, mask, P, docs
+    (888, 3, 4, 2, 128, 0, 1, 3, None),
+    (888, 3, 4, 1, 128, 1, 1, 3, None),
+    (1200, 4, 2, 2, 64, 0, 0, 4, None),
+    (960, 4, 2, 2, 128, 0, 2, 4, [0, 100, 101, 400, 700, 960]),
+]
+
+
+def _key_valid(T, seed, frac=0.3):
+    """About frac of the keys padded, a run of 150 (whole empty 64-key
+    tiles), key 0 (an empty row under causal masks); the last key kept."""
+    g = torch.Generator().manual_seed(seed)
+    kv = torch.rand(T, generator=g) >= frac
+    start = int(torch.randint(0, max(T - 150, 1), (1,), generator=g))
+    kv[start:start + 150] = False
+    kv[0] = False
+    kv[-1] = True
+    return kv
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+@pytest.mark.parametrize("case", range(len(KP_BWD)))
+def test_16bit_backward_key_padding(ra, case, dt):
+    T, N, Hq, Hkv, d, layout, mask, P, docs = KP_BWD[case]
+    _say(dt, "backward key padding", KP_BWD[case])
+    t16 = TORCH16[dt]
+    qh, kh, vh = W.random_qkv(T, Hq, Hkv, d, dt, 4000 + case)
+    gh = W.random_dout(T, Hq, d, dt, 4000 + case)
+    kv = _key_valid(T, 4000 + case)
+    q, k, v, g = (x.cuda() for x in (qh, kh, vh, gh))
+    lay = "striped" if layout == 1 else "contiguous"
+    kvd = kv.cuda()
+    out, lse = ra.forward(q, k, v, n_blocks=N, layout=lay, causal=mask == 1, cu_seqlens=docs, max_ring_passes=P,
+                          out_dtype=t16, return_lse=True, key_valid=kvd)
+    dq, dk, dv = ra.backward(q, k, v, out, lse, g, n_blocks=N, layout=lay, causal=mask == 1, cu_seqlens=docs,
+                             max_ring_passes=P, key_valid=kvd)
+    ref = oracle.backward(qh, kh, vh, gh, n_blocks=N, layout=layout, mask=mask, max_ring_passes=P, cu_seqlens=docs,
+                          key_valid=kv)
+    # Rows left with two or three keys carry large dS: the per-element bound
+    # from the arithmetic is the bar there, with the mean bar of the others.
+    bounds = _rounding_bounds(qh, kh, vh, gh, N, layout, mask, P, docs, dt, key_valid=kv)
+    for name, got, r, bd in zip(("dq", "dk", "dv"), (dq, dk, dv), ref, bounds):
+        gn = got.cpu().double().numpy()
+        _check_bound(gn, r, bd, name)
+        assert np.abs(gn - r).mean() <= TOL16[dt][1], (name, float(np.abs(gn - r).mean()))
+    assert not dk[~kvd].any() and not dv[~kvd].any()
 
 
 def test_bf16_backward_packed_qkv_views(ra):

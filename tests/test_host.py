@@ -148,8 +148,8 @@ def test_forward_and_step_refuse_bad_arguments_before_any_gpu_work(lib):
     R = ctypes.byref
 
     def fwd(qq=q, kk=k, vv=v, n_blocks=4, layout=0, mask=1, P=4, cu=None, n_docs=0, scale=0.1, ws_bytes=1 << 40,
-            out_dtype=ra.RA_BF16, o=out):
-        return F(R(qq), R(kk), R(vv), o, out_dtype, None, n_blocks, layout, mask, P, cu, n_docs, scale, 0, ws,
+            out_dtype=ra.RA_BF16, o=out, kv=None):
+        return F(R(qq), R(kk), R(vv), o, out_dtype, None, n_blocks, layout, mask, P, cu, n_docs, kv, scale, 0, ws,
                  ws_bytes, None, None)
 
     assert fwd(n_blocks=5) == ra.RA_E_ARG             # 64 % 5
@@ -177,12 +177,19 @@ def test_forward_and_step_refuse_bad_arguments_before_any_gpu_work(lib):
 
     S = lib.ring_attn_step
     state = ctypes.c_void_p(1 << 23)
-    assert S(R(q), R(k), R(v), state, state, state, 1, -1.0, 0, 0, 0, 1, None, 0, None, None) == ra.RA_E_ARG
-    assert S(R(q), R(k), R(v), None, state, state, 1, 0.1, 0, 0, 0, 1, None, 0, None, None) == ra.RA_E_ARG
-    assert S(R(q), R(k), R(v), state, state, state, 1, 0.1, 0, 0, 0, 0, None, 0, None, None) == ra.RA_E_ARG
-    assert S(R(q), R(k), R(v), state, state, state, 1, 0.1, 2, 0, 0, 1, None, 0, None, None) == ra.RA_E_ARG
-    assert S(R(q), R(_fake(64, 2, 64)), R(v), state, state, state, 1, 0.1, 0, 0, 0, 1, None, 0, None,
+    assert S(R(q), R(k), R(v), state, state, state, 1, -1.0, 0, 0, 0, 1, None, 0, None, None, None) == ra.RA_E_ARG
+    assert S(R(q), R(k), R(v), None, state, state, 1, 0.1, 0, 0, 0, 1, None, 0, None, None, None) == ra.RA_E_ARG
+    assert S(R(q), R(k), R(v), state, state, state, 1, 0.1, 0, 0, 0, 0, None, 0, None, None, None) == ra.RA_E_ARG
+    assert S(R(q), R(k), R(v), state, state, state, 1, 0.1, 2, 0, 0, 1, None, 0, None, None, None) == ra.RA_E_ARG
+    assert S(R(q), R(_fake(64, 2, 64)), R(v), state, state, state, 1, 0.1, 0, 0, 0, 1, None, 0, None, None,
              None) == ra.RA_E_ARG
+    bits_misaligned = ctypes.c_void_p((1 << 24) + 4)
+    assert S(R(q), R(k), R(v), state, state, state, 1, 0.1, 0, 0, 0, 1, None, 0, bits_misaligned, None,
+             None) == ra.RA_E_ARG
+    P_ = lib.ring_attn_pack_key_mask
+    assert P_(None, 64, 1, ctypes.c_void_p(1 << 24), None) == ra.RA_E_ARG
+    assert P_(ctypes.c_void_p(1 << 23), 64, 0, ctypes.c_void_p(1 << 24), None) == ra.RA_E_ARG
+    assert P_(ctypes.c_void_p(1 << 23), 64, 1, bits_misaligned, None) == ra.RA_E_ARG
 
 
 def test_workspace_size_grows_with_prefetch(lib):
@@ -202,7 +209,7 @@ def test_backward_refuses_bad_arguments_before_any_gpu_work(lib):
     def bwd(qq=q, kk=k, vv=v, oo=out, gg=dout, ll=lse, dq=g, n_blocks=4, layout=0, mask=1, P=4, cu=None,
             n_docs=0, scale=0.1, ws_bytes=1 << 40, grad=ra.RA_F32):
         return lib.ring_attn_backward(R(qq), R(kk), R(vv), R(oo), R(gg), ll, dq, g, g, grad, n_blocks, layout,
-                                      mask, P, cu, n_docs, scale, ws, ws_bytes, None)
+                                      mask, P, cu, n_docs, None, scale, ws, ws_bytes, None)
 
     assert bwd(n_blocks=5) == ra.RA_E_ARG             # 64 % 5
     assert bwd(P=0) == ra.RA_E_ARG
