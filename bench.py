@@ -1,7 +1,7 @@
 """Benchmark of the one-GPU ring-attention forward.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--prefetch]
-                    [--backward] [--no-cpu-baseline]
+                    [--backward] [--no-cpu-baseline] [--dtype bf16|f16] [--key-padding FRAC]
 
 A step is one ring_attn_forward call: every ring step of every virtual device
 plus the fused finalize, on synthetic bf16 inputs already resident in HBM.
@@ -19,10 +19,15 @@ pairs the mask lets through.  Prints one JSON line.
 kernel and the dk/dv kernel), with the forward's out and lse and a seeded
 dout resident in HBM; FLOP = 10 * d * Hq * allowed pairs (the five
 contractions of the backward: S, dP, dV, dK, dQ), fp32 gradients.
+
+--dtype f16 runs the same shapes in fp16.  --key-padding FRAC adds a seeded
+key-padding mask (about FRAC of the keys padded, plus a run of whole padded
+tiles); the allowed pairs, and so the FLOP, then count real keys only.
 """
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -107,6 +112,10 @@ def main():
     ap.add_argument("--prefetch", action="store_true")
     ap.add_argument("--backward", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--dtype", choices=["bf16", "f16"], default="bf16",
+                    help="16-bit input type (the workloads are quoted in bf16; f16 runs the same shapes)")
+    ap.add_argument("--key-padding", type=float, default=0.0, metavar="FRAC",
+                    help="add a seeded key-padding mask padding about FRAC of the keys (full causal rings only)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="instead of the benchmark, run a plain device copy of BYTES bytes 5 times "
                          "(reference reading for the HBM byte counters)")
@@ -136,6 +145,8 @@ def main():
     if w.dtype != "bf16":
         print("bench workloads are the bf16 long-context ones", file=sys.stderr)
         sys.exit(2)
+    w = dataclasses.replace(w, dtype=args.dtype)
+    t16 = torch.bfloat16 if args.dtype == "bf16" else torch.float16
     x = W.make_inputs(w)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -147,21 +158,31 @@ def main():
     cu = x.get("cu_seqlens")
     n_docs = 0 if cu is None else cu.numel() - 1
     plan = ra.ring_attn_plan(w.T, w.n_blocks, layout=w.layout, mask_mode=w.mask,
-                             max_ring_passes=w.max_ring_passes, cu_seqlens_host=cu, dtype=torch.bfloat16,
+                             max_ring_passes=w.max_ring_passes, cu_seqlens_host=cu, dtype=t16,
                              head_dim=w.d)
+    key_valid = None
+    if args.key_padding > 0:
+        if w.mask != 1 or w.max_ring_passes < w.n_blocks:
+            print("--key-padding is measured on full causal rings", file=sys.stderr)
+            sys.exit(2)
+        kv = W.random_key_valid(w.T, w.seed, args.key_padding)
+        # allowed pairs per head: a real key t' is seen by the queries t >= t'
+        plan["allowed_pairs"] = int((kv.to(torch.int64) * (w.T - torch.arange(w.T))).sum())
+        key_valid = kv.to(dev)
+        args.no_cpu_baseline = True  # the CPU baseline leg samples the unpadded workload
     flop = 4.0 * w.d * w.Hq * plan["allowed_pairs"]
-    out = torch.empty(w.T, w.Hq, w.d, device=dev, dtype=torch.bfloat16)
+    out = torch.empty(w.T, w.Hq, w.d, device=dev, dtype=t16)
     lse = torch.empty(w.Hq, w.T, device=dev, dtype=torch.float32)
     ws = torch.empty(ra.ring_attn_forward_workspace_size(q, k, w.n_blocks, n_docs, args.prefetch), device=dev,
                      dtype=torch.uint8)
     stream = torch.cuda.current_stream()
     if args.backward:
-        return bench_backward(args, ra, W, w, x, q, k, v, cu, out, lse, plan, stream)
+        return bench_backward(args, ra, W, w, x, q, k, v, cu, out, lse, plan, stream, key_valid)
 
     def step():
         ra.ring_attn_forward(q, k, v, out, lse, n_blocks=w.n_blocks, layout=w.layout, mask_mode=w.mask,
-                             max_ring_passes=w.max_ring_passes, cu_seqlens_host=cu, scale=w.scale,
-                             prefetch=args.prefetch, workspace=ws, stream=stream)
+                             max_ring_passes=w.max_ring_passes, cu_seqlens_host=cu, key_valid=key_valid,
+                             scale=w.scale, prefetch=args.prefetch, workspace=ws, stream=stream)
 
     for _ in range(args.warmup):
         step()
@@ -180,7 +201,8 @@ def main():
     n_launch = min(w.max_ring_passes, w.n_blocks) if args.prefetch else 1
     value = flop / (ms_wall * 1e-3) / 1e12
     achieved = flop / (ms_event * 1e-3) / 1e12
-    traffic = traffic_from_profile(w.name, args.prefetch)
+    # the counter record is the bf16 kernel without a key mask
+    traffic = traffic_from_profile(w.name, args.prefetch) if args.dtype == "bf16" and key_valid is None else None
 
     res = {
         "metric": "causal-adjusted attention TFLOP/s and % bf16 MFMA peak, 32K ring fwd, 1 GPU",
@@ -193,12 +215,12 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": args.dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "tokens": w.T, "q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": w.d,
                    "ring_blocks": w.n_blocks, "layout": ["contiguous", "striped"][w.layout],
                    "mask": ["none", "causal", "doc-causal"][w.mask], "max_ring_passes": w.max_ring_passes,
-                   "prefetch": bool(args.prefetch), "flop_per_step": flop,
+                   "prefetch": bool(args.prefetch), "key_padding": args.key_padding, "flop_per_step": flop,
                    "allowed_pairs_per_head": plan["allowed_pairs"]},
         "pct_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         # achieved: the forward's FLOP over its event-timed duration on the
@@ -214,7 +236,7 @@ def main():
     print(json.dumps(res), flush=True)
 
 
-def bench_backward(args, ra, W, w, x, q, k, v, cu, out, lse, plan, stream):
+def bench_backward(args, ra, W, w, x, q, k, v, cu, out, lse, plan, stream, key_valid=None):
     import torch
 
     dev = q.device
@@ -222,10 +244,10 @@ def bench_backward(args, ra, W, w, x, q, k, v, cu, out, lse, plan, stream):
     ws_f = torch.empty(ra.ring_attn_forward_workspace_size(q, k, w.n_blocks, n_docs, False), device=dev,
                        dtype=torch.uint8)
     ra.ring_attn_forward(q, k, v, out, lse, n_blocks=w.n_blocks, layout=w.layout, mask_mode=w.mask,
-                         max_ring_passes=w.max_ring_passes, cu_seqlens_host=cu, scale=w.scale, prefetch=False,
-                         workspace=ws_f, stream=stream)
+                         max_ring_passes=w.max_ring_passes, cu_seqlens_host=cu, key_valid=key_valid, scale=w.scale,
+                         prefetch=False, workspace=ws_f, stream=stream)
     del ws_f
-    dout = W.random_dout(w.T, w.Hq, w.d, "bf16", w.seed).to(dev)
+    dout = W.random_dout(w.T, w.Hq, w.d, args.dtype, w.seed).to(dev)
     dq = torch.empty(w.T, w.Hq, w.d, device=dev, dtype=torch.float32)
     dk = torch.empty(w.T, w.Hkv, w.d, device=dev, dtype=torch.float32)
     dv = torch.empty_like(dk)
@@ -235,7 +257,7 @@ def bench_backward(args, ra, W, w, x, q, k, v, cu, out, lse, plan, stream):
     def step():
         ra.ring_attn_backward(q, k, v, out, dout, lse, dq, dk, dv, n_blocks=w.n_blocks, layout=w.layout,
                               mask_mode=w.mask, max_ring_passes=w.max_ring_passes, cu_seqlens_host=cu,
-                              scale=w.scale, workspace=ws, stream=stream)
+                              key_valid=key_valid, scale=w.scale, workspace=ws, stream=stream)
 
     for _ in range(args.warmup):
         step()
@@ -263,12 +285,12 @@ def bench_backward(args, ra, W, w, x, q, k, v, cu, out, lse, plan, stream):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": args.dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "pass": "backward", "tokens": w.T, "q_heads": w.Hq, "kv_heads": w.Hkv,
                    "head_dim": w.d, "ring_blocks": w.n_blocks, "layout": ["contiguous", "striped"][w.layout],
                    "mask": ["none", "causal", "doc-causal"][w.mask], "max_ring_passes": w.max_ring_passes,
-                   "grad_dtype": "f32", "flop_per_step": flop, "allowed_pairs_per_head": plan["allowed_pairs"]},
+                   "grad_dtype": "f32", "key_padding": args.key_padding, "flop_per_step": flop, "allowed_pairs_per_head": plan["allowed_pairs"]},
         "pct_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         # the three backward kernels together, event-timed on the launch stream;
         # traffic: HBM bytes per launch of the dominant one (dk/dv) from the
@@ -276,7 +298,8 @@ def bench_backward(args, ra, W, w, x, q, k, v, cu, out, lse, plan, stream):
         "roofline": {"bound": "mfma", "kernel": "bwd_prep_kernel<__bf16> + bwd_dq_kernel<__bf16, 128, false> + " + BWD_KERNEL,
                      "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic_from_profile(w.name, False, backward=True),
+                     "traffic": traffic_from_profile(w.name, False, backward=True)
+                     if args.dtype == "bf16" and key_valid is None else None,
                      "traffic_kernel": BWD_KERNEL,
                      "event_ms_per_step": round(ms_event, 4),
                      "timing": "hip events on the launch stream around the timed backward calls"},

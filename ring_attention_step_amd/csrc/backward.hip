@@ -440,19 +440,35 @@ __global__ __launch_bounds__(DQ_THREADS, 1) void bwd_dq_kernel(const BwdArgs a) 
     // validity word of its tile (all ones without a mask).
     int kb_cur = 0;
     uint64_t kw = ~0ull;
+
     auto key_word = [&](const Cursor& c) __attribute__((always_inline)) {
         typedef const __attribute__((address_space(4))) uint64_t* cwp;
         return *(cwp)(a.kbits + kb_cur + 2 * c.kt);
     };
     auto compute = [&](const bf16* ks, const bf16* vs, const Cursor& c) __attribute__((always_inline)) {
         const int64_t w0 = (int64_t)c.kt * BW_T;
-        const bool full = c.kt != ragged_kt && c.kt >= cc_flo && c.kt <= cc_fhi && (!KP || kw == ~0ull);
+        const bool full = c.kt != ragged_kt && c.kt >= cc_flo && c.kt <= cc_fhi;
         // Allowed keys shifted by -4 half, relative to the tile (|x| <= B + 4).
         const int x_lo = w_lo - (int)w0 - 4 * half, x_hi = w_hi - (int)w0 - 4 * half;
 #pragma unroll
         for (int kb = 0; kb < 2; kb++) {
             // S^T and dP^T: keys 32 kb .. + 31 of the tile (rows) x this wave's rows.
             f32x16 s = f32x16{}, dp = f32x16{};
+            if (KP) {
+                // Key-padding mask on the matrix core: one extra 16-deep product
+                // adds -inf (padded key, A row = lane r at k = 0) or 0 to every
+                // score of key 32 kb + r (B = 1 at k = 0 for every query).
+                // Both operands are rebuilt here from a lane id the compiler cannot
+                // trace (an empty asm), so it keeps no loop-invariant copy of them.
+                int l = threadIdx.x & 63;
+                __asm__ volatile("" : "+v"(l));
+                const bool lo_half = l < 32;
+                const uint32_t word = kb ? (uint32_t)(kw >> 32) : (uint32_t)kw;
+                bf16x8 bias = bf16x8{}, one = bf16x8{};
+                bias[0] = (lo_half && !((word >> (l & 31)) & 1u)) ? to16<E>(-INFINITY) : to16<E>(0.0f);
+                one[0] = lo_half ? to16<E>(1.0f) : to16<E>(0.0f);
+                s = mfma<E>(bias, one, s);
+            }
 #pragma unroll
             for (int kc = 0; kc < D / 16; kc++) {
                 s = mfma<E>(ops.row(ks, kb, kc), qf[kc], s);
@@ -464,23 +480,20 @@ __global__ __launch_bounds__(DQ_THREADS, 1) void bwd_dq_kernel(const BwdArgs a) 
             // visible tiles take a copy without the mask (the branch holds
             // vector work only, so the accumulators stay in place).
             bf16x8 b0, b1;
-            auto softmax = [&](auto full_t, auto padded_t) __attribute__((always_inline)) {
-                constexpr bool FULL = decltype(full_t)::value, PADDED = decltype(padded_t)::value;
-                const uint64_t wl = kw >> (4 * half);  // padded keys: bit x of this half's word
+            auto softmax = [&](auto full_t) __attribute__((always_inline)) {
+                constexpr bool FULL = decltype(full_t)::value;
                 f32x16 dsv;
 #pragma unroll
                 for (int i = 0; i < 16; i++) {
                     const int x = 32 * kb + 8 * (i / 4) + (i % 4);
                     float arg = fmaf(s[i], a.c2, -lse2);
                     if (!FULL) arg = ((x >= x_lo) & (x < x_hi)) ? arg : -INFINITY;
-                    if (PADDED) arg = ((wl >> x) & 1) ? arg : -INFINITY;
                     dsv[i] = __builtin_amdgcn_exp2f(arg) * (dp[i] - drow);
                 }
                 acc_to_b<E>(dsv, b0, b1);
             };
-            if (__builtin_amdgcn_readfirstlane((int)full)) softmax(std::true_type{}, std::false_type{});
-            else if (!KP || kw == ~0ull) softmax(std::false_type{}, std::false_type{});
-            else softmax(std::false_type{}, std::true_type{});
+            if (__builtin_amdgcn_readfirstlane((int)full)) softmax(std::true_type{});
+            else softmax(std::false_type{});
             // dq^T += K^T dS^T over the two 16-key chunks of this half.
 #pragma unroll
             for (int db = 0; db < D / 32; db++) {

@@ -531,6 +531,22 @@ __global__ __launch_bounds__(THREADS, 1) void step_bf16_kernel(const StepArgs a)
         for (int db = 0; db < D / 32; db++)
             v_off[db] = vrow * D + 8 * ((4 * db + 2 * g16 + ((j16 & 3) >> 1)) ^ TL::swz_v(vrow)) + 4 * (j16 & 1);
     }
+    // Key-padding mask on the matrix core: S^T of a 32-key block starts from
+    // one extra 16-deep product whose A operand holds, for key row r (lane r,
+    // k = 0), 0 if the key is real and -inf if it is padded, and whose B
+    // operand holds 1 at k = 0 for every query: every score of a padded key
+    // becomes exactly -inf, every other score gains exactly 0.  Position-full
+    // tiles keep their mask-free softmax.
+    bf16x8 q_one = bf16x8{};
+    if (KP && half == 0) q_one[0] = to16<E>(1.0f);
+    auto s_init = [&](int kb) __attribute__((always_inline)) {
+        if (!KP) return f32x16{};
+        const uint32_t word = kb ? (uint32_t)(kw >> 32) : (uint32_t)kw;
+        const bool pad = half == 0 && !((word >> col) & 1u);
+        bf16x8 bias = bf16x8{};
+        bias[0] = pad ? to16<E>(-INFINITY) : to16<E>(0.0f);
+        return mma<E>(bias, q_one, f32x16{});
+    };
     auto k_frag = [&](const bf16* ks, int n) __attribute__((always_inline)) {
         return *(const bf16x8*)(ks + k_off[n >> 1] + 32 * D * (n & 1));
     };
@@ -552,8 +568,8 @@ __global__ __launch_bounds__(THREADS, 1) void step_bf16_kernel(const StepArgs a)
             va[i] = v_frag(i);
             ka[i] = k_frag(ks, i);
         }
-        s[0] = f32x16{};
-        s[1] = f32x16{};
+        s[0] = s_init(0);
+        s[1] = s_init(1);
 #pragma unroll
         for (int i = 0; i < NS; i++) {
             const int q = i / (D / 32), db = i % (D / 32);
@@ -568,30 +584,19 @@ __global__ __launch_bounds__(THREADS, 1) void step_bf16_kernel(const StepArgs a)
     // ks is the tile's K stage buffer, intact through this phase (the next
     // load into it is issued two phases later).
     auto v_phase = [&](int kt, const bf16* ks) __attribute__((always_inline)) {
-        const bool full = kt >= cc_flo && kt <= cc_fhi && kt != ragged_kt && (!KP || kw == ~0ull);
+        const bool full = kt >= cc_flo && kt <= cc_fhi && kt != ragged_kt;
         auto mask = [&]() __attribute__((always_inline)) {
             if (!full) {
                 // Register i of s[kb] holds tile key 32 kb + 8 (i/4) + 4 half + i%4;
                 // the allowed keys shifted by -4 half leave a constant to compare.
                 const int x_lo = w_lo - kt * BK - 4 * half, x_hi = w_hi - kt * BK - 4 * half;
-                if (!KP || kw == ~0ull) {
 #pragma unroll
-                    for (int kb = 0; kb < 2; kb++)
+                for (int kb = 0; kb < 2; kb++)
 #pragma unroll
-                        for (int i = 0; i < 16; i++) {
-                            const int x = 32 * kb + 8 * (i / 4) + (i % 4);
-                            if (x < x_lo || x >= x_hi) s[kb][i] = -INFINITY;
-                        }
-                } else {  // padded keys of the tile as well: bit x of this half's word
-                    const uint64_t wl = kw >> (4 * half);
-#pragma unroll
-                    for (int kb = 0; kb < 2; kb++)
-#pragma unroll
-                        for (int i = 0; i < 16; i++) {
-                            const int x = 32 * kb + 8 * (i / 4) + (i % 4);
-                            if (x < x_lo || x >= x_hi || !((wl >> x) & 1)) s[kb][i] = -INFINITY;
-                        }
-                }
+                    for (int i = 0; i < 16; i++) {
+                        const int x = 32 * kb + 8 * (i / 4) + (i % 4);
+                        if (x < x_lo || x >= x_hi) s[kb][i] = -INFINITY;
+                    }
             }
         };
         mask();
@@ -649,8 +654,8 @@ __global__ __launch_bounds__(THREADS, 1) void step_bf16_kernel(const StepArgs a)
         if (!RING) rebase();
         float lt = probs();
         if (RING && __ballot(!(lt <= kTileSumMax) || mrc == -INFINITY)) {
-            s[0] = f32x16{};
-            s[1] = f32x16{};
+            s[0] = s_init(0);
+            s[1] = s_init(1);
 #pragma unroll
             for (int i = 0; i < NS; i++)
                 s[i & 1] = mma<E>(k_frag(ks, i), qf[i >> 1], s[i & 1]);

@@ -149,16 +149,7 @@ def test_f32_fully_masked_step_leaves_empty_state(ra):
 
 
 def _key_valid(T, seed, frac=0.3):
-    """Seeded key-padding mask: about frac of the keys padded at random, a
-    run of 150 padded keys (whole 64-key tiles with no key left), key 0
-    padded (under causal masks row 0 keeps no key) and the last key kept."""
-    g = torch.Generator().manual_seed(seed)
-    kv = torch.rand(T, generator=g) >= frac
-    start = int(torch.randint(0, max(T - 150, 1), (1,), generator=g))
-    kv[start:start + 150] = False
-    kv[0] = False
-    kv[-1] = True
-    return kv
+    return W.random_key_valid(T, seed, frac)
 
 
 # ---------------------------------------------------------------------------

@@ -174,15 +174,7 @@ KP_BWD = [
 
 
 def _key_valid(T, seed, frac=0.3):
-    """About frac of the keys padded, a run of 150 (whole empty 64-key
-    tiles), key 0 (an empty row under causal masks); the last key kept."""
-    g = torch.Generator().manual_seed(seed)
-    kv = torch.rand(T, generator=g) >= frac
-    start = int(torch.randint(0, max(T - 150, 1), (1,), generator=g))
-    kv[start:start + 150] = False
-    kv[0] = False
-    kv[-1] = True
-    return kv
+    return W.random_key_valid(T, seed, frac)
 
 
 @pytest.mark.parametrize("dt", ["bf16", "f16"])

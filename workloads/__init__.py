@@ -151,5 +151,19 @@ def random_dout(T: int, Hq: int, d: int, dtype: str, seed: int):
     return _to_dtype(torch.randn(T, Hq, d, generator=g), dtype)
 
 
+def random_key_valid(T: int, seed: int, frac: float = 0.3) -> torch.Tensor:
+    """Seeded key-padding mask [T] (True = real key): each key padded with
+    probability frac, plus one run of 150 padded keys (whole 64-key tiles
+    with no real key), key 0 padded (under a causal mask row 0 keeps no
+    key) and the last key kept."""
+    g = torch.Generator().manual_seed(seed)
+    kv = torch.rand(T, generator=g) >= frac
+    start = int(torch.randint(0, max(T - 150, 1), (1,), generator=g))
+    kv[start:start + 150] = False
+    kv[0] = False
+    kv[-1] = True
+    return kv
+
+
 def random_doc_cu_seqlens(T: int, lo: int, hi: int, seed: int) -> torch.Tensor:
     return torch.from_numpy(doc_cu_seqlens(seed, T, lo, hi))
