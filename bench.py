@@ -43,11 +43,13 @@ PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak (AMD published f
 DEFAULT_WORKLOAD = "causal32k_h32_d128_8blk"
 KERNEL = "step_bf16_kernel<__bf16, 128, true, true, false>"
 BWD_KERNEL = "bwd_dkdv_kernel<__bf16, 128>"
+# The kernels' sources plus the driver that sets their launch order (a
+# traffic record is only valid for the code and the order it was taken with).
 KERNEL_SOURCES = ["ring_attention_step_amd/csrc/step_bf16.hip", "ring_attention_step_amd/csrc/plan.h",
-                  "ring_attention_step_amd/csrc/kernels.h"]
+                  "ring_attention_step_amd/csrc/kernels.h", "ring_attention_step_amd/csrc/api.hip"]
 BWD_KERNEL_SOURCES = ["ring_attention_step_amd/csrc/backward.hip", "ring_attention_step_amd/csrc/bwd_kernels.h",
                       "ring_attention_step_amd/csrc/plan.h",
-                      "ring_attention_step_amd/csrc/kernels.h"]
+                      "ring_attention_step_amd/csrc/kernels.h", "ring_attention_step_amd/csrc/api.hip"]
 
 
 def _code_only(text: str) -> str:

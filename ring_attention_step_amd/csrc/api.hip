@@ -718,7 +718,12 @@ ra_status ring_attn_backward(const ra_tensor* q, const ra_tensor* k, const ra_te
     const bool striped = layout == RA_LAYOUT_STRIPED;
     auto pos0 = [&](int64_t blk) { return striped ? blk : blk * B; };
     std::vector<std::vector<int64_t>> fwd((size_t)N), rev((size_t)N);
-    for (int64_t s = 0; s < r.passes; s++)
+    // Visiting order: the gradients are sums with no required order, so each
+    // chain takes the diagonal pair (step 0: a block with itself, where the
+    // tiles of one group stop at different points under causal masks) last;
+    // the group's tiles then walk every other block in step, and its L2
+    // serves their shared K/V (or q/dout) tiles.
+    for (int64_t s = r.passes - 1; s >= 0; s--)
         for (const StepPair& sp : plan.steps[s]) {
             fwd[sp.i].push_back(pos0(sp.j));
             rev[sp.j].push_back(pos0(sp.i));
