@@ -269,7 +269,7 @@ def ring_attn_backward_workspace_size(q, n_blocks: int, n_docs: int = 0) -> int:
 def ring_attn_backward(q, k, v, out, dout, lse, dq, dk, dv, *, n_blocks: int, layout: int, mask_mode: int,
                        max_ring_passes: int, cu_seqlens_host=None, key_valid=None, scale: float,
                        workspace: torch.Tensor, stream=None):
-    """Gradients of the ring forward: dq [T, Hq, d], dk / dv [T, Hkv, d] (contiguous, fp32 or bf16, written
+    """Gradients of the ring forward: dq [T, Hq, d], dk / dv [T, Hkv, d] (contiguous, fp32 or the inputs' 16-bit type, written
     in full) from the forward's out [T, Hq, d] and lse [Hq, T] and the output gradient dout [T, Hq, d]."""
     qt, kt, vt = _tensor(q, "q"), _tensor(k, "k"), _tensor(v, "v")
     ot, gt = _tensor(out, "out"), _tensor(dout, "dout")

@@ -102,11 +102,11 @@ struct Workspace {
     float* O = nullptr;
     float* m = nullptr;
     float* l = nullptr;
-    char* vt = nullptr;     // packed V^T of all blocks (bf16 path): [N][Hkv][d][Bp]
-    RingWork* works = nullptr;    // one-launch ring forward (bf16): N works
+    char* vt = nullptr;     // packed V^T of all blocks (16-bit path): [N][Hkv][d][Bp]
+    RingWork* works = nullptr;    // one-launch ring forward (16-bit): N works
     RingEntry* entries = nullptr; //   and up to N x N chain entries
     uint32_t* kbits = nullptr;    // key-padding bits of every block: [N][key_words(B)]
-    char* kv = nullptr;     // prefetch double buffers: K [2][N][B][Hkv][d], then V (f32) or V^T (bf16)
+    char* kv = nullptr;     // prefetch double buffers: K [2][N][B][Hkv][d], then V (f32) or V^T (16-bit)
     size_t k_half = 0;      // bytes of the K double buffer
     size_t total = 0;
 };
