@@ -132,11 +132,48 @@ BWD_SMALL = [
 ]
 
 
-def _fwd_bwd(ra, q, k, v, dout, *, N, lay, mask, P, docs, out_dtype, grad_dtype=torch.float32):
+def _fwd_bwd(ra, q, k, v, dout, *, N, lay, mask, P, docs, out_dtype, grad_dtype=torch.float32, key_valid=None):
     out, lse = ra.forward(q, k, v, n_blocks=N, layout=lay, causal=mask == 1, cu_seqlens=docs, max_ring_passes=P,
-                          out_dtype=out_dtype, return_lse=True)
+                          out_dtype=out_dtype, return_lse=True, key_valid=key_valid)
     return ra.backward(q, k, v, out, lse, dout, n_blocks=N, layout=lay, causal=mask == 1, cu_seqlens=docs,
-                       max_ring_passes=P, grad_dtype=grad_dtype)
+                       max_ring_passes=P, grad_dtype=grad_dtype, key_valid=key_valid)
+
+
+def _rounding_bounds_rows(q, k, v, g, N, layout, mask, P, docs, dt, heads, toks, key_valid=None):
+    """_rounding_bounds for a dout that is zero outside the listed (head, token)
+    rows, each head h of q reading kv head h of k / v: dq bounds of those rows
+    [n, d], and dk / dv bounds [T, H, d] summed over those rows only."""
+    T, H, d = q.shape
+    scale = 1.0 / np.sqrt(d)
+    u = U16[dt]
+    qn, kn, vn, gn = (x.double().numpy() for x in (q, k, v, g))
+    ref = oracle.forward(q, k, v, n_blocks=N, layout=layout, mask=mask, max_ring_passes=P, cu_seqlens=docs,
+                         rows=(heads, toks), key_valid=key_valid)
+    t_all = np.arange(T)
+    B = T // N
+    blk = t_all % N if layout == 1 else t_all // B
+    doc = np.searchsorted(np.asarray(docs[1:]), t_all, side="right") if mask == 2 else None
+    kvm = None if key_valid is None else np.asarray(key_valid, dtype=bool)
+    bq = np.zeros((len(toks), d))
+    bk, bv = np.zeros((T, H, d)), np.zeros((T, H, d))
+    for r, (h, t) in enumerate(zip(heads, toks)):
+        ok = (blk[t] - blk) % N < min(P, N)
+        if mask >= 1:
+            ok &= t_all <= t
+        if mask == 2:
+            ok &= doc == doc[t]
+        if kvm is not None:
+            ok &= kvm
+        if not np.isfinite(ref["lse"][r]):
+            continue
+        Pr = np.where(ok, np.exp(np.where(ok, scale * (kn[:, h] @ qn[t, h]) - ref["lse"][r], -np.inf)), 0.0)
+        dS = Pr * (vn[:, h] @ gn[t, h] - gn[t, h] @ ref["out"][r])
+        dD = u * (np.abs(gn[t, h]) * (np.abs(ref["out"][r]) + Pr @ np.abs(vn[:, h]))).sum()
+        w = 2 * u * np.abs(dS) + Pr * dD
+        bq[r] = scale * (w @ np.abs(kn[:, h]))
+        bk[:, h] += scale * np.outer(w, np.abs(qn[t, h]))
+        bv[:, h] += u * np.outer(Pr, np.abs(gn[t, h]))
+    return bq, bk, bv
 
 
 @pytest.mark.parametrize("dt", ["bf16", "f16"])
@@ -244,12 +281,14 @@ def _sample_pairs(w, rng, heads, n_per_head):
     return np.array([p[0] for p in pairs]), np.array([p[1] for p in pairs])
 
 
-@pytest.mark.parametrize("name,dt", [("causal32k_h32_d128_8blk", "bf16"),
-                                     ("gqa_striped64k_h32kv8_d128_16blk", "bf16"),
-                                     ("varlen_packed128k_h32_d128_8blk_p4", "bf16"),
-                                     ("causal32k_h32_d128_8blk", "f16")])
-def test_long_workload_sparse_dout(ra, name, dt):
+@pytest.mark.parametrize("name,dt,padded", [("causal32k_h32_d128_8blk", "bf16", False),
+                                            ("gqa_striped64k_h32kv8_d128_16blk", "bf16", False),
+                                            ("varlen_packed128k_h32_d128_8blk_p4", "bf16", False),
+                                            ("causal32k_h32_d128_8blk", "f16", False),
+                                            ("gqa_striped64k_h32kv8_d128_16blk", "bf16", True)])
+def test_long_workload_sparse_dout(ra, name, dt, padded):
     w = dataclasses.replace(W.WORKLOADS[name], dtype=dt)
+    kv = W.random_key_valid(w.T, w.seed, 0.1) if padded else None
     _say(name, "generating inputs")
     x = W.make_inputs(w)
     if w.packed:
@@ -270,7 +309,7 @@ def test_long_workload_sparse_dout(ra, name, dt):
     lay = "striped" if w.layout else "contiguous"
     _say(name, "forward + backward on", len(toks), "rows of heads", q_sel)
     dq, dk, dv = _fwd_bwd(ra, q, k, v, dout.cuda(), N=w.n_blocks, lay=lay, mask=w.mask, P=w.max_ring_passes,
-                          docs=cu, out_dtype=TORCH16[dt])
+                          docs=cu, out_dtype=TORCH16[dt], key_valid=None if kv is None else kv.cuda())
     torch.cuda.synchronize()
     # oracle on the selected heads only, each query head with its own kv head
     sub_q = x["q"][:, q_sel]
@@ -282,10 +321,21 @@ def test_long_workload_sparse_dout(ra, name, dt):
     ref_dq, ref_dk, ref_dv = oracle.backward(sub_q, sub_k, sub_v, sub_g, n_blocks=w.n_blocks, layout=w.layout,
                                              mask=w.mask, max_ring_passes=w.max_ring_passes, cu_seqlens=cu,
                                              scale=w.scale, rows=(np.array([idx[int(h)] for h in heads]), toks),
-                                             rows_dkdv=True)
-    _check(dq.cpu()[toks, heads].double().numpy(), ref_dq, name + " dq rows", dt)
-    _check(dk.cpu()[:, kv_sel].double().numpy(), ref_dk, name + " dk", dt)
-    _check(dv.cpu()[:, kv_sel].double().numpy(), ref_dv, name + " dv", dt)
+                                             rows_dkdv=True, key_valid=kv)
+    got = (dq.cpu()[toks, heads].double().numpy(), dk.cpu()[:, kv_sel].double().numpy(),
+           dv.cpu()[:, kv_sel].double().numpy())
+    if kv is None:
+        for gn, r, what in zip(got, (ref_dq, ref_dk, ref_dv), ("dq rows", "dk", "dv")):
+            _check(gn, r, name + " " + what, dt)
+    else:
+        # rows left with few keys by the padding: the per-element bound, and the mean bar
+        bounds = _rounding_bounds_rows(sub_q, sub_k, sub_v, sub_g, w.n_blocks, w.layout, w.mask,
+                                       w.max_ring_passes, cu, dt, np.array([idx[int(h)] for h in heads]), toks,
+                                       key_valid=kv)
+        for gn, r, bd, what in zip(got, (ref_dq, ref_dk, ref_dv), bounds, ("dq rows", "dk", "dv")):
+            _check_bound(gn, r, bd, name + " " + what)
+            assert np.abs(gn - r).mean() <= TOL16[dt][1], (what, float(np.abs(gn - r).mean()))
+        assert not dk[~kv.cuda()].any() and not dv[~kv.cuda()].any()
     # every other row and kv head: exactly zero
     dq_rest = dq.clone()
     dq_rest[toks, heads] = 0
