@@ -20,7 +20,7 @@ pytestmark = pytest.mark.gpu
 
 F32_TOL = 1e-5
 BF16_MAX, BF16_MEAN = 2e-2, 1e-2
-TOL16 = {"bf16": (BF16_MAX, BF16_MEAN), "f16": (BF16_MAX / 8, BF16_MEAN / 8)}
+TOL16 = {"bf16": (BF16_MAX, BF16_MEAN), "f16": (BF16_MAX / 8, BF16_MEAN / 8), "f32": (F32_TOL, F32_TOL)}
 TORCH16 = {"bf16": torch.bfloat16, "f16": torch.float16}
 
 
@@ -259,7 +259,7 @@ def test_pack_key_mask_bits(ra):
         assert np.array_equal(bits, want), n
 
 
-@pytest.mark.parametrize("dt", ["bf16", "f16"])
+@pytest.mark.parametrize("dt", ["bf16", "f16", "f32"])
 def test_16bit_step_api_key_bits(ra, dt):
     """ring_attn_step with a key block's packed padding bits (striped block
     as strided views): the state must equal the oracle's block state."""
