@@ -284,6 +284,24 @@ def test_16bit_step_api_key_bits(ra, dt):
     _check_bf16(out[ok], ref["out"][ok], "key-bits step", dt)
 
 
+@pytest.mark.parametrize("N", [64, 65])
+def test_forward_at_and_past_the_longest_ring_chain(ra, N):
+    """64 ring blocks run as one launch (one chain block per lane); 65 take
+    one launch per ring step.  Both against the oracle, with the tallies."""
+    T, H, d = N * 24, 2, 128
+    _say("bf16 forward blocks", N)
+    qh, kh, vh = W.random_qkv(T, H, H, d, "bf16", 5100 + N)
+    for layout in (0, 1):
+        out, lse, st = ra.forward(*_dev(qh, kh, vh), n_blocks=N, layout="striped" if layout else "contiguous",
+                                  causal=True, out_dtype=torch.float32, return_lse=True, return_stats=True)
+        ref = oracle.forward(qh, kh, vh, n_blocks=N, layout=layout, mask=oracle.MASK_CAUSAL)
+        _check_bf16(out.cpu().double().numpy(), ref["out"], "out %d blocks layout %d" % (N, layout))
+        assert np.abs(lse.cpu().double().numpy() - ref["lse"]).max() <= 1e-3
+        tal = oracle.tallies(T, N, layout=layout, mask=oracle.MASK_CAUSAL, tile_q=st["tile_q"], tile_k=st["tile_k"])
+        for key, val in tal.items():
+            assert st[key] == val, key
+
+
 def test_bf16_ring_late_score_jumps(ra):
     """Scores that jump far above a row's running reference late in its chain:
     under a causal ring, device i visits blocks i, i-1, ..., 0, so keys of

@@ -242,6 +242,30 @@ def test_16bit_backward_key_padding(ra, case, dt):
     assert not dk[~kvd].any() and not dv[~kvd].any()
 
 
+@pytest.mark.parametrize("layout", [0, 1])
+def test_backward_at_the_longest_ring_chain(ra, layout):
+    """n_blocks = 64, the most ring blocks a chain table holds (one per
+    lane): 24-row blocks, every tile ragged, forward and backward."""
+    T, N, H, d = 64 * 24, 64, 2, 128
+    _say("bf16 backward 64 blocks", layout)
+    qh, kh, vh = W.random_qkv(T, H, H, d, "bf16", 5000 + layout)
+    gh = W.random_dout(T, H, d, "bf16", 5000 + layout)
+    q, k, v, g = (x.cuda() for x in (qh, kh, vh, gh))
+    lay = "striped" if layout == 1 else "contiguous"
+    dq, dk, dv = _fwd_bwd(ra, q, k, v, g, N=N, lay=lay, mask=1, P=N, docs=None, out_dtype=torch.bfloat16)
+    ref = oracle.backward(qh, kh, vh, gh, n_blocks=N, layout=layout, mask=1)
+    bounds = _rounding_bounds(qh, kh, vh, gh, N, layout, 1, N, None, "bf16")
+    for name, got, r, bd in zip(("dq", "dk", "dv"), (dq, dk, dv), ref, bounds):
+        gn = got.cpu().double().numpy()
+        _check(gn, r, name)
+        _check_bound(gn, r, bd, name)
+    with pytest.raises(ra.RingAttnError):  # one block more than a chain table holds
+        T2 = 65 * 16
+        q2, k2, v2 = (x.cuda() for x in W.random_qkv(T2, H, H, d, "bf16", 1))
+        o2, l2 = ra.forward(q2, k2, v2, n_blocks=65, causal=True, return_lse=True)
+        ra.backward(q2, k2, v2, o2, l2, torch.zeros_like(q2), n_blocks=65, causal=True)
+
+
 def test_bf16_backward_packed_qkv_views(ra):
     """Strided q / k / v views of one [T, 3, H, d] tensor give the gradients of
     contiguous copies, bit for bit."""
