@@ -21,6 +21,9 @@
  *  - Arguments are checked before anything is enqueued: a bad argument returns
  *    RA_E_ARG (or RA_E_UNSUPPORTED for a valid but unimplemented combination)
  *    with no side effects.  A failed launch returns RA_E_HIP.
+ *  - An empty sequence (T = 0) or empty query block needs no buffers: its
+ *    tensor, output, state and gradient pointers may be NULL, and the call
+ *    returns RA_OK after the argument checks without any GPU work.
  *  - Tensors are [tokens, heads, head_dim] views with element strides; the
  *    head_dim stride must be 1.  This covers plain [T, H, d] tensors, striped
  *    ring blocks (token stride multiplied by N) and the packed [T, 3, H, d]

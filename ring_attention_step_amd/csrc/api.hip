@@ -27,7 +27,7 @@ size_t elem_size(ra_dtype t) { return is16(t) ? 2 : 4; }
 bool valid_dtype(int t) { return t == RA_F32 || is16(t); }
 
 bool tensor_ok(const ra_tensor* x) {
-    return x && x->data && valid_dtype(x->dtype) && x->n_tok >= 0 && x->n_head >= 1 && x->head_dim >= 1 &&
+    return x && (x->data || x->n_tok == 0) && valid_dtype(x->dtype) && x->n_tok >= 0 && x->n_head >= 1 && x->head_dim >= 1 &&
            x->stride_tok >= 0 && x->stride_head >= 0;
 }
 
@@ -225,7 +225,8 @@ ra_status ring_attn_step(const ra_tensor* q_blk, const ra_tensor* k_blk, const r
     if (k_blk->head_dim != d || v_blk->head_dim != d) return RA_E_ARG;
     if (k_blk->n_tok != v_blk->n_tok || k_blk->n_head != v_blk->n_head) return RA_E_ARG;
     if (q_blk->n_head % k_blk->n_head) return RA_E_ARG;
-    if (!O || !m || !l || !scale_ok(scale) || pos_stride < 1) return RA_E_ARG;
+    if ((!O || !m || !l) && q_blk->n_tok > 0) return RA_E_ARG;  // no state for an empty block
+    if (!scale_ok(scale) || pos_stride < 1) return RA_E_ARG;
     if (mask_mode < RA_MASK_NONE || mask_mode > RA_MASK_DOC_CAUSAL) return RA_E_ARG;
     if (mask_mode == RA_MASK_DOC_CAUSAL && (!cu_seqlens || n_docs < 1)) return RA_E_ARG;
     if (mask_mode == RA_MASK_DOC_CAUSAL && pos_stride != 1) return RA_E_UNSUPPORTED;
@@ -356,7 +357,7 @@ ra_status ring_attn_forward(const ra_tensor* q, const ra_tensor* k, const ra_ten
                             const uint8_t* key_valid, float scale, int prefetch, void* workspace,
                             size_t workspace_bytes, ra_stats* stats, void* stream) {
     // ---- arguments ----
-    if (!tensor_ok(q) || !tensor_ok(k) || !tensor_ok(v) || !out) return RA_E_ARG;
+    if (!tensor_ok(q) || !tensor_ok(k) || !tensor_ok(v) || (!out && q->n_tok > 0)) return RA_E_ARG;
     if (q->dtype != k->dtype || q->dtype != v->dtype || !valid_dtype(out_dtype)) return RA_E_ARG;
     const int64_t T = q->n_tok, Hq = q->n_head, Hkv = k->n_head, d = q->head_dim;
     if (k->n_tok != T || v->n_tok != T || v->n_head != Hkv || k->head_dim != d || v->head_dim != d) return RA_E_ARG;
@@ -391,6 +392,14 @@ ra_status ring_attn_forward(const ra_tensor* q, const ra_tensor* k, const ra_ten
     Workspace ws = carve(workspace, T, n_blocks, Hq, Hkv, d, n_docs, q->dtype, prefetch != 0);
     if (!workspace || workspace_bytes < ws.total) return RA_E_WORKSPACE;
     if ((uintptr_t)workspace % kAlign) return RA_E_WORKSPACE;
+    if (T == 0) {  // an empty sequence: nothing to launch
+        if (stats) {
+            std::memset(stats, 0, sizeof *stats);
+            stats->tile_q = tq;
+            stats->tile_k = tk;
+        }
+        return RA_OK;
+    }
 
     hipStream_t st = (hipStream_t)stream;
     Ring r;
@@ -655,7 +664,8 @@ ra_status ring_attn_backward(const ra_tensor* q, const ra_tensor* k, const ra_te
                              void* stream) {
     // ---- arguments ----
     if (!tensor_ok(q) || !tensor_ok(k) || !tensor_ok(v) || !tensor_ok(out) || !tensor_ok(dout)) return RA_E_ARG;
-    if (!lse || !dq || !dk || !dv || !valid_dtype(grad_dtype)) return RA_E_ARG;
+    if ((!lse || !dq || !dk || !dv) && q->n_tok > 0) return RA_E_ARG;  // an empty sequence needs no buffers
+    if (!valid_dtype(grad_dtype)) return RA_E_ARG;
     if (q->dtype != k->dtype || q->dtype != v->dtype || dout->dtype != q->dtype) return RA_E_ARG;
     const int64_t T = q->n_tok, Hq = q->n_head, Hkv = k->n_head, d = q->head_dim;
     if (k->n_tok != T || v->n_tok != T || v->n_head != Hkv || k->head_dim != d || v->head_dim != d) return RA_E_ARG;

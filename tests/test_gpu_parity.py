@@ -302,6 +302,20 @@ def test_forward_at_and_past_the_longest_ring_chain(ra, N):
             assert st[key] == val, key
 
 
+def test_empty_sequence(ra):
+    """T = 0 through the binding: empty out and lse, zero tallies, empty gradients."""
+    _say("empty sequence")
+    for dt in (torch.bfloat16, torch.float16, torch.float32):
+        q = torch.empty(0, 4, 128, device="cuda", dtype=dt)
+        k = torch.empty(0, 2, 128, device="cuda", dtype=dt)
+        out, lse, st = ra.forward(q, k, k, n_blocks=4, causal=True, return_lse=True, return_stats=True)
+        assert out.shape == (0, 4, 128) and lse.shape == (4, 0) and st["tiles_partial"] == 0
+        if dt != torch.float32:
+            dq, dk, dv = ra.backward(q, k, k, out, lse, q, n_blocks=4, causal=True)
+            assert dq.shape == (0, 4, 128) and dk.shape == (0, 2, 128) and dv.shape == (0, 2, 128)
+    torch.cuda.synchronize()
+
+
 def test_bf16_ring_late_score_jumps(ra):
     """Scores that jump far above a row's running reference late in its chain:
     under a causal ring, device i visits blocks i, i-1, ..., 0, so keys of

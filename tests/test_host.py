@@ -192,6 +192,22 @@ def test_forward_and_step_refuse_bad_arguments_before_any_gpu_work(lib):
     assert P_(ctypes.c_void_p(1 << 23), 64, 1, bits_misaligned, None) == ra.RA_E_ARG
 
 
+def test_empty_sequence_needs_no_buffers_and_launches_nothing(lib):
+    """T = 0 (torch gives empty tensors a null data pointer): every entry point
+    returns RA_OK before any GPU call, the forward's tallies all zero."""
+    R = ctypes.byref
+    q, k = _fake(0, 4, 128, ptr=0), _fake(0, 2, 128, ptr=0)
+    ws = ctypes.c_void_p(1 << 22)
+    st = ra.RaStats()
+    assert lib.ring_attn_forward(R(q), R(k), R(k), None, ra.RA_BF16, None, 4, 0, 1, 4, None, 0, None, 0.1, 0, ws,
+                                 1 << 40, R(st), None) == ra.RA_OK
+    assert st.as_dict()["tiles_full"] == 0 and st.as_dict()["allowed_pairs"] == 0 and st.tile_q > 0
+    assert lib.ring_attn_backward(R(q), R(k), R(k), R(q), R(q), None, None, None, None, ra.RA_F32, 4, 0, 1, 4,
+                                  None, 0, None, 0.1, ws, 1 << 40, None) == ra.RA_OK
+    assert lib.ring_attn_step(R(q), R(k), R(k), None, None, None, 1, 0.1, 1, 0, 0, 1, None, 0, None, None,
+                              None) == ra.RA_OK
+
+
 def test_workspace_size_grows_with_prefetch(lib):
     q, k = _fake(4096, 32, 128), _fake(4096, 8, 128)
     a = lib.ring_attn_forward_workspace_size(ctypes.byref(q), ctypes.byref(k), 8, 0, 0)
