@@ -1,0 +1,122 @@
+"""First-order rounding bounds of the 16-bit GPU path, per output element,
+computed in fp64 from the oracle's results (test infrastructure: the GPU
+parity tests compare against these; nothing here is on the product path)."""
+import numpy as np
+
+import oracle
+
+U16 = {"bf16": 2.0 ** -8, "f16": 2.0 ** -11}  # unit roundoff of the 16-bit type (8 / 11 significant bits)
+
+
+def allowed(T, N, layout, mask, P, docs, key_valid=None):
+    """[T, T] allowed (query, key) pairs: ring visibility, mask, key padding."""
+    t = np.arange(T)
+    B = T // N
+    blk = t % N if layout == 1 else t // B
+    ok = (blk[:, None] - blk[None, :]) % N < min(P, N)
+    if mask >= 1:
+        ok &= t[None, :] <= t[:, None]
+    if mask == 2:
+        doc = np.searchsorted(np.asarray(docs[1:]), t, side="right")
+        ok &= doc[:, None] == doc[None, :]
+    if key_valid is not None:
+        ok &= np.asarray(key_valid, dtype=bool)[None, :]
+    return ok
+
+
+def backward_bounds(qh, kh, vh, gh, N, layout, mask, P, docs, dt, key_valid=None):
+    """First-order bounds on the 16-bit backward's error, per gradient element.
+    With u the unit roundoff of the 16-bit type and, per (query t, key j),
+    P, dP = dout.v, D = dout.out, dS = P (dP - D) from the fp64 oracle:
+      the kernels round dS to 16 bits (and the dK side may use a 16-bit P),
+      <= 2 u |dS|;  D comes from the forward's 16-bit out, whose error is
+      <= u |out| (its rounding) + u sum_j P |v_j| (the forward's 16-bit P),
+      so |dD| <= u sum_c |dout_c| (|out_c| + (P |v|)_c) and dS moves by P |dD|;
+      dv uses a 16-bit P: <= u P |dout|.
+    Hence |d dq_t| <= scale sum_j w_tj |k_j|, |d dk_j| <= scale sum_t w_tj |q_t|
+    with w = 2 u |dS| + P |dD|, and |d dv_j| <= u sum_t P_tj |dout_t|.  fp32
+    accumulation adds terms of order 2^-24 times the sums, far below these."""
+    T, Hq, d = qh.shape
+    Hkv = kh.shape[1]
+    scale = 1.0 / np.sqrt(d)
+    q, k, v, g = (x.double().numpy() for x in (qh, kh, vh, gh))
+    ref = oracle.forward(qh, kh, vh, n_blocks=N, layout=layout, mask=mask, max_ring_passes=P, cu_seqlens=docs,
+                         key_valid=key_valid)
+    out, lse = ref["out"], ref["lse"]
+    ok = allowed(T, N, layout, mask, P, docs, key_valid)
+    u = U16[dt]
+    bq, bk, bv = np.zeros((T, Hq, d)), np.zeros((T, Hkv, d)), np.zeros((T, Hkv, d))
+    grp = Hq // Hkv
+    for h in range(Hq):
+        gk = h // grp
+        use = ok & np.isfinite(lse[h])[:, None]
+        s = scale * (q[:, h] @ k[:, gk].T)
+        Pm = np.where(use, np.exp(np.where(use, s - lse[h][:, None], -np.inf)), 0.0)
+        dS = Pm * (g[:, h] @ v[:, gk].T - (g[:, h] * out[:, h]).sum(1)[:, None])
+        dD = u * (np.abs(g[:, h]) * (np.abs(out[:, h]) + Pm @ np.abs(v[:, gk]))).sum(1)[:, None]
+        w = 2 * u * np.abs(dS) + Pm * dD
+        bq[:, h] += scale * (w @ np.abs(k[:, gk]))
+        bk[:, gk] += scale * (w.T @ np.abs(q[:, h]))
+        bv[:, gk] += u * (Pm.T @ np.abs(g[:, h]))
+    return bq, bk, bv
+
+
+def forward_bound(qh, kh, vh, N, layout, mask, P, docs, dt, key_valid=None):
+    """Bound on |out - out_exact| for the fp32 output of the 16-bit forward:
+    the kernel rounds each weight P_j (relative to its running reference) to
+    16 bits before the P.V product and divides by the unrounded fp32 sum, so
+    out moves by at most u sum_j p_j |v_j| with p the normalised weights."""
+    T, Hq, d = qh.shape
+    Hkv = kh.shape[1]
+    scale = 1.0 / np.sqrt(d)
+    q, k, v = (x.double().numpy() for x in (qh, kh, vh))
+    ref = oracle.forward(qh, kh, vh, n_blocks=N, layout=layout, mask=mask, max_ring_passes=P, cu_seqlens=docs,
+                         key_valid=key_valid)
+    ok = allowed(T, N, layout, mask, P, docs, key_valid)
+    u = U16[dt]
+    b = np.zeros((T, Hq, d))
+    grp = Hq // Hkv
+    for h in range(Hq):
+        gk = h // grp
+        lse = ref["lse"][h]
+        use = ok & np.isfinite(lse)[:, None]
+        p = np.where(use, np.exp(np.where(use, scale * (q[:, h] @ k[:, gk].T) - lse[:, None], -np.inf)), 0.0)
+        b[:, h] = u * (p @ np.abs(v[:, gk]))
+    return b
+
+
+def backward_bounds_rows(q, k, v, g, N, layout, mask, P, docs, dt, heads, toks, key_valid=None):
+    """backward_bounds for a dout that is zero outside the listed (head, token)
+    rows, each head h of q reading kv head h of k / v: dq bounds of those rows
+    [n, d], and dk / dv bounds [T, H, d] summed over those rows only."""
+    T, H, d = q.shape
+    scale = 1.0 / np.sqrt(d)
+    u = U16[dt]
+    qn, kn, vn, gn = (x.double().numpy() for x in (q, k, v, g))
+    ref = oracle.forward(q, k, v, n_blocks=N, layout=layout, mask=mask, max_ring_passes=P, cu_seqlens=docs,
+                         rows=(heads, toks), key_valid=key_valid)
+    t_all = np.arange(T)
+    B = T // N
+    blk = t_all % N if layout == 1 else t_all // B
+    doc = np.searchsorted(np.asarray(docs[1:]), t_all, side="right") if mask == 2 else None
+    kvm = None if key_valid is None else np.asarray(key_valid, dtype=bool)
+    bq = np.zeros((len(toks), d))
+    bk, bv = np.zeros((T, H, d)), np.zeros((T, H, d))
+    for r, (h, t) in enumerate(zip(heads, toks)):
+        ok = (blk[t] - blk) % N < min(P, N)
+        if mask >= 1:
+            ok &= t_all <= t
+        if mask == 2:
+            ok &= doc == doc[t]
+        if kvm is not None:
+            ok &= kvm
+        if not np.isfinite(ref["lse"][r]):
+            continue
+        Pr = np.where(ok, np.exp(np.where(ok, scale * (kn[:, h] @ qn[t, h]) - ref["lse"][r], -np.inf)), 0.0)
+        dS = Pr * (vn[:, h] @ gn[t, h] - gn[t, h] @ ref["out"][r])
+        dD = u * (np.abs(gn[t, h]) * (np.abs(ref["out"][r]) + Pr @ np.abs(vn[:, h]))).sum()
+        w = 2 * u * np.abs(dS) + Pr * dD
+        bq[r] = scale * (w @ np.abs(kn[:, h]))
+        bk[:, h] += scale * np.outer(w, np.abs(qn[t, h]))
+        bv[:, h] += u * np.outer(Pr, np.abs(gn[t, h]))
+    return bq, bk, bv

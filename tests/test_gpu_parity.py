@@ -15,6 +15,7 @@ import torch
 
 import oracle
 import workloads as W
+from bounds import forward_bound
 
 pytestmark = pytest.mark.gpu
 
@@ -39,6 +40,15 @@ def _say(*a):
 
 def _dev(*xs):
     return [x.cuda() for x in xs]
+
+
+def _check_fwd_bound(out, ref, bound, what):
+    """Every element within the first-order rounding bound of the 16-bit
+    forward (widened by 2^-10 of itself and 1e-6 for the fp32 terms)."""
+    err = np.abs(out - ref)
+    lim = bound * (1 + 2.0 ** -10) + 1e-6
+    _say(what, "max err / bound", float((err / lim).max()))
+    assert (err <= lim).all(), (what, float(err.max()), float((err / lim).max()))
 
 
 def _check_bf16(out, ref, what, dt="bf16"):
@@ -185,6 +195,8 @@ def test_16bit_forward_small(ra, case, dt):
                               max_ring_passes=P, out_dtype=torch.float32, return_lse=True, return_stats=True)
     ref = oracle.forward(qh, kh, vh, n_blocks=N, layout=layout, mask=mask, max_ring_passes=P, cu_seqlens=docs)
     _check_bf16(out.cpu().double().numpy(), ref["out"], "out", dt)
+    _check_fwd_bound(out.cpu().double().numpy(), ref["out"], forward_bound(qh, kh, vh, N, layout, mask, P, docs, dt),
+                     "out")
     assert np.abs(lse.cpu().double().numpy() - ref["lse"]).max() <= 1e-3
     tal = oracle.tallies(T, N, layout=layout, mask=mask, max_ring_passes=P, cu_seqlens=docs,
                          tile_q=st["tile_q"], tile_k=st["tile_k"])
@@ -219,9 +231,11 @@ def test_16bit_forward_key_padding(ra, case, dt):
               return_lse=True)
     ref = oracle.forward(qh, kh, vh, n_blocks=N, layout=layout, mask=mask, max_ring_passes=P, cu_seqlens=docs,
                          key_valid=kv)
+    bound = forward_bound(qh, kh, vh, N, layout, mask, P, docs, dt, key_valid=kv)
     for prefetch in (False, True):
         out, lse = ra.forward(q, k, v, key_valid=kv.cuda(), prefetch=prefetch, **kw)
         _check_bf16(out.cpu().double().numpy(), ref["out"], "out prefetch=%d" % prefetch, dt)
+        _check_fwd_bound(out.cpu().double().numpy(), ref["out"], bound, "out prefetch=%d" % prefetch)
         got_lse = lse.cpu().double().numpy()
         empty = np.isneginf(ref["lse"])
         assert np.array_equal(np.isneginf(got_lse), empty)
