@@ -41,11 +41,14 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak (AMD published figure)
 DEFAULT_WORKLOAD = "causal32k_h32_d128_8blk"
-KERNEL = "step_bf16_kernel<__bf16, 128, true, true, false>"
+KERNEL = "ring_fwd_kernel<__bf16, 128, false>"
+# the per-ring-step kernel that the prefetching forward launches once per step
+STEP_KERNEL = "step_bf16_kernel<__bf16, 128, true, true, false>"
 BWD_KERNEL = "bwd_dkdv_kernel<__bf16, 128>"
 # The kernels' sources plus the driver that sets their launch order (a
 # traffic record is only valid for the code and the order it was taken with).
-KERNEL_SOURCES = ["ring_attention_step_amd/csrc/step_bf16.hip", "ring_attention_step_amd/csrc/plan.h",
+KERNEL_SOURCES = ["ring_attention_step_amd/csrc/ring_fwd.hip", "ring_attention_step_amd/csrc/step_bf16.hip",
+                  "ring_attention_step_amd/csrc/plan.h",
                   "ring_attention_step_amd/csrc/kernels.h", "ring_attention_step_amd/csrc/api.hip"]
 BWD_KERNEL_SOURCES = ["ring_attention_step_amd/csrc/backward.hip", "ring_attention_step_amd/csrc/bwd_kernels.h",
                       "ring_attention_step_amd/csrc/plan.h",
@@ -228,7 +231,7 @@ def main():
         # achieved: the forward's FLOP over its event-timed duration on the
         # launch stream, which also holds the V^T pack (about 1% of it): a
         # slight underestimate of the step kernel's own rate.
-        "roofline": {"bound": "mfma", "kernel": KERNEL, "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
+        "roofline": {"bound": "mfma", "kernel": STEP_KERNEL if args.prefetch else KERNEL, "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                      "launches_per_step": n_launch, "event_ms_per_step": round(ms_event, 4),
                      "timing": "hip events on the launch stream around the timed steps, incl. the V^T pack"},

@@ -21,8 +21,12 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libring_attn.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
-HIP_SOURCES = ["api.hip", "step_bf16.hip", "step_f32.hip", "finalize_merge.hip", "pack_vt.hip", "key_bits.hip",
-               "backward.hip"]
+HIP_SOURCES = ["api.hip", "step_bf16.hip", "ring_fwd.hip", "step_f32.hip", "finalize_merge.hip", "pack_vt.hip",
+               "key_bits.hip", "backward.hip"]
+# Per-file code generation options.  ring_fwd.hip keeps its score accumulators
+# in VGPRs (the vector ALU reads them) and its Q operands in AGPRs: the VGPR
+# form of the matrix instructions.
+EXTRA_FLAGS = {"ring_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 CPP_SOURCES = ["plan.cpp"]
 ARCH = "gfx950"
 
@@ -45,7 +49,7 @@ def build(verbose: bool = False) -> str:
             obj = os.path.join(tmpdir, src + ".o")
             objs.append(obj)
             cmds.append([hipcc(), "-x", "hip", "--offload-arch=" + ARCH, "-Xclang", "-target-feature", "-Xclang",
-                         "-packed-fp32-ops", "-munsafe-fp-atomics", *_common_flags(), "-c",
+                         "-packed-fp32-ops", "-munsafe-fp-atomics", *EXTRA_FLAGS.get(src, []), *_common_flags(), "-c",
                          os.path.join(CSRC, src), "-o", obj])
         for src in CPP_SOURCES:
             obj = os.path.join(tmpdir, src + ".o")

@@ -79,6 +79,9 @@ constexpr int kBf16TileQ = 256, kBf16TileK = 64;
 constexpr int kF32TileQ = 64, kF32TileK = 64;
 
 hipError_t launch_step_bf16(const StepArgs& a, hipStream_t stream);
+// The one-launch ring forward (works set, packed V^T): eight waves of 32
+// query rows each per workgroup, each wave its own software pipeline.
+hipError_t launch_ring_fwd(const StepArgs& a, hipStream_t stream);
 hipError_t launch_step_f32(const StepArgs& a, hipStream_t stream);
 hipError_t launch_finalize(const float* O, const float* m, const float* l, int64_t Hq, int64_t Bq,
                            int64_t d, void* out, int out_kind, int64_t out_stride_tok,

@@ -843,6 +843,7 @@ hipError_t launch_step16(const StepArgs& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_step_bf16(const StepArgs& a, hipStream_t stream) {
+    if (a.works) return launch_ring_fwd(a, stream);
     // KP: with a key-padding mask (the unmasked kernels carry none of its code)
     if (a.kbits) return a.f16 ? launch_step16<f16, true>(a, stream) : launch_step16<bf16, true>(a, stream);
     return a.f16 ? launch_step16<f16, false>(a, stream) : launch_step16<bf16, false>(a, stream);
