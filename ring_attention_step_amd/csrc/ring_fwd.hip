@@ -505,8 +505,11 @@ __global__ __launch_bounds__(THREADS, 1) void ring_fwd_kernel(const StepArgs a) 
                 p_cur[i / 8][i % 8] = to16<E>(pv);
             }
         }
+        // P is packed here, among the matrix instructions, not after the
+        // slow-path branch (the slow path recomputes it).
+        __asm__ volatile("" : "+v"(p_cur[0]), "+v"(p_cur[1]));
         float lt = (ps[0] + ps[1]) + (ps[2] + ps[3]);
-        if (__ballot(!(lt <= kUnitSumMax) || mrc == -INFINITY)) {
+        if (__builtin_expect(__ballot(!(lt <= kUnitSumMax) || mrc == -INFINITY) != 0, 0)) {
             rebase(s_cur);
             lt = probs_all(s_cur, p_cur);
         }
