@@ -155,7 +155,11 @@ ra_status ring_attn_finalize(const float* O, const float* m, const float* l, int
 ra_status ring_attn_merge(void* out_acc, float* lse_acc, const void* out_blk, const float* lse_blk,
                           ra_dtype dtype, int64_t Hq, int64_t rows, int64_t d, void* stream);
 
-/* Bytes of device workspace ring_attn_forward needs for these shapes. */
+/* Bytes of device workspace ring_attn_forward needs for these shapes.  The
+ * fp32 per-step state (O [T, Hq, d], m and l [Hq, T]) is included only when
+ * the per-step path can run: fp32 inputs, prefetch != 0, n_blocks > 64, or
+ * more query tiles x heads x blocks than fit an int32.  16-bit inputs
+ * otherwise need the packed V^T, the chain tables and the key bits only. */
 size_t ring_attn_forward_workspace_size(const ra_tensor* q, const ra_tensor* k, int32_t n_blocks,
                                         int32_t n_docs, int prefetch);
 

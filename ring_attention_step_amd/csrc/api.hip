@@ -111,6 +111,19 @@ struct Workspace {
     size_t total = 0;
 };
 
+// Whether a forward with these shapes may take the per-step path, whose
+// state (unnormalised O, m, l of every row) lives in the workspace between
+// steps: fp32 inputs, the side-stream prefetch, or a ring the one-launch
+// kernel cannot hold (longer chains than its table, too many workgroups).
+// Otherwise the one-launch ring runs and keeps the state in registers.
+bool fwd_needs_state(int64_t T, int64_t N, int64_t Hq, int64_t d, ra_dtype dt, bool prefetch) {
+    if (!is16(dt) || prefetch || N > kMaxRingChain) return true;
+    int tq = 0, tk = 0;
+    if (kernel_for(dt, d, &tq, &tk) != RA_OK || tq <= 0) return true;
+    const int64_t n_qtiles = (T / N + tq - 1) / tq;
+    return n_qtiles * Hq * N > INT32_MAX;
+}
+
 Workspace carve(void* base, int64_t T, int64_t N, int64_t Hq, int64_t Hkv, int64_t d, int64_t n_docs, ra_dtype dt,
                 bool prefetch) {
     Workspace w;
@@ -126,9 +139,11 @@ Workspace carve(void* base, int64_t T, int64_t N, int64_t Hq, int64_t Hkv, int64
     const size_t vt_bytes = is16(dt) ? (size_t)N * Hkv * d * vt_padded_keys(B) * 2 : 0;
     w.counters = (unsigned long long*)take(4 * sizeof(unsigned long long));
     w.cu = (int32_t*)take(sizeof(int32_t) * (size_t)(n_docs + 1));
-    w.O = (float*)take(sizeof(float) * (size_t)(T * Hq * d));
-    w.m = (float*)take(sizeof(float) * (size_t)(T * Hq));
-    w.l = (float*)take(sizeof(float) * (size_t)(T * Hq));
+    if (N > 0 && fwd_needs_state(T, N, Hq, d, dt, prefetch)) {
+        w.O = (float*)take(sizeof(float) * (size_t)(T * Hq * d));
+        w.m = (float*)take(sizeof(float) * (size_t)(T * Hq));
+        w.l = (float*)take(sizeof(float) * (size_t)(T * Hq));
+    }
     w.kbits = (uint32_t*)take(sizeof(uint32_t) * (size_t)(N * key_words(B)));
     if (is16(dt)) {
         w.vt = take(vt_bytes);
@@ -533,6 +548,8 @@ ra_status ring_attn_forward(const ra_tensor* q, const ra_tensor* k, const ra_ten
         }
     }
 
+    // (the workspace holds the per-step state whenever this path can run)
+    if (!ring_done && !fwd_needs_state(T, N, Hq, d, q->dtype, prefetch != 0)) return RA_E_UNSUPPORTED;
     for (int64_t s = 0; s < (ring_done ? 0 : r.passes); s++) {
         const std::vector<StepPair>& pairs = plan.steps[s];
         const bool use_buf = pf && s > 0;

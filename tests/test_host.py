@@ -213,7 +213,31 @@ def test_workspace_size_grows_with_prefetch(lib):
     a = lib.ring_attn_forward_workspace_size(ctypes.byref(q), ctypes.byref(k), 8, 0, 0)
     b = lib.ring_attn_forward_workspace_size(ctypes.byref(q), ctypes.byref(k), 8, 0, 1)
     state = 4096 * 32 * 128 * 4 + 2 * 4096 * 32 * 4
-    assert a >= state and b >= a + 2 * 2 * 4096 * 8 * 128 * 2
+    # prefetch adds the per-step state and the K / V^T double buffers
+    assert b >= a + state + 2 * 2 * 4096 * 8 * 128 * 2
+
+
+def _ws(lib, T, Hq, Hkv, d, N, dtype, prefetch=0):
+    q, k = _fake(T, Hq, d, dtype), _fake(T, Hkv, d, dtype)
+    return lib.ring_attn_forward_workspace_size(ctypes.byref(q), ctypes.byref(k), N, 0, prefetch)
+
+
+def test_one_launch_workspace_has_no_per_step_state(lib):
+    # Causal 32K tokens, 32 heads, d = 128, 8 blocks in bf16: the one-launch
+    # ring keeps O / m / l in registers, so the workspace is the packed V^T
+    # (32768 x 32 x 128 x 2 bytes, keys padded per block) and small tables;
+    # the fp32 state planes (512 MiB + 8 MiB) appear only where the per-step
+    # path can run.
+    T, H, d, N = 32768, 32, 128, 8
+    state = T * H * d * 4 + 2 * T * H * 4
+    vt = T * H * d * 2
+    ws16 = _ws(lib, T, H, H, d, N, ra.RA_BF16)
+    assert vt <= ws16 < vt + (8 << 20)
+    assert _ws(lib, T, H, H, d, N, ra.RA_F16) == ws16
+    assert _ws(lib, T, H, H, d, N, ra.RA_F32) >= state               # fp32 inputs: per-step path
+    assert _ws(lib, T, H, H, d, N, ra.RA_BF16, prefetch=1) >= ws16 + state
+    assert _ws(lib, T, H, H, d, 128, ra.RA_BF16) >= vt + state       # chains longer than 64 blocks
+    assert _ws(lib, T, H, H, d, 64, ra.RA_BF16) < vt + (8 << 20)
 
 
 def test_backward_refuses_bad_arguments_before_any_gpu_work(lib):
