@@ -190,6 +190,10 @@ size_t ring_attn_forward_workspace_size(const ra_tensor* q, const ra_tensor* k, 
  *     block, modelled on one GPU).  For fp32 inputs the results are
  *     bit-identical to prefetch = 0; for 16-bit inputs they agree to 16-bit rounding
  *     (the state hand-off changes the reference P is rounded against).
+ *     Each GPU has one copy stream and one pair of event sets for this path:
+ *     concurrent prefetch calls on one device (any host threads, any
+ *     streams) enqueue one after another and their copies share that
+ *     stream.
  *   stats: nullable HOST pointer; when given the call synchronises `stream`
  *     and fills it.
  */

@@ -113,10 +113,42 @@ def _gpu(x: torch.Tensor, name: str):
         raise ValueError("%s must be a GPU tensor" % name)
 
 
-def _tensor(x: torch.Tensor, name: str) -> RaTensor:
-    _gpu(x, name)
-    if x.dim() != 3 or x.stride(2) != 1:
+def _view3(x: torch.Tensor, name: str):
+    if not isinstance(x, torch.Tensor) or x.dim() != 3 or x.stride(2) != 1:
         raise ValueError("%s must be a [tokens, heads, head_dim] view with unit head_dim stride" % name)
+
+
+def _f32_buffer(x, shape, name: str):
+    """A contiguous float32 tensor of exactly this shape (the library writes all of it)."""
+    if not isinstance(x, torch.Tensor) or tuple(x.shape) != tuple(shape) or x.dtype != torch.float32 \
+            or not x.is_contiguous():
+        raise ValueError("%s must be a contiguous float32 tensor of shape %s" % (name, list(shape)))
+
+
+def _forward_operands(q, k, v, out, lse):
+    """Shapes, dtypes and layouts of a forward's tensors, checked before any pointer is taken:
+    q [T, Hq, d], k / v [T, Hkv, d] views of one dtype, out [T, Hq, d] contiguous (float32 or
+    q's dtype), lse None or [Hq, T] float32 contiguous."""
+    for x, name in ((q, "q"), (k, "k"), (v, "v")):
+        _view3(x, name)
+    T, Hq, d = q.shape
+    if k.shape[0] != T or k.shape[2] != d or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("k and v must be [T, Hkv, d] views with q's T and d")
+    if Hq % k.shape[1]:
+        raise ValueError("q's head count must be a multiple of k's")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k and v must share one dtype")
+    if not isinstance(out, torch.Tensor) or tuple(out.shape) != (T, Hq, d) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [T, Hq, d] tensor")
+    if out.dtype not in (torch.float32, q.dtype):
+        raise ValueError("out must be float32 or q's dtype")
+    if lse is not None:
+        _f32_buffer(lse, (Hq, T), "lse")
+
+
+def _tensor(x: torch.Tensor, name: str) -> RaTensor:
+    _view3(x, name)
+    _gpu(x, name)
     return RaTensor(x.data_ptr(), _dtype_code(x.dtype), x.shape[0], x.shape[1], x.shape[2], x.stride(0),
                     x.stride(1))
 
@@ -146,11 +178,14 @@ def ring_attn_step(q_blk, k_blk, v_blk, O, m, l, *, first_step: bool, scale: flo
     """One ring step on the GPU; O [Hq, Bq, d], m / l [Hq, Bq] fp32 are updated in place.
     cu_seqlens: int32 GPU tensor (doc-causal); key_bits: the key block's padding mask from
     ring_attn_pack_key_mask; stats: int64 GPU tensor of 3 counters (added to)."""
+    _view3(q_blk, "q_blk")
+    Bq, Hq, d = q_blk.shape
+    _f32_buffer(O, (Hq, Bq, d), "O")
+    _f32_buffer(m, (Hq, Bq), "m")
+    _f32_buffer(l, (Hq, Bq), "l")
     qt, kt, vt = _tensor(q_blk, "q_blk"), _tensor(k_blk, "k_blk"), _tensor(v_blk, "v_blk")
     for x, name in ((O, "O"), (m, "m"), (l, "l")):
         _gpu(x, name)
-        if x.dtype != torch.float32 or not x.is_contiguous():
-            raise ValueError("%s must be contiguous float32" % name)
     n_docs = 0
     if cu_seqlens is not None:
         _gpu(cu_seqlens, "cu_seqlens")
@@ -198,11 +233,18 @@ def _key_valid(key_valid, T: int):
 
 def ring_attn_finalize(O, m, l, out, lse=None, *, stream=None):
     """out[u, h, :] = O[h, u, :] / l[h, u]; lse[h, u] = m + ln l.  out: [Bq, Hq, d] view."""
+    if not isinstance(O, torch.Tensor) or O.dim() != 3:
+        raise ValueError("O must be a [Hq, Bq, d] tensor")
+    Hq, Bq, d = O.shape
+    _f32_buffer(O, (Hq, Bq, d), "O")
+    _f32_buffer(m, (Hq, Bq), "m")
+    _f32_buffer(l, (Hq, Bq), "l")
+    if not isinstance(out, torch.Tensor) or out.dim() != 3 or out.stride(2) != 1 or tuple(out.shape) != (Bq, Hq, d):
+        raise ValueError("out must be a [Bq, Hq, d] view with unit last stride")
+    if lse is not None:
+        _f32_buffer(lse, (Hq, Bq), "lse")
     for x, name in ((O, "O"), (m, "m"), (l, "l"), (out, "out")):
         _gpu(x, name)
-    Hq, Bq, d = O.shape
-    if out.dim() != 3 or out.stride(2) != 1 or tuple(out.shape) != (Bq, Hq, d):
-        raise ValueError("out must be a [Bq, Hq, d] view with unit last stride")
     if lse is not None:
         _gpu(lse, "lse")
     st = load_library().ring_attn_finalize(O.data_ptr(), m.data_ptr(), l.data_ptr(), Hq, Bq, d, out.data_ptr(),
@@ -213,15 +255,16 @@ def ring_attn_finalize(O, m, l, out, lse=None, *, stream=None):
 
 def ring_attn_merge(out_acc, lse_acc, out_blk, lse_blk, *, stream=None):
     """In-place log-sum-exp merge; out_* [rows, Hq, d] contiguous, lse_* [Hq, rows] fp32."""
-    for x, name in ((out_acc, "out_acc"), (lse_acc, "lse_acc"), (out_blk, "out_blk"), (lse_blk, "lse_blk")):
-        _gpu(x, name)
-        if not x.is_contiguous():
-            raise ValueError("%s must be contiguous" % name)
+    for x, name in ((out_acc, "out_acc"), (out_blk, "out_blk")):
+        if not isinstance(x, torch.Tensor) or x.dim() != 3 or not x.is_contiguous():
+            raise ValueError("%s must be a contiguous [rows, Hq, d] tensor" % name)
     if out_acc.dtype != out_blk.dtype or out_acc.shape != out_blk.shape:
         raise ValueError("out_acc and out_blk must match")
     rows, Hq, d = out_acc.shape
-    if tuple(lse_acc.shape) != (Hq, rows) or tuple(lse_blk.shape) != (Hq, rows):
-        raise ValueError("lse must be [Hq, rows]")
+    _f32_buffer(lse_acc, (Hq, rows), "lse_acc")
+    _f32_buffer(lse_blk, (Hq, rows), "lse_blk")
+    for x, name in ((out_acc, "out_acc"), (lse_acc, "lse_acc"), (out_blk, "out_blk"), (lse_blk, "lse_blk")):
+        _gpu(x, name)
     st = load_library().ring_attn_merge(out_acc.data_ptr(), lse_acc.data_ptr(), out_blk.data_ptr(),
                                         lse_blk.data_ptr(), _dtype_code(out_acc.dtype), Hq, rows, d,
                                         _stream(stream))
@@ -239,10 +282,9 @@ def ring_attn_forward(q, k, v, out, lse, *, n_blocks: int, layout: int, mask_mod
                       want_stats: bool = False, stream=None):
     """The whole one-GPU ring; out [T, Hq, d] contiguous; lse [Hq, T] fp32 or None.
     Returns the tallies (dict) when want_stats (this synchronises the stream)."""
+    _forward_operands(q, k, v, out, lse)
     qt, kt, vt = _tensor(q, "q"), _tensor(k, "k"), _tensor(v, "v")
     _gpu(out, "out")
-    if not out.is_contiguous():
-        raise ValueError("out must be contiguous")
     if lse is not None:
         _gpu(lse, "lse")
     _gpu(workspace, "workspace")

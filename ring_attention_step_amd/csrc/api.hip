@@ -5,6 +5,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <memory>
 #include <mutex>
 #include <vector>
 
@@ -70,21 +71,25 @@ hipError_t launch(const StepArgs& a, ra_dtype dt, hipStream_t st) {
 }
 
 // Side stream + events used by the prefetch path, created once per device.
+// A prefetch forward holds `enqueue` while it records and waits on them, so
+// that calls from several host threads cannot interleave their event pairs.
 struct PrefetchCtx {
     hipStream_t copy = nullptr;
     hipEvent_t copied[2] = {nullptr, nullptr};
     hipEvent_t consumed[2] = {nullptr, nullptr};
+    std::mutex enqueue;
 };
 
 hipError_t prefetch_ctx(PrefetchCtx** out) {
     static std::mutex mu;
-    static std::vector<PrefetchCtx> ctx;
+    static std::vector<std::unique_ptr<PrefetchCtx>> ctx;
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
     std::lock_guard<std::mutex> g(mu);
     if ((int)ctx.size() <= dev) ctx.resize(dev + 1);
-    PrefetchCtx& c = ctx[dev];
+    if (!ctx[dev]) ctx[dev].reset(new PrefetchCtx);
+    PrefetchCtx& c = *ctx[dev];
     if (!c.copy) {
         if ((e = hipStreamCreateWithFlags(&c.copy, hipStreamNonBlocking)) != hipSuccess) return e;
         for (int b = 0; b < 2; b++) {
@@ -300,8 +305,10 @@ ra_status ring_attn_step(const ra_tensor* q_blk, const ra_tensor* k_blk, const r
 ra_status ring_attn_finalize(const float* O, const float* m, const float* l, int64_t Hq, int64_t Bq, int64_t d,
                              void* out, ra_dtype out_dtype, int64_t out_stride_tok, int64_t out_stride_head,
                              float* lse, void* stream) {
-    if (!O || !m || !l || !out || Hq < 1 || Bq < 0 || d < 1 || !valid_dtype(out_dtype)) return RA_E_ARG;
+    if (Hq < 1 || Bq < 0 || d < 1 || !valid_dtype(out_dtype)) return RA_E_ARG;
     if (out_stride_tok < 0 || out_stride_head < 0) return RA_E_ARG;
+    if (Bq == 0) return RA_OK;  // an empty block: its pointers may be NULL
+    if (!O || !m || !l || !out) return RA_E_ARG;
     if (launch_finalize(O, m, l, Hq, Bq, d, out, (int)out_dtype, out_stride_tok, out_stride_head, lse,
                         (hipStream_t)stream) != hipSuccess)
         return RA_E_HIP;
@@ -310,8 +317,9 @@ ra_status ring_attn_finalize(const float* O, const float* m, const float* l, int
 
 ra_status ring_attn_merge(void* out_acc, float* lse_acc, const void* out_blk, const float* lse_blk,
                           ra_dtype dtype, int64_t Hq, int64_t rows, int64_t d, void* stream) {
-    if (!out_acc || !lse_acc || !out_blk || !lse_blk || !valid_dtype(dtype) || Hq < 1 || rows < 0 || d < 1)
-        return RA_E_ARG;
+    if (!valid_dtype(dtype) || Hq < 1 || rows < 0 || d < 1) return RA_E_ARG;
+    if (rows == 0) return RA_OK;  // nothing to merge: the pointers may be NULL
+    if (!out_acc || !lse_acc || !out_blk || !lse_blk) return RA_E_ARG;
     if (launch_merge(out_acc, lse_acc, out_blk, lse_blk, (int)dtype, Hq, rows, d, (hipStream_t)stream) !=
         hipSuccess)
         return RA_E_HIP;
@@ -404,10 +412,7 @@ ra_status ring_attn_forward(const ra_tensor* q, const ra_tensor* k, const ra_ten
     const int64_t N = n_blocks, B = T / N;
     const int64_t n_qtiles = (B + tq - 1) / tq;
     if (n_qtiles * Hq * kMaxPairs > INT32_MAX) return RA_E_UNSUPPORTED;
-    Workspace ws = carve(workspace, T, n_blocks, Hq, Hkv, d, n_docs, q->dtype, prefetch != 0);
-    if (!workspace || workspace_bytes < ws.total) return RA_E_WORKSPACE;
-    if ((uintptr_t)workspace % kAlign) return RA_E_WORKSPACE;
-    if (T == 0) {  // an empty sequence: nothing to launch
+    if (T == 0) {  // an empty sequence: nothing to launch, no workspace needed
         if (stats) {
             std::memset(stats, 0, sizeof *stats);
             stats->tile_q = tq;
@@ -415,6 +420,9 @@ ra_status ring_attn_forward(const ra_tensor* q, const ra_tensor* k, const ra_ten
         }
         return RA_OK;
     }
+    Workspace ws = carve(workspace, T, n_blocks, Hq, Hkv, d, n_docs, q->dtype, prefetch != 0);
+    if (!workspace || workspace_bytes < ws.total) return RA_E_WORKSPACE;
+    if ((uintptr_t)workspace % kAlign) return RA_E_WORKSPACE;
 
     hipStream_t st = (hipStream_t)stream;
     Ring r;
@@ -431,8 +439,10 @@ ra_status ring_attn_forward(const ra_tensor* q, const ra_tensor* k, const ra_ten
     const int64_t out_tok = Hq * d;  // out is [T, Hq, d] contiguous
 
     PrefetchCtx* pf = nullptr;
+    std::unique_lock<std::mutex> pf_lock;
     if (prefetch && r.passes > 1) {
         if (prefetch_ctx(&pf) != hipSuccess) return RA_E_HIP;
+        pf_lock = std::unique_lock<std::mutex>(pf->enqueue);
     }
 
     // ---- enqueue ----
@@ -726,10 +736,10 @@ ra_status ring_attn_backward(const ra_tensor* q, const ra_tensor* k, const ra_te
     const int64_t n_qtiles = (B + bwd_tile_q() - 1) / bwd_tile_q();
     const int64_t n_ktiles = (B + bwd_tile_k() - 1) / bwd_tile_k();
     if (N * Hq * n_qtiles * 256 > INT32_MAX || N * Hkv * n_ktiles * 256 > INT32_MAX) return RA_E_UNSUPPORTED;
+    if (T == 0) return RA_OK;  // an empty sequence needs no workspace
     BwdWorkspace ws = carve_bwd(workspace, T, N, Hq, n_docs);
     if (!workspace || workspace_bytes < ws.total) return RA_E_WORKSPACE;
     if ((uintptr_t)workspace % kAlign) return RA_E_WORKSPACE;
-    if (T == 0) return RA_OK;
 
     // ---- ring visits: device i's key blocks (ring order) and block j's visitors ----
     Ring r;

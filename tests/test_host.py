@@ -206,6 +206,17 @@ def test_empty_sequence_needs_no_buffers_and_launches_nothing(lib):
                                   None, 0, None, 0.1, ws, 1 << 40, None) == ra.RA_OK
     assert lib.ring_attn_step(R(q), R(k), R(k), None, None, None, 1, 0.1, 1, 0, 0, 1, None, 0, None, None,
                               None) == ra.RA_OK
+    # no workspace either
+    assert lib.ring_attn_forward(R(q), R(k), R(k), None, ra.RA_BF16, None, 4, 0, 1, 4, None, 0, None, 0.1, 0, None,
+                                 0, None, None) == ra.RA_OK
+    assert lib.ring_attn_backward(R(q), R(k), R(k), R(q), R(q), None, None, None, None, ra.RA_F32, 4, 0, 1, 4,
+                                  None, 0, None, 0.1, None, 0, None) == ra.RA_OK
+    # an empty block's state, and an empty merge, with NULL pointers
+    assert lib.ring_attn_finalize(None, None, None, 4, 0, 128, None, ra.RA_BF16, 512, 128, None, None) == ra.RA_OK
+    assert lib.ring_attn_merge(None, None, None, None, ra.RA_BF16, 4, 0, 128, None) == ra.RA_OK
+    # a non-empty one still needs them
+    assert lib.ring_attn_finalize(None, None, None, 4, 1, 128, None, ra.RA_BF16, 512, 128, None, None) == ra.RA_E_ARG
+    assert lib.ring_attn_merge(None, None, None, None, ra.RA_BF16, 4, 1, 128, None) == ra.RA_E_ARG
 
 
 def test_workspace_size_grows_with_prefetch(lib):
