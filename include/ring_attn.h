@@ -52,7 +52,8 @@ typedef enum {
     RA_E_ARG = 1,          /* invalid argument (shape, stride, pointer, value) */
     RA_E_UNSUPPORTED = 2,  /* valid but not implemented (dtype / head_dim / mask combination) */
     RA_E_HIP = 3,          /* a HIP runtime call or kernel launch failed */
-    RA_E_WORKSPACE = 4     /* workspace missing or smaller than ring_attn_forward_workspace_size */
+    RA_E_WORKSPACE = 4,    /* workspace missing or smaller than ring_attn_forward_workspace_size */
+    RA_E_TOO_LARGE = 5     /* shapes need more scratch than ring_attn_forward_noalloc holds */
 } ra_status;
 
 /* Element types.  16-bit values round to nearest even wherever the library
@@ -202,6 +203,30 @@ ra_status ring_attn_forward(const ra_tensor* q, const ra_tensor* k, const ra_ten
                             ra_mask mask_mode, int32_t max_ring_passes, const int32_t* cu_seqlens_host,
                             int32_t n_docs, const uint8_t* key_valid, float scale, int prefetch, void* workspace,
                             size_t workspace_bytes, ra_stats* stats, void* stream);
+
+/*
+ * ring_attn_forward without any device allocation, for callers that cannot
+ * allocate: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  Same arguments and results as ring_attn_forward
+ * with prefetch = 0, except that the workspace is a fixed array of
+ * ring_attn_forward_noalloc_scratch_bytes() (64 MiB) of device memory inside
+ * the library, one per GPU, which each GPU holds until the process ends.
+ * Shapes whose forward workspace (ring_attn_forward_workspace_size with
+ * prefetch = 0) exceeds it return RA_E_TOO_LARGE before any GPU work.  The
+ * caller still passes every input and output.  The call makes no device
+ * allocation (its host-side planning uses ordinary host memory).
+ * Every call on one GPU uses that GPU's one array, which keeps the last
+ * call's contents: calls that overlap on one GPU (several streams or host
+ * threads) race and must be ordered by the caller.
+ */
+ra_status ring_attn_forward_noalloc(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v, void* out,
+                                    ra_dtype out_dtype, float* lse, int32_t n_blocks, ra_layout layout,
+                                    ra_mask mask_mode, int32_t max_ring_passes,
+                                    const int32_t* cu_seqlens_host, int32_t n_docs,
+                                    const uint8_t* key_valid, float scale, ra_stats* stats, void* stream);
+
+/* Bytes of the fixed scratch ring_attn_forward_noalloc works in. */
+size_t ring_attn_forward_noalloc_scratch_bytes(void);
 
 /* Bytes of device workspace ring_attn_backward needs for these shapes. */
 size_t ring_attn_backward_workspace_size(const ra_tensor* q, int32_t n_blocks, int32_t n_docs);

@@ -24,7 +24,7 @@ import torch  # loaded first: the library then binds to torch's HIP runtime
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libring_attn.so")
 
-RA_OK, RA_E_ARG, RA_E_UNSUPPORTED, RA_E_HIP, RA_E_WORKSPACE = range(5)
+RA_OK, RA_E_ARG, RA_E_UNSUPPORTED, RA_E_HIP, RA_E_WORKSPACE, RA_E_TOO_LARGE = range(6)
 RA_F32, RA_BF16, RA_F16 = 0, 1, 2
 RA_MASK_NONE, RA_MASK_CAUSAL, RA_MASK_DOC_CAUSAL = 0, 1, 2
 RA_LAYOUT_CONTIGUOUS, RA_LAYOUT_STRIPED = 0, 1
@@ -78,6 +78,10 @@ def load_library():
     lib.ring_attn_forward_workspace_size.restype = _sz
     lib.ring_attn_forward.argtypes = [P(RaTensor), P(RaTensor), P(RaTensor), _vp, _int, _vp, _i32, _int, _int,
                                       _i32, _vp, _i32, _vp, _f32, _int, _vp, _sz, P(RaStats), _vp]
+    lib.ring_attn_forward_noalloc.argtypes = [P(RaTensor), P(RaTensor), P(RaTensor), _vp, _int, _vp, _i32, _int,
+                                              _int, _i32, _vp, _i32, _vp, _f32, P(RaStats), _vp]
+    lib.ring_attn_forward_noalloc_scratch_bytes.argtypes = []
+    lib.ring_attn_forward_noalloc_scratch_bytes.restype = _sz
     lib.ring_attn_backward_workspace_size.argtypes = [P(RaTensor), _i32, _i32]
     lib.ring_attn_backward_workspace_size.restype = _sz
     lib.ring_attn_backward.argtypes = [P(RaTensor), P(RaTensor), P(RaTensor), P(RaTensor), P(RaTensor), _vp, _vp,
@@ -86,7 +90,7 @@ def load_library():
     lib.ring_attn_tile_shape.argtypes = [_int, _i64, P(_i32), P(_i32)]
     lib.ring_attn_status_string.argtypes = [_int]
     lib.ring_attn_status_string.restype = ctypes.c_char_p
-    for fn in ("ring_attn_step", "ring_attn_finalize", "ring_attn_merge", "ring_attn_forward",
+    for fn in ("ring_attn_step", "ring_attn_finalize", "ring_attn_merge", "ring_attn_forward", "ring_attn_forward_noalloc",
                "ring_attn_plan", "ring_attn_tile_shape", "ring_attn_backward", "ring_attn_pack_key_mask"):
         getattr(lib, fn).restype = _int
     _lib = lib
@@ -303,6 +307,41 @@ def ring_attn_forward(q, k, v, out, lse, *, n_blocks: int, layout: int, mask_mod
     return stats.as_dict() if want_stats else None
 
 
+def ring_attn_forward_noalloc(q, k, v, out, lse, *, n_blocks: int, layout: int, mask_mode: int,
+                              max_ring_passes: int, cu_seqlens_host=None, key_valid=None, scale: float,
+                              want_stats: bool = False, stream=None):
+    """ring_attn_forward (no prefetch) in the library's fixed per-GPU scratch: no device memory is
+    allocated, here or in the library.  key_valid, when given, must already be a contiguous [T]
+    bool / uint8 GPU tensor.  Overlapping calls on one GPU race for the scratch."""
+    _forward_operands(q, k, v, out, lse)
+    qt, kt, vt = _tensor(q, "q"), _tensor(k, "k"), _tensor(v, "v")
+    _gpu(out, "out")
+    if lse is not None:
+        _gpu(lse, "lse")
+    cu_ptr, n_docs, cu_keep = None, 0, None
+    if cu_seqlens_host is not None:
+        cu_keep = torch.as_tensor(cu_seqlens_host).to(device="cpu", dtype=torch.int32).contiguous()
+        cu_ptr, n_docs = cu_keep.data_ptr(), cu_keep.numel() - 1
+    kv_ptr = None
+    if key_valid is not None:
+        _gpu(key_valid, "key_valid")
+        if key_valid.dim() != 1 or key_valid.shape[0] != q.shape[0] or not key_valid.is_contiguous() \
+                or key_valid.dtype not in (torch.bool, torch.uint8):
+            raise ValueError("key_valid must be a contiguous [T] bool or uint8 tensor")
+        kv_ptr = key_valid.data_ptr()
+    stats = RaStats()
+    st = load_library().ring_attn_forward_noalloc(
+        ctypes.byref(qt), ctypes.byref(kt), ctypes.byref(vt), out.data_ptr(), _dtype_code(out.dtype), _ptr(lse),
+        int(n_blocks), int(layout), int(mask_mode), int(max_ring_passes), cu_ptr, n_docs, kv_ptr, float(scale),
+        ctypes.byref(stats) if want_stats else None, _stream(stream))
+    _check("ring_attn_forward_noalloc", st)
+    return stats.as_dict() if want_stats else None
+
+
+def ring_attn_forward_noalloc_scratch_bytes() -> int:
+    return int(load_library().ring_attn_forward_noalloc_scratch_bytes())
+
+
 def ring_attn_backward_workspace_size(q, n_blocks: int, n_docs: int = 0) -> int:
     qt = _tensor(q, "q")
     return int(load_library().ring_attn_backward_workspace_size(ctypes.byref(qt), int(n_blocks), int(n_docs)))
@@ -428,4 +467,4 @@ def backward(q, k, v, out, lse, dout, *, n_blocks: int, layout: str = "contiguou
 __all__ = ["ring_attn_step", "ring_attn_finalize", "ring_attn_merge", "ring_attn_forward_workspace_size",
            "ring_attn_forward", "ring_attn_plan", "ring_attn_tile_shape", "ring_attn_backward_workspace_size",
            "ring_attn_backward", "ring_attn_pack_key_mask", "forward", "forward_qkvpacked", "backward",
-           "load_library", "RingAttnError"]
+           "ring_attn_forward_noalloc", "ring_attn_forward_noalloc_scratch_bytes", "load_library", "RingAttnError"]

@@ -101,6 +101,31 @@ hipError_t prefetch_ctx(PrefetchCtx** out) {
     return hipSuccess;
 }
 
+// Workspace of ring_attn_forward_noalloc: a fixed array in device memory,
+// one copy per GPU, held until the process ends.  Host code never passes the
+// array's name to a kernel or copy (on the host it is only a stand-in): each
+// device's address comes from hipGetSymbolAddress, taken once per device with
+// that device current.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+hipError_t scratch_address(void** out) {
+    static std::mutex mu;
+    static std::vector<void*> addr;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> g(mu);
+    if ((int)addr.size() <= dev) addr.resize(dev + 1, nullptr);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        if ((e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch))) != hipSuccess) return e;
+        addr[dev] = p;
+    }
+    *out = addr[dev];
+    return hipSuccess;
+}
+
 struct Workspace {
     unsigned long long* counters = nullptr;  // 4 x u64
     int32_t* cu = nullptr;
@@ -212,6 +237,7 @@ const char* ring_attn_status_string(ra_status s) {
         case RA_E_UNSUPPORTED: return "unsupported dtype / head_dim / mask combination";
         case RA_E_HIP: return "HIP runtime error";
         case RA_E_WORKSPACE: return "workspace missing or too small";
+        case RA_E_TOO_LARGE: return "shapes need more than the fixed scratch of ring_attn_forward_noalloc";
     }
     return "unknown status";
 }
@@ -676,6 +702,24 @@ ra_status ring_attn_forward(const ra_tensor* q, const ra_tensor* k, const ra_ten
     }
     return RA_OK;
 }
+
+ra_status ring_attn_forward_noalloc(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v, void* out,
+                                    ra_dtype out_dtype, float* lse, int32_t n_blocks, ra_layout layout,
+                                    ra_mask mask_mode, int32_t max_ring_passes, const int32_t* cu_seqlens_host,
+                                    int32_t n_docs, const uint8_t* key_valid, float scale, ra_stats* stats,
+                                    void* stream) {
+    // Invalid shapes size to 0 here and are refused by ring_attn_forward.
+    if (q && k) {
+        const int32_t docs = mask_mode == RA_MASK_DOC_CAUSAL ? n_docs : 0;
+        if (ring_attn_forward_workspace_size(q, k, n_blocks, docs, 0) > kScratchBytes) return RA_E_TOO_LARGE;
+    }
+    void* ws = nullptr;
+    if (scratch_address(&ws) != hipSuccess) return RA_E_HIP;
+    return ring_attn_forward(q, k, v, out, out_dtype, lse, n_blocks, layout, mask_mode, max_ring_passes,
+                             cu_seqlens_host, n_docs, key_valid, scale, 0, ws, kScratchBytes, stats, stream);
+}
+
+size_t ring_attn_forward_noalloc_scratch_bytes(void) { return kScratchBytes; }
 
 size_t ring_attn_backward_workspace_size(const ra_tensor* q, int32_t n_blocks, int32_t n_docs) {
     if (!q || n_blocks < 1 || n_docs < 0 || q->n_tok < 0 || q->n_head < 1) return 0;

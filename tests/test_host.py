@@ -49,7 +49,7 @@ def test_library_links_no_torch():
 
 
 def test_status_strings(lib):
-    for s in range(5):
+    for s in range(6):
         assert lib.ring_attn_status_string(s)
 
 
@@ -305,3 +305,14 @@ def test_backward_workspace_size(lib):
     assert n >= 4096 * 32 * 4 + 2 * 8 * 8 * 8
     assert lib.ring_attn_backward_workspace_size(ctypes.byref(q), 3, 0) == 0   # 4096 % 3
     assert lib.ring_attn_backward_workspace_size(ctypes.byref(q), 8, 1000) > n
+
+
+def test_noalloc_forward_refuses_shapes_beyond_its_scratch_before_any_gpu_work(lib):
+    # 65536 tokens x 8 kv heads x d 128 in bf16: the packed V^T alone is
+    # 128 MiB, over the fixed 64 MiB scratch; fake (never dereferenced)
+    # addresses, refused before any HIP call.
+    assert lib.ring_attn_forward_noalloc_scratch_bytes() == 64 << 20
+    q, k = _fake(65536, 8, 128), _fake(65536, 8, 128)
+    R = ctypes.byref
+    assert lib.ring_attn_forward_noalloc(R(q), R(k), R(k), ctypes.c_void_p(1 << 21), ra.RA_BF16, None, 8, 0, 1, 8,
+                                         None, 0, None, 0.1, None, None) == ra.RA_E_TOO_LARGE
