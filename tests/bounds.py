@@ -2,6 +2,7 @@
 computed in fp64 from the oracle's results (test infrastructure: the GPU
 parity tests compare against these; nothing here is on the product path)."""
 import numpy as np
+import torch
 
 import oracle
 
@@ -120,3 +121,75 @@ def backward_bounds_rows(q, k, v, g, N, layout, mask, P, docs, dt, heads, toks, 
         bk[:, h] += scale * np.outer(w, np.abs(qn[t, h]))
         bv[:, h] += u * np.outer(Pr, np.abs(gn[t, h]))
     return bq, bk, bv
+
+
+def forward_bound_rows(qh, kh, vh, N, layout, mask, P, docs, dt, heads, toks, lse, key_valid=None, chunk=512):
+    """forward_bound for the listed (head, token) rows only, without a [T, T]
+    matrix: each chunk of one head's rows is scored against the key range its
+    mask can allow.  lse: the oracle's lse of those rows.  Returns the bound
+    [n, d] and, per row, the number of keys it takes (n_keys) and the fp32
+    error bound of its lse:
+      the kernel's l is a recursive fp32 sum of n_keys positive terms,
+      |d ln l| <= (n_keys + 8) 2^-24 (a few rescales and the final ln add
+      8 more roundings); the scores are fp32 sums of d exact 16-bit products,
+      |d s| <= scale d 2^-24 sum_i |q_i| max_j |k_j,i|, which moves lse by as
+      much; and the result is an fp32 number, 2^-24 |lse|.
+    The weights are evaluated in fp32 on torch's threaded CPU ops (their
+    relative error, below 1e-5, is covered by widening the bound by 1e-3)."""
+    T, Hq, d = qh.shape
+    Hkv = kh.shape[1]
+    grp = Hq // Hkv
+    scale = 1.0 / np.sqrt(d)
+    u = U16[dt]
+    heads, toks = np.asarray(heads), np.asarray(toks)
+    t_all = torch.arange(T)
+    B = T // N
+    blk = t_all % N if layout == 1 else t_all // B
+    doc = torch.searchsorted(torch.as_tensor(np.asarray(docs[1:]), dtype=torch.int64), t_all, right=True) \
+        if mask == 2 else None
+    starts = np.asarray(docs[:-1]) if mask == 2 else None
+    kvm = None if key_valid is None else torch.as_tensor(np.asarray(key_valid, dtype=bool))
+    passes = min(P, N)
+    lse_all = np.asarray(lse)
+    bound = np.zeros((len(toks), d))
+    n_keys = np.zeros(len(toks), dtype=np.int64)
+    lse_tol = np.zeros(len(toks))
+    for h in np.unique(heads):
+        g = int(h) // grp
+        q = qh[:, int(h)].float()
+        k = kh[:, g].float()
+        va = vh[:, g].float().abs()
+        kmax = k.abs().max(dim=0).values.double().numpy()
+        sel = np.nonzero(heads == h)[0]
+        sel = sel[np.argsort(toks[sel], kind="stable")]
+        for c0 in range(0, len(sel), chunk):
+            idx = sel[c0:c0 + chunk]
+            rt_np = toks[idx]
+            rt = torch.as_tensor(rt_np)
+            lo, hi = 0, T
+            if mask >= 1:
+                hi = int(rt_np.max()) + 1
+            if mask == 2:
+                lo = int(starts[int(doc[int(rt_np.min())])])
+            keys = torch.arange(lo, hi)
+            ok = torch.ones(len(idx), hi - lo, dtype=torch.bool)
+            if passes < N:
+                ok &= (blk[rt][:, None] - blk[keys][None, :]) % N < passes
+            if mask >= 1:
+                ok &= keys[None, :] <= rt[:, None]
+            if mask == 2:
+                ok &= doc[keys][None, :] == doc[rt][:, None]
+            if kvm is not None:
+                ok &= kvm[keys][None, :]
+            lr = torch.as_tensor(lse_all[idx])
+            fin = torch.isfinite(lr)
+            ok &= fin[:, None]
+            s = (q[rt] @ k[keys].T) * scale - torch.where(fin, lr, torch.zeros_like(lr)).float()[:, None]
+            p = torch.where(ok, torch.exp(s), torch.zeros_like(s))
+            bound[idx] = (u * (1 + 1e-3)) * (p @ va[keys]).double().numpy()
+            n_keys[idx] = ok.sum(dim=1).numpy()
+            qa = q[rt].double().abs().numpy()
+            lr_np = lse_all[idx]
+            lse_tol[idx] = (2.0 ** -24) * (n_keys[idx] + 8) + scale * d * 2.0 ** -24 * (qa @ kmax) \
+                + 2.0 ** -24 * np.where(np.isfinite(lr_np), np.abs(lr_np), 0.0)
+    return bound, n_keys, lse_tol

@@ -15,7 +15,7 @@ import torch
 
 import oracle
 import workloads as W
-from bounds import forward_bound
+from bounds import forward_bound, forward_bound_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -490,6 +490,80 @@ def test_16bit_finalize_and_merge_round_the_fp32_results(ra, dt):
     torch.cuda.synchronize()
     assert torch.equal(lacc16, lacc32)
     assert torch.equal(acc16, acc32.to(TORCH16[dt]))
+    # both against the oracle's merge of the same two partial results: the
+    # fp32 one within a few fp32 roundings of the operands, the 16-bit one
+    # within the 16-bit rounding of the result on top (unit roundoff u)
+    oa, ob64 = o16.double().cpu().numpy(), ob.double().cpu().numpy()
+    ro, rl = oracle.merge(oa, lse.t().double().cpu().numpy(), ob64, lb.t().double().cpu().numpy())
+    f32_err = 2.0 ** -21 * (np.abs(oa) + np.abs(ob64) + 1.0)
+    e32 = np.abs(acc32.double().cpu().numpy() - ro)
+    e16 = np.abs(acc16.double().cpu().numpy() - ro)
+    u = {"bf16": 2.0 ** -8, "f16": 2.0 ** -11}[dt]
+    _say(dt, "merge vs oracle: fp32 err / tol", float((e32 / f32_err).max()), "16-bit err / tol",
+         float((e16 / (u * np.abs(ro) + f32_err)).max()))
+    assert (e32 <= f32_err).all()
+    assert (e16 <= u * np.abs(ro) + f32_err).all()
+    got_l = lacc32.t().double().cpu().numpy()
+    assert np.array_equal(np.isneginf(got_l), np.isneginf(rl))
+    fin = np.isfinite(rl)
+    assert (np.abs(got_l[fin] - rl[fin]) <= 2.0 ** -21 * (1 + np.abs(rl[fin]))).all()
+
+
+@pytest.mark.parametrize("name", ["p4_ring4_b8_d16", "p2_1024tok_d2_16blk"])
+@pytest.mark.parametrize("layout", [0, 1])
+@pytest.mark.parametrize("mask", [0, 1])
+def test_f32_prefetch_is_bit_identical(ra, name, layout, mask):
+    """fp32 inputs: the prefetching per-step path (its 2-D copies of K and V
+    into the double buffer) gives exactly the results of prefetch = 0, and
+    both meet the fp32 bar against the oracle."""
+    w = W.WORKLOADS[name]
+    x = W.make_inputs(w)
+    _say("f32 prefetch", name, "layout", layout, "mask", mask)
+    q, k, v = _dev(x["q"], x["k"], x["v"])
+    lay = "striped" if layout == 1 else "contiguous"
+    kw = dict(n_blocks=w.n_blocks, layout=lay, causal=mask == 1, scale=w.scale, return_lse=True)
+    a_out, a_lse = ra.forward(q, k, v, prefetch=False, **kw)
+    b_out, b_lse = ra.forward(q, k, v, prefetch=True, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(a_out, b_out) and torch.equal(a_lse, b_lse)
+    ref = oracle.forward(x["q"], x["k"], x["v"], n_blocks=w.n_blocks, layout=layout, mask=mask, scale=w.scale)
+    assert np.abs(a_out.cpu().double().numpy() - ref["out"]).max() <= F32_TOL
+    assert np.abs(a_lse.cpu().double().numpy() - ref["lse"]).max() <= F32_TOL
+
+
+F32_MASKED = [
+    # T, N, Hq, Hkv, d, layout, mask, P, docs
+    (960, 4, 2, 1, 40, 0, 2, 4, [0, 100, 101, 400, 700, 960]),   # doc-causal, GQA
+    (960, 4, 2, 2, 40, 0, 2, 2, [0, 100, 101, 400, 700, 960]),   # doc-causal, P < N
+    (2048, 4, 2, 2, 64, 0, 2, 3, "random"),
+    (1024, 8, 2, 2, 64, 0, 1, 3, None),                          # causal, P < N
+    (1024, 8, 4, 2, 64, 1, 1, 3, None),                          # striped causal, P < N
+    (1000, 4, 2, 2, 16, 0, 0, 2, None),                          # no mask, P < N, ragged tiles
+]
+
+
+@pytest.mark.parametrize("case", range(len(F32_MASKED)))
+def test_f32_doc_causal_and_pass_limits(ra, case):
+    """The fp32 kernel under document-causal masks and ring pass limits
+    against the oracle at the fp32 bar, with and without prefetch (bit-equal)."""
+    T, N, Hq, Hkv, d, layout, mask, P, docs = F32_MASKED[case]
+    if docs == "random":
+        docs = W.random_doc_cu_seqlens(T, 16, 900, seed=case).tolist()
+    _say("f32 masked", F32_MASKED[case][:8])
+    qh, kh, vh = W.random_qkv(T, Hq, Hkv, d, "f32", 4000 + case)
+    q, k, v = _dev(qh, kh, vh)
+    lay = "striped" if layout == 1 else "contiguous"
+    kw = dict(n_blocks=N, layout=lay, causal=mask == 1, cu_seqlens=docs, max_ring_passes=P, return_lse=True)
+    out, lse = ra.forward(q, k, v, prefetch=False, **kw)
+    out_p, lse_p = ra.forward(q, k, v, prefetch=True, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out_p) and torch.equal(lse, lse_p)
+    ref = oracle.forward(qh, kh, vh, n_blocks=N, layout=layout, mask=mask, max_ring_passes=P, cu_seqlens=docs)
+    assert np.abs(out.cpu().double().numpy() - ref["out"]).max() <= F32_TOL
+    got_lse = lse.cpu().double().numpy()
+    empty = np.isneginf(ref["lse"])
+    assert np.array_equal(np.isneginf(got_lse), empty)
+    assert np.abs(got_lse[~empty] - ref["lse"][~empty]).max() <= F32_TOL
 
 
 # ---------------------------------------------------------------------------
@@ -505,10 +579,69 @@ def _sample_rows(w, rng, n=48):
     return np.asarray(heads), np.asarray(toks)
 
 
-@pytest.mark.parametrize("name,dt,padded", [("causal32k_h32_d128_8blk", "bf16", False),
-                                            ("gqa_striped64k_h32kv8_d128_16blk", "bf16", False),
-                                            ("varlen_packed128k_h32_d128_8blk_p4", "bf16", False),
-                                            ("causal32k_h32_d128_8blk", "f16", False),
+# Two query heads per long workload whose every row is checked; for the GQA
+# one they read different kv heads (group of 4: kv heads 1 and 5).
+FULL_HEADS = {"causal32k_h32_d128_8blk": (3, 29), "gqa_striped64k_h32kv8_d128_16blk": (5, 22),
+              "varlen_packed128k_h32_d128_8blk_p4": (3, 29)}
+
+
+@pytest.mark.parametrize("name", list(FULL_HEADS))
+def test_long_workload_every_row_of_two_heads(ra, name):
+    """The benchmark launch at full size (every virtual device and query tile
+    of the two heads): each output element within the first-order rounding
+    bound of the 16-bit forward against the fp64 oracle, each lse within its
+    fp32 summation bound, -inf exactly where a row takes no key.  On the
+    causal 32K workload the prefetching per-step path is checked the same
+    way against the same oracle rows."""
+    w = W.WORKLOADS[name]
+    _say(name, "generating inputs")
+    x = W.make_inputs(w)
+    if w.packed:
+        qkv = x["qkv"].cuda()
+        q, k, v = qkv[:, 0], qkv[:, 1], qkv[:, 2]
+    else:
+        q, k, v = _dev(x["q"], x["k"], x["v"])
+    cu = x.get("cu_seqlens")
+    layout = "striped" if w.layout else "contiguous"
+    runs = {}
+    for prefetch in ((False, True) if name == "causal32k_h32_d128_8blk" else (False,)):
+        _say(name, "forward, prefetch", prefetch)
+        out, lse = ra.forward(q, k, v, n_blocks=w.n_blocks, layout=layout, causal=w.mask == 1, cu_seqlens=cu,
+                              max_ring_passes=w.max_ring_passes, out_dtype=torch.float32, return_lse=True,
+                              prefetch=prefetch)
+        torch.cuda.synchronize()
+        runs[prefetch] = (out.cpu(), lse.cpu())
+        del out, lse
+    del q, k, v
+    torch.cuda.empty_cache()
+    hs = FULL_HEADS[name]
+    heads = np.repeat(np.asarray(hs), w.T)
+    toks = np.tile(np.arange(w.T), len(hs))
+    group = w.Hq // w.Hkv
+    qs = x["q"][:, list(hs)]
+    ks = x["k"][:, [h // group for h in hs]]
+    vs = x["v"][:, [h // group for h in hs]]
+    local = np.repeat(np.arange(len(hs)), w.T)
+    _say(name, "oracle on", len(toks), "rows")
+    ref = oracle.forward(qs, ks, vs, n_blocks=w.n_blocks, layout=w.layout, mask=w.mask,
+                         max_ring_passes=w.max_ring_passes, cu_seqlens=cu, scale=w.scale, rows=(local, toks))
+    _say(name, "bounds")
+    bound, n_keys, lse_tol = forward_bound_rows(qs, ks, vs, w.n_blocks, w.layout, w.mask, w.max_ring_passes, cu,
+                                                w.dtype, local, toks, ref["lse"])
+    empty = n_keys == 0
+    assert np.array_equal(np.isneginf(ref["lse"]), empty)
+    for prefetch, (out, lse) in runs.items():
+        what = "%s prefetch=%s" % (name, prefetch)
+        got = out[toks, heads].double().numpy()
+        _check_fwd_bound(got, ref["out"], bound, what)
+        got_lse = lse[heads, toks].double().numpy()
+        assert np.array_equal(np.isneginf(got_lse), empty), what
+        err = np.abs(got_lse[~empty] - ref["lse"][~empty])
+        _say(what, "lse max err / tol", float((err / lse_tol[~empty]).max()))
+        assert (err <= lse_tol[~empty]).all(), what
+
+
+@pytest.mark.parametrize("name,dt,padded", [("causal32k_h32_d128_8blk", "f16", False),
                                             ("gqa_striped64k_h32kv8_d128_16blk", "bf16", True)])
 def test_long_workload_sampled_rows(ra, name, dt, padded):
     w = dataclasses.replace(W.WORKLOADS[name], dtype=dt)
