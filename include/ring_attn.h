@@ -228,6 +228,20 @@ ra_status ring_attn_forward_noalloc(const ra_tensor* q, const ra_tensor* k, cons
 /* Bytes of the fixed scratch ring_attn_forward_noalloc works in. */
 size_t ring_attn_forward_noalloc_scratch_bytes(void);
 
+/*
+ * Test hook, for checking the prefetch path's event ordering (not for
+ * production use): from now on every prefetch forward enqueues a bounded
+ * wait of copy_delay_us microseconds on its copy stream before each step's
+ * copies, and of compute_delay_us on the caller's stream before each step's
+ * compute (0 = none, the default; at most 100000 each, else RA_E_ARG).  The
+ * results must not change: each step's compute waits for its copies, and
+ * each copy waits until the step that last read its buffer is done (the
+ * "Ring Attention simulation" gist waits twice per step so that a receive
+ * buffer is never read before it is written nor overwritten while read).
+ * Process-wide; no GPU work at the call.
+ */
+ra_status ring_attn_test_prefetch_delays(uint32_t copy_delay_us, uint32_t compute_delay_us);
+
 /* Bytes of device workspace ring_attn_backward needs for these shapes. */
 size_t ring_attn_backward_workspace_size(const ra_tensor* q, int32_t n_blocks, int32_t n_docs);
 

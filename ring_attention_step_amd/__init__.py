@@ -82,6 +82,8 @@ def load_library():
                                               _int, _i32, _vp, _i32, _vp, _f32, P(RaStats), _vp]
     lib.ring_attn_forward_noalloc_scratch_bytes.argtypes = []
     lib.ring_attn_forward_noalloc_scratch_bytes.restype = _sz
+    lib.ring_attn_test_prefetch_delays.argtypes = [ctypes.c_uint32, ctypes.c_uint32]
+    lib.ring_attn_test_prefetch_delays.restype = _int
     lib.ring_attn_backward_workspace_size.argtypes = [P(RaTensor), _i32, _i32]
     lib.ring_attn_backward_workspace_size.restype = _sz
     lib.ring_attn_backward.argtypes = [P(RaTensor), P(RaTensor), P(RaTensor), P(RaTensor), P(RaTensor), _vp, _vp,
@@ -336,6 +338,13 @@ def ring_attn_forward_noalloc(q, k, v, out, lse, *, n_blocks: int, layout: int, 
         ctypes.byref(stats) if want_stats else None, _stream(stream))
     _check("ring_attn_forward_noalloc", st)
     return stats.as_dict() if want_stats else None
+
+
+def ring_attn_test_prefetch_delays(copy_delay_us: int, compute_delay_us: int):
+    """Test hook: bounded waits before every prefetch step's copies (copy stream) and compute
+    (caller's stream); 0 turns them off."""
+    _check("ring_attn_test_prefetch_delays",
+           load_library().ring_attn_test_prefetch_delays(int(copy_delay_us), int(compute_delay_us)))
 
 
 def ring_attn_forward_noalloc_scratch_bytes() -> int:

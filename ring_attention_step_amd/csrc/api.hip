@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstring>
 #include <memory>
@@ -79,6 +80,12 @@ struct PrefetchCtx {
     hipEvent_t consumed[2] = {nullptr, nullptr};
     std::mutex enqueue;
 };
+
+// Test hook of the prefetch path (0 = off): a bounded wait enqueued before
+// every step's copies on the copy stream, and before every step's compute
+// on the caller's stream, so that a test can make either side run late.
+std::atomic<uint32_t> g_copy_delay_us{0}, g_compute_delay_us{0};
+constexpr uint32_t kMaxDelayUs = 100000;
 
 hipError_t prefetch_ctx(PrefetchCtx** out) {
     static std::mutex mu;
@@ -599,6 +606,8 @@ ra_status ring_attn_forward(const ra_tensor* q, const ra_tensor* k, const ra_ten
         if (use_buf) {
             // The copy engine may overwrite this slot once step s-2 has read it.
             if (s >= 2 && hipStreamWaitEvent(pf->copy, pf->consumed[slot], 0) != hipSuccess) return RA_E_HIP;
+            if (const uint32_t us = g_copy_delay_us.load())
+                if (launch_spin(us, pf->copy) != hipSuccess) return RA_E_HIP;
             for (const StepPair& sp : pairs) {
                 const char* kb = (const char*)k->data + row_off(sp.j, k->stride_tok) * es;
                 const size_t kpitch = (size_t)(striped ? N : 1) * k->stride_tok * es;
@@ -619,6 +628,10 @@ ra_status ring_attn_forward(const ra_tensor* q, const ra_tensor* k, const ra_ten
             }
             if (hipEventRecord(pf->copied[slot], pf->copy) != hipSuccess) return RA_E_HIP;
             if (hipStreamWaitEvent(st, pf->copied[slot], 0) != hipSuccess) return RA_E_HIP;
+        }
+        if (pf) {
+            if (const uint32_t us = g_compute_delay_us.load())
+                if (launch_spin(us, st) != hipSuccess) return RA_E_HIP;
         }
         for (size_t c0 = 0; c0 < pairs.size(); c0 += kMaxPairs) {
             StepArgs a = base;
@@ -720,6 +733,13 @@ ra_status ring_attn_forward_noalloc(const ra_tensor* q, const ra_tensor* k, cons
 }
 
 size_t ring_attn_forward_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+ra_status ring_attn_test_prefetch_delays(uint32_t copy_delay_us, uint32_t compute_delay_us) {
+    if (copy_delay_us > kMaxDelayUs || compute_delay_us > kMaxDelayUs) return RA_E_ARG;
+    g_copy_delay_us.store(copy_delay_us);
+    g_compute_delay_us.store(compute_delay_us);
+    return RA_OK;
+}
 
 size_t ring_attn_backward_workspace_size(const ra_tensor* q, int32_t n_blocks, int32_t n_docs) {
     if (!q || n_blocks < 1 || n_docs < 0 || q->n_tok < 0 || q->n_head < 1) return 0;

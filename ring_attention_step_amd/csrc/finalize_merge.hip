@@ -111,6 +111,26 @@ hipError_t launch_merge(void* out_acc, float* lse_acc, const void* out_blk, cons
     return hipGetLastError();
 }
 
+// One wave that waits `ticks` of the constant-rate wall clock, then exits
+// (a bounded delay on a stream; used only by the prefetch ordering test hook).
+__global__ void spin_kernel(uint64_t ticks) {
+    const uint64_t t0 = wall_clock64();
+    while (wall_clock64() - t0 < ticks) __builtin_amdgcn_s_sleep(8);
+}
+
+hipError_t launch_spin(uint32_t us, hipStream_t stream) {
+    static int khz = 0;  // wall-clock rate of device 0's kind (the only GPU model this library targets)
+    if (!khz) {
+        int dev = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e == hipSuccess) e = hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev);
+        if (e != hipSuccess) return e;
+        if (khz <= 0) khz = 100000;
+    }
+    spin_kernel<<<1, 64, 0, stream>>>((uint64_t)us * (uint64_t)khz / 1000u);
+    return hipGetLastError();
+}
+
 hipError_t launch_fill_u64(unsigned long long* p, int64_t n, hipStream_t stream) {
     if (n == 0) return hipSuccess;
     fill_u64_kernel<<<grid_for(n, 256), 256, 0, stream>>>(p, n);

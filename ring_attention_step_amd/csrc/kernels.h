@@ -90,6 +90,8 @@ hipError_t launch_merge(void* out_acc, float* lse_acc, const void* out_blk, cons
                         int kind, int64_t Hq, int64_t rows, int64_t d, hipStream_t stream);
 // out_kind / kind: element type of out (0 fp32, 1 bf16, 2 fp16).
 hipError_t launch_fill_u64(unsigned long long* p, int64_t n, hipStream_t stream);
+// A bounded wait of `us` microseconds on `stream` (one wave).
+hipError_t launch_spin(uint32_t us, hipStream_t stream);
 
 // Key-padding bits of ring blocks: for block j < n_blocks and row w < B,
 // bit w % 32 of bits[j * words_per_block + w / 32] = (key_valid[pos] != 0),

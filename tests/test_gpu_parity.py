@@ -365,6 +365,37 @@ def test_bf16_packed_qkv_views(ra):
     _check_bf16(out.cpu().double().numpy(), ref["out"], "packed")
 
 
+@pytest.mark.parametrize("copy_us,compute_us", [(400, 0), (0, 400), (250, 250)])
+def test_prefetch_event_ordering_under_forced_delays(ra, copy_us, compute_us):
+    """The prefetch path's double buffer under adversarial timing: a bounded
+    wait before every step's copies (copies land late: a step that did not
+    wait for them would read the buffer's previous contents) or before every
+    step's compute (compute runs late: a copy that did not wait for the step
+    reading its buffer would overwrite it mid-read).  Results stay bit-exact:
+    fp32 equals prefetch = 0, and the 16-bit path equals its undelayed self."""
+    w = W.WORKLOADS["p2_1024tok_d2_16blk"]
+    x = W.make_inputs(w)
+    q32, k32, v32 = _dev(x["q"], x["k"], x["v"])
+    kw32 = dict(n_blocks=w.n_blocks, scale=w.scale, causal=True, return_lse=True)
+    qh, kh, vh = W.random_qkv(2048, 4, 2, 128, "bf16", 77)
+    q16, k16, v16 = _dev(qh, kh, vh)
+    kw16 = dict(n_blocks=8, causal=True, out_dtype=torch.float32, return_lse=True)
+    base32 = ra.forward(q32, k32, v32, prefetch=False, **kw32)
+    base16 = ra.forward(q16, k16, v16, prefetch=True, **kw16)
+    torch.cuda.synchronize()
+    _say("prefetch delays copy", copy_us, "us, compute", compute_us, "us")
+    try:
+        ra.ring_attn_test_prefetch_delays(copy_us, compute_us)
+        for rep in range(2):
+            got32 = ra.forward(q32, k32, v32, prefetch=True, **kw32)
+            got16 = ra.forward(q16, k16, v16, prefetch=True, **kw16)
+            torch.cuda.synchronize()
+            assert torch.equal(got32[0], base32[0]) and torch.equal(got32[1], base32[1]), rep
+            assert torch.equal(got16[0], base16[0]) and torch.equal(got16[1], base16[1]), rep
+    finally:
+        ra.ring_attn_test_prefetch_delays(0, 0)
+
+
 @pytest.mark.parametrize("dt", ["bf16", "f16"])
 def test_16bit_prefetch_matches_one_launch_ring(ra, dt):
     """The side-stream prefetch path (one launch per ring step, state through

@@ -316,3 +316,9 @@ def test_noalloc_forward_refuses_shapes_beyond_its_scratch_before_any_gpu_work(l
     R = ctypes.byref
     assert lib.ring_attn_forward_noalloc(R(q), R(k), R(k), ctypes.c_void_p(1 << 21), ra.RA_BF16, None, 8, 0, 1, 8,
                                          None, 0, None, 0.1, None, None) == ra.RA_E_TOO_LARGE
+
+
+def test_prefetch_delay_hook_bounds(lib):
+    assert lib.ring_attn_test_prefetch_delays(100001, 0) == ra.RA_E_ARG
+    assert lib.ring_attn_test_prefetch_delays(0, 100001) == ra.RA_E_ARG
+    assert lib.ring_attn_test_prefetch_delays(0, 0) == ra.RA_OK
