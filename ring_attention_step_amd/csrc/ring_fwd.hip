@@ -198,11 +198,6 @@ __global__ __launch_bounds__(THREADS, 1) void ring_fwd_kernel(const StepArgs a) 
         ds_max = doc_start(a.cu, a.n_docs, t_max);
     }
     const int nkt = (int)((a.Bk + BK - 1) / BK);
-    auto tile_cls = [&](int kt, int64_t k_pos0) __attribute__((always_inline)) {
-        const int64_t w0 = (int64_t)kt * BK, w1 = (a.Bk < w0 + BK ? a.Bk : w0 + BK) - 1;
-        return classify(a.mask, t_min, t_max, ds_min, ds_max, k_pos0 + w0 * a.pos_stride,
-                        k_pos0 + w1 * a.pos_stride);
-    };
     // The chain table: per block of the chain its non-skipped key tiles
     // [lo, hi] (skips are a prefix under doc-causal and a suffix under causal
     // masks), the fully visible ones [flo, fhi], the key-padding word offset,
@@ -222,19 +217,49 @@ __global__ __launch_bounds__(THREADS, 1) void ring_fwd_kernel(const StepArgs a) 
             koff = re.k_off;
             voff = re.vt_off;
             kpos = re.k_pos0;
-            hi = nkt - 1;
-            while (lo <= hi && tile_cls(lo, kpos) == kSkip) lo++;
-            while (hi >= lo && tile_cls(hi, kpos) == kSkip) hi--;
-            flo = lo;
-            fhi = hi;
-            while (flo <= fhi && tile_cls(flo, kpos) != kFull) flo++;
-            while (fhi >= flo && tile_cls(fhi, kpos) != kFull) fhi--;
-            if (a.stats && head == 0)
-                for (int kt = lo; kt <= hi; kt++) {
-                    const Cls c = tile_cls(kt, kpos);
-                    nfull += c == kFull;
-                    npart += c == kPartial;
+            // Each condition of classify() on a key tile is monotone in the
+            // tile index (key positions grow with it): the skipped tiles are
+            // a prefix (keys before the first row's document) and a suffix
+            // (keys after the last row), the full ones a range.  Bisection on
+            // the same conditions replaces a tile-by-tile scan.
+            auto tk_first = [&](int kt) { return kpos + (int64_t)kt * BK * a.pos_stride; };
+            auto tk_last = [&](int kt) {
+                const int64_t w1 = (a.Bk < (int64_t)kt * BK + BK ? a.Bk : (int64_t)kt * BK + BK) - 1;
+                return kpos + w1 * a.pos_stride;
+            };
+            // first kt in [0, nkt) where the monotone (false, then true) predicate holds, else nkt
+            auto first_true = [&](auto&& pred) {
+                int l = 0, h = nkt;
+                while (l < h) {
+                    const int m = (l + h) >> 1;
+                    if (pred(m)) h = m; else l = m + 1;
                 }
+                return l;
+            };
+            if (a.mask == kMaskNone) {
+                hi = nkt - 1;
+                flo = 0;
+                fhi = nkt - 1;
+            } else {
+                if (a.mask == kMaskDoc) lo = first_true([&](int kt) { return tk_last(kt) >= ds_min; });
+                hi = first_true([&](int kt) { return tk_first(kt) > t_max; }) - 1;
+                flo = a.mask == kMaskDoc ? first_true([&](int kt) { return tk_first(kt) >= ds_max; }) : 0;
+                fhi = first_true([&](int kt) { return tk_last(kt) > t_min; }) - 1;
+                if (flo < lo) flo = lo;
+                if (fhi > hi) fhi = hi;
+            }
+            if (lo > hi) {  // nothing visible
+                lo = 0;
+                hi = -1;
+            }
+            if (flo > fhi) {  // no full tile: an empty range
+                flo = hi + 1;
+                fhi = hi;
+            }
+            if (a.stats && head == 0) {
+                nfull = (unsigned)(fhi - flo + 1);
+                npart = (unsigned)(hi - lo + 1) - nfull;
+            }
             if (wave == 0) {
                 tab_i[0][lane] = lo;
                 tab_i[1][lane] = hi;
