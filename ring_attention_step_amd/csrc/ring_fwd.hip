@@ -192,6 +192,20 @@ __global__ __launch_bounds__(THREADS, 1) void ring_fwd_kernel(const StepArgs a) 
     const int64_t u0 = (int64_t)qt * BQ;
     const int64_t u_last = (a.Bq < u0 + BQ ? a.Bq : u0 + BQ) - 1;
     const int64_t t_min = q_pos0 + u0 * a.pos_stride, t_max = q_pos0 + u_last * a.pos_stride;
+
+    // This lane's query row.  Its Q and its document start are fetched first,
+    // so that their latency overlaps the chain table's loads below.
+    const int64_t urow = u0 + wave * 32 + col;
+    const bool row_ok = urow < a.Bq;
+    const int64_t t_row = q_pos0 + urow * a.pos_stride;
+    // Q^T as the B operand: lane holds q[row][16 kc + 8 half .. +7].
+    bf16x8 qf[D / 16];
+    {
+        const bf16* qp = (const bf16*)a.q + q_off + head * a.q_head_stride + urow * a.q_row_stride + 8 * half;
+#pragma unroll
+        for (int kc = 0; kc < D / 16; kc++) qf[kc] = row_ok ? *(const bf16x8*)(qp + 16 * kc) : bf16x8{};
+    }
+    const int64_t ds_row = (row_ok && a.mask == kMaskDoc) ? doc_start(a.cu, a.n_docs, t_row) : 0;
     int64_t ds_min = 0, ds_max = 0;
     if (a.mask == kMaskDoc) {
         ds_min = doc_start(a.cu, a.n_docs, t_min);
@@ -300,10 +314,6 @@ __global__ __launch_bounds__(THREADS, 1) void ring_fwd_kernel(const StepArgs a) 
     // it may see, as an index range [w_lo, w_hi) (keys at k_pos0 + w *
     // pos_stride): causal: w * pos_stride <= t - k_pos0;  doc-causal
     // (pos_stride 1) also w >= doc_start(t) - k_pos0;  and always w < Bk.
-    const int64_t urow = u0 + wave * 32 + col;
-    const bool row_ok = urow < a.Bq;
-    const int64_t t_row = q_pos0 + urow * a.pos_stride;
-    const int64_t ds_row = (row_ok && a.mask == kMaskDoc) ? doc_start(a.cu, a.n_docs, t_row) : 0;
     int w_lo = 0, w_hi = (int)a.Bk;
     auto row_bounds = [&](int64_t k_pos0) __attribute__((always_inline)) {
         w_lo = 0;
@@ -322,6 +332,7 @@ __global__ __launch_bounds__(THREADS, 1) void ring_fwd_kernel(const StepArgs a) 
     // A chain with no tile for this q-tile: its rows see no key (empty rows:
     // out = 0, lse = -inf).
     if (nT == 0) {
+        wait_loads_but<0>();  // the Q loads
         if (!row_ok) return;
         char* ob = (char*)a.out;
         const int64_t oe = out_off + urow * a.out_row_stride + head * a.out_head_stride + 4 * half;
@@ -337,13 +348,6 @@ __global__ __launch_bounds__(THREADS, 1) void ring_fwd_kernel(const StepArgs a) 
         return;
     }
 
-    // Q^T as the B operand: lane holds q[row][16 kc + 8 half .. +7].
-    bf16x8 qf[D / 16];
-    {
-        const bf16* qp = (const bf16*)a.q + q_off + head * a.q_head_stride + urow * a.q_row_stride + 8 * half;
-#pragma unroll
-        for (int kc = 0; kc < D / 16; kc++) qf[kc] = row_ok ? *(const bf16x8*)(qp + 16 * kc) : bf16x8{};
-    }
 
     // ---- cursors and loads ----
     const bf16* const k_all = (const bf16*)a.k + kvh * a.k_head_stride;
@@ -595,9 +599,8 @@ __global__ __launch_bounds__(THREADS, 1) void ring_fwd_kernel(const StepArgs a) 
 
 #pragma unroll
     for (int db = 0; db < D / 32; db++) o[db] = f32x16{};
-    // Q is in registers before any tile load is issued (the waits below then
-    // count tile loads only).
-    wait_loads_but<0>();
+    // The Q loads were issued before any tile load: the wait for batch A below
+    // covers them too (vector-memory loads complete in issue order).
     // Batch A: K_0, V_0, K_1; batch B: K_2, V_1.  V buffer 3 stands for
     // V_{-1} (P_{-1} = 0 multiplies it): zeroed.
     issue_k(kbuf(0), k_addr(ck), ck.kt);
