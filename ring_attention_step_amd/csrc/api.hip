@@ -141,6 +141,7 @@ struct Workspace {
     float* l = nullptr;
     char* vt = nullptr;     // packed V^T of all blocks (16-bit path): [N][Hkv][d][Bp]
     RingWork* works = nullptr;    // one-launch ring forward (16-bit): N works
+    unsigned* wq = nullptr;       //   its 8 work-queue counters
     RingEntry* entries = nullptr; //   and up to N x N chain entries
     uint32_t* kbits = nullptr;    // key-padding bits of every block: [N][key_words(B)]
     char* kv = nullptr;     // prefetch double buffers: K [2][N][B][Hkv][d], then V (f32) or V^T (16-bit)
@@ -185,6 +186,7 @@ Workspace carve(void* base, int64_t T, int64_t N, int64_t Hq, int64_t Hkv, int64
     if (is16(dt)) {
         w.vt = take(vt_bytes);
         w.works = (RingWork*)take(sizeof(RingWork) * (size_t)N);
+        w.wq = (unsigned*)take(8 * sizeof(unsigned));
         w.entries = (RingEntry*)take(sizeof(RingEntry) * (size_t)N * (size_t)N);
     }
     if (prefetch) {
@@ -584,6 +586,9 @@ ra_status ring_attn_forward(const ra_tensor* q, const ra_tensor* k, const ra_ten
                 a.vt_head_stride = d * Bp;
                 a.works = ws.works;
                 a.entries = ws.entries;
+                a.wq = ws.wq;
+                // the work queues start at zero (a fill kernel, no memset node under graph capture)
+                if (launch_fill_u64((unsigned long long*)ws.wq, 4, st) != hipSuccess) return RA_E_HIP;
                 a.n_pairs = (int32_t)works.size();
                 if (launch(a, q->dtype, st) != hipSuccess) return RA_E_HIP;
             }

@@ -67,6 +67,7 @@ struct StepArgs {
     // RingWork entries (pairs[] is unused), each finalised at its end.
     const RingWork* works;
     const RingEntry* entries;
+    unsigned* wq;                          // its 8 work-queue counters, zero at the launch
     // Key-padding mask (nullable): bit w % 32 of word kb_off + w / 32 is set
     // when key row w of a block takes part; a block's bits are whole 64-key
     // tiles (2 words each, 8-byte aligned), zero past its last row.

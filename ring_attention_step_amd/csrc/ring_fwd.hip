@@ -164,13 +164,27 @@ __global__ __launch_bounds__(THREADS, 1) void ring_fwd_kernel(const StepArgs a) 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int half = lane >> 5, col = lane & 31;
+    // The chain table of the current item (see below) and the item number.
+    __shared__ int tab_i[5][kMaxRingChain];
+    __shared__ int64_t tab_l[3][kMaxRingChain];
+    __shared__ int item_s;
 
-    // Workgroup -> (work, head, q-tile): consecutive workgroup ids go to the
-    // 8 XCDs in turn; (work, head) groups are dealt to the XCDs round robin,
-    // each group's q-tiles on one XCD (its L2 serves the group's key/value
-    // tiles), heavy works first; within a group the q-tiles with the most key
-    // tiles (causal) start first.
-    const int nwg = gridDim.x, b = blockIdx.x;
+    // Items are (work, head, q-tile) triples, numbered so that consecutive
+    // numbers go to the 8 XCDs in turn; (work, head) groups are dealt to the
+    // XCDs round robin, each group's q-tiles on one XCD (its L2 serves the
+    // group's key/value tiles), heavy works first; within a group the q-tiles
+    // with the most key tiles (causal) come first.  The launch holds one
+    // workgroup per compute unit; workgroup w (on XCD w mod 8 under the
+    // round-robin dispatch) takes the items of queue w mod 8 (numbers = that
+    // queue index mod 8, in order), and when its queue is empty takes the
+    // next item of another queue: XCDs that run faster (clocks differ between
+    // them under a power cap) or whose items are shorter take more work, and
+    // the launch ends when the work ends.
+    const int n_items = a.n_qtiles * a.Hq * a.n_pairs;
+    const int own_q = blockIdx.x & 7;
+    unsigned q_done = 0;  // thread 0: queues found empty
+    auto run_item = [&](const int b) __attribute__((always_inline)) {
+    const int nwg = n_items;
     const int n_groups = nwg / a.n_qtiles;
     int grp_id, qt;
     if (n_groups % 8 == 0) {
@@ -217,8 +231,6 @@ __global__ __launch_bounds__(THREADS, 1) void ring_fwd_kernel(const StepArgs a) 
     // masks), the fully visible ones [flo, fhi], the key-padding word offset,
     // its offsets and first key position.  Computed one block per lane, then
     // kept in LDS, where the cursors read it when they move on to a block.
-    __shared__ int tab_i[5][kMaxRingChain];
-    __shared__ int64_t tab_l[3][kMaxRingChain];
     int nT = 0;  // tiles of the whole chain; tallies counted once per q-tile
     {
         int lo = 0, hi = -1, flo = 0, fhi = -1;
@@ -662,13 +674,49 @@ __global__ __launch_bounds__(THREADS, 1) void ring_fwd_kernel(const StepArgs a) 
     if (half == 0 && a.lse)
         a.lse[lse_off + head * a.lse_head_stride + urow * a.lse_row_stride] =
             ltot > 0.f ? mx * a.scale + logf(ltot) : -INFINITY;
+    };  // run_item
+
+    // Every fetch tries each queue at most once, and a queue once found empty
+    // is not tried again: the loop ends for every workgroup once all queues
+    // are drained.  The barriers keep the item number and the LDS (tables,
+    // tile buffers) of one item apart from the next.
+    for (;;) {
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            int it = -1;
+            for (int k = 0; k < 8 && it < 0; k++) {
+                const int y = (own_q + k) & 7;
+                if ((q_done >> y) & 1u) continue;
+                const int len = y < n_items ? (n_items - y + 7) / 8 : 0;
+                const unsigned i = atomicAdd(&a.wq[y], 1u);
+                if ((int)i < len) it = 8 * (int)i + y;
+                else q_done |= 1u << y;
+            }
+            item_s = it;
+        }
+        __syncthreads();
+        const int b = __builtin_amdgcn_readfirstlane(item_s);
+        if (b < 0) break;
+        run_item(b);
+    }
 }
 
 template <typename E, bool KP>
 hipError_t launch16(const StepArgs& a, hipStream_t stream) {
-    const int64_t nwg = (int64_t)a.n_qtiles * a.Hq * a.n_pairs;
-    if (nwg == 0) return hipSuccess;
-    const dim3 grid((unsigned)nwg), block(THREADS);
+    const int64_t n_items = (int64_t)a.n_qtiles * a.Hq * a.n_pairs;
+    if (n_items == 0) return hipSuccess;
+    if (!a.wq || n_items > INT32_MAX) return hipErrorInvalidValue;
+    static int n_cu[64] = {0};  // compute units per device, queried once
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    if (!n_cu[dev]) {
+        int c = 0;
+        if ((e = hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+        n_cu[dev] = c > 0 ? c : 1;
+    }
+    const dim3 grid((unsigned)(n_items < n_cu[dev] ? n_items : n_cu[dev])), block(THREADS);
     if (a.d == 128) ring_fwd_kernel<E, 128, KP><<<grid, block, 0, stream>>>(a);
     else if (a.d == 64) ring_fwd_kernel<E, 64, KP><<<grid, block, 0, stream>>>(a);
     else return hipErrorInvalidValue;
