@@ -83,7 +83,13 @@ typedef struct {
  * block j) visited at some ring step; a tile is tile_q query rows x tile_k key
  * columns of a block pair (the last tile on each side may be short).  SKIP: no
  * allowed (query, key) pair, never computed; FULL: every pair allowed,
- * computed without a mask; PARTIAL: computed with a per-element mask. */
+ * computed without a mask; PARTIAL: computed with a per-element mask.
+ * tile_q / tile_k: the tile shape counted.  ring_attn_forward's 16-bit
+ * one-launch ring gives each work item the h query heads of a kv head that
+ * share its key/value tiles (h the largest power of two <= 8 dividing
+ * Hq / Hkv; grouped-query attention, named on the flash-attention scrape
+ * page), and tiles of tile_q / h rows: its tallies count those (tile_q =
+ * 256 / h); ring_attn_plan and ring_attn_tile_shape give the 256-row tile. */
 typedef struct {
     int64_t block_pairs_visited, block_pairs_skipped, block_pairs_full, block_pairs_partial;
     int64_t tiles_skipped, tiles_full, tiles_partial;

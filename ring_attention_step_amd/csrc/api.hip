@@ -470,6 +470,15 @@ ra_status ring_attn_forward(const ra_tensor* q, const ra_tensor* k, const ra_ten
     r.cu = cu_seqlens_host;
     r.n_docs = n_docs;
     const Plan plan = make_plan(r, tq, tk);
+    // The one-launch ring serves hpi query heads of a kv head per work item
+    // (the largest power of two <= 8 dividing the group), tq / hpi rows each;
+    // its tiles, and so its tallies, are tq / hpi rows tall.
+    int hpi = 1;
+    if (is16(q->dtype))
+        while (hpi < 8 && (Hq / Hkv) % (2 * hpi) == 0) hpi *= 2;
+    const int tq_ring = tq / hpi;
+    const int64_t n_qtiles_ring = (B + tq_ring - 1) / tq_ring;
+    const Plan plan_ring = hpi > 1 ? make_plan(r, tq_ring, tk) : Plan{};
     const bool striped = layout == RA_LAYOUT_STRIPED;
     const int64_t out_tok = Hq * d;  // out is [T, Hq, d] contiguous
 
@@ -543,7 +552,7 @@ ra_status ring_attn_forward(const ra_tensor* q, const ra_tensor* k, const ra_ten
             for (const StepPair& sp : plan.steps[s]) chain[sp.i].push_back(sp.j);
         size_t longest = 0;
         for (const auto& c : chain) longest = std::max(longest, c.size());
-        if (longest <= (size_t)kMaxRingChain && n_qtiles * Hq * N <= INT32_MAX) {
+        if (longest <= (size_t)kMaxRingChain && n_qtiles_ring * (Hq / hpi) * N <= INT32_MAX) {
             std::vector<int32_t> order;
             for (int64_t i = 0; i < N; i++)
                 if (!chain[i].empty()) order.push_back((int32_t)i);
@@ -587,6 +596,8 @@ ra_status ring_attn_forward(const ra_tensor* q, const ra_tensor* k, const ra_ten
                 a.works = ws.works;
                 a.entries = ws.entries;
                 a.wq = ws.wq;
+                a.hpi = hpi;
+                a.n_qtiles = (int32_t)n_qtiles_ring;
                 // the work queues start at zero (a fill kernel, no memset node under graph capture)
                 if (launch_fill_u64((unsigned long long*)ws.wq, 4, st) != hipSuccess) return RA_E_HIP;
                 a.n_pairs = (int32_t)works.size();
@@ -711,11 +722,13 @@ ra_status ring_attn_forward(const ra_tensor* q, const ra_tensor* k, const ra_ten
         stats->block_pairs_skipped = plan.skipped;
         stats->block_pairs_full = plan.full;
         stats->block_pairs_partial = plan.partial;
-        stats->tiles_skipped = (int64_t)c[0] + plan.tiles_in_skipped_pairs;
+        // the one-launch ring counted tiles of its own height
+        const bool ring_tiles = ring_done && hpi > 1;
+        stats->tiles_skipped = (int64_t)c[0] + (ring_tiles ? plan_ring : plan).tiles_in_skipped_pairs;
         stats->tiles_full = (int64_t)c[1];
         stats->tiles_partial = (int64_t)c[2];
         stats->allowed_pairs = allowed_pairs(r);
-        stats->tile_q = tq;
+        stats->tile_q = ring_tiles ? tq_ring : tq;
         stats->tile_k = tk;
     }
     return RA_OK;

@@ -1,12 +1,15 @@
 // The ring forward in one launch on the gfx950 matrix cores: 16-bit Q, K, V
 // (bf16 or fp16, the kernel's E), fp32 accumulation.
 //
-// A workgroup owns tile_q = 256 query rows of one head of one virtual device
-// and walks that device's visited key/value blocks in ring order ("Ring
-// Attention" glossary page, worked example: device i holds key/value block
-// i - s at step s), the online-softmax state (running reference, denominator,
-// unnormalised output) staying in registers from the first block to the fused
-// finalize.  Eight waves of 32 query rows, two per SIMD.
+// A work item is 256 query rows of one virtual device: 256 rows of one head,
+// or, when several query heads share a kv head (grouped-query attention),
+// 256 / h rows of each of h heads of one group, so that the key/value tiles
+// it streams serve them all.  It walks the device's visited key/value blocks
+// in ring order ("Ring Attention" glossary page, worked example: device i
+// holds key/value block i - s at step s), the online-softmax state (running
+// reference, denominator, unnormalised output) staying in registers from the
+// first block to the fused finalize.  Eight waves of 32 query rows, two per
+// SIMD.
 //
 // Every wave runs the whole pipeline by itself -- no phases shared with the
 // other wave of its SIMD -- so that the two waves of a SIMD issue LDS reads,
@@ -169,8 +172,8 @@ __global__ __launch_bounds__(THREADS, 1) void ring_fwd_kernel(const StepArgs a) 
     __shared__ int64_t tab_l[3][kMaxRingChain];
     __shared__ int item_s;
 
-    // Items are (work, head, q-tile) triples, numbered so that consecutive
-    // numbers go to the 8 XCDs in turn; (work, head) groups are dealt to the
+    // Items are (work, head block, q-tile) triples, numbered so that
+    // consecutive numbers go to the 8 XCDs in turn; (work, head block) groups are dealt to the
     // XCDs round robin, each group's q-tiles on one XCD (its L2 serves the
     // group's key/value tiles), heavy works first; within a group the q-tiles
     // with the most key tiles (causal) come first.  The launch holds one
@@ -180,7 +183,7 @@ __global__ __launch_bounds__(THREADS, 1) void ring_fwd_kernel(const StepArgs a) 
     // next item of another queue: XCDs that run faster (clocks differ between
     // them under a power cap) or whose items are shorter take more work, and
     // the launch ends when the work ends.
-    const int n_items = a.n_qtiles * a.Hq * a.n_pairs;
+    const int n_items = a.n_qtiles * (a.Hq / a.hpi) * a.n_pairs;
     const int own_q = blockIdx.x & 7;
     unsigned q_done = 0;  // thread 0: queues found empty
     auto run_item = [&](const int b) __attribute__((always_inline)) {
@@ -195,21 +198,27 @@ __global__ __launch_bounds__(THREADS, 1) void ring_fwd_kernel(const StepArgs a) 
         grp_id = b / a.n_qtiles;
         qt = a.n_qtiles - 1 - b % a.n_qtiles;
     }
-    const int head = grp_id % a.Hq;
-    const int widx = grp_id / a.Hq;
-    const int kvh = head / a.group;
+    // An item covers hpi query heads of one kv head (hpi divides the group),
+    // 256 / hpi rows of each: wave w takes head w / (8 / hpi) of the item and
+    // its row block w mod (8 / hpi), so that every key/value tile loaded into
+    // LDS serves all hpi heads.
+    const int hpi = a.hpi, wph = WAVES / hpi, rpi = 32 * wph;
+    const int head_blk = grp_id % (a.Hq / hpi);
+    const int widx = grp_id / (a.Hq / hpi);
+    const int head = head_blk * hpi + wave / wph;
+    const int kvh = head_blk * hpi / a.group;
 
     const RingWork& wk = a.works[widx];
     const int64_t q_off = wk.q_off, q_pos0 = wk.q_pos0, out_off = wk.out_off, lse_off = wk.lse_off;
     const int e_first = wk.first, n_ent = wk.count;
 
-    const int64_t u0 = (int64_t)qt * BQ;
-    const int64_t u_last = (a.Bq < u0 + BQ ? a.Bq : u0 + BQ) - 1;
+    const int64_t u0 = (int64_t)qt * rpi;
+    const int64_t u_last = (a.Bq < u0 + rpi ? a.Bq : u0 + rpi) - 1;
     const int64_t t_min = q_pos0 + u0 * a.pos_stride, t_max = q_pos0 + u_last * a.pos_stride;
 
     // This lane's query row.  Its Q and its document start are fetched first,
     // so that their latency overlaps the chain table's loads below.
-    const int64_t urow = u0 + wave * 32 + col;
+    const int64_t urow = u0 + (wave % wph) * 32 + col;
     const bool row_ok = urow < a.Bq;
     const int64_t t_row = q_pos0 + urow * a.pos_stride;
     // Q^T as the B operand: lane holds q[row][16 kc + 8 half .. +7].
@@ -282,7 +291,7 @@ __global__ __launch_bounds__(THREADS, 1) void ring_fwd_kernel(const StepArgs a) 
                 flo = hi + 1;
                 fhi = hi;
             }
-            if (a.stats && head == 0) {
+            if (a.stats && head_blk == 0) {
                 nfull = (unsigned)(fhi - flo + 1);
                 npart = (unsigned)(hi - lo + 1) - nfull;
             }
@@ -305,7 +314,7 @@ __global__ __launch_bounds__(THREADS, 1) void ring_fwd_kernel(const StepArgs a) 
             n_full += __builtin_amdgcn_readlane((int)nfull, e);
             n_part += __builtin_amdgcn_readlane((int)npart, e);
         }
-        if (a.stats && head == 0 && threadIdx.x == 0) {
+        if (a.stats && head_blk == 0 && threadIdx.x == 0) {
             atomicAdd(&a.stats[0], (unsigned long long)n_skip);
             atomicAdd(&a.stats[1], (unsigned long long)n_full);
             atomicAdd(&a.stats[2], (unsigned long long)n_part);
@@ -703,7 +712,8 @@ __global__ __launch_bounds__(THREADS, 1) void ring_fwd_kernel(const StepArgs a) 
 
 template <typename E, bool KP>
 hipError_t launch16(const StepArgs& a, hipStream_t stream) {
-    const int64_t n_items = (int64_t)a.n_qtiles * a.Hq * a.n_pairs;
+    if (a.hpi < 1 || a.hpi > WAVES || (a.hpi & (a.hpi - 1)) || a.group % a.hpi) return hipErrorInvalidValue;
+    const int64_t n_items = (int64_t)a.n_qtiles * (a.Hq / a.hpi) * a.n_pairs;
     if (n_items == 0) return hipSuccess;
     if (!a.wq || n_items > INT32_MAX) return hipErrorInvalidValue;
     static int n_cu[64] = {0};  // compute units per device, queried once
