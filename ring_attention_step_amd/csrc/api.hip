@@ -207,6 +207,7 @@ struct BwdWorkspace {
     BwdWork* rworks = nullptr;      // N
     int64_t* rpartners = nullptr;   // N x N
     uint32_t* kbits = nullptr;      // key-padding bits: [N][key_words(B)]
+    unsigned* wq = nullptr;         // 16 work-queue counters of the dq and dk/dv kernels
     size_t total = 0;
 };
 
@@ -228,6 +229,7 @@ BwdWorkspace carve_bwd(void* base, int64_t T, int64_t N, int64_t Hq, int64_t n_d
     w.rworks = (BwdWork*)take(sizeof(BwdWork) * (size_t)N);
     w.rpartners = (int64_t*)take(sizeof(int64_t) * (size_t)(N * N));
     w.kbits = (uint32_t*)take(sizeof(uint32_t) * (size_t)(N * key_words(N > 0 ? T / N : 0)));
+    w.wq = (unsigned*)take(16 * sizeof(unsigned));
     w.total = off;
     return w;
 }
@@ -934,6 +936,9 @@ ra_status ring_attn_backward(const ra_tensor* q, const ra_tensor* k, const ra_te
     a.partners = ws.partners;
     a.rworks = ws.rworks;
     a.rpartners = ws.rpartners;
+    // the kernels' work queues start at zero (a fill kernel, no memset node under graph capture)
+    a.wq = ws.wq;
+    if (launch_fill_u64((unsigned long long*)ws.wq, 8, st) != hipSuccess) return RA_E_HIP;
     if (launch_backward(a, st) != hipSuccess) return RA_E_HIP;
     return RA_OK;
 }

@@ -284,13 +284,36 @@ __device__ __forceinline__ void xcd_map(int b, int nwg, int per_group, int& grou
     }
 }
 
-// Non-skipped streamed tiles of a block: [lo, hi] (hi < lo when none).
-template <typename Cls3>
-__device__ __forceinline__ void tile_range(int n_tiles, Cls3 cls, int& lo, int& hi) {
-    lo = 0;
-    hi = n_tiles - 1;
-    while (lo <= hi && cls(lo) == kSkip) lo++;
-    while (hi >= lo && cls(hi) == kSkip) hi--;
+// First index in [0, n) where a predicate that is false, then true, holds
+// (n when it never does).  Every condition of classify() on a streamed tile
+// is monotone in the tile index (positions grow with it; document starts
+// too), so the skipped prefix and suffix and the fully visible range of a
+// block are found by bisection on those conditions.
+template <typename Pred>
+__device__ __forceinline__ int first_true(int n, Pred pred) {
+    int l = 0, h = n;
+    while (l < h) {
+        const int m = (l + h) >> 1;
+        if (pred(m)) h = m;
+        else l = m + 1;
+    }
+    return l;
+}
+
+// The non-skipped range [lo, hi] and the fully visible one [flo, fhi] of a
+// block, normalised: (0, -1) when nothing is visible, (hi + 1, hi) when no
+// tile is full.
+__device__ __forceinline__ void tile_bounds_fix(int& lo, int& hi, int& flo, int& fhi) {
+    if (flo < lo) flo = lo;
+    if (fhi > hi) fhi = hi;
+    if (lo > hi) {
+        lo = 0;
+        hi = -1;
+    }
+    if (flo > fhi) {
+        flo = hi + 1;
+        fhi = hi;
+    }
 }
 
 // ---- dq ----
@@ -304,6 +327,11 @@ __global__ __launch_bounds__(DQ_THREADS, 1) void bwd_dq_kernel(const BwdArgs a) 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int half = lane >> 5, col = lane & 31;
+    __shared__ int item_s;
+    const int n_items = a.n_works * a.Hq * a.n_qtiles;
+    const int own_q = blockIdx.x & 7;
+    unsigned q_done = 0;  // thread 0: queues found empty
+    auto run_item = [&](const int b) __attribute__((always_inline)) {
     // Workgroup -> (device, head, q-tile): the q-tiles of one (device, head)
     // group share every K/V tile they stream, so they run on one XCD (whose
     // L2 then serves the re-reads); consecutive workgroup ids go to the 8
@@ -311,7 +339,7 @@ __global__ __launch_bounds__(DQ_THREADS, 1) void bwd_dq_kernel(const BwdArgs a) 
     // group the q-tiles run last first (under causal masks they have the
     // most keys).
     int grp_id, qi;
-    xcd_map(blockIdx.x, gridDim.x, a.n_qtiles, grp_id, qi);
+    xcd_map(b, n_items, a.n_qtiles, grp_id, qi);
     const int qt = a.n_qtiles - 1 - qi;
     const int head = grp_id % a.Hq;
     const int widx = grp_id / a.Hq;
@@ -348,10 +376,6 @@ __global__ __launch_bounds__(DQ_THREADS, 1) void bwd_dq_kernel(const BwdArgs a) 
     const int64_t ds_min = a.mask == kMaskDoc ? doc_start(a.cu, a.n_docs, t_min) : 0;
     const int64_t ds_max = a.mask == kMaskDoc ? doc_start(a.cu, a.n_docs, t_max) : 0;
     const int nkt = (int)((B + BW_T - 1) / BW_T);
-    auto cls_of = [&](int64_t kp, int kt) __attribute__((always_inline)) {
-        const int64_t w0 = (int64_t)kt * BW_T, w1 = (B < w0 + BW_T ? B : w0 + BW_T) - 1;
-        return classify(a.mask, t_min, t_max, ds_min, ds_max, kp + w0 * ps, kp + w1 * ps);
-    };
     // The chain table, one visited block per lane (lane e < count holds
     // block e): its first position, non-skipped key tiles [lo, hi] and fully
     // visible ones [flo, fhi] (contiguous, between the partial tiles).  The
@@ -365,10 +389,20 @@ __global__ __launch_bounds__(DQ_THREADS, 1) void bwd_dq_kernel(const BwdArgs a) 
     if (lane < w.count) {
         const int64_t kp = a.partners[w.first + lane];
         tb_kp = (int)kp;
-        tile_range(nkt, [&](int x) { return cls_of(kp, x); }, tb_lo, tb_hi);
-        int flo = tb_lo, fhi = tb_hi;
-        while (flo <= fhi && cls_of(kp, flo) != kFull) flo++;
-        while (fhi >= flo && cls_of(kp, fhi) != kFull) fhi--;
+        // classify()'s conditions on key tile x of this block (rows [t_min, t_max])
+        auto tk_first = [&](int x) { return kp + (int64_t)x * BW_T * ps; };
+        auto tk_last = [&](int x) { return kp + ((B < (int64_t)x * BW_T + BW_T ? B : (int64_t)x * BW_T + BW_T) - 1) * ps; };
+        int flo = 0, fhi = nkt - 1;
+        tb_hi = nkt - 1;
+        if (a.mask != kMaskNone) {
+            if (a.mask == kMaskDoc) {
+                tb_lo = first_true(nkt, [&](int x) { return tk_last(x) >= ds_min; });
+                flo = first_true(nkt, [&](int x) { return tk_first(x) >= ds_max; });
+            }
+            tb_hi = first_true(nkt, [&](int x) { return tk_first(x) > t_max; }) - 1;
+            fhi = first_true(nkt, [&](int x) { return tk_last(x) > t_min; }) - 1;
+        }
+        tile_bounds_fix(tb_lo, tb_hi, flo, fhi);
         tb_full = flo | ((fhi + 1) << 16);
     }
     auto rl32 = [&](int x, int e) __attribute__((always_inline)) { return __builtin_amdgcn_readlane(x, e); };
@@ -576,6 +610,32 @@ __global__ __launch_bounds__(DQ_THREADS, 1) void bwd_dq_kernel(const BwdArgs a) 
             if (a.grad16) *(bf16x4*)(ob + 2 * e) = bf16x4{to16<E>(x0), to16<E>(x1), to16<E>(x2), to16<E>(x3)};
             else *(f32x4*)(ob + 4 * e) = f32x4{x0, x1, x2, x3};
         }
+    };  // run_item
+
+    // One workgroup per compute unit takes items from the queue of its XCD
+    // (numbers = that queue index mod 8, in order), then from the other
+    // queues: see the forward's ring kernel.  Each fetch tries every queue at
+    // most once, and an empty queue is not tried again, so the loop ends for
+    // every workgroup once all queues are drained.
+    for (;;) {
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            int it = -1;
+            for (int k = 0; k < 8 && it < 0; k++) {
+                const int y = (own_q + k) & 7;
+                if ((q_done >> y) & 1u) continue;
+                const int len = y < n_items ? (n_items - y + 7) / 8 : 0;
+                const unsigned i = atomicAdd(&a.wq[0 + y], 1u);
+                if ((int)i < len) it = 8 * (int)i + y;
+                else q_done |= 1u << y;
+            }
+            item_s = it;
+        }
+        __syncthreads();
+        const int b = __builtin_amdgcn_readfirstlane(item_s);
+        if (b < 0) break;
+        run_item(b);
+    }
 }
 
 // ---- dk, dv ----
@@ -601,11 +661,16 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(const BwdArgs a
     const int role = wave >> 2;  // 0: dV, 1: dK
     const int kw = wave & 3;     // which 32 keys of the workgroup
     const int half = lane >> 5, col = lane & 31;
+    __shared__ int item_s;
+    const int n_items = a.n_rworks * a.Hkv * a.n_ktiles;
+    const int own_q = blockIdx.x & 7;
+    unsigned q_done = 0;  // thread 0: queues found empty
+    auto run_item = [&](const int b) __attribute__((always_inline)) {
     // Workgroup -> (key block, kv head, key tile), the key tiles of one
     // (block, kv head) group on one XCD, as for dq; they run first to last
     // (under causal masks the first keys have the most queries).
     int grp_id, kt;
-    xcd_map(blockIdx.x, gridDim.x, a.n_ktiles, grp_id, kt);
+    xcd_map(b, n_items, a.n_ktiles, grp_id, kt);
     const int kvh = grp_id % a.Hkv;
     const int ridx = grp_id / a.Hkv;
     const BwdWork w = a.rworks[ridx];
@@ -634,13 +699,6 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(const BwdArgs a
     const int64_t wl = (B < wk0 + BW_TK ? B : wk0 + BW_TK) - 1;  // last key of the workgroup
     const int64_t tk_min = w.pos0 + wk0 * ps, tk_max = w.pos0 + wl * ps;
     const int nqt = (int)((B + BW_T - 1) / BW_T);
-    auto cls_of = [&](int64_t qp, int qt) __attribute__((always_inline)) {
-        const int64_t u0 = (int64_t)qt * BW_T, u1 = (B < u0 + BW_T ? B : u0 + BW_T) - 1;
-        const int64_t t0 = qp + u0 * ps, t1 = qp + u1 * ps;
-        const int64_t ds0 = a.mask == kMaskDoc ? doc_start(a.cu, a.n_docs, t0) : 0;
-        const int64_t ds1 = a.mask == kMaskDoc ? doc_start(a.cu, a.n_docs, t1) : 0;
-        return classify(a.mask, t0, t1, ds0, ds1, tk_min, tk_max);
-    };
     // The table of visiting query blocks, one per lane (lane e < count
     // holds block e): its first position, non-skipped query tiles [lo, hi]
     // and fully visible ones [flo, fhi]; read with readlane in the loop,
@@ -649,11 +707,21 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(const BwdArgs a
     int64_t tb_qp = 0;
     if (lane < w.count) {
         tb_qp = a.rpartners[w.first + lane];
-        tile_range(nqt, [&](int x) { return cls_of(tb_qp, x); }, tb_lo, tb_hi);
-        tb_flo = tb_lo;
-        tb_fhi = tb_hi;
-        while (tb_flo <= tb_fhi && cls_of(tb_qp, tb_flo) != kFull) tb_flo++;
-        while (tb_fhi >= tb_flo && cls_of(tb_qp, tb_fhi) != kFull) tb_fhi--;
+        // classify()'s conditions on query tile x of this block (keys [tk_min, tk_max])
+        auto t_first = [&](int x) { return tb_qp + (int64_t)x * BW_T * ps; };
+        auto t_last = [&](int x) { return tb_qp + ((B < (int64_t)x * BW_T + BW_T ? B : (int64_t)x * BW_T + BW_T) - 1) * ps; };
+        tb_hi = nqt - 1;
+        tb_flo = 0;
+        tb_fhi = nqt - 1;
+        if (a.mask != kMaskNone) {
+            tb_lo = first_true(nqt, [&](int x) { return t_last(x) >= tk_min; });
+            tb_flo = first_true(nqt, [&](int x) { return t_first(x) >= tk_max; });
+            if (a.mask == kMaskDoc) {
+                tb_hi = first_true(nqt, [&](int x) { return tk_max < doc_start(a.cu, a.n_docs, t_first(x)); }) - 1;
+                tb_fhi = first_true(nqt, [&](int x) { return doc_start(a.cu, a.n_docs, t_last(x)) > tk_min; }) - 1;
+            }
+        }
+        tile_bounds_fix(tb_lo, tb_hi, tb_flo, tb_fhi);
     }
     auto rl32 = [&](int x, int e) __attribute__((always_inline)) { return __builtin_amdgcn_readlane(x, e); };
     auto rl64 = [&](int64_t x, int e) __attribute__((always_inline)) {
@@ -934,6 +1002,32 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(const BwdArgs a
             if (a.grad16) *(bf16x4*)(ob + 2 * e) = bf16x4{to16<E>(x0), to16<E>(x1), to16<E>(x2), to16<E>(x3)};
             else *(f32x4*)(ob + 4 * e) = f32x4{x0, x1, x2, x3};
         }
+    };  // run_item
+
+    // One workgroup per compute unit takes items from the queue of its XCD
+    // (numbers = that queue index mod 8, in order), then from the other
+    // queues: see the forward's ring kernel.  Each fetch tries every queue at
+    // most once, and an empty queue is not tried again, so the loop ends for
+    // every workgroup once all queues are drained.
+    for (;;) {
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            int it = -1;
+            for (int k = 0; k < 8 && it < 0; k++) {
+                const int y = (own_q + k) & 7;
+                if ((q_done >> y) & 1u) continue;
+                const int len = y < n_items ? (n_items - y + 7) / 8 : 0;
+                const unsigned i = atomicAdd(&a.wq[8 + y], 1u);
+                if ((int)i < len) it = 8 * (int)i + y;
+                else q_done |= 1u << y;
+            }
+            item_s = it;
+        }
+        __syncthreads();
+        const int b = __builtin_amdgcn_readfirstlane(item_s);
+        if (b < 0) break;
+        run_item(b);
+    }
 }
 
 template <typename E>
@@ -943,8 +1037,16 @@ hipError_t launch_backward16(const BwdArgs& a, hipStream_t stream) {
         const int blocks = (int)((threads + 255) / 256 < 8192 ? (threads + 255) / 256 : 8192);
         bwd_prep_kernel<E><<<blocks, 256, 0, stream>>>(a);
     }
-    const int64_t ndq = (int64_t)a.n_works * a.Hq * a.n_qtiles;
-    const int64_t ndk = (int64_t)a.n_rworks * a.Hkv * a.n_ktiles;
+    // one workgroup per compute unit (fewer when there are fewer items)
+    const int64_t ndq_items = (int64_t)a.n_works * a.Hq * a.n_qtiles;
+    const int64_t ndk_items = (int64_t)a.n_rworks * a.Hkv * a.n_ktiles;
+    if ((ndq_items > 0 || ndk_items > 0) && !a.wq) return hipErrorInvalidValue;
+    if (ndq_items > INT32_MAX || ndk_items > INT32_MAX) return hipErrorInvalidValue;
+    int n_cu = 0;
+    hipError_t e = cu_count(&n_cu);
+    if (e != hipSuccess) return e;
+    const int64_t ndq = ndq_items < n_cu ? ndq_items : n_cu;
+    const int64_t ndk = ndk_items < n_cu ? ndk_items : n_cu;
     if (ndq > 0) {
         // KP: with a key-padding mask (the unmasked kernel carries none of its code)
         if (a.kbits) {

@@ -45,6 +45,7 @@ struct BwdArgs {
     const uint32_t* kbits;
     int32_t kb_words;
     int32_t f16;                   // 16-bit values are fp16, else bf16 (picks the kernels)
+    unsigned* wq;                  // 16 work-queue counters (dq 0..7, dk/dv 8..15), zero at the launch
 };
 constexpr int kBwdPad = 256;       // floats of padding after Lse2 and after Dsum
 int bwd_tile_q();

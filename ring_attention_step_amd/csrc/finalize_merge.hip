@@ -111,6 +111,21 @@ hipError_t launch_merge(void* out_acc, float* lse_acc, const void* out_blk, cons
     return hipGetLastError();
 }
 
+hipError_t cu_count(int* n) {
+    static int cache[64] = {0};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    if (!cache[dev]) {
+        int c = 0;
+        if ((e = hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+        cache[dev] = c > 0 ? c : 1;
+    }
+    *n = cache[dev];
+    return hipSuccess;
+}
+
 // One wave that waits `ticks` of the constant-rate wall clock, then exits
 // (a bounded delay on a stream; used only by the prefetch ordering test hook).
 __global__ void spin_kernel(uint64_t ticks) {

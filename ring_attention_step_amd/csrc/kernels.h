@@ -93,6 +93,8 @@ hipError_t launch_merge(void* out_acc, float* lse_acc, const void* out_blk, cons
                         int kind, int64_t Hq, int64_t rows, int64_t d, hipStream_t stream);
 // out_kind / kind: element type of out (0 fp32, 1 bf16, 2 fp16).
 hipError_t launch_fill_u64(unsigned long long* p, int64_t n, hipStream_t stream);
+// Compute units of the current device (queried once per device).
+hipError_t cu_count(int* n);
 // A bounded wait of `us` microseconds on `stream` (one wave).
 hipError_t launch_spin(uint32_t us, hipStream_t stream);
 

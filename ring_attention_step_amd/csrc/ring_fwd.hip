@@ -716,17 +716,10 @@ hipError_t launch16(const StepArgs& a, hipStream_t stream) {
     const int64_t n_items = (int64_t)a.n_qtiles * (a.Hq / a.hpi) * a.n_pairs;
     if (n_items == 0) return hipSuccess;
     if (!a.wq || n_items > INT32_MAX) return hipErrorInvalidValue;
-    static int n_cu[64] = {0};  // compute units per device, queried once
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
+    int n_cu = 0;  // one workgroup per compute unit
+    const hipError_t e = cu_count(&n_cu);
     if (e != hipSuccess) return e;
-    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-    if (!n_cu[dev]) {
-        int c = 0;
-        if ((e = hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
-        n_cu[dev] = c > 0 ? c : 1;
-    }
-    const dim3 grid((unsigned)(n_items < n_cu[dev] ? n_items : n_cu[dev])), block(THREADS);
+    const dim3 grid((unsigned)(n_items < n_cu ? n_items : n_cu)), block(THREADS);
     if (a.d == 128) ring_fwd_kernel<E, 128, KP><<<grid, block, 0, stream>>>(a);
     else if (a.d == 64) ring_fwd_kernel<E, 64, KP><<<grid, block, 0, stream>>>(a);
     else return hipErrorInvalidValue;
