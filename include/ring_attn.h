@@ -177,8 +177,10 @@ size_t ring_attn_forward_workspace_size(const ra_tensor* q, const ra_tensor* k, 
  * max_ring_passes (GitHub issue: the maximum number of ring passes; one pass
  * is one step).  Pairs the mask skips entirely are not run.  16-bit inputs
  * without prefetch: one launch runs the whole ring, every query tile of
- * every virtual device taking its device's steps in ring order with the
- * state kept on chip, then writing its normalised output.  Otherwise one
+ * every virtual device taking its device's blocks with the state kept on
+ * chip, then writing its normalised output; as every block is resident it
+ * takes them in ring order but the device's own block last (the merged
+ * result is the same sum in any order, rounding aside).  Otherwise one
  * launch per step covers every active virtual device, the state goes
  * through the workspace between steps, and a device's last active step
  * writes its normalised output.

@@ -552,6 +552,14 @@ ra_status ring_attn_forward(const ra_tensor* q, const ra_tensor* k, const ra_ten
         std::vector<std::vector<int32_t>> chain((size_t)N);
         for (int64_t s = 0; s < r.passes; s++)
             for (const StepPair& sp : plan.steps[s]) chain[sp.i].push_back(sp.j);
+        // Every block of a chain is resident, and the online-softmax merge
+        // gives the same sum in any order, so the chain takes the device's
+        // own block last: under a causal mask that block is the partly
+        // visible one, whose tile count differs between the query tiles of a
+        // group, and with it first those tiles would read every later block
+        // out of step (and miss the XCD's L2).
+        for (int64_t i = 0; i < N; i++)
+            if (chain[i].size() > 1 && chain[i].front() == i) std::rotate(chain[i].begin(), chain[i].begin() + 1, chain[i].end());
         size_t longest = 0;
         for (const auto& c : chain) longest = std::max(longest, c.size());
         if (longest <= (size_t)kMaxRingChain && n_qtiles_ring * (Hq / hpi) * N <= INT32_MAX) {
