@@ -70,6 +70,7 @@ constexpr int NBUF = 4;              // LDS buffers per operand
 constexpr int LA = 4;                // LDS operand read-ahead (slots)
 constexpr float kLazyRescale = 8.0f;
 constexpr float kUnitSumMax = 16384.0f;  // 2^(kLazyRescale + 6)
+constexpr int kCuLds = 4096;             // document starts kept in LDS (more: searched in global memory)
 static_assert(BQ == 32 * WAVES && BK == 64, "lane layouts assume 32 rows per wave and 64-key tiles");
 
 // C += A B on the 32x32x16 matrix core for element type E (operands as 16-bit
@@ -171,6 +172,24 @@ __global__ __launch_bounds__(THREADS, 1) void ring_fwd_kernel(const StepArgs a) 
     __shared__ int tab_i[5][kMaxRingChain];
     __shared__ int64_t tab_l[3][kMaxRingChain];
     __shared__ int item_s;
+    // The document starts (cu_seqlens) of a doc-causal launch, copied once
+    // per workgroup: every item searches them, and a binary search in LDS
+    // takes a fraction of the time of one through dependent global loads.
+    __shared__ int32_t cu_s[kCuLds];
+    const bool cu_lds = a.mask == kMaskDoc && a.n_docs + 1 <= kCuLds;
+    if (cu_lds)
+        for (int i = threadIdx.x; i <= a.n_docs; i += THREADS) cu_s[i] = a.cu[i];
+    // (the item loop's first barrier publishes the copy)
+    auto doc_of = [&](int64_t t) __attribute__((always_inline)) {
+        if (!cu_lds) return doc_start(a.cu, a.n_docs, t);
+        int lo = 0, hi = a.n_docs - 1;  // the last cu[x] <= t, as doc_start
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (cu_s[mid] <= t) lo = mid;
+            else hi = mid - 1;
+        }
+        return (int64_t)cu_s[lo];
+    };
 
     // Items are (work, head block, q-tile) triples, numbered so that
     // consecutive numbers go to the 8 XCDs in turn; (work, head block) groups are dealt to the
@@ -228,11 +247,11 @@ __global__ __launch_bounds__(THREADS, 1) void ring_fwd_kernel(const StepArgs a) 
 #pragma unroll
         for (int kc = 0; kc < D / 16; kc++) qf[kc] = row_ok ? *(const bf16x8*)(qp + 16 * kc) : bf16x8{};
     }
-    const int64_t ds_row = (row_ok && a.mask == kMaskDoc) ? doc_start(a.cu, a.n_docs, t_row) : 0;
+    const int64_t ds_row = (row_ok && a.mask == kMaskDoc) ? doc_of(t_row) : 0;
     int64_t ds_min = 0, ds_max = 0;
     if (a.mask == kMaskDoc) {
-        ds_min = doc_start(a.cu, a.n_docs, t_min);
-        ds_max = doc_start(a.cu, a.n_docs, t_max);
+        ds_min = doc_of(t_min);
+        ds_max = doc_of(t_max);
     }
     const int nkt = (int)((a.Bk + BK - 1) / BK);
     // The chain table: per block of the chain its non-skipped key tiles
