@@ -42,7 +42,6 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak (AMD published figure)
 PEAK_FP32_VECTOR_TFLOPS = 157.3  # MI355X fp32 vector peak (AMD published figure)
 DEFAULT_WORKLOAD = "causal32k_h32_d128_8blk"
-KERNEL = "ring_fwd_kernel<__bf16, 128, false>"
 # the per-ring-step kernel that the prefetching forward launches once per step
 STEP_KERNEL = "step_bf16_kernel<__bf16, 128, true, true, false>"
 BWD_KERNEL = "bwd_dkdv_kernel<__bf16, 128>"
@@ -61,6 +60,14 @@ def _code_only(text: str) -> str:
     text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
     text = re.sub(r"//[^\n]*", " ", text)
     return " ".join(text.split())
+
+
+def ring_kernel_name(w, key_padding=0.0) -> str:
+    """The one-launch kernel instance a workload runs: element type, head
+    dimension, key-padding mask, q-tile-major item order (striped blocks)."""
+    e = "_Float16" if w.dtype == "f16" else "__bf16"
+    b = lambda x: "true" if x else "false"
+    return "ring_fwd_kernel<%s, %d, %s, %s>" % (e, w.d, b(key_padding > 0), b(w.layout == 1))
 
 
 def kernel_source_sha(sources=KERNEL_SOURCES) -> str:
@@ -305,7 +312,8 @@ def main():
         # achieved: the forward's FLOP over its event-timed duration on the
         # launch stream, which also holds the V^T pack (about 1% of it): a
         # slight underestimate of the step kernel's own rate.
-        "roofline": {"bound": "mfma", "kernel": STEP_KERNEL if args.prefetch else KERNEL, "achieved": round(achieved, 3),
+        "roofline": {"bound": "mfma", "kernel": STEP_KERNEL if args.prefetch else ring_kernel_name(w, args.key_padding),
+                     "achieved": round(achieved, 3),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic, "launches_per_step": m["n_launch"],
                      "event_ms_per_step": round(m["ms_event"], 4),

@@ -558,8 +558,15 @@ ra_status ring_attn_forward(const ra_tensor* q, const ra_tensor* k, const ra_ten
         // visible one, whose tile count differs between the query tiles of a
         // group, and with it first those tiles would read every later block
         // out of step (and miss the XCD's L2).
-        for (int64_t i = 0; i < N; i++)
-            if (chain[i].size() > 1 && chain[i].front() == i) std::rotate(chain[i].begin(), chain[i].begin() + 1, chain[i].end());
+        // Striped blocks are the exception: there every pair is cut by the
+        // causal diagonal alike, so the chains all take ascending block order
+        // and the items run q-tile first (the same key tiles at the same time
+        // on an XCD, whatever the device).
+        for (int64_t i = 0; i < N; i++) {
+            if (striped) std::sort(chain[i].begin(), chain[i].end());
+            else if (chain[i].size() > 1 && chain[i].front() == i)
+                std::rotate(chain[i].begin(), chain[i].begin() + 1, chain[i].end());
+        }
         size_t longest = 0;
         for (const auto& c : chain) longest = std::max(longest, c.size());
         if (longest <= (size_t)kMaxRingChain && n_qtiles_ring * (Hq / hpi) * N <= INT32_MAX) {
@@ -607,6 +614,7 @@ ra_status ring_attn_forward(const ra_tensor* q, const ra_tensor* k, const ra_ten
                 a.entries = ws.entries;
                 a.wq = ws.wq;
                 a.hpi = hpi;
+                a.qt_major = striped;
                 a.n_qtiles = (int32_t)n_qtiles_ring;
                 // the work queues start at zero (a fill kernel, no memset node under graph capture)
                 if (launch_fill_u64((unsigned long long*)ws.wq, 4, st) != hipSuccess) return RA_E_HIP;

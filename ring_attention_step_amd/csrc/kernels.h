@@ -70,6 +70,7 @@ struct StepArgs {
     unsigned* wq;                          // its 8 work-queue counters, zero at the launch
     int32_t hpi;                           // query heads per work item (a power of two dividing the
                                            // group, <= 8); rows per item 256 / hpi; n_qtiles counts those
+    int32_t qt_major;                      // items numbered q-tile first (else (work, head block) first)
     // Key-padding mask (nullable): bit w % 32 of word kb_off + w / 32 is set
     // when key row w of a block takes part; a block's bits are whole 64-key
     // tiles (2 words each, 8-byte aligned), zero past its last row.

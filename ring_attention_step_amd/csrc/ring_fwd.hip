@@ -154,7 +154,7 @@ __device__ __forceinline__ float other_half(float x) {
     return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
 }
 
-template <typename E, int D, bool KP>
+template <typename E, int D, bool KP, bool QM>
 __global__ __launch_bounds__(THREADS, 1) void ring_fwd_kernel(const StepArgs a) {
     using TL = Tiles<D>;
     constexpr int LPW = TL::LPW, NSLOT = TL::NSLOT, SPS = TL::SPS;
@@ -195,7 +195,12 @@ __global__ __launch_bounds__(THREADS, 1) void ring_fwd_kernel(const StepArgs a) 
     // consecutive numbers go to the 8 XCDs in turn; (work, head block) groups are dealt to the
     // XCDs round robin, each group's q-tiles on one XCD (its L2 serves the
     // group's key/value tiles), heavy works first; within a group the q-tiles
-    // with the most key tiles (causal) come first.  The launch holds one
+    // with the most key tiles (causal) come first.  With QM (qt_major) the XCD
+    // instead runs one q-tile of all its groups before the next q-tile: where
+    // every block of a chain is cut by the mask alike (striped blocks), items
+    // with equal q-tiles and one chain order walk the same key tiles in step,
+    // while items of one group but different q-tiles would drift apart by
+    // whole blocks.  The launch holds one
     // workgroup per compute unit; workgroup w (on XCD w mod 8 under the
     // round-robin dispatch) takes the items of queue w mod 8 (numbers = that
     // queue index mod 8, in order), and when its queue is empty takes the
@@ -209,10 +214,19 @@ __global__ __launch_bounds__(THREADS, 1) void ring_fwd_kernel(const StepArgs a) 
     const int nwg = n_items;
     const int n_groups = nwg / a.n_qtiles;
     int grp_id, qt;
-    if (n_groups % 8 == 0) {
+    if (n_groups % 8 == 0) {  // rank r = b / 8 on the item's XCD
         const int r = b / 8;
-        grp_id = b % 8 + 8 * (r / a.n_qtiles);
-        qt = a.n_qtiles - 1 - r % a.n_qtiles;
+        if (QM) {
+            const int per_xcd = n_groups / 8;
+            grp_id = b % 8 + 8 * (r % per_xcd);
+            qt = a.n_qtiles - 1 - r / per_xcd;
+        } else {
+            grp_id = b % 8 + 8 * (r / a.n_qtiles);
+            qt = a.n_qtiles - 1 - r % a.n_qtiles;
+        }
+    } else if (QM) {
+        grp_id = b % n_groups;
+        qt = a.n_qtiles - 1 - b / n_groups;
     } else {
         grp_id = b / a.n_qtiles;
         qt = a.n_qtiles - 1 - b % a.n_qtiles;
@@ -739,9 +753,15 @@ hipError_t launch16(const StepArgs& a, hipStream_t stream) {
     const hipError_t e = cu_count(&n_cu);
     if (e != hipSuccess) return e;
     const dim3 grid((unsigned)(n_items < n_cu ? n_items : n_cu)), block(THREADS);
-    if (a.d == 128) ring_fwd_kernel<E, 128, KP><<<grid, block, 0, stream>>>(a);
-    else if (a.d == 64) ring_fwd_kernel<E, 64, KP><<<grid, block, 0, stream>>>(a);
-    else return hipErrorInvalidValue;
+    if (a.d == 128) {
+        if (a.qt_major) ring_fwd_kernel<E, 128, KP, true><<<grid, block, 0, stream>>>(a);
+        else ring_fwd_kernel<E, 128, KP, false><<<grid, block, 0, stream>>>(a);
+    } else if (a.d == 64) {
+        if (a.qt_major) ring_fwd_kernel<E, 64, KP, true><<<grid, block, 0, stream>>>(a);
+        else ring_fwd_kernel<E, 64, KP, false><<<grid, block, 0, stream>>>(a);
+    } else {
+        return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 
