@@ -205,6 +205,12 @@ size_t ring_attn_forward_workspace_size(const ra_tensor* q, const ra_tensor* k, 
  *     stream.
  *   stats: nullable HOST pointer; when given the call synchronises `stream`
  *     and fills it.
+ * Host tables (the chain tables the call plans, cu_seqlens) reach the device
+ * through pinned host buffers of the library (a ring of 8 per GPU, allocated
+ * on first use and grown as needed, held until the process ends) by copies
+ * enqueued on `stream`: the caller's host arrays may be reused as soon as the
+ * call returns, and the host may run up to 8 calls ahead of the GPU before a
+ * call waits for the copies of an earlier one.
  */
 ra_status ring_attn_forward(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v, void* out,
                             ra_dtype out_dtype, float* lse, int32_t n_blocks, ra_layout layout,
@@ -222,7 +228,8 @@ ra_status ring_attn_forward(const ra_tensor* q, const ra_tensor* k, const ra_ten
  * Shapes whose forward workspace (ring_attn_forward_workspace_size with
  * prefetch = 0) exceeds it return RA_E_TOO_LARGE before any GPU work.  The
  * caller still passes every input and output.  The call makes no device
- * allocation (its host-side planning uses ordinary host memory).
+ * or pinned host allocation: its host-side planning uses ordinary host
+ * memory, and its tables are copied to the array straight from that memory.
  * Every call on one GPU uses that GPU's one array, which keeps the last
  * call's contents: calls that overlap on one GPU (several streams or host
  * threads) race and must be ordered by the caller.
@@ -277,6 +284,8 @@ size_t ring_attn_backward_workspace_size(const ra_tensor* q, int32_t n_blocks, i
  *   dq [T, Hq, d], dk / dv [T, Hkv, d]: contiguous, 16-byte aligned,
  *     grad_dtype (fp32 or the inputs' type), every element written.
  *   workspace: ring_attn_backward_workspace_size bytes, 256-byte aligned.
+ * Its host tables travel as ring_attn_forward's do (pinned buffers, the same
+ * ring per GPU).
  */
 ra_status ring_attn_backward(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v, const ra_tensor* out,
                              const ra_tensor* dout, const float* lse, void* dq, void* dk, void* dv,

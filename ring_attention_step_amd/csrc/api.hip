@@ -108,6 +108,92 @@ hipError_t prefetch_ctx(PrefetchCtx** out) {
     return hipSuccess;
 }
 
+// Host-to-device copies of the per-call tables (chain tables, document
+// boundaries).  They are gathered into one pinned host buffer, taken from a
+// per-device ring of kStageSlots, and copied with plain DMA transfers on the
+// caller's stream; a slot is refilled only after the event recorded behind
+// its last copies has completed.  The host thus hands the copies to the
+// stream without the runtime's pageable staging, and may run up to
+// kStageSlots calls ahead of the GPU.  With pinned = false (callers that must
+// not allocate) the same copies go straight from the callers' host memory.
+constexpr int kStageSlots = 8;
+
+struct StageDev {
+    std::mutex mu;
+    char* buf[kStageSlots] = {};
+    size_t cap[kStageSlots] = {};
+    hipEvent_t done[kStageSlots] = {};
+    bool recorded[kStageSlots] = {};
+    unsigned next = 0;
+};
+
+class HostStager {
+  public:
+    explicit HostStager(bool pinned) : pinned_(pinned) {}
+    // Queues n bytes at src for dst; src must stay valid until flush().
+    void add(void* dst, const void* src, size_t n) {
+        if (n == 0) return;
+        recs_.push_back({dst, src, n, bytes_});
+        bytes_ += align_up(n);
+    }
+    hipError_t flush(hipStream_t st) {
+        if (recs_.empty()) return hipSuccess;
+        hipError_t e;
+        if (!pinned_) {
+            for (const Rec& r : recs_)
+                if ((e = hipMemcpyAsync(r.dst, r.src, r.n, hipMemcpyHostToDevice, st)) != hipSuccess) return e;
+            recs_.clear();
+            return hipSuccess;
+        }
+        StageDev* sd = nullptr;
+        if ((e = stage_dev(&sd)) != hipSuccess) return e;
+        std::lock_guard<std::mutex> g(sd->mu);
+        const int slot = (int)(sd->next++ % kStageSlots);
+        if (!sd->done[slot] && (e = hipEventCreateWithFlags(&sd->done[slot], hipEventDisableTiming)) != hipSuccess)
+            return e;
+        if (sd->recorded[slot] && (e = hipEventSynchronize(sd->done[slot])) != hipSuccess)
+            return e;  // the slot's last copies have landed
+        if (sd->cap[slot] < bytes_) {
+            if (sd->buf[slot] && (e = hipHostFree(sd->buf[slot])) != hipSuccess) return e;
+            sd->buf[slot] = nullptr;
+            sd->cap[slot] = 0;
+            const size_t cap = std::max<size_t>(bytes_, (size_t)64 << 10);
+            if ((e = hipHostMalloc((void**)&sd->buf[slot], cap, hipHostMallocDefault)) != hipSuccess) return e;
+            sd->cap[slot] = cap;
+        }
+        for (const Rec& r : recs_) std::memcpy(sd->buf[slot] + r.off, r.src, r.n);
+        for (const Rec& r : recs_)
+            if ((e = hipMemcpyAsync(r.dst, sd->buf[slot] + r.off, r.n, hipMemcpyHostToDevice, st)) != hipSuccess)
+                return e;
+        recs_.clear();
+        if ((e = hipEventRecord(sd->done[slot], st)) != hipSuccess) return e;
+        sd->recorded[slot] = true;
+        return hipSuccess;
+    }
+
+  private:
+    struct Rec {
+        void* dst;
+        const void* src;
+        size_t n, off;
+    };
+    static hipError_t stage_dev(StageDev** out) {
+        static std::mutex mu;
+        static std::vector<std::unique_ptr<StageDev>> devs;  // kept until the process ends
+        int dev = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e != hipSuccess) return e;
+        std::lock_guard<std::mutex> g(mu);
+        if ((int)devs.size() <= dev) devs.resize(dev + 1);
+        if (!devs[dev]) devs[dev].reset(new StageDev);
+        *out = devs[dev].get();
+        return hipSuccess;
+    }
+    bool pinned_;
+    std::vector<Rec> recs_;
+    size_t bytes_ = 0;
+};
+
 // Workspace of ring_attn_forward_noalloc: a fixed array in device memory,
 // one copy per GPU, held until the process ends.  Host code never passes the
 // array's name to a kernel or copy (on the host it is only a stand-in): each
@@ -411,11 +497,13 @@ ra_status ring_attn_plan(int64_t T, int32_t n_blocks, ra_layout layout, ra_mask 
     return RA_OK;
 }
 
-ra_status ring_attn_forward(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v, void* out,
-                            ra_dtype out_dtype, float* lse, int32_t n_blocks, ra_layout layout, ra_mask mask_mode,
-                            int32_t max_ring_passes, const int32_t* cu_seqlens_host, int32_t n_docs,
-                            const uint8_t* key_valid, float scale, int prefetch, void* workspace,
-                            size_t workspace_bytes, ra_stats* stats, void* stream) {
+// The forward behind both entry points; pinned selects how the per-call
+// tables travel to the device (see HostStager).
+static ra_status forward_impl(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v, void* out,
+                              ra_dtype out_dtype, float* lse, int32_t n_blocks, ra_layout layout, ra_mask mask_mode,
+                              int32_t max_ring_passes, const int32_t* cu_seqlens_host, int32_t n_docs,
+                              const uint8_t* key_valid, float scale, int prefetch, void* workspace,
+                              size_t workspace_bytes, ra_stats* stats, void* stream, bool pinned) {
     // ---- arguments ----
     if (!tensor_ok(q) || !tensor_ok(k) || !tensor_ok(v) || (!out && q->n_tok > 0)) return RA_E_ARG;
     if (q->dtype != k->dtype || q->dtype != v->dtype || !valid_dtype(out_dtype)) return RA_E_ARG;
@@ -493,9 +581,8 @@ ra_status ring_attn_forward(const ra_tensor* q, const ra_tensor* k, const ra_ten
 
     // ---- enqueue ----
     if (stats && launch_fill_u64(ws.counters, 4, st) != hipSuccess) return RA_E_HIP;
-    if (n_docs > 0 && hipMemcpyAsync(ws.cu, cu_seqlens_host, sizeof(int32_t) * (size_t)(n_docs + 1),
-                                     hipMemcpyHostToDevice, st) != hipSuccess)
-        return RA_E_HIP;
+    HostStager stage(pinned);  // flushed before the first kernel that reads a table
+    if (n_docs > 0) stage.add(ws.cu, cu_seqlens_host, sizeof(int32_t) * (size_t)(n_docs + 1));
     const int64_t kbw = key_words(B);  // key-padding words per block; block j's at j * kbw
     if (key_valid && launch_pack_key_bits(key_valid, 1, N, B, striped, kbw, ws.kbits, st) != hipSuccess)
         return RA_E_HIP;
@@ -598,11 +685,9 @@ ra_status ring_attn_forward(const ra_tensor* q, const ra_tensor* k, const ra_ten
                 }
             }
             if (!works.empty()) {
-                if (hipMemcpyAsync(ws.works, works.data(), sizeof(RingWork) * works.size(), hipMemcpyHostToDevice,
-                                   st) != hipSuccess ||
-                    hipMemcpyAsync(ws.entries, entries.data(), sizeof(RingEntry) * entries.size(),
-                                   hipMemcpyHostToDevice, st) != hipSuccess)
-                    return RA_E_HIP;
+                stage.add(ws.works, works.data(), sizeof(RingWork) * works.size());
+                stage.add(ws.entries, entries.data(), sizeof(RingEntry) * entries.size());
+                if (stage.flush(st) != hipSuccess) return RA_E_HIP;
                 StepArgs a = base;
                 a.k = k->data;
                 a.k_row_stride = (striped ? N : 1) * k->stride_tok;
@@ -627,6 +712,7 @@ ra_status ring_attn_forward(const ra_tensor* q, const ra_tensor* k, const ra_ten
 
     // (the workspace holds the per-step state whenever this path can run)
     if (!ring_done && !fwd_needs_state(T, N, Hq, d, q->dtype, prefetch != 0)) return RA_E_UNSUPPORTED;
+    if (stage.flush(st) != hipSuccess) return RA_E_HIP;
     for (int64_t s = 0; s < (ring_done ? 0 : r.passes); s++) {
         const std::vector<StepPair>& pairs = plan.steps[s];
         const bool use_buf = pf && s > 0;
@@ -752,6 +838,15 @@ ra_status ring_attn_forward(const ra_tensor* q, const ra_tensor* k, const ra_ten
     return RA_OK;
 }
 
+ra_status ring_attn_forward(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v, void* out,
+                            ra_dtype out_dtype, float* lse, int32_t n_blocks, ra_layout layout, ra_mask mask_mode,
+                            int32_t max_ring_passes, const int32_t* cu_seqlens_host, int32_t n_docs,
+                            const uint8_t* key_valid, float scale, int prefetch, void* workspace,
+                            size_t workspace_bytes, ra_stats* stats, void* stream) {
+    return forward_impl(q, k, v, out, out_dtype, lse, n_blocks, layout, mask_mode, max_ring_passes, cu_seqlens_host,
+                        n_docs, key_valid, scale, prefetch, workspace, workspace_bytes, stats, stream, true);
+}
+
 ra_status ring_attn_forward_noalloc(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v, void* out,
                                     ra_dtype out_dtype, float* lse, int32_t n_blocks, ra_layout layout,
                                     ra_mask mask_mode, int32_t max_ring_passes, const int32_t* cu_seqlens_host,
@@ -764,8 +859,9 @@ ra_status ring_attn_forward_noalloc(const ra_tensor* q, const ra_tensor* k, cons
     }
     void* ws = nullptr;
     if (scratch_address(&ws) != hipSuccess) return RA_E_HIP;
-    return ring_attn_forward(q, k, v, out, out_dtype, lse, n_blocks, layout, mask_mode, max_ring_passes,
-                             cu_seqlens_host, n_docs, key_valid, scale, 0, ws, kScratchBytes, stats, stream);
+    // (its tables go to the device straight from host memory: no pinned staging buffer is allocated)
+    return forward_impl(q, k, v, out, out_dtype, lse, n_blocks, layout, mask_mode, max_ring_passes, cu_seqlens_host,
+                        n_docs, key_valid, scale, 0, ws, kScratchBytes, stats, stream, false);
 }
 
 size_t ring_attn_forward_noalloc_scratch_bytes(void) { return kScratchBytes; }
@@ -887,19 +983,13 @@ ra_status ring_attn_backward(const ra_tensor* q, const ra_tensor* k, const ra_te
     flatten(rev, rworks, rpartners);
 
     hipStream_t st = (hipStream_t)stream;
-    if (n_docs > 0 && hipMemcpyAsync(ws.cu, cu_seqlens_host, sizeof(int32_t) * (size_t)(n_docs + 1),
-                                     hipMemcpyHostToDevice, st) != hipSuccess)
-        return RA_E_HIP;
-    if (hipMemcpyAsync(ws.works, works.data(), sizeof(BwdWork) * works.size(), hipMemcpyHostToDevice, st) !=
-            hipSuccess ||
-        hipMemcpyAsync(ws.rworks, rworks.data(), sizeof(BwdWork) * rworks.size(), hipMemcpyHostToDevice, st) !=
-            hipSuccess)
-        return RA_E_HIP;
-    if (!partners.empty() && (hipMemcpyAsync(ws.partners, partners.data(), sizeof(int64_t) * partners.size(),
-                                             hipMemcpyHostToDevice, st) != hipSuccess ||
-                              hipMemcpyAsync(ws.rpartners, rpartners.data(), sizeof(int64_t) * rpartners.size(),
-                                             hipMemcpyHostToDevice, st) != hipSuccess))
-        return RA_E_HIP;
+    HostStager stage(true);
+    if (n_docs > 0) stage.add(ws.cu, cu_seqlens_host, sizeof(int32_t) * (size_t)(n_docs + 1));
+    stage.add(ws.works, works.data(), sizeof(BwdWork) * works.size());
+    stage.add(ws.rworks, rworks.data(), sizeof(BwdWork) * rworks.size());
+    stage.add(ws.partners, partners.data(), sizeof(int64_t) * partners.size());
+    stage.add(ws.rpartners, rpartners.data(), sizeof(int64_t) * rpartners.size());
+    if (stage.flush(st) != hipSuccess) return RA_E_HIP;
     if (key_valid && launch_pack_key_bits(key_valid, 1, N, B, striped, key_words(B), ws.kbits, st) != hipSuccess)
         return RA_E_HIP;
 

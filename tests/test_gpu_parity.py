@@ -211,6 +211,38 @@ def test_16bit_forward_small(ra, case, dt):
     assert torch.equal(out16, out.to(TORCH16[dt]))
 
 
+def test_16bit_forward_host_tables_stay_valid_when_the_host_runs_ahead(ra):
+    """Twelve doc-causal forwards with different document tables are enqueued
+    behind a long GPU wait, so the host runs more calls ahead than the
+    library's ring of pinned staging buffers holds and each buffer is refilled
+    only after its earlier copies were consumed; every result must equal the
+    same call made on an idle GPU, bit for bit."""
+    T, N, Hq, Hkv, d = 1200, 4, 4, 2, 64
+    qh, kh, vh = W.random_qkv(T, Hq, Hkv, d, "bf16", 77)
+    q, k, v = _dev(qh, kh, vh)
+    tables = [W.random_doc_cu_seqlens(T, 40, 700, seed=300 + i) for i in range(12)]
+    n_docs = max(t.numel() - 1 for t in tables)
+    ws = torch.empty(ra.ring_attn_forward_workspace_size(q, k, N, n_docs), dtype=torch.uint8, device="cuda")
+    kw = dict(n_blocks=N, layout=0, mask_mode=2, max_ring_passes=N, scale=d ** -0.5, prefetch=False, workspace=ws)
+    expect = []
+    for t in tables:
+        o = torch.empty(T, Hq, d, dtype=torch.float32, device="cuda")
+        ra.ring_attn_forward(q, k, v, o, None, cu_seqlens_host=t.clone(), **kw)
+        torch.cuda.synchronize()
+        expect.append(o)
+    outs = [torch.full((T, Hq, d), float("nan"), device="cuda") for _ in tables]
+    torch.cuda.synchronize()
+    torch.cuda._sleep(200_000_000)  # the stream stays busy while the calls below are enqueued
+    for t, o in zip(tables, outs):
+        host = t.clone()
+        ra.ring_attn_forward(q, k, v, o, None, cu_seqlens_host=host, **kw)
+        host.fill_(T)  # the caller's array may change once the call has returned
+    torch.cuda.synchronize()
+    _say("host-ahead forwards", len(tables), "documents up to", n_docs)
+    for i, (o, e) in enumerate(zip(outs, expect)):
+        assert torch.equal(o, e), i
+
+
 KP_SMALL = [
     # T, N, Hq, Hkv, d, layout, mask, P, docs
     (888, 3, 4, 2, 128, 0, 1, 3, None),       # ragged tiles
