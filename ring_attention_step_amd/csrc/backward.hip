@@ -25,17 +25,18 @@
 //  * bwd_dkdv: one workgroup (8 waves) per (key/value block, KV head,
 //    128-key tile), walking the query blocks that visit the block, every
 //    query head of the KV head's group, in 64-row query tiles streamed
-//    through LDS.  Each 32 keys have two waves, their keys (and values) held
-//    in registers, with S = Q K^T so that one key sits in each lane:
-//      dV wave:  S = Q K^T, P, dv^T += dout^T P;
-//      dK wave:  S = Q K^T, dP = dout V^T, dS = P (dP - D), dk^T += q^T dS,
-//    the last products through transposing reads of the dout and q tiles.
-//    S is computed twice (1.25x the matrix-core work of one wave doing
-//    both), but each wave holds one set of 32 x d accumulators, so two
-//    waves fit per SIMD and hide each other's latency.
-// Both stream their tiles through a three-stage LDS ring filled by direct
-// global -> LDS loads issued two tiles ahead; a tile's loads have two tiles
-// of compute to land.  Tiles that the mask skips entirely are never loaded:
+//    through LDS.  Each 32 keys have two waves on one SIMD, the dV wave
+//    holding their keys and the dK wave their values in registers, with
+//    S = Q K^T so that one key sits in each lane:
+//      dV wave:  S = Q K^T, P (handed to the dK wave through LDS), dv^T += dout^T P;
+//      dK wave:  dP = dout V^T, dS = P (dP - D), dk^T += q^T dS,
+//    the last products through transposing reads of the dout and q tiles;
+//    the dK wave runs one query tile behind the dV wave, so P crosses a
+//    barrier instead of being waited for.  Each wave holds one set of
+//    32 x d accumulators, so two waves fit per SIMD.
+// dq streams its tiles through a three-stage LDS ring filled by direct
+// global -> LDS loads issued two tiles ahead; dk/dv through three stages
+// loaded one tile ahead (two are read per iteration).  Tiles that the mask skips entirely are never loaded:
 // per block the non-skipped tiles form one contiguous range (causal: a
 // skipped prefix or suffix; doc-causal: both), found before the walk.
 //
@@ -65,6 +66,7 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 template <int I>
 using ic = std::integral_constant<int, I>;
@@ -152,6 +154,26 @@ __device__ __forceinline__ void issue_loads(bf16* dst, int base_n, const char* t
         __builtin_amdgcn_global_load_lds(tile + o, (lds_void*)(dst + gofs + 512 * i), 16, 0, 0);
     }
 }
+
+// One 1 KB block by a direct-to-LDS buffer load: lane l's 16 bytes at
+// base + voff land at LDS byte address lds + 16 l.  The resource is a raw
+// buffer at base (no stride, no bound; every offset lies inside the tensor or
+// its padding).  Written in asm, so that the compiler does not pair LDS reads
+// with these loads: once a wave picks its stage at run time it cannot tell
+// the stages apart and would wait for every load before each read; the
+// waits are explicit (wait_loads_but, barriers).  M0 holds the LDS address;
+// one wait state separates its write from the load.
+__device__ __forceinline__ void dma16(uint32_t lds, const char* base, uint32_t voff) {
+    const uint64_t b = (uint64_t)base;
+    i32x4 r;
+    r[0] = (int)(uint32_t)b;
+    r[1] = (int)(uint32_t)(b >> 32);
+    r[2] = -1;
+    r[3] = 0x00020000;
+    __asm__ volatile("s_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"{m0}"(lds), "v"(voff), "s"(r) : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)(lds_void*)p; }
 
 // MFMA operand offsets (elements) into a swizzled [rows][D] tile:
 //  row operand (A or B) of row 32 rb + col, dims 16 kc + 8 half .. + 7;
@@ -643,19 +665,17 @@ template <typename E, int D>
 __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(const BwdArgs a) {
     constexpr int TE = BW_T * D;
     constexpr int NQ = TE / 512 / KV_WAVES;  // loads per wave per stage for each of q and dout
-    constexpr int NL = 2 * NQ + 1;  // + this wave's copy of the tile's lse2 / D rows
-    // Three stages, one array each: the q tile, the dout tile, then lse2 of
+    // Three stages in one array, each the q tile, the dout tile, then lse2 of
     // the tile's 64 rows and their D (1 KB, the upper half a duplicate
     // written by lanes 32..63).  Every wave loads that last KB (the same
-    // bytes): each wave then issues the same number of loads per stage, and
-    // its reads need no per-wave offset (with one, the compiler loses track
-    // of which stage they read and waits for every load in flight).
+    // bytes), so that each wave issues the same 2 NQ + 1 loads per stage.
     constexpr int SE = 2 * TE + 512;  // elements of one stage
-    __shared__ __attribute__((aligned(16))) bf16 st0[SE], st1[SE], st2[SE];
-    // P of the current tile, handed from each dV wave to its dK partner:
-    // [32-key group][half][4-register group][lane] 4 floats (accumulator
-    // order), so that each 16-byte access of a wave is contiguous.
-    __shared__ __attribute__((aligned(16))) float p_lds[KV_WAVES / 2][2][4][64 * 4];
+    __shared__ __attribute__((aligned(16))) bf16 st[3 * SE];
+    // P of a tile, handed from each dV wave to its dK partner one iteration
+    // later, double-buffered by tile parity: [parity][32-key group][half sb]
+    // [operand h][lane] 8 16-bit values (accumulator registers 8 h .. 8 h + 7),
+    // so that each 16-byte access of a wave is contiguous.
+    __shared__ bf16x8 p_lds[2][KV_WAVES / 2][2][2][64];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int role = wave >> 2;  // 0: dV, 1: dK
@@ -802,7 +822,8 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(const BwdArgs a
         const int64_t dd = a.Dsum - a.Lse2;
         off_l[0] = (uint32_t)(4 * (l32 < 16 ? 4 * l32 : dd + 4 * (l32 - 16)));
     }
-    auto issue = [&](bf16* qs, bf16* gs, float* ls, const Cursor& c) __attribute__((always_inline)) {
+    // Loads of one tile into stage sx: q, dout, then the lse2 / D block.
+    auto issue = [&](int sx, const Cursor& c) __attribute__((always_inline)) {
         const int hq = kvh * a.group + c.h;
         const int64_t u0 = (int64_t)c.qt * BW_T;
         const int64_t row0 = c.qp + u0 * ps;  // token of the tile's first row
@@ -811,32 +832,32 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(const BwdArgs a
         const int64_t qloc = ps == 1 ? c.qp : c.qp * B;  // block-local index of row 0 (striped: block = qp)
         const char* lb = (const char*)(a.Lse2 + hq * a.T + qloc + u0);
         const bool rag = c.qt == ragged_qt;
-        uint32_t oq[NQ], og[NQ];
+        const uint32_t l_st = lds_addr(st) + (uint32_t)(2 * SE) * (uint32_t)sx;
 #pragma unroll
         for (int i = 0; i < NQ; i++) {
-            oq[i] = rag ? chunk_offset<D>(lane, wave * NQ + i, q_rs, last_ragged) : off_q[i];
-            og[i] = rag ? chunk_offset<D>(lane, wave * NQ + i, g_rs, last_ragged) : off_g[i];
+            const uint32_t oq = rag ? chunk_offset<D>(lane, wave * NQ + i, q_rs, last_ragged) : off_q[i];
+            dma16(l_st + 1024u * (uint32_t)(wave * NQ + i), qb, oq);
         }
-        issue_loads<NQ>(qs, wave * NQ, qb, oq);
-        issue_loads<NQ>(gs, wave * NQ, gb, og);
-        issue_loads<1>((bf16*)ls, 0, lb, off_l);
-        __asm__ volatile("; tile issued" ::: "memory");
+#pragma unroll
+        for (int i = 0; i < NQ; i++) {
+            const uint32_t og = rag ? chunk_offset<D>(lane, wave * NQ + i, g_rs, last_ragged) : off_g[i];
+            dma16(l_st + 2u * TE + 1024u * (uint32_t)(wave * NQ + i), gb, og);
+        }
+        dma16(l_st + 4u * TE, lb, off_l[0]);
     };
 
-    int cc_flo = 0, cc_fhi = -1;  // fully visible tiles of the compute cursor's block
-    // A tile in two phases with a workgroup barrier between them; the waves
-    // of one 32-key group (dV wave, dK wave) share a SIMD, and in each phase
-    // one of them carries the softmax arithmetic while the other mostly
-    // runs the matrix core.
-    //  phase 1  dV wave: S = q K^T, P (to LDS, and kept as bf16);  dK wave: dP = dout V^T
-    //  phase 2  dV wave: dv^T += dout^T P;  dK wave: P from LDS, dS = P (dP - D), dk^T += q^T dS
-    // Register i of S / dP / P holds tile row 32 sb + 8 (i/4) + 4 half + i%4.
-    float* const p_mine = &p_lds[kw][0][0][lane * 4];  // + (4 sb + q4) * 256
-    // Both roles run the same matrix-core instruction stream on role-selected
-    // operands (so the accumulators stay in place); role-specific work is
-    // vector arithmetic only.  x[sb] carries phase 1's product of half sb to
-    // phase 2: the dK wave's dP, or the dV wave's P as bf16 operands (first
-    // 8 registers).
+    int cc_flo = 0, cc_fhi = -1;  // fully visible tiles of the dV wave's current block
+    // Software pipeline with one workgroup barrier per iteration.  Iteration
+    // j (j = 0 .. nT) reads query tiles j and j - 1 from two of the three
+    // stages while the third receives tile j + 1:
+    //   dV wave:  dv^T += dout_{j-1}^T P_{j-1};  S_j = q_j K^T;  P_j (to LDS, kept as bf16)
+    //   dK wave:  dP_{j-1} = dout_{j-1} V^T;  dS = P_{j-1} (dP - D), P from LDS;  dk^T += q_{j-1}^T dS
+    // The two waves of a 32-key group share a SIMD and order their matrix
+    // and vector work oppositely, so that one's exp (or dS) arithmetic runs
+    // beside the other's matrix products; P crosses the barrier between
+    // them, never inside an iteration.  Register i of S / dP / P holds tile
+    // row 32 sb + 8 (i/4) + 4 half + i%4.  x[sb] holds S or dP of half sb,
+    // then P or dS as bf16 operands (first 8 registers).
     f32x16 x[2];
     auto b16 = [&](int sb, int h) __attribute__((always_inline)) {
         return __builtin_bit_cast(bf16x8, f32x4{x[sb][4 * h], x[sb][4 * h + 1], x[sb][4 * h + 2], x[sb][4 * h + 3]});
@@ -846,87 +867,76 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(const BwdArgs a
 #pragma unroll
         for (int e = 0; e < 4; e++) x[sb][4 * h + e] = y[e];
     };
-    const int row_src = role ? TE : 0;  // phase 1 rows: q (dV wave) or dout (dK wave)
-    const int tr_src = role ? 0 : TE;   // phase 2 columns: dout (dV wave) or q (dK wave)
-    auto phase1_mfma = [&](const bf16* qs) __attribute__((always_inline)) {
-        // S = q K^T (dV wave) or dP = dout V^T (dK wave), both halves.
+    const bool is_dv = __builtin_amdgcn_readfirstlane(role) == 0;
+    // S = q K^T (dV wave, t = q tile) or dP = dout V^T (dK wave, t = dout tile), both halves.
+    auto row_set = [&](const bf16* t) __attribute__((always_inline)) {
 #pragma unroll
         for (int sb = 0; sb < 2; sb++) {
             x[sb] = f32x16{};
 #pragma unroll
-            for (int kc = 0; kc < D / 16; kc++) x[sb] = mfma<E>(ops.row(qs + row_src, sb, kc), opf[kc], x[sb]);
+            for (int kc = 0; kc < D / 16; kc++) x[sb] = mfma<E>(ops.row(t, sb, kc), opf[kc], x[sb]);
         }
     };
-    auto phase1_p = [&](const float* lw, int64_t u0, auto full_t) __attribute__((always_inline)) {
-        constexpr bool FULL = decltype(full_t)::value;
-        {
-            // P (a masked row's exponent becomes -inf), to LDS for the dK
-            // wave and kept as bf16 operands.
-            const int x_lo = u_lo - (int)u0 - 4 * half, x_hi = u_hi - (int)u0 - 4 * half;
+    // dv^T += dout^T P (dV wave, t = dout tile) or dk^T += q^T dS (dK wave, t = q tile).
+    auto tr_set = [&](const bf16* t) __attribute__((always_inline)) {
 #pragma unroll
-            for (int sb = 0; sb < 2; sb++) {
-                f32x16 pv;
-#pragma unroll
-                for (int g4 = 0; g4 < 4; g4++) {
-                    const f32x4 l4 = *(const f32x4*)(lw + 32 * sb + 8 * g4 + 4 * half);
-#pragma unroll
-                    for (int r = 0; r < 4; r++) {
-                        const int i = 4 * g4 + r, xr = 32 * sb + 8 * g4 + r;
-                        float arg = fmaf(x[sb][i], a.c2, -l4[r]);
-                        if (!FULL) arg = ((xr >= x_lo) & (xr < x_hi)) ? arg : -INFINITY;
-                        pv[i] = __builtin_amdgcn_exp2f(arg);
-                    }
-                }
-#pragma unroll
-                for (int q4 = 0; q4 < 4; q4++)
-                    *(f32x4*)(p_mine + (4 * sb + q4) * 256) =
-                        f32x4{pv[4 * q4], pv[4 * q4 + 1], pv[4 * q4 + 2], pv[4 * q4 + 3]};
-                bf16x8 b0, b1;
-                acc_to_b<E>(pv, b0, b1);
-                set_b16(sb, 0, b0);
-                set_b16(sb, 1, b1);
-            }
-        }
-    };
-    auto phase2 = [&](const bf16* qs, const float* lw) __attribute__((always_inline)) {
-#pragma unroll
-        for (int sb = 0; sb < 2; sb++) {
-            if (__builtin_amdgcn_readfirstlane(role) == 1) {
-                // dS = P (dP - D); a masked row has P = 0 and a finite D
-                // (rows past a block read the next rows or zeroed padding).
-                f32x16 dsv;
-#pragma unroll
-                for (int g4 = 0; g4 < 4; g4++) {
-                    const f32x4 d4 = *(const f32x4*)(lw + 64 + 32 * sb + 8 * g4 + 4 * half);
-                    const f32x4 p4 = *(const f32x4*)(p_mine + (4 * sb + g4) * 256);
-#pragma unroll
-                    for (int r = 0; r < 4; r++) dsv[4 * g4 + r] = p4[r] * (x[sb][4 * g4 + r] - d4[r]);
-                }
-                bf16x8 e0, e1;
-                acc_to_b<E>(dsv, e0, e1);
-                set_b16(sb, 0, e0);
-                set_b16(sb, 1, e1);
-            }
-            // dv^T += dout^T P (dV wave) or dk^T += q^T dS (dK wave).
+        for (int sb = 0; sb < 2; sb++)
 #pragma unroll
             for (int db = 0; db < D / 32; db++) {
-                acc[db] = mfma<E>(ops.tr(qs + tr_src, 2 * sb, db), b16(sb, 0), acc[db]);
-                acc[db] = mfma<E>(ops.tr(qs + tr_src, 2 * sb + 1, db), b16(sb, 1), acc[db]);
+                acc[db] = mfma<E>(ops.tr(t, 2 * sb, db), b16(sb, 0), acc[db]);
+                acc[db] = mfma<E>(ops.tr(t, 2 * sb + 1, db), b16(sb, 1), acc[db]);
             }
+    };
+    // P of the dV wave's tile (a masked row's exponent becomes -inf), to LDS
+    // at pw and kept as bf16 operands.
+    auto p_step = [&](const float* lw, int64_t u0, bf16x8* pw, auto full_t) __attribute__((always_inline)) {
+        constexpr bool FULL = decltype(full_t)::value;
+        const int x_lo = u_lo - (int)u0 - 4 * half, x_hi = u_hi - (int)u0 - 4 * half;
+#pragma unroll
+        for (int sb = 0; sb < 2; sb++) {
+            f32x16 pv;
+#pragma unroll
+            for (int g4 = 0; g4 < 4; g4++) {
+                const f32x4 l4 = *(const f32x4*)(lw + 32 * sb + 8 * g4 + 4 * half);
+#pragma unroll
+                for (int r = 0; r < 4; r++) {
+                    const int i = 4 * g4 + r, xr = 32 * sb + 8 * g4 + r;
+                    float arg = fmaf(x[sb][i], a.c2, -l4[r]);
+                    if (!FULL) arg = ((xr >= x_lo) & (xr < x_hi)) ? arg : -INFINITY;
+                    pv[i] = __builtin_amdgcn_exp2f(arg);
+                }
+            }
+            bf16x8 b0, b1;
+            acc_to_b<E>(pv, b0, b1);
+            pw[(2 * sb) * 64 + lane] = b0;
+            pw[(2 * sb + 1) * 64 + lane] = b1;
+            set_b16(sb, 0, b0);
+            set_b16(sb, 1, b1);
         }
     };
-    auto compute = [&](const bf16* qs, const bf16* gs, const float* ls, const Cursor& c)
-                       __attribute__((always_inline)) {
-        const int64_t u0 = (int64_t)c.qt * BW_T;
-        const bool full = c.qt != ragged_qt && c.qt >= cc_flo && c.qt <= cc_fhi;
-        const float* lw = ls;
-        phase1_mfma(qs);
-        if (__builtin_amdgcn_readfirstlane(role) == 0) {
-            if (__builtin_amdgcn_readfirstlane((int)full)) phase1_p(lw, u0, std::true_type{});
-            else phase1_p(lw, u0, std::false_type{});
+    // dS = P (dP - D) of the dK wave's tile, P from pr; a masked row has
+    // P = 0 and a finite D (rows past a block read the next rows or zeroed
+    // padding).
+    auto ds_step = [&](const float* lw, const bf16x8* pr) __attribute__((always_inline)) {
+#pragma unroll
+        for (int sb = 0; sb < 2; sb++) {
+            const bf16x8 p0 = pr[(2 * sb) * 64 + lane], p1 = pr[(2 * sb + 1) * 64 + lane];
+            f32x16 dsv;
+#pragma unroll
+            for (int g4 = 0; g4 < 4; g4++) {
+                const f32x4 d4 = *(const f32x4*)(lw + 64 + 32 * sb + 8 * g4 + 4 * half);
+#pragma unroll
+                for (int r = 0; r < 4; r++) {
+                    const int i = 4 * g4 + r;
+                    const float pi = from16<E>(i < 8 ? p0[i] : p1[i - 8]);
+                    dsv[i] = pi * (x[sb][i] - d4[r]);
+                }
+            }
+            bf16x8 e0, e1;
+            acc_to_b<E>(dsv, e0, e1);
+            set_b16(sb, 0, e0);
+            set_b16(sb, 1, e1);
         }
-        phase_barrier();  // P of this tile is in LDS
-        phase2(qs, lw);
     };
 
     Cursor cl{0, 0, 0, 0, -1, 0};
@@ -934,54 +944,50 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(const BwdArgs a
         enter(cl, 0);
         if (cl.hi < cl.lo) cur_next(cl);  // empty first block: step onto the first real tile
     }
-    Cursor cc = cl;
+    Cursor cc = cl;  // the dV wave's tile
     auto enter_block = [&](const Cursor& c) __attribute__((always_inline)) {
         key_bounds(c.qp);
         cc_flo = rl32(tb_flo, c.e);
         cc_fhi = rl32(tb_fhi, c.e);
     };
-    if (nT > 0) enter_block(cc);
-    auto iteration = [&](int j, auto slot) __attribute__((always_inline)) {
-        constexpr int S = decltype(slot)::value;
-        bf16* const qc = S == 0 ? st0 : (S == 1 ? st1 : st2);
-        bf16* const gc = qc + TE;
-        float* const lc = (float*)(qc + 2 * TE);
-        bf16* const qn = S == 0 ? st2 : (S == 1 ? st0 : st1);
-        bf16* const gn = qn + TE;
-        float* const ln = (float*)(qn + 2 * TE);
-        if (j + 2 < nT) cur_next(cl);
-        issue(qn, gn, ln, cl);
-        compute(qc, gc, lc, cc);
-        if (j + 1 < nT) {
-            const int e_was = cc.e;
-            cur_next(cc);
-            if (cc.e != e_was) enter_block(cc);
-        }
-        wait_loads_but<NL>();
-        phase_barrier();
-    };
     if (nT > 0) {
+        enter_block(cc);
+        issue(0, cl);
         wait_loads_but<0>();
-        const Cursor c0 = cl;
-        if (nT > 1) cur_next(cl);
-        issue(st0, st0 + TE, (float*)(st0 + 2 * TE), c0);
-        issue(st1, st1 + TE, (float*)(st1 + 2 * TE), cl);
-        wait_loads_but<NL>();
         phase_barrier();
-        // Whole triples of tiles in the loop, the rest after it: the loop
-        // body is straight-line code, so at every point the compiler knows
-        // exactly which stage's loads are still in flight (a conditional
-        // iteration inside the loop would give it paths on which the stage
-        // about to be read had just been issued, and a wait for all loads).
-        int j = 0;
-        for (; j + 3 <= nT; j += 3) {
-            iteration(j, ic<0>{});
-            iteration(j + 1, ic<1>{});
-            iteration(j + 2, ic<2>{});
+        int s_cur = 0;  // stage of tile j
+        for (int j = 0; j <= nT; j++) {
+            const int s_prv = s_cur == 0 ? 2 : s_cur - 1, s_nxt = s_cur == 2 ? 0 : s_cur + 1;
+            if (j + 1 < nT) {
+                cur_next(cl);
+                issue(s_nxt, cl);
+            }
+            const bf16* const t_cur = st + s_cur * SE;
+            const bf16* const t_prv = st + s_prv * SE;
+            if (is_dv && j >= 1) tr_set(t_prv + TE);  // dv += dout_{j-1}^T P_{j-1}
+            if (is_dv ? j < nT : j >= 1) {
+                row_set(is_dv ? t_cur : t_prv + TE);
+                if (is_dv) {
+                    const int64_t u0 = (int64_t)cc.qt * BW_T;
+                    const bool full = cc.qt != ragged_qt && cc.qt >= cc_flo && cc.qt <= cc_fhi;
+                    bf16x8* const pw = &p_lds[j & 1][kw][0][0][0];
+                    const float* const lw = (const float*)(t_cur + 2 * TE);
+                    if (__builtin_amdgcn_readfirstlane((int)full)) p_step(lw, u0, pw, std::true_type{});
+                    else p_step(lw, u0, pw, std::false_type{});
+                } else {
+                    ds_step((const float*)(t_prv + 2 * TE), &p_lds[(j - 1) & 1][kw][0][0][0]);
+                }
+            }
+            if (!is_dv && j >= 1) tr_set(t_prv);  // dk += q_{j-1}^T dS
+            if (j + 1 < nT) {
+                const int e_was = cc.e;
+                cur_next(cc);
+                if (cc.e != e_was) enter_block(cc);
+            }
+            wait_loads_but<0>();  // this wave's loads of tile j + 1
+            phase_barrier();      // ... and every wave's; P_j is in LDS
+            s_cur = s_nxt;
         }
-        if (j < nT) iteration(j, ic<0>{});
-        if (j + 1 < nT) iteration(j + 1, ic<1>{});
-        wait_loads_but<0>();
     }
 
     if (!key_ok) return;
