@@ -78,6 +78,13 @@ constexpr int KV_THREADS = 64 * KV_WAVES;
 constexpr int BW_TQ = 32 * DQ_WAVES;       // query rows per dq workgroup
 constexpr int BW_TK = 32 * (KV_WAVES / 2); // keys per dk/dv workgroup
 constexpr int BW_T = 64;                   // rows of a streamed tile (keys for dq, queries for dk/dv)
+// The LDS operands of a run of matrix instructions are read kla() instructions
+// ahead into a ring of registers, each step of the run fenced by a
+// scheduling barrier: read next to its use, every operand would stall its
+// instruction for the whole LDS latency (the compiler's own schedule does
+// that to save registers).
+template <int D>
+constexpr int kla() { return D == 128 ? 4 : 2; }
 constexpr float kLog2e = 1.4426950408889634f;
 static_assert(kBwdPad >= 64, "a 64-row tile may read 63 rows past the last block");
 
@@ -139,20 +146,6 @@ __device__ __forceinline__ uint32_t chunk_offset(int lane, int n, uint32_t rs_by
     const int r = s / CH;
     const uint32_t row = (uint32_t)(r < last_row ? r : last_row);
     return row * rs_bytes + 16u * (uint32_t)((s % CH) ^ swz<D>(r));
-}
-
-// Issue this wave's NL direct loads of one tile (16 bytes per lane each):
-// load i writes the 1 KB block of slots 64 (base_n + i) .. + 63.
-template <int NL>
-__device__ __forceinline__ void issue_loads(bf16* dst, int base_n, const char* tile, const uint32_t (&off)[NL]) {
-    int gofs = base_n * 512;
-    __asm__ volatile("" : "+s"(gofs));
-#pragma unroll
-    for (int i = 0; i < NL; i++) {
-        uint32_t o = off[i];
-        __asm__ volatile("" : "+v"(o));  // keeps the uniform-base + 32-bit lane offset form
-        __builtin_amdgcn_global_load_lds(tile + o, (lds_void*)(dst + gofs + 512 * i), 16, 0, 0);
-    }
 }
 
 // One 1 KB block by a direct-to-LDS buffer load: lane l's 16 bytes at
@@ -343,8 +336,7 @@ template <typename E, int D, bool KP>
 __global__ __launch_bounds__(DQ_THREADS, 1) void bwd_dq_kernel(const BwdArgs a) {
     constexpr int TE = BW_T * D;              // elements of one [64][D] tile
     constexpr int NL = 2 * (TE / 512 / DQ_WAVES);  // loads per wave per stage: K tile, then V tile
-    // Three stages, one array each (K tile, then V tile): the compiler can
-    // then tell the direct loads into one stage from the reads of another.
+    // Three stages, one array each (K tile, then V tile).
     __shared__ bf16 st0[2 * TE], st1[2 * TE], st2[2 * TE];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -486,9 +478,12 @@ __global__ __launch_bounds__(DQ_THREADS, 1) void bwd_dq_kernel(const BwdArgs a) 
             ok[i] = rag ? chunk_offset<D>(lane, wave * (NL / 2) + i, k_rs, last_ragged) : off_k[i];
             ov[i] = rag ? chunk_offset<D>(lane, wave * (NL / 2) + i, v_rs, last_ragged) : off_v[i];
         }
-        issue_loads<NL / 2>(ks, wave * (NL / 2), k_head + row0 * a.k_st * 2, ok);
-        issue_loads<NL / 2>(vs, wave * (NL / 2), v_head + row0 * a.v_st * 2, ov);
-        __asm__ volatile("; tile issued" ::: "memory");
+        const uint32_t lk = lds_addr(ks) + 1024u * (uint32_t)(wave * (NL / 2));
+        const uint32_t lv = lds_addr(vs) + 1024u * (uint32_t)(wave * (NL / 2));
+#pragma unroll
+        for (int i = 0; i < NL / 2; i++) dma16(lk + 1024u * i, k_head + row0 * a.k_st * 2, ok[i]);
+#pragma unroll
+        for (int i = 0; i < NL / 2; i++) dma16(lv + 1024u * i, v_head + row0 * a.v_st * 2, ov[i]);
     };
 
     int cc_flo = 0, cc_fhi = -1;  // fully visible tiles of the compute cursor's block
@@ -525,10 +520,23 @@ __global__ __launch_bounds__(DQ_THREADS, 1) void bwd_dq_kernel(const BwdArgs a) 
                 one[0] = lo_half ? to16<E>(1.0f) : to16<E>(0.0f);
                 s = mfma<E>(bias, one, s);
             }
+            {
+                // K rows (even n) and V rows (odd n), read KLA instructions
+                // ahead into a ring of registers (next to its use, each read
+                // would stall its instruction for the whole LDS latency).
+                constexpr int NR = 2 * (D / 16), KLA = kla<D>();
+                auto rd = [&](int n) __attribute__((always_inline)) { return ops.row(n % 2 ? vs : ks, kb, n / 2); };
+                bf16x8 ring[KLA];
 #pragma unroll
-            for (int kc = 0; kc < D / 16; kc++) {
-                s = mfma<E>(ops.row(ks, kb, kc), qf[kc], s);
-                dp = mfma<E>(ops.row(vs, kb, kc), gf[kc], dp);
+                for (int n = 0; n < KLA; n++) ring[n] = rd(n);
+#pragma unroll
+                for (int n = 0; n < NR; n++) {
+                    const bf16x8 fr = ring[n % KLA];
+                    if (n + KLA < NR) ring[n % KLA] = rd(n + KLA);
+                    if (n % 2 == 0) s = mfma<E>(fr, qf[n / 2], s);
+                    else dp = mfma<E>(fr, gf[n / 2], dp);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
             }
             // dS^T = P^T (dP^T - D); register i holds key 32 kb + 8 (i/4) + 4 half + i%4.
             // A masked key's exponent becomes -inf (P = 0, dS = 0): selects,
@@ -550,11 +558,22 @@ __global__ __launch_bounds__(DQ_THREADS, 1) void bwd_dq_kernel(const BwdArgs a) 
             };
             if (__builtin_amdgcn_readfirstlane((int)full)) softmax(std::true_type{});
             else softmax(std::false_type{});
-            // dq^T += K^T dS^T over the two 16-key chunks of this half.
+            // dq^T += K^T dS^T over the two 16-key chunks of this half
+            // (instruction n: block db = n / 2, chunk n % 2), operands read ahead.
+            {
+                constexpr int NR = 2 * (D / 32);
+                constexpr int LA = kla<D>() < NR ? kla<D>() : NR;
+                auto rd = [&](int n) __attribute__((always_inline)) { return ops.tr(ks, 2 * kb + n % 2, n / 2); };
+                bf16x8 ring[LA];
 #pragma unroll
-            for (int db = 0; db < D / 32; db++) {
-                dq[db] = mfma<E>(ops.tr(ks, 2 * kb, db), b0, dq[db]);
-                dq[db] = mfma<E>(ops.tr(ks, 2 * kb + 1, db), b1, dq[db]);
+                for (int n = 0; n < LA; n++) ring[n] = rd(n);
+#pragma unroll
+                for (int n = 0; n < NR; n++) {
+                    const bf16x8 fr = ring[n % LA];
+                    if (n + LA < NR) ring[n % LA] = rd(n + LA);
+                    dq[n / 2] = mfma<E>(fr, n % 2 ? b1 : b0, dq[n / 2]);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
             }
         }
     };
@@ -603,11 +622,8 @@ __global__ __launch_bounds__(DQ_THREADS, 1) void bwd_dq_kernel(const BwdArgs a) 
         issue(st1, st1 + TE, cl);
         wait_loads_but<NL>();
         phase_barrier();
-        // Whole triples of tiles in the loop, the rest after it: the loop
-        // body is straight-line code, so at every point the compiler knows
-        // exactly which stage's loads are still in flight (a conditional
-        // iteration inside the loop would give it paths on which the stage
-        // about to be read had just been issued, and a wait for all loads).
+        // Whole triples of tiles in the loop, the rest after it, so that
+        // every stage is a fixed array in the loop body.
         int j = 0;
         for (; j + 3 <= nT; j += 3) {
             iteration(j, ic<0>{});
@@ -868,24 +884,38 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(const BwdArgs a
         for (int e = 0; e < 4; e++) x[sb][4 * h + e] = y[e];
     };
     const bool is_dv = __builtin_amdgcn_readfirstlane(role) == 0;
+    constexpr int NR = 2 * (D / 16), KLA = kla<D>();  // instructions per run (both halves), operands read KLA ahead
     // S = q K^T (dV wave, t = q tile) or dP = dout V^T (dK wave, t = dout tile), both halves.
     auto row_set = [&](const bf16* t) __attribute__((always_inline)) {
+        bf16x8 ring[KLA];
 #pragma unroll
-        for (int sb = 0; sb < 2; sb++) {
-            x[sb] = f32x16{};
+        for (int n = 0; n < KLA; n++) ring[n] = ops.row(t, n / (D / 16), n % (D / 16));
+        x[0] = x[1] = f32x16{};
 #pragma unroll
-            for (int kc = 0; kc < D / 16; kc++) x[sb] = mfma<E>(ops.row(t, sb, kc), opf[kc], x[sb]);
+        for (int n = 0; n < NR; n++) {
+            const bf16x8 fr = ring[n % KLA];
+            if (n + KLA < NR) ring[n % KLA] = ops.row(t, (n + KLA) / (D / 16), (n + KLA) % (D / 16));
+            x[n / (D / 16)] = mfma<E>(fr, opf[n % (D / 16)], x[n / (D / 16)]);
+            __builtin_amdgcn_sched_barrier(0);  // keeps each read KLA instructions ahead of its use
         }
     };
     // dv^T += dout^T P (dV wave, t = dout tile) or dk^T += q^T dS (dK wave, t = q tile).
+    // Instruction n: half sb = n / (D/16), block db = (n / 2) % (D/32), 16-row chunk h = n % 2.
     auto tr_set = [&](const bf16* t) __attribute__((always_inline)) {
+        auto rd = [&](int n) __attribute__((always_inline)) {
+            return ops.tr(t, 2 * (n / (D / 16)) + n % 2, (n / 2) % (D / 32));
+        };
+        bf16x8 ring[KLA];
 #pragma unroll
-        for (int sb = 0; sb < 2; sb++)
+        for (int n = 0; n < KLA; n++) ring[n] = rd(n);
 #pragma unroll
-            for (int db = 0; db < D / 32; db++) {
-                acc[db] = mfma<E>(ops.tr(t, 2 * sb, db), b16(sb, 0), acc[db]);
-                acc[db] = mfma<E>(ops.tr(t, 2 * sb + 1, db), b16(sb, 1), acc[db]);
-            }
+        for (int n = 0; n < NR; n++) {
+            const bf16x8 fr = ring[n % KLA];
+            if (n + KLA < NR) ring[n % KLA] = rd(n + KLA);
+            const int db = (n / 2) % (D / 32);
+            acc[db] = mfma<E>(fr, b16(n / (D / 16), n % 2), acc[db]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
     };
     // P of the dV wave's tile (a masked row's exponent becomes -inf), to LDS
     // at pw and kept as bf16 operands.
