@@ -179,8 +179,9 @@ size_t ring_attn_forward_workspace_size(const ra_tensor* q, const ra_tensor* k, 
  * without prefetch: one launch runs the whole ring, every query tile of
  * every virtual device taking its device's blocks with the state kept on
  * chip, then writing its normalised output; as every block is resident it
- * takes them in ring order but the device's own block last (the merged
- * result is the same sum in any order, rounding aside).  Otherwise one
+ * takes them in ring order but the device's own block last (striped
+ * layout: in ascending block order), the merged result being the same sum
+ * in any order, rounding aside.  Otherwise one
  * launch per step covers every active virtual device, the state goes
  * through the workspace between steps, and a device's last active step
  * writes its normalised output.
