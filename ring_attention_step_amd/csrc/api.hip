@@ -961,6 +961,15 @@ ra_status ring_attn_backward(const ra_tensor* q, const ra_tensor* k, const ra_te
             fwd[sp.i].push_back(pos0(sp.j));
             rev[sp.j].push_back(pos0(sp.i));
         }
+    // Striped blocks are cut by the causal diagonal alike in every pair: all
+    // chains take ascending block order there, and the kernels number their
+    // items tile index first, so that the items running together on an XCD
+    // stream the same tiles at the same time.
+    if (striped)
+        for (int64_t i = 0; i < N; i++) {
+            std::sort(fwd[i].begin(), fwd[i].end());
+            std::sort(rev[i].begin(), rev[i].end());
+        }
     std::vector<BwdWork> works, rworks;
     std::vector<int64_t> partners, rpartners;
     auto flatten = [&](std::vector<std::vector<int64_t>>& lists, std::vector<BwdWork>& wv, std::vector<int64_t>& pv) {
@@ -1043,6 +1052,7 @@ ra_status ring_attn_backward(const ra_tensor* q, const ra_tensor* k, const ra_te
     a.rworks = ws.rworks;
     a.rpartners = ws.rpartners;
     // the kernels' work queues start at zero (a fill kernel, no memset node under graph capture)
+    a.qt_major = striped;
     a.wq = ws.wq;
     if (launch_fill_u64((unsigned long long*)ws.wq, 8, st) != hipSuccess) return RA_E_HIP;
     if (launch_backward(a, st) != hipSuccess) return RA_E_HIP;

@@ -299,6 +299,42 @@ __device__ __forceinline__ void xcd_map(int b, int nwg, int per_group, int& grou
     }
 }
 
+// The tile-index-major numbering of striped layouts (QM): XCD b % 8 runs
+// one tile index of all its groups before the next (rank r = b / 8: index
+// r / per, group b % 8 + 8 (r % per)), so that the items running together
+// stream the same tiles; else plain index-major order.  Every pair of a
+// striped chain is cut by the causal diagonal alike, so items of one tile
+// index and one chain order read the same tiles in step, while items of
+// one group but different indices drift apart by whole blocks.
+__device__ __forceinline__ void xcd_map_qm(int b, int nwg, int per_group, int& group, int& idx) {
+    const int n_groups = nwg / per_group;
+    if (n_groups % 8 == 0) {
+        const int r = b / 8, per = n_groups / 8;
+        group = b % 8 + 8 * (r % per);
+        idx = r / per;
+    } else {
+        group = b % n_groups;
+        idx = b / n_groups;
+    }
+}
+
+// Group -> (head, block index) for H heads: under QM with H a multiple of 8
+// (and the groups dealt evenly), XCD y = group % 8 takes heads y H/8 ..
+// y H/8 + H/8 - 1, whole kv-head groups of a grouped-query layout when H/8
+// is a multiple of the group, so that one L2 serves their shared tiles;
+// else head = group % H.
+template <bool QM>
+__device__ __forceinline__ void group_head(int group, int n_groups, int H, int& head, int& blk) {
+    if (QM && H % 8 == 0 && n_groups % 8 == 0) {
+        const int g = group / 8, hx = H / 8;
+        head = (group % 8) * hx + g % hx;
+        blk = g / hx;
+    } else {
+        head = group % H;
+        blk = group / H;
+    }
+}
+
 // First index in [0, n) where a predicate that is false, then true, holds
 // (n when it never does).  Every condition of classify() on a streamed tile
 // is monotone in the tile index (positions grow with it; document starts
@@ -332,7 +368,7 @@ __device__ __forceinline__ void tile_bounds_fix(int& lo, int& hi, int& flo, int&
 }
 
 // ---- dq ----
-template <typename E, int D, bool KP>
+template <typename E, int D, bool KP, bool QM>
 __global__ __launch_bounds__(DQ_THREADS, 1) void bwd_dq_kernel(const BwdArgs a) {
     constexpr int TE = BW_T * D;              // elements of one [64][D] tile
     constexpr int NL = 2 * (TE / 512 / DQ_WAVES);  // loads per wave per stage: K tile, then V tile
@@ -352,11 +388,11 @@ __global__ __launch_bounds__(DQ_THREADS, 1) void bwd_dq_kernel(const BwdArgs a) 
     // XCDs in turn, so groups are dealt to the XCDs round robin.  Within a
     // group the q-tiles run last first (under causal masks they have the
     // most keys).
-    int grp_id, qi;
-    xcd_map(b, n_items, a.n_qtiles, grp_id, qi);
+    int grp_id, qi, head, widx;
+    if (QM) xcd_map_qm(b, n_items, a.n_qtiles, grp_id, qi);
+    else xcd_map(b, n_items, a.n_qtiles, grp_id, qi);
+    group_head<QM>(grp_id, n_items / a.n_qtiles, a.Hq, head, widx);
     const int qt = a.n_qtiles - 1 - qi;
-    const int head = grp_id % a.Hq;
-    const int widx = grp_id / a.Hq;
     const int kvh = head / a.group;
     const BwdWork w = a.works[widx];
     const int64_t B = a.B, ps = a.pos_stride;
@@ -677,7 +713,7 @@ __global__ __launch_bounds__(DQ_THREADS, 1) void bwd_dq_kernel(const BwdArgs a) 
 }
 
 // ---- dk, dv ----
-template <typename E, int D>
+template <typename E, int D, bool QM>
 __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(const BwdArgs a) {
     constexpr int TE = BW_T * D;
     constexpr int NQ = TE / 512 / KV_WAVES;  // loads per wave per stage for each of q and dout
@@ -705,10 +741,10 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(const BwdArgs a
     // Workgroup -> (key block, kv head, key tile), the key tiles of one
     // (block, kv head) group on one XCD, as for dq; they run first to last
     // (under causal masks the first keys have the most queries).
-    int grp_id, kt;
-    xcd_map(b, n_items, a.n_ktiles, grp_id, kt);
-    const int kvh = grp_id % a.Hkv;
-    const int ridx = grp_id / a.Hkv;
+    int grp_id, kt, kvh, ridx;
+    if (QM) xcd_map_qm(b, n_items, a.n_ktiles, grp_id, kt);
+    else xcd_map(b, n_items, a.n_ktiles, grp_id, kt);
+    group_head<QM>(grp_id, n_items / a.n_ktiles, a.Hkv, kvh, ridx);
     const BwdWork w = a.rworks[ridx];
     const int64_t B = a.B, ps = a.pos_stride;
     const int64_t wk0 = (int64_t)kt * BW_TK;
@@ -1083,20 +1119,31 @@ hipError_t launch_backward16(const BwdArgs& a, hipStream_t stream) {
     if (e != hipSuccess) return e;
     const int64_t ndq = ndq_items < n_cu ? ndq_items : n_cu;
     const int64_t ndk = ndk_items < n_cu ? ndk_items : n_cu;
+    if (a.d != 128 && a.d != 64) return hipErrorInvalidValue;
     if (ndq > 0) {
-        // KP: with a key-padding mask (the unmasked kernel carries none of its code)
-        if (a.kbits) {
-            if (a.d == 128) bwd_dq_kernel<E, 128, true><<<(unsigned)ndq, DQ_THREADS, 0, stream>>>(a);
-            else if (a.d == 64) bwd_dq_kernel<E, 64, true><<<(unsigned)ndq, DQ_THREADS, 0, stream>>>(a);
-            else return hipErrorInvalidValue;
-        } else if (a.d == 128) bwd_dq_kernel<E, 128, false><<<(unsigned)ndq, DQ_THREADS, 0, stream>>>(a);
-        else if (a.d == 64) bwd_dq_kernel<E, 64, false><<<(unsigned)ndq, DQ_THREADS, 0, stream>>>(a);
-        else return hipErrorInvalidValue;
+        // KP: with a key-padding mask (the unmasked kernel carries none of its code);
+        // QM: the tile-major item order of striped layouts
+        const int v = (a.kbits ? 2 : 0) + (a.qt_major ? 1 : 0);
+        auto dq = [&](auto d_t) {
+            constexpr int Dc = decltype(d_t)::value;
+            switch (v) {
+                case 0: bwd_dq_kernel<E, Dc, false, false><<<(unsigned)ndq, DQ_THREADS, 0, stream>>>(a); break;
+                case 1: bwd_dq_kernel<E, Dc, false, true><<<(unsigned)ndq, DQ_THREADS, 0, stream>>>(a); break;
+                case 2: bwd_dq_kernel<E, Dc, true, false><<<(unsigned)ndq, DQ_THREADS, 0, stream>>>(a); break;
+                default: bwd_dq_kernel<E, Dc, true, true><<<(unsigned)ndq, DQ_THREADS, 0, stream>>>(a); break;
+            }
+        };
+        if (a.d == 128) dq(ic<128>{});
+        else dq(ic<64>{});
     }
     if (ndk > 0) {
-        if (a.d == 128) bwd_dkdv_kernel<E, 128><<<(unsigned)ndk, KV_THREADS, 0, stream>>>(a);
-        else if (a.d == 64) bwd_dkdv_kernel<E, 64><<<(unsigned)ndk, KV_THREADS, 0, stream>>>(a);
-        else return hipErrorInvalidValue;
+        auto dkdv = [&](auto d_t) {
+            constexpr int Dc = decltype(d_t)::value;
+            if (a.qt_major) bwd_dkdv_kernel<E, Dc, true><<<(unsigned)ndk, KV_THREADS, 0, stream>>>(a);
+            else bwd_dkdv_kernel<E, Dc, false><<<(unsigned)ndk, KV_THREADS, 0, stream>>>(a);
+        };
+        if (a.d == 128) dkdv(ic<128>{});
+        else dkdv(ic<64>{});
     }
     return hipGetLastError();
 }

@@ -46,6 +46,7 @@ struct BwdArgs {
     int32_t kb_words;
     int32_t f16;                   // 16-bit values are fp16, else bf16 (picks the kernels)
     unsigned* wq;                  // 16 work-queue counters (dq 0..7, dk/dv 8..15), zero at the launch
+    int32_t qt_major;              // items numbered tile index first (striped blocks), else group first
 };
 constexpr int kBwdPad = 256;       // floats of padding after Lse2 and after Dsum
 int bwd_tile_q();
