@@ -44,7 +44,6 @@ PEAK_FP32_VECTOR_TFLOPS = 157.3  # MI355X fp32 vector peak (AMD published figure
 DEFAULT_WORKLOAD = "causal32k_h32_d128_8blk"
 # the per-ring-step kernel that the prefetching forward launches once per step
 STEP_KERNEL = "step_bf16_kernel<__bf16, 128, true, true, false>"
-BWD_KERNEL = "bwd_dkdv_kernel<__bf16, 128>"
 # The kernels' sources plus the driver that sets their launch order (a
 # traffic record is only valid for the code and the order it was taken with).
 KERNEL_SOURCES = ["ring_attention_step_amd/csrc/ring_fwd.hip", "ring_attention_step_amd/csrc/step_bf16.hip",
@@ -68,6 +67,18 @@ def ring_kernel_name(w, key_padding=0.0) -> str:
     e = "_Float16" if w.dtype == "f16" else "__bf16"
     b = lambda x: "true" if x else "false"
     return "ring_fwd_kernel<%s, %d, %s, %s>" % (e, w.d, b(key_padding > 0), b(w.layout == 1))
+
+
+def bwd_kernel_names(w, key_padding=0.0, dkdv_only=False) -> str:
+    """The backward kernel instances a workload runs (striped layouts take the
+    tile-index-major item order)."""
+    e = "_Float16" if w.dtype == "f16" else "__bf16"
+    b = lambda x: "true" if x else "false"
+    dkdv = "bwd_dkdv_kernel<%s, %d, %s>" % (e, w.d, b(w.layout == 1))
+    if dkdv_only:
+        return dkdv
+    return "bwd_prep_kernel<%s> + bwd_dq_kernel<%s, %d, %s, %s> + %s" % (e, e, w.d, b(key_padding > 0),
+                                                                        b(w.layout == 1), dkdv)
 
 
 def kernel_source_sha(sources=KERNEL_SOURCES) -> str:
@@ -387,12 +398,12 @@ def bench_backward(args, ra, W, w, x, q, k, v, cu, out, lse, plan, stream, key_v
         # the three backward kernels together, event-timed on the launch stream;
         # traffic: HBM bytes per launch of the dominant one (dk/dv) from the
         # committed counter record
-        "roofline": {"bound": "mfma", "kernel": "bwd_prep_kernel<__bf16> + bwd_dq_kernel<__bf16, 128, false> + " + BWD_KERNEL,
+        "roofline": {"bound": "mfma", "kernel": bwd_kernel_names(w, args.key_padding),
                      "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic_from_profile(w.name, False, backward=True)
                      if args.dtype == "bf16" and key_valid is None else None,
-                     "traffic_kernel": BWD_KERNEL,
+                     "traffic_kernel": bwd_kernel_names(w, args.key_padding, dkdv_only=True),
                      "event_ms_per_step": round(ms_event, 4),
                      "timing": "hip events on the launch stream around the timed backward calls"},
     }

@@ -181,6 +181,7 @@ SMALL = [
     (1024, 4, 8, 1, 128, 0, 1, 4, None),      # 8 query heads per kv head: 32-row work items
     (900, 3, 6, 2, 64, 1, 1, 3, None),        # groups of 3: one head per item, striped
     (1200, 4, 8, 2, 128, 0, 2, 2, [0, 130, 700, 1200]),  # 4 heads per item, doc-causal, P < N
+    (1024, 8, 16, 8, 128, 1, 1, 8, None),     # striped, groups a multiple of 8: q-tile-major items per XCD
 ]
 
 

@@ -75,6 +75,7 @@ BWD_SMALL = [
     (2048, 4, 2, 1, 128, 0, 2, 2, "random", "f32"),
     (256, 1, 2, 2, 128, 0, 1, 1, None, "bf16"),     # one virtual device
     (520, 8, 2, 2, 128, 1, 1, 8, None, "bf16"),     # B = 65: 1-row ragged tails
+    (1024, 8, 16, 8, 128, 1, 1, 8, None, "bf16"),   # striped, heads a multiple of 8: tile-major items, kv groups per XCD
 ]
 
 
