@@ -958,12 +958,20 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(const BwdArgs a
     auto p_step = [&](const float* lw, int64_t u0, bf16x8* pw, auto full_t) __attribute__((always_inline)) {
         constexpr bool FULL = decltype(full_t)::value;
         const int x_lo = u_lo - (int)u0 - 4 * half, x_hi = u_hi - (int)u0 - 4 * half;
+        // every LDS input first, in one batch (read one by one next to their
+        // uses, each would wait out the whole LDS latency in turn)
+        f32x4 lr[2][4];
+#pragma unroll
+        for (int sb = 0; sb < 2; sb++)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; g4++) lr[sb][g4] = *(const f32x4*)(lw + 32 * sb + 8 * g4 + 4 * half);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int sb = 0; sb < 2; sb++) {
             f32x16 pv;
 #pragma unroll
             for (int g4 = 0; g4 < 4; g4++) {
-                const f32x4 l4 = *(const f32x4*)(lw + 32 * sb + 8 * g4 + 4 * half);
+                const f32x4 l4 = lr[sb][g4];
 #pragma unroll
                 for (int r = 0; r < 4; r++) {
                     const int i = 4 * g4 + r, xr = 32 * sb + 8 * g4 + r;
@@ -984,13 +992,24 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(const BwdArgs a
     // P = 0 and a finite D (rows past a block read the next rows or zeroed
     // padding).
     auto ds_step = [&](const float* lw, const bf16x8* pr) __attribute__((always_inline)) {
+        // every LDS input first, in one batch (as in p_step)
+        bf16x8 pp[2][2];
+        f32x4 dr[2][4];
 #pragma unroll
         for (int sb = 0; sb < 2; sb++) {
-            const bf16x8 p0 = pr[(2 * sb) * 64 + lane], p1 = pr[(2 * sb + 1) * 64 + lane];
+#pragma unroll
+            for (int h = 0; h < 2; h++) pp[sb][h] = pr[(2 * sb + h) * 64 + lane];
+#pragma unroll
+            for (int g4 = 0; g4 < 4; g4++) dr[sb][g4] = *(const f32x4*)(lw + 64 + 32 * sb + 8 * g4 + 4 * half);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int sb = 0; sb < 2; sb++) {
+            const bf16x8 p0 = pp[sb][0], p1 = pp[sb][1];
             f32x16 dsv;
 #pragma unroll
             for (int g4 = 0; g4 < 4; g4++) {
-                const f32x4 d4 = *(const f32x4*)(lw + 64 + 32 * sb + 8 * g4 + 4 * half);
+                const f32x4 d4 = dr[sb][g4];
 #pragma unroll
                 for (int r = 0; r < 4; r++) {
                     const int i = 4 * g4 + r;
