@@ -211,7 +211,9 @@ size_t ring_attn_forward_workspace_size(const ra_tensor* q, const ra_tensor* k, 
  * on first use and grown as needed, held until the process ends) by copies
  * enqueued on `stream`: the caller's host arrays may be reused as soon as the
  * call returns, and the host may run up to 8 calls ahead of the GPU before a
- * call waits for the copies of an earlier one.
+ * call waits for the copies of an earlier one.  The staging is per call, so a
+ * call is not meant for capture into a HIP graph (a replay would copy
+ * whatever a later call left in the buffer).
  */
 ra_status ring_attn_forward(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v, void* out,
                             ra_dtype out_dtype, float* lse, int32_t n_blocks, ra_layout layout,
