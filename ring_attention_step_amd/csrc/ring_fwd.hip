@@ -5,10 +5,12 @@
 // or, when several query heads share a kv head (grouped-query attention),
 // 256 / h rows of each of h heads of one group, so that the key/value tiles
 // it streams serve them all.  It walks the device's visited key/value blocks
-// in ring order ("Ring Attention" glossary page, worked example: device i
-// holds key/value block i - s at step s), the online-softmax state (running
-// reference, denominator, unnormalised output) staying in registers from the
-// first block to the fused finalize.  Eight waves of 32 query rows, two per
+// ("Ring Attention" glossary page, worked example: device i holds key/value
+// block i - s at step s) in the order the host's chain table gives: ring
+// order with the device's own block last, or ascending block order for
+// striped layouts (the merged sum is the same in any order).  The
+// online-softmax state (running reference, denominator, unnormalised output)
+// stays in registers from the first block to the fused finalize.  Eight waves of 32 query rows, two per
 // SIMD.
 //
 // Every wave runs the whole pipeline by itself -- no phases shared with the
