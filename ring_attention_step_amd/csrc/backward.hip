@@ -806,7 +806,21 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(const BwdArgs a
     struct Cursor {
         int e, h, qt, lo, hi;
         int64_t qp;  // position of the query block's row 0
+        // Byte addresses of the tile's first q row, dout row and lse2 entry;
+        // moved by a constant per tile within a (block, head) run.
+        const char *qb, *gb, *lb;
     };
+    const int hq0 = kvh * a.group;
+    auto set_ptrs = [&](Cursor& c) __attribute__((always_inline)) {
+        const int hq = hq0 + c.h;
+        const int64_t u0 = (int64_t)c.qt * BW_T;
+        const int64_t row0 = c.qp + u0 * ps;  // token of the tile's first row
+        c.qb = (const char*)((const bf16*)a.q + row0 * a.q_st + hq * a.q_sh);
+        c.gb = (const char*)((const bf16*)a.dout + row0 * a.do_st + hq * a.do_sh);
+        const int64_t qloc = ps == 1 ? c.qp : c.qp * B;  // block-local index of row 0 (striped: block = qp)
+        c.lb = (const char*)(a.Lse2 + hq * a.T + qloc + u0);
+    };
+    const int64_t q_ts = BW_T * ps * a.q_st * 2, g_ts = BW_T * ps * a.do_st * 2, l_ts = BW_T * 4;
     auto enter = [&](Cursor& c, int e) __attribute__((always_inline)) {
         c.e = e;
         c.h = 0;
@@ -819,6 +833,13 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(const BwdArgs a
     auto cur_next = [&](Cursor& c) __attribute__((always_inline)) {
         Cursor n = c;
         n.qt++;
+        if (n.qt <= n.hi) {  // the next tile of the same block and head
+            n.qb += q_ts;
+            n.gb += g_ts;
+            n.lb += l_ts;
+            c = n;
+            return;
+        }
         while (n.qt > n.hi) {
             if (n.h + 1 < a.group && n.lo <= n.hi) {
                 n.h++;
@@ -829,6 +850,7 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(const BwdArgs a
                 return;
             }
         }
+        set_ptrs(n);
         c = n;
     };
     int nT = 0;
@@ -876,13 +898,7 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(const BwdArgs a
     }
     // Loads of one tile into stage sx: q, dout, then the lse2 / D block.
     auto issue = [&](int sx, const Cursor& c) __attribute__((always_inline)) {
-        const int hq = kvh * a.group + c.h;
-        const int64_t u0 = (int64_t)c.qt * BW_T;
-        const int64_t row0 = c.qp + u0 * ps;  // token of the tile's first row
-        const char* qb = (const char*)((const bf16*)a.q + row0 * a.q_st + hq * a.q_sh);
-        const char* gb = (const char*)((const bf16*)a.dout + row0 * a.do_st + hq * a.do_sh);
-        const int64_t qloc = ps == 1 ? c.qp : c.qp * B;  // block-local index of row 0 (striped: block = qp)
-        const char* lb = (const char*)(a.Lse2 + hq * a.T + qloc + u0);
+        const char *qb = c.qb, *gb = c.gb, *lb = c.lb;
         const bool rag = c.qt == ragged_qt;
         const uint32_t l_st = lds_addr(st) + (uint32_t)(2 * SE) * (uint32_t)sx;
 #pragma unroll
@@ -1028,6 +1044,7 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(const BwdArgs a
     if (w.count > 0) {
         enter(cl, 0);
         if (cl.hi < cl.lo) cur_next(cl);  // empty first block: step onto the first real tile
+        set_ptrs(cl);
     }
     Cursor cc = cl;  // the dV wave's tile
     auto enter_block = [&](const Cursor& c) __attribute__((always_inline)) {
