@@ -514,6 +514,10 @@ __global__ __launch_bounds__(THREADS, 1) void ring_fwd_kernel(const StepArgs a) 
     f32x16 o[D / 32];
     float mx = -INFINITY;   // raw q.k maximum at the last move of the reference
     float mrc = -INFINITY;  // reference (log2 units) the accumulators are relative to
+    // The fast path's FMA term: minus the reference, or +inf while the row
+    // has none, which turns every P of the fast path into inf or NaN and so
+    // sends the unit to the slow path through the same sum test.
+    float nref = INFINITY;
     float lsum = 0.f;       // this lane's share of the denominator
     // P of one unit against the current reference, and this lane's sum.
     auto probs_all = [&](const f32x16& s, bf16x8 (&p)[2]) __attribute__((always_inline)) {
@@ -546,7 +550,10 @@ __global__ __launch_bounds__(THREADS, 1) void ring_fwd_kernel(const StepArgs a) 
         const bool need = mnc > mrc + kLazyRescale;  // false while the row has no key
         if (__ballot(need)) {
             const float alpha = need ? __builtin_amdgcn_exp2f(mrc - mnc) : 1.f;
-            if (need) mrc = mnc;
+            if (need) {
+                mrc = mnc;
+                nref = -mnc;
+            }
             lsum *= alpha;
 #pragma unroll
             for (int db = 0; db < D / 32; db++) o[db] *= alpha;
@@ -570,7 +577,6 @@ __global__ __launch_bounds__(THREADS, 1) void ring_fwd_kernel(const StepArgs a) 
         if (un.masked) apply_mask(s_cur, un);
         f32x16 sn = s_init(word_next);
         float ps[4];
-        const float mref = mrc == -INFINITY ? 0.f : mrc;
 #pragma unroll
         for (int n = 0; n < NSLOT; n++) {
             const bf16x8 fr = ring[n % LA];
@@ -585,7 +591,7 @@ __global__ __launch_bounds__(THREADS, 1) void ring_fwd_kernel(const StepArgs a) 
 #pragma unroll
             for (int v = 0; v < SPS; v++) {
                 const int i = n * SPS + v;
-                const float pv = __builtin_amdgcn_exp2f(fmaf(s_cur[i], a.c2, -mref));
+                const float pv = __builtin_amdgcn_exp2f(fmaf(s_cur[i], a.c2, nref));
                 ps[i % 4] = i < 4 ? pv : ps[i % 4] + pv;
                 p_cur[i / 8][i % 8] = to16<E>(pv);
             }
@@ -594,7 +600,7 @@ __global__ __launch_bounds__(THREADS, 1) void ring_fwd_kernel(const StepArgs a) 
         // slow-path branch (the slow path recomputes it).
         __asm__ volatile("" : "+v"(p_cur[0]), "+v"(p_cur[1]));
         float lt = (ps[0] + ps[1]) + (ps[2] + ps[3]);
-        if (__builtin_expect(__ballot(!(lt <= kUnitSumMax) || mrc == -INFINITY) != 0, 0)) {
+        if (__builtin_expect(__ballot(!(lt <= kUnitSumMax)) != 0, 0)) {
             rebase(s_cur);
             lt = probs_all(s_cur, p_cur);
         }
@@ -618,7 +624,11 @@ __global__ __launch_bounds__(THREADS, 1) void ring_fwd_kernel(const StepArgs a) 
     const char* v_pend = nullptr;  // V^T address of the tile the K cursor loaded last
     uint64_t kw = ~0ull;           // key-padding word of the compute cursor's tile
 
-    auto iteration = [&](int j) __attribute__((always_inline)) {
+    // jm = j mod NBUF as a compile-time constant: every LDS buffer address
+    // of the iteration is then a constant offset (no address arithmetic in
+    // the steps).
+    auto iteration = [&](int j, auto jm) __attribute__((always_inline)) {
+        constexpr int J = decltype(jm)::value;
         wait_loads_but<2 * LPW>();
         tile_barrier();
         const char* const v_base = v_pend;
@@ -626,8 +636,8 @@ __global__ __launch_bounds__(THREADS, 1) void ring_fwd_kernel(const StepArgs a) 
         const char* const k_base = k_addr(ck);
         const int k_kt = ck.kt;
         v_pend = v_addr(ck);
-        bf16* const v_dst = vbuf(j + 2);
-        bf16* const k_dst = kbuf(j + 3);
+        bf16* const v_dst = vbuf(J + 2);
+        bf16* const k_dst = kbuf(J + 3);
         const int kt = cc.kt;
         const bool full = kt >= cc_flo && kt <= cc_fhi && kt != ragged_kt;
         // with a key mask: tile j+1's word, its latency hidden behind step 2j
@@ -637,9 +647,9 @@ __global__ __launch_bounds__(THREADS, 1) void ring_fwd_kernel(const StepArgs a) 
             cur_next(cn);
             kw_next = key_word(cn);
         }
-        step(sA, pA, unit_of(kt, 0, full), sB, kbuf(j), 1, vbuf(j + 3), 1, pB, kbuf(j + 1), 0, vbuf(j), 0,
+        step(sA, pA, unit_of(kt, 0, full), sB, kbuf(J), 1, vbuf(J + 3), 1, pB, kbuf(J + 1), 0, vbuf(J), 0,
              (uint32_t)(kw >> 32), [&](int i) __attribute__((always_inline)) { issue_v1(v_dst, v_base, i); });
-        step(sB, pB, unit_of(kt, 1, full), sA, kbuf(j + 1), 0, vbuf(j), 0, pA, kbuf(j + 1), 1, vbuf(j), 1,
+        step(sB, pB, unit_of(kt, 1, full), sA, kbuf(J + 1), 0, vbuf(J), 0, pA, kbuf(J + 1), 1, vbuf(J), 1,
              (uint32_t)kw_next, [&](int i) __attribute__((always_inline)) { issue_k1(k_dst, k_base, k_kt, i); });
         kw = kw_next;
         if (j + 1 < nT) {  // the compute cursor moves on to tile j + 1
@@ -681,7 +691,23 @@ __global__ __launch_bounds__(THREADS, 1) void ring_fwd_kernel(const StepArgs a) 
     }
 #pragma unroll
     for (int n = 0; n < LA; n++) ring[n] = frag(kbuf(0), 1, vbuf(3), 1, n);
-    for (int j = 0; j < nT; j++) iteration(j);
+    // Whole groups of NBUF iterations, then the 0 to NBUF - 1 left over (j
+    // is a multiple of NBUF after the loop).
+    static_assert(NBUF == 4, "the unrolled tile loop below");
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+    int j = 0;
+    for (; j + NBUF <= nT; j += NBUF) {
+        iteration(j, I0{});
+        iteration(j + 1, I1{});
+        iteration(j + 2, I2{});
+        iteration(j + 3, I3{});
+    }
+    if (j < nT) iteration(j, I0{});
+    if (j + 1 < nT) iteration(j + 1, I1{});
+    if (j + 2 < nT) iteration(j + 2, I2{});
     // PV of the last unit (nT-1, 1) from V_{nT-1}; the ring holds its first
     // operands (the S slots' fragments are unused).
 #pragma unroll
