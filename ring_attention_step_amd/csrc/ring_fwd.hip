@@ -441,6 +441,29 @@ __global__ __launch_bounds__(THREADS, 1) void ring_fwd_kernel(const StepArgs a) 
     auto v_addr = [&](const Cursor& c) __attribute__((always_inline)) {
         return (const char*)v_all + tab64(1, c.e) * 2 + (int64_t)c.kt * (BK * 2);
     };
+    // The load cursor also carries the K and V^T addresses of its tile,
+    // stepped by one tile inside a block: it reads the chain table only when
+    // it enters a new block, not at every tile (a table read right after the
+    // tile barrier would stall both waves of the SIMD on its LDS latency).
+    struct LCursor {
+        Cursor c;
+        const char* kp;
+        const char* vp;
+    };
+    auto lc_next = [&](LCursor& l) __attribute__((always_inline)) {
+        if (l.c.kt < l.c.hi) {
+            l.c.kt++;
+            l.kp += k_tile_bytes;
+            l.vp += BK * 2;
+            return;
+        }
+        const int e_was = l.c.e;
+        cur_next(l.c);  // past the chain's end it stays on the last tile
+        if (l.c.e != e_was) {
+            l.kp = k_addr(l.c);
+            l.vp = v_addr(l.c);
+        }
+    };
     // Fragment wave * LPW + i of a K or V^T tile (load i of this wave).
     auto issue_k1 = [&](bf16* dst, const char* base, int kt, int i) __attribute__((always_inline)) {
         const int f = wave * LPW + i, kc = f % TL::KC;
@@ -616,9 +639,9 @@ __global__ __launch_bounds__(THREADS, 1) void ring_fwd_kernel(const StepArgs a) 
     // iterations earlier; during step 2j it loads V_{j+2} into the buffer of
     // V_{j-2}, during step 2j+1 K_{j+3} into that of K_{j-1}; past the chain's
     // end the last tile is re-read, so that every iteration issues one batch.
-    Cursor ck{-1, 0, -1};  // K load cursor
-    cur_next(ck);
-    Cursor cc = ck;        // compute cursor (tile j)
+    LCursor ck{Cursor{-1, 0, -1}, nullptr, nullptr};  // K load cursor
+    lc_next(ck);
+    Cursor cc = ck.c;      // compute cursor (tile j)
     int cc_flo = tab32(2, cc.e), cc_fhi = tab32(3, cc.e);
     row_bounds(tab64(2, cc.e));
     const char* v_pend = nullptr;  // V^T address of the tile the K cursor loaded last
@@ -632,10 +655,10 @@ __global__ __launch_bounds__(THREADS, 1) void ring_fwd_kernel(const StepArgs a) 
         wait_loads_but<2 * LPW>();
         tile_barrier();
         const char* const v_base = v_pend;
-        cur_next(ck);  // past the chain's end it stays on the last tile
-        const char* const k_base = k_addr(ck);
-        const int k_kt = ck.kt;
-        v_pend = v_addr(ck);
+        lc_next(ck);  // past the chain's end it stays on the last tile
+        const char* const k_base = ck.kp;
+        const int k_kt = ck.c.kt;
+        v_pend = ck.vp;
         bf16* const v_dst = vbuf(J + 2);
         bf16* const k_dst = kbuf(J + 3);
         const int kt = cc.kt;
@@ -669,15 +692,15 @@ __global__ __launch_bounds__(THREADS, 1) void ring_fwd_kernel(const StepArgs a) 
     // covers them too (vector-memory loads complete in issue order).
     // Batch A: K_0, V_0, K_1; batch B: K_2, V_1.  V buffer 3 stands for
     // V_{-1} (P_{-1} = 0 multiplies it): zeroed.
-    issue_k(kbuf(0), k_addr(ck), ck.kt);
-    issue_v(vbuf(0), v_addr(ck));
-    cur_next(ck);
-    issue_k(kbuf(1), k_addr(ck), ck.kt);
-    v_pend = v_addr(ck);
-    cur_next(ck);
-    issue_k(kbuf(2), k_addr(ck), ck.kt);
+    issue_k(kbuf(0), ck.kp, ck.c.kt);
+    issue_v(vbuf(0), ck.vp);
+    lc_next(ck);
+    issue_k(kbuf(1), ck.kp, ck.c.kt);
+    v_pend = ck.vp;
+    lc_next(ck);
+    issue_k(kbuf(2), ck.kp, ck.c.kt);
     issue_v(vbuf(1), v_pend);
-    v_pend = v_addr(ck);
+    v_pend = ck.vp;
     for (int i = threadIdx.x; i < TL::ELEMS / 8; i += THREADS) ((bf16x8*)vbuf(3))[i] = bf16x8{};
     wait_loads_but<2 * LPW>();  // batch A
     tile_barrier();
