@@ -626,19 +626,28 @@ static ra_status forward_impl(const ra_tensor* q, const ra_tensor* k, const ra_t
     };
     auto row_off = [&](int64_t blk, int64_t stride_tok) { return striped ? blk * stride_tok : blk * B * stride_tok; };
 
-    if (use_vt && launch_pack_vt(v->data, v->stride_tok, v->stride_head, N, B, striped, Hkv, d, ws.vt, st) !=
-                      hipSuccess)
-        return RA_E_HIP;
-
     // ---- bf16 without the side-stream prefetch: the whole ring in one launch ----
     // Each device's visited (non-skipped) blocks in ring order form its
     // chain; one workgroup per (device, head, q-tile) runs the chain with
     // the state in registers and finalises at its end.
-    bool ring_done = false;
+    std::vector<std::vector<int32_t>> chain;
+    size_t longest = 0;
     if (use_vt && !pf) {
-        std::vector<std::vector<int32_t>> chain((size_t)N);
+        chain.resize((size_t)N);
         for (int64_t s = 0; s < r.passes; s++)
             for (const StepPair& sp : plan.steps[s]) chain[sp.i].push_back(sp.j);
+        for (const auto& c : chain) longest = std::max(longest, c.size());
+    }
+    const bool one_launch =
+        use_vt && !pf && longest <= (size_t)kMaxRingChain && n_qtiles_ring * (Hq / hpi) * N <= INT32_MAX;
+    // V^T in matrix-fragment order for the one-launch kernel, in rows for
+    // the per-step kernel
+    if (use_vt && launch_pack_vt(v->data, v->stride_tok, v->stride_head, N, B, striped, Hkv, d, one_launch, ws.vt,
+                                 st) != hipSuccess)
+        return RA_E_HIP;
+
+    bool ring_done = false;
+    if (one_launch) {
         // Every block of a chain is resident, and the online-softmax merge
         // gives the same sum in any order, so the chain takes the device's
         // own block last: under a causal mask that block is the partly
@@ -654,9 +663,7 @@ static ra_status forward_impl(const ra_tensor* q, const ra_tensor* k, const ra_t
             else if (chain[i].size() > 1 && chain[i].front() == i)
                 std::rotate(chain[i].begin(), chain[i].begin() + 1, chain[i].end());
         }
-        size_t longest = 0;
-        for (const auto& c : chain) longest = std::max(longest, c.size());
-        if (longest <= (size_t)kMaxRingChain && n_qtiles_ring * (Hq / hpi) * N <= INT32_MAX) {
+        {
             std::vector<int32_t> order;
             for (int64_t i = 0; i < N; i++)
                 if (!chain[i].empty()) order.push_back((int32_t)i);

@@ -110,10 +110,14 @@ hipError_t launch_pack_key_bits(const uint8_t* key_valid, int64_t row_stride, in
 // Packed V^T of the ring blocks: vt[j][g][c][p] (p < Bp = B rounded up to the
 // key tile) holds V of key w of block j, kv head g, dim c, where p is w with
 // bits 2 and 3 swapped inside each 16-key group (the order in which the S^T
-// accumulators hold their keys); zero for w >= B.
+// accumulators hold their keys); zero for w >= B.  frag: the same values in
+// the one-launch ring kernel's fragment order (its LDS tile layout): in the
+// region of (j, g), tile kt of 64 keys at kt * 64 * d, fragment f at 512 f,
+// lane l's eight positions 16 (f / (d/32)) + 8 (l / 32) .. +7 of dim row
+// 32 (f % (d/32)) + l % 32 at 8 l.
 int64_t vt_padded_keys(int64_t B);
 hipError_t launch_pack_vt(const void* v, int64_t v_stride_tok, int64_t v_stride_head, int64_t N, int64_t B,
-                          int striped, int64_t Hkv, int64_t d, void* vt, hipStream_t stream);
+                          int striped, int64_t Hkv, int64_t d, bool frag, void* vt, hipStream_t stream);
 hipError_t launch_empty_rows(void* out, int out_kind, int64_t out_off, int64_t out_row_stride,
                              int64_t out_head_stride, float* lse, int64_t lse_off,
                              int64_t lse_row_stride, int64_t lse_head_stride, int64_t rows,

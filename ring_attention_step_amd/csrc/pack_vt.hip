@@ -7,6 +7,13 @@
 // group the keys are stored as 0-3, 8-11, 4-7, 12-15 -- the order in which a
 // lane half of the S^T accumulator holds them -- so each lane half's eight
 // keys of a 16-key chunk are contiguous.  Keys w >= B are zero.
+//
+// FRAG: the same values in the order of the one-launch ring kernel's LDS
+// tiles, so that each of its 1 KB tile loads reads 1 KB of contiguous memory
+// (with rows of V^T, a load gathers 32 B from each of 32 rows): the region of
+// (j, g) holds its 64-key tiles one after the other, tile kt as D / 8
+// fragments of 512 elements, fragment f = c16 * (D / 32) + db holding, for
+// lane l, positions 16 c16 + 8 (l / 32) .. +7 of dim row 32 db + l % 32.
 #include "kernels.h"
 
 namespace ra {
@@ -20,7 +27,7 @@ constexpr int KEYS = 64;  // keys per workgroup
 
 __device__ __forceinline__ int swap_bits_2_3(int p) { return (p & ~12) | ((p & 4) << 1) | ((p & 8) >> 1); }
 
-template <int D>
+template <int D, bool FRAG>
 __global__ __launch_bounds__(256) void pack_vt_kernel(const bf16* v, int64_t st_tok, int64_t st_head, int64_t N,
                                                       int64_t B, int striped, int64_t Bp, bf16* vt) {
     __shared__ unsigned short tile[KEYS][D + 8];  // +8: spread the column reads over banks
@@ -38,6 +45,20 @@ __global__ __launch_bounds__(256) void pack_vt_kernel(const bf16* v, int64_t st_
         *(u32x4*)&tile[key][col] = x;
     }
     __syncthreads();
+    if (FRAG) {
+        // 16 bytes per lane of a fragment, consecutive threads consecutive
+        // 16-byte pieces (Bp is a multiple of the 64-key tile)
+        bf16* out = vt + ((j * Hkv + g) * D) * Bp + w0 * D;
+        for (int c = threadIdx.x; c < D * KEYS / 8; c += 256) {
+            const int f = c / 64, l = c % 64;
+            const int dim = 32 * (f % (D / 32)) + l % 32, p0 = 16 * (f / (D / 32)) + 8 * (l / 32);
+            u16x8 x;
+#pragma unroll
+            for (int e = 0; e < 8; e++) x[e] = tile[swap_bits_2_3(p0 + e)][dim];
+            *(u16x8*)(out + 8 * c) = x;
+        }
+        return;
+    }
     // write D rows x 64 positions, 8 positions (16 bytes) per thread per step
     bf16* out = vt + ((j * Hkv + g) * D) * Bp;
     for (int c = threadIdx.x; c < D * KEYS / 8; c += 256) {
@@ -55,14 +76,21 @@ __global__ __launch_bounds__(256) void pack_vt_kernel(const bf16* v, int64_t st_
 int64_t vt_padded_keys(int64_t B) { return (B + kBf16TileK - 1) / kBf16TileK * kBf16TileK; }
 
 hipError_t launch_pack_vt(const void* v, int64_t st_tok, int64_t st_head, int64_t N, int64_t B, int striped,
-                          int64_t Hkv, int64_t d, void* vt, hipStream_t stream) {
+                          int64_t Hkv, int64_t d, bool frag, void* vt, hipStream_t stream) {
+    static_assert(KEYS == kBf16TileK, "one workgroup per key tile of the fragment order");
     const int64_t Bp = vt_padded_keys(B);
     if (Bp == 0 || Hkv == 0 || N == 0) return hipSuccess;
     const dim3 grid((unsigned)((Bp + KEYS - 1) / KEYS), (unsigned)Hkv, (unsigned)N);
-    if (d == 128)
-        pack_vt_kernel<128><<<grid, 256, 0, stream>>>((const bf16*)v, st_tok, st_head, N, B, striped, Bp, (bf16*)vt);
+    const bf16* vb = (const bf16*)v;
+    bf16* o = (bf16*)vt;
+    if (d == 128 && frag)
+        pack_vt_kernel<128, true><<<grid, 256, 0, stream>>>(vb, st_tok, st_head, N, B, striped, Bp, o);
+    else if (d == 128)
+        pack_vt_kernel<128, false><<<grid, 256, 0, stream>>>(vb, st_tok, st_head, N, B, striped, Bp, o);
+    else if (d == 64 && frag)
+        pack_vt_kernel<64, true><<<grid, 256, 0, stream>>>(vb, st_tok, st_head, N, B, striped, Bp, o);
     else if (d == 64)
-        pack_vt_kernel<64><<<grid, 256, 0, stream>>>((const bf16*)v, st_tok, st_head, N, B, striped, Bp, (bf16*)vt);
+        pack_vt_kernel<64, false><<<grid, 256, 0, stream>>>(vb, st_tok, st_head, N, B, striped, Bp, o);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();

@@ -421,25 +421,26 @@ __global__ __launch_bounds__(THREADS, 1) void ring_fwd_kernel(const StepArgs a) 
         if (kt <= hi) c = Cursor{e, kt, hi};
     };
     const uint32_t k_rs_bytes = (uint32_t)(a.k_row_stride * 2);
-    const uint32_t v_rs_bytes = (uint32_t)(a.vt_row_stride * 2);
     // Lane offsets of the fragment loads.  A wave's K fragments all lie in
     // one key half (kh = wave * LPW / (D/16)): the lane offset holds row
     // 32 kh + col of the tile, or, for a ragged last tile of a block, that
     // row clamped to the block's last row (rows past it are masked), and
     // chunk half of the fragment's 32 bytes; the uniform part goes to the
-    // base.  V^T fragments: dim row col of the fragment, chunk half.
+    // base.  V^T is packed in this fragment order (64-key tiles of D / 8
+    // fragments, lane l's 16 bytes at 16 l), so a V^T fragment load reads
+    // 1 KB of contiguous memory at 16 l.
     const int kh_w = wave * LPW / TL::KC;
     const int lr_ragged = (int)((a.Bk - 1) % BK);
     const uint32_t ld_k = (uint32_t)(32 * kh_w + col) * k_rs_bytes + 16u * (uint32_t)half;
     const uint32_t ld_k_rag =
         (uint32_t)(32 * kh_w + col < lr_ragged ? 32 * kh_w + col : lr_ragged) * k_rs_bytes + 16u * (uint32_t)half;
-    const uint32_t ld_v = (uint32_t)col * v_rs_bytes + 16u * (uint32_t)half;
+    const uint32_t ld_v = 16u * (uint32_t)lane;
     const int64_t k_tile_bytes = (int64_t)BK * a.k_row_stride * 2;
     auto k_addr = [&](const Cursor& c) __attribute__((always_inline)) {
         return (const char*)k_all + tab64(0, c.e) * 2 + (int64_t)c.kt * k_tile_bytes;
     };
     auto v_addr = [&](const Cursor& c) __attribute__((always_inline)) {
-        return (const char*)v_all + tab64(1, c.e) * 2 + (int64_t)c.kt * (BK * 2);
+        return (const char*)v_all + tab64(1, c.e) * 2 + (int64_t)c.kt * (TL::ELEMS * 2);
     };
     // The load cursor also carries the K and V^T addresses of its tile,
     // stepped by one tile inside a block: it reads the chain table only when
@@ -454,7 +455,7 @@ __global__ __launch_bounds__(THREADS, 1) void ring_fwd_kernel(const StepArgs a) 
         if (l.c.kt < l.c.hi) {
             l.c.kt++;
             l.kp += k_tile_bytes;
-            l.vp += BK * 2;
+            l.vp += TL::ELEMS * 2;
             return;
         }
         const int e_was = l.c.e;
@@ -470,8 +471,8 @@ __global__ __launch_bounds__(THREADS, 1) void ring_fwd_kernel(const StepArgs a) 
         dma_frag(lds_addr(dst) + 1024u * f, base + 32 * kc, kt == ragged_kt ? ld_k_rag : ld_k);
     };
     auto issue_v1 = [&](bf16* dst, const char* base, int i) __attribute__((always_inline)) {
-        const int f = wave * LPW + i, c = f / TL::DB, db = f % TL::DB;
-        dma_frag(lds_addr(dst) + 1024u * f, base + (int64_t)(32 * db) * v_rs_bytes + 32 * c, ld_v);
+        const int f = wave * LPW + i;
+        dma_frag(lds_addr(dst) + 1024u * f, base + 1024 * f, ld_v);
     };
     auto issue_k = [&](bf16* dst, const char* base, int kt) __attribute__((always_inline)) {
 #pragma unroll
