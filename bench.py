@@ -47,7 +47,7 @@ STEP_KERNEL = "step_bf16_kernel<__bf16, 128, true, true, false>"
 # The kernels' sources plus the driver that sets their launch order (a
 # traffic record is only valid for the code and the order it was taken with).
 KERNEL_SOURCES = ["ring_attention_step_amd/csrc/ring_fwd.hip", "ring_attention_step_amd/csrc/step_bf16.hip",
-                  "ring_attention_step_amd/csrc/plan.h",
+                  "ring_attention_step_amd/csrc/pack_vt.hip", "ring_attention_step_amd/csrc/plan.h",
                   "ring_attention_step_amd/csrc/kernels.h", "ring_attention_step_amd/csrc/api.hip"]
 BWD_KERNEL_SOURCES = ["ring_attention_step_amd/csrc/backward.hip", "ring_attention_step_amd/csrc/bwd_kernels.h",
                       "ring_attention_step_amd/csrc/plan.h",
