@@ -483,12 +483,16 @@ __global__ __launch_bounds__(THREADS, 1) void ring_fwd_kernel(const StepArgs a) 
         for (int i = 0; i < LPW; i++) issue_v1(dst, base, i);
     };
 
-    // Key-padding mask: the validity word of a tile (bit w: key row w is
-    // real; all ones without a mask), a scalar load.
-    auto key_word = [&](const Cursor& c) __attribute__((always_inline)) -> uint64_t {
+    // Key-padding mask: the validity word of tile kt of the block whose
+    // words start at kb (bit w: key row w is real; all ones without a
+    // mask), a scalar load.
+    auto key_word_at = [&](int kb, int kt) __attribute__((always_inline)) -> uint64_t {
         if (!KP) return ~0ull;
         typedef const __attribute__((address_space(4))) uint64_t* cwp;
-        return *(cwp)(a.kbits + tab32(4, c.e) + 2 * c.kt);
+        return *(cwp)(a.kbits + kb + 2 * kt);
+    };
+    auto key_word = [&](const Cursor& c) __attribute__((always_inline)) -> uint64_t {
+        return KP ? key_word_at(tab32(4, c.e), c.kt) : ~0ull;
     };
     // With a key-padding mask, S^T of a unit starts from one extra 16-deep
     // product whose A operand holds, for key row r (lane r, k = 0), 0 if the
@@ -644,6 +648,7 @@ __global__ __launch_bounds__(THREADS, 1) void ring_fwd_kernel(const StepArgs a) 
     lc_next(ck);
     Cursor cc = ck.c;      // compute cursor (tile j)
     int cc_flo = tab32(2, cc.e), cc_fhi = tab32(3, cc.e);
+    int cc_kb = KP ? tab32(4, cc.e) : 0;  // key-padding words of the compute cursor's block
     row_bounds(tab64(2, cc.e));
     const char* v_pend = nullptr;  // V^T address of the tile the K cursor loaded last
     uint64_t kw = ~0ull;           // key-padding word of the compute cursor's tile
@@ -665,11 +670,16 @@ __global__ __launch_bounds__(THREADS, 1) void ring_fwd_kernel(const StepArgs a) 
         const int kt = cc.kt;
         const bool full = kt >= cc_flo && kt <= cc_fhi && kt != ragged_kt;
         // with a key mask: tile j+1's word, its latency hidden behind step 2j
+        // (the chain table is read only when tile j+1 opens a new block)
         uint64_t kw_next = ~0ull;
         if (KP && j + 1 < nT) {
-            Cursor cn = cc;
-            cur_next(cn);
-            kw_next = key_word(cn);
+            if (cc.kt < cc.hi) {
+                kw_next = key_word_at(cc_kb, cc.kt + 1);
+            } else {
+                Cursor cn = cc;
+                cur_next(cn);
+                kw_next = key_word(cn);
+            }
         }
         step(sA, pA, unit_of(kt, 0, full), sB, kbuf(J), 1, vbuf(J + 3), 1, pB, kbuf(J + 1), 0, vbuf(J), 0,
              (uint32_t)(kw >> 32), [&](int i) __attribute__((always_inline)) { issue_v1(v_dst, v_base, i); });
@@ -682,6 +692,7 @@ __global__ __launch_bounds__(THREADS, 1) void ring_fwd_kernel(const StepArgs a) 
             if (cc.e != e_was) {
                 cc_flo = tab32(2, cc.e);
                 cc_fhi = tab32(3, cc.e);
+                if (KP) cc_kb = tab32(4, cc.e);
                 row_bounds(tab64(2, cc.e));
             }
         }
